@@ -1,0 +1,67 @@
+"""ctypes front end of ``recursive.c`` (TEST INFRASTRUCTURE ONLY).
+
+Sequential float64 BaKron-recursive (quadtree divide and conquer with naive
+leaves), for shapes too large for the numpy forms in ``reference``.  See the
+header of ``recursive.c`` for the algorithm and the pages it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "recursive.c")
+_LIB = os.path.join(_HERE, "liboracle_recursive.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile recursive.c with gcc (float64, OpenMP, no FMA contraction)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-march=x86-64-v2", "-fopenmp", "-ffp-contract=off",
+                               "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB)
+        f = lib.oracle_bakron_recursive
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 6 + \
+                     [ctypes.c_int64] + [ctypes.c_void_p] * 3
+        _lib = lib
+    return _lib
+
+
+def bakron_recursive(W, PA, PB, s, z, maxq, leaf: int = 32, threads: int | None = None):
+    """Returns (codes int32, V float64, E float64), all m x n."""
+    lib = _load()
+    W = np.ascontiguousarray(W, dtype=np.float64)
+    PA = np.ascontiguousarray(PA, dtype=np.float64)
+    PB = np.ascontiguousarray(PB, dtype=np.float64)
+    s = np.ascontiguousarray(s, dtype=np.float32)
+    z = np.ascontiguousarray(z, dtype=np.float32)
+    maxq = np.ascontiguousarray(maxq, dtype=np.int32)
+    m, n = W.shape
+    if PA.shape != (n, n) or PB.shape != (m, m) or s.shape != (m,) or z.shape != (m,) or maxq.shape != (m,):
+        raise ValueError("shape mismatch")
+    codes = np.zeros((m, n), dtype=np.int32)
+    V = np.zeros((m, n))
+    E = np.zeros((m, n))
+    if threads is not None:
+        os.environ["OMP_NUM_THREADS"] = str(int(threads))
+    rc = lib.oracle_bakron_recursive(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
+                                     s.ctypes.data, z.ctypes.data, maxq.ctypes.data, int(leaf),
+                                     codes.ctypes.data, V.ctypes.data, E.ctypes.data)
+    if rc != 0:
+        raise RuntimeError("oracle_bakron_recursive failed with %d" % rc)
+    return codes, V, E

@@ -1,0 +1,310 @@
+"""Float64 reference forms of the BaKron solve (TEST INFRASTRUCTURE ONLY).
+
+Only tests, the smoke check and the bench CPU baseline may use this module.
+
+Notation (from [S], setup paragraph and Corollary 3.4): W is m x n, row i is
+an output coordinate and column j an input coordinate.  The Hessian of the
+layer loss is approximated by A (x) B with A (n x n) on the input side and
+B (m x m) on the output side, so that for Delta = V - W the loss proxy is
+vec(Delta)^T (A (x) B) vec(Delta) = ||B^(1/2) Delta A^(1/2)||_F^2 with the
+column-major vec.  GPTQ is the special case B = I ([S] setup; [N5]).
+
+Readings taken where the pages are silent (each is listed in the design doc):
+
+* Damping: A_d = A + frac * mean(diag A) * I, frac = 0.01, and the same for
+  B.  The pages do not mention damping; this is the usual GPTQ convention.
+* RevCholesky(A) ([S] Corollary 3.4) is the lower-triangular L with
+  A = L^T L.  It is the only reading under which ||L(B)(V-W)L(A)^T||_F^2
+  equals the A (x) B loss.
+* Processing order: GPTQ on vec(W) in column-major order ([S], BaKron-naive),
+  equivalently any order that visits (i, j) after every (i', j') with
+  i' <= i and j' <= j ([S], BaKron-antidiagonal: an entry's update only
+  reaches entries below and to the right of it; Theorem 3.2).
+* The base quantizer is modular ([A]); here it is a uniform grid per output
+  row: x = w/s_i + z_i, code c = clamp(rint(x), 0, maxq_i) with
+  round-half-to-even, value v = s_i (c - z_i).  The rounding decision is
+  taken in float32 (x formed as float32(float32(w) / s) + z in float32), the
+  precision of the kernels, so that both sides decide in the same
+  precision.  Everything else here is float64.
+* A clipped entry keeps its full error (GPTQ convention).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "damp", "rev_cholesky", "normalized_inverse", "factor", "quantize",
+    "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform",
+    "objective", "objective_from_errors", "implied_errors", "validate",
+    "order_colmajor", "order_rowmajor", "order_antidiagonal",
+]
+
+_f32 = np.float32
+
+
+# ---------------------------------------------------------------- factor step
+
+def damp(A: np.ndarray, frac: float = 0.01) -> np.ndarray:
+    """A + frac * mean(diag(A)) * I in float64 (damping reading, see header)."""
+    A = np.asarray(A, dtype=np.float64)
+    A = 0.5 * (A + A.T)
+    return A + frac * np.mean(np.diag(A)) * np.eye(A.shape[0])
+
+
+def rev_cholesky(Ad: np.ndarray) -> np.ndarray:
+    """RevCholesky ([S] Corollary 3.4): lower L with Ad = L^T L.
+
+    Written as the flip of the textbook Cholesky: with J the exchange matrix,
+    J Ad J = C C^T (C lower); then L = J C^T J is lower triangular and
+    L^T L = J C C^T J = Ad.
+    Raises numpy.linalg.LinAlgError when Ad is not positive definite.
+    """
+    Ad = np.asarray(Ad, dtype=np.float64)
+    C = np.linalg.cholesky(Ad[::-1, ::-1])
+    return np.ascontiguousarray(C.T[::-1, ::-1])
+
+
+def normalized_inverse(L: np.ndarray) -> np.ndarray:
+    """P = L^-1 diag(L): unit lower triangular.
+
+    Derived from [S] (GPTQ on vec(W) with Hessian A (x) B): with Ad = L^T L,
+    the upper Cholesky factor of Ad^-1 is L^-T, so GPTQ's normalised update
+    row for index j is column j of L^-1 scaled by L_jj, i.e. column j of P.
+    """
+    L = np.asarray(L, dtype=np.float64)
+    n = L.shape[0]
+    Li = np.linalg.solve(L, np.eye(n))        # library triangular-capable solve
+    Li = np.tril(Li)
+    return Li * np.diag(L)[None, :]
+
+
+def factor(A: np.ndarray, frac: float = 0.01) -> dict:
+    """Damping, RevCholesky and the normalised inverse of one Kronecker factor."""
+    Ad = damp(A, frac)
+    L = rev_cholesky(Ad)
+    return {"Ad": Ad, "L": L, "P": normalized_inverse(L)}
+
+
+# ------------------------------------------------------------ base quantizer
+
+def quantize(w, s, z, maxq):
+    """Uniform grid of one output row: returns (code, value).
+
+    The decision x = w/s + z is formed in float32 (the kernels' precision);
+    the value s (c - z) is returned in float64.  Works elementwise on arrays.
+    """
+    x = (np.asarray(w, dtype=np.float64).astype(_f32) / np.asarray(s, dtype=_f32)).astype(_f32) \
+        + np.asarray(z, dtype=_f32)
+    x = np.asarray(x, dtype=_f32)
+    c = np.minimum(np.maximum(np.rint(x), _f32(0)), np.asarray(maxq).astype(_f32))
+    c = c.astype(np.float64)
+    v = np.asarray(s, dtype=np.float64) * (c - np.asarray(z, dtype=np.float64))
+    return c, v
+
+
+def _values(codes, s, z):
+    return np.asarray(s, np.float64)[:, None] * (np.asarray(codes, np.float64) - np.asarray(z, np.float64)[:, None])
+
+
+# --------------------------------------------------- O1a: brute force on vec(W)
+
+def gptq_vectorized(W, Ad, Bd, s, z, maxq):
+    """GPTQ run directly on vec(W) with the explicit Hessian H = Ad (x) Bd.
+
+    This is the definition BaKron-naive starts from ([S], derivation: GPTQ in
+    the vectorised domain with Hessian A (x) B).  Column-major vec: index
+    p = j*m + i, and numpy.kron(Ad, Bd)[(j,i),(j',i')] = Ad[j,j'] Bd[i,i'].
+    GPTQ step (textbook): with H^-1 = U^T U (U upper), quantize w_p, then
+    w_q -= (w_p - v_p) / U_pp * U_pq for q > p.  Only for m*n <= 4096.
+    Returns (codes, V) as m x n arrays.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    if m * n > 4096:
+        raise ValueError("brute force is limited to m*n <= 4096")
+    H = np.kron(np.asarray(Ad, np.float64), np.asarray(Bd, np.float64))
+    Hinv = np.linalg.inv(H)
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    U = np.linalg.cholesky(Hinv).T            # upper, Hinv = U^T U
+    w = W.flatten(order="F").copy()
+    codes = np.zeros(m * n)
+    vals = np.zeros(m * n)
+    for p in range(m * n):
+        i = p % m
+        c, v = quantize(w[p], s[i], z[i], maxq[i])
+        codes[p], vals[p] = c, v
+        err = (w[p] - v) / U[p, p]
+        w[p:] -= err * U[p, p:]
+    return codes.reshape((m, n), order="F"), vals.reshape((m, n), order="F")
+
+
+# ------------------------------------------------ O1b: BaKron-naive, any order
+
+def order_colmajor(m, n):
+    return [(i, j) for j in range(n) for i in range(m)]
+
+
+def order_rowmajor(m, n):
+    return [(i, j) for i in range(m) for j in range(n)]
+
+
+def order_antidiagonal(m, n):
+    return [(i, k - i) for k in range(m + n - 1) for i in range(max(0, k - n + 1), min(m - 1, k) + 1)]
+
+
+def bakron_naive(W, PA, PB, s, z, maxq, order=None):
+    """BaKron-naive in the matrix domain ([S], derivation, first variant).
+
+    One entry at a time; after quantizing (i, j) with raw error e, every entry
+    to its bottom-right receives W~[i', j'] -= e * PB[i', i] * PA[j', j]
+    (Proposition 3.1 turns the vec-domain rank-1 GPTQ update into this outer
+    product).  ``order`` is any linear extension of the bottom-right partial
+    order (Theorem 3.2); default column-major.
+    Returns (codes, V, E) with E the raw errors w~ - v.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    PA = np.asarray(PA, np.float64)
+    PB = np.asarray(PB, np.float64)
+    Wt = W.copy()
+    C = np.zeros((m, n))
+    V = np.zeros((m, n))
+    E = np.zeros((m, n))
+    for (i, j) in (order if order is not None else order_colmajor(m, n)):
+        c, v = quantize(Wt[i, j], s[i], z[i], maxq[i])
+        e = Wt[i, j] - v
+        C[i, j], V[i, j], E[i, j] = c, v, e
+        Wt[i:, j:] -= e * np.outer(PB[i:, i], PA[j:, j])
+    return C, V, E
+
+
+# ------------------------------------------------ O1c: BaKron-antidiagonal
+
+def bakron_antidiagonal(W, PA, PB, s, z, maxq):
+    """BaKron-antidiagonal ([S], derivation, second variant).
+
+    All entries with i + j = k are quantized together (they do not update one
+    another), then their errors are pushed to the rest of the matrix at once:
+    W~ -= PB E_k PA^T, where E_k holds the raw errors of anti-diagonal k.
+    Because PB and PA are lower triangular this only touches entries below
+    and to the right of each source; the self term leaves w~_ij = v_ij.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    PA = np.asarray(PA, np.float64)
+    PB = np.asarray(PB, np.float64)
+    Wt = W.copy()
+    C = np.zeros((m, n))
+    V = np.zeros((m, n))
+    E = np.zeros((m, n))
+    for k in range(m + n - 1):
+        ii = np.arange(max(0, k - n + 1), min(m - 1, k) + 1)
+        jj = k - ii
+        c, v = quantize(Wt[ii, jj], np.asarray(s)[ii], np.asarray(z)[ii], np.asarray(maxq)[ii])
+        e = Wt[ii, jj] - v
+        C[ii, jj], V[ii, jj], E[ii, jj] = c, v, e
+        Ek = np.zeros((m, n))
+        Ek[ii, jj] = e
+        Wt -= PB @ Ek @ PA.T
+    return C, V, E
+
+
+# ------------------------------------------------ O1d: inverse-free L-form
+
+def bakron_lform(W, LA, LB, s, z, maxq, order=None):
+    """The same rounding written with L(A), L(B) only (no inverse).
+
+    From W - V = PB E PA^T and PB^-1 = diag(LB)^-1 LB (likewise for A), the
+    value an entry is rounded from is
+      w~_ij = W_ij + sum over strict predecessors (i', j') of
+              LB[i, i'] LA[j, j'] (W - V)_{i'j'} / (LB_ii LA_jj),
+    i.e. a nearest-plane recursion in the L(B) (x) L(A) lattice basis
+    ([S] Corollary 3.4 uses the same factors).  ``order`` as in bakron_naive.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    LA = np.asarray(LA, np.float64)
+    LB = np.asarray(LB, np.float64)
+    D = np.zeros((m, n))          # (W - V) on processed entries, 0 elsewhere
+    C = np.zeros((m, n))
+    V = np.zeros((m, n))
+    E = np.zeros((m, n))
+    for (i, j) in (order if order is not None else order_colmajor(m, n)):
+        acc = LB[i, : i + 1] @ D[: i + 1, : j + 1] @ LA[j, : j + 1]
+        wt = W[i, j] + acc / (LB[i, i] * LA[j, j])
+        c, v = quantize(wt, s[i], z[i], maxq[i])
+        C[i, j], V[i, j], E[i, j] = c, v, wt - v
+        D[i, j] = W[i, j] - v
+    return C, V, E
+
+
+# ----------------------------------------------------------------- objective
+
+def objective(W, V, LA, LB) -> float:
+    """||L(B) (V - W) L(A)^T||_F^2 ([S] Corollary 3.4), in float64."""
+    D = np.asarray(V, np.float64) - np.asarray(W, np.float64)
+    M = np.asarray(LB, np.float64) @ D @ np.asarray(LA, np.float64).T
+    return float(np.sum(M * M))
+
+
+def objective_from_errors(E, LA, LB) -> float:
+    """sum_ij (LB_ii LA_jj e_ij)^2; equals ``objective`` because
+    L(B)(W - V)L(A)^T = diag(LB) E diag(LA) (derived from W - V = PB E PA^T)."""
+    M = np.diag(np.asarray(LB, np.float64))[:, None] * np.asarray(E, np.float64) \
+        * np.diag(np.asarray(LA, np.float64))[None, :]
+    return float(np.sum(M * M))
+
+
+def implied_errors(W, V, LA, LB) -> np.ndarray:
+    """The raw errors E that any run producing V must have had.
+
+    Inverts W - V = PB E PA^T: E = diag(LB)^-1 LB (W - V) LA^T diag(LA)^-1.
+    """
+    D = np.asarray(W, np.float64) - np.asarray(V, np.float64)
+    M = np.asarray(LB, np.float64) @ D @ np.asarray(LA, np.float64).T
+    return M / (np.diag(LB)[:, None] * np.diag(LA)[None, :])
+
+
+# ----------------------------------------------------------------- validator
+
+def validate(W, codes, s, z, maxq, LA, LB, tau=1e-4) -> dict:
+    """Check that ``codes`` is a BaKron output for (W, A (x) B, grid), any size.
+
+    For a sequence of rounding decisions, the value entry (i, j) is rounded
+    from is w~_ij = v_ij + e_ij with E = ``implied_errors`` (it depends only
+    on decisions that precede (i, j)).  A valid output has, at every entry,
+    code == clamp(rint(w~/s + z)).  Near a rounding boundary float32 and
+    float64 may legitimately disagree (Theorem 3.2's equality is exact only
+    in exact arithmetic), so a mismatch is a "tie" when x lies within
+    ``tau`` grid steps of the boundary and the codes are adjacent.
+
+    Returns counts: entries, mismatches, ties (allowed), bad (outside the
+    tie band or more than one step apart), max_step, min_margin.
+    """
+    W = np.asarray(W, np.float64)
+    m, n = W.shape
+    codes = np.asarray(codes, np.float64)
+    V = _values(codes, s, z)
+    E = implied_errors(W, V, LA, LB)
+    Wt = V + E
+    ss = np.broadcast_to(np.asarray(s)[:, None], (m, n))
+    zz = np.broadcast_to(np.asarray(z)[:, None], (m, n))
+    mq = np.broadcast_to(np.asarray(maxq)[:, None], (m, n))
+    cexp, _ = quantize(Wt, ss, zz, mq)
+    x = (Wt.astype(_f32) / ss.astype(_f32)).astype(_f32) + zz.astype(_f32)
+    x = x.astype(np.float64)
+    bnd = np.clip(np.floor(x) + 0.5, 0.5, mq - 0.5)
+    margin = np.abs(x - bnd)
+    diff = codes - cexp
+    mism = diff != 0
+    ties = mism & (margin < tau) & (np.abs(diff) == 1)
+    bad = mism & ~ties
+    return {
+        "entries": int(m * n),
+        "mismatches": int(mism.sum()),
+        "ties": int(ties.sum()),
+        "bad": int(bad.sum()),
+        "max_step": int(np.abs(diff).max()) if m * n else 0,
+        "min_margin": float(margin.min()) if m * n else float("inf"),
+        "bad_index": [tuple(map(int, t)) for t in np.argwhere(bad)[:8]],
+    }
