@@ -1,0 +1,206 @@
+#!/usr/bin/env python
+"""Benchmark of the BaKron hot path on one MI355X.
+
+One step = the whole hot path on one synthetic layer, inputs already in HBM:
+bakron_factor(A) + bakron_factor(B) (damping, reverse Cholesky, normalised
+inverse) + bakron_solve (leaf sweeps, error propagation, objective).
+Default workload: the 8192 x 8192 layer (mixed 2/3-bit grids, 2.80 bits per
+weight, log-normal channel scales, 8192 samples per factor).
+
+Prints ONE JSON line.  `value` is seconds per step (time-like: lower is
+better).  `roofline` describes the kernel with the largest share of the
+step, timed with HIP events around each of its launches (the *_profiled
+entry points, on the stream the kernels run on) in a separate pass over the
+same inputs.  `cpu_baseline` is the float64 oracle (C, OpenMP) on a bounded
+leading block of the same workload, scaled by the cubic work ratio.
+
+Only --gpus 1 is supported: the solve of one matrix runs on one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
+PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
+PAGES_8192_SECONDS = 1.839        # the pages' BaKron time at 8192 x 8192 (another GPU): context
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="sq8192_mixed")
+    ap.add_argument("--cpu-sample", type=int, default=3072,
+                    help="edge of the leading block the oracle baseline solves (0 = skip)")
+    ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel roofline pass")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: only --gpus 1 is supported; the BaKron solve of one matrix runs on one GPU "
+              "(layers are independent, so more GPUs would take more layers, not split one).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import two_sided_hessian_amd as B
+    import workloads as WL
+
+    spec = WL.by_name(args.config)
+    m, n = spec.m, spec.n
+    t0 = time.time()
+    d = WL.generate(spec)
+    log(f"[bench] generated {spec.name} {m}x{n} in {time.time() - t0:.1f}s")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = {k: torch.from_numpy(np.ascontiguousarray(d[k])).to(dev) for k in ("W", "A", "B", "scale", "zero", "maxq")}
+    fa = (torch.empty((n, n), device=dev), torch.empty((n, n), device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
+    fb = (torch.empty((m, m), device=dev), torch.empty((m, m), device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
+    ws_fa = B._binding.workspace(B.factor_workspace_bytes(n), dev)
+    ws_fb = B._binding.workspace(B.factor_workspace_bytes(m), dev)
+    ws_s = B._binding.workspace(B.solve_workspace_bytes(m, n), dev)
+    out = {"V": torch.empty((m, n), device=dev), "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
+           "objective": torch.empty(1, dtype=torch.float64, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None, profile=None):
+        B.factor(T["A"], 0.01, out=fa, ws=ws_fa, stream=stream, profile=profile)
+        B.factor(T["B"], 0.01, out=fb, ws=ws_fb, stream=stream, profile=profile)
+        if ev is not None:
+            ev.record(stream)
+        B.solve(T["W"], fa[0], fa[1], fb[0], fb[1], T["scale"], T["zero"], T["maxq"], out=out, ws=ws_s,
+                stream=stream, profile=profile)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done")
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    starts[0].record(stream)
+    for k in range(args.steps):
+        step(mids[k])
+        starts[k + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    step_ms = [starts[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
+    factor_ms = [starts[k].elapsed_time(mids[k]) for k in range(args.steps)]
+    solve_ms = [mids[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
+    ms_per_step = float(np.mean(step_ms))
+    info = (int(fa[2].item()), int(fb[2].item()))
+    obj = float(out["objective"].item())
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (factor {np.mean(factor_ms):.3f} ms, "
+        f"solve {np.mean(solve_ms):.3f} ms), wall {wall:.3f}s, info {info}, objective {obj:.6e}")
+    if info != (0, 0):
+        raise SystemExit(f"factor reported a non-positive pivot: {info}")
+
+    alg_solve = float(m) * n * (m + n)
+    alg_factor = 2.0 * (float(m) ** 3 + float(n) ** 3) / 3.0
+    solve_s = float(np.median(solve_ms)) / 1e3
+
+    roofline = None
+    kernels = None
+    if not args.no_profile:
+        prof = []
+        step(profile=prof)
+        torch.cuda.synchronize()
+        agg = {}
+        for r in prof:
+            a = agg.setdefault(r["name"], {"launches": 0, "total_ms": 0.0, "alg_flops": 0.0, "alg_bytes": 0.0})
+            for k in ("launches", "total_ms", "alg_flops", "alg_bytes"):
+                a[k] += r[k]
+        kernels = {k: {"launches": v["launches"], "total_ms": round(v["total_ms"], 4),
+                       "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3),
+                       "alg_tflops": round(v["alg_flops"] / (v["total_ms"] * 1e-3) / 1e12, 3) if v["total_ms"] > 0 else None,
+                       "alg_gbs": round(v["alg_bytes"] / (v["total_ms"] * 1e-3) / 1e9, 1) if v["total_ms"] > 0 else None}
+                   for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"])}
+        dom = max(agg.items(), key=lambda kv: kv[1]["total_ms"])
+        name, v = dom
+        mfma = name in ("k_prop_rows", "k_prop_cols", "k_f_panel", "k_f_syrk", "k_f_right", "k_f_left")
+        secs = v["total_ms"] * 1e-3
+        if mfma:
+            ach = v["alg_flops"] / secs / 1e12
+            roofline = {"kernel": name, "bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+                        "launches": v["launches"], "avg_launch_us": round(1e6 * secs / v["launches"], 3)}
+        else:
+            ach = v["alg_bytes"] / secs / 1e9
+            roofline = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                        "launches": v["launches"], "avg_launch_us": round(1e6 * secs / v["launches"], 3)}
+        log(f"[bench] kernels: {json.dumps(kernels)}")
+
+    cpu = None
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(d, args.cpu_sample, m, n)
+
+    res = {
+        "metric": "seconds per m×n BaKron solve (8192×8192 fp32) + achieved fp32 MFMA TFLOP/s",
+        "value": round(ms_per_step / 1e3, 6),
+        "unit": "s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round((ms_per_step / 1e3) / PAGES_8192_SECONDS, 6) if (m, n) == (8192, 8192) else None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "m": m, "n": n, "samples": spec.samples,
+                   "bits": "mixed 2/3 (2.80 bpw)" if spec.mixed_low_rows else spec.bits,
+                   "damping": 0.01, "step": "factor(A) + factor(B) + solve"},
+        "solve_s": round(solve_s, 6),
+        "factor_s": round(float(np.median(factor_ms)) / 1e3, 6),
+        "solve_alg_tflops": round(alg_solve / solve_s / 1e12, 3),
+        "solve_alg_frac": round(alg_solve / solve_s / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+        "factor_alg_tflops": round(alg_factor / (float(np.median(factor_ms)) / 1e3) / 1e12, 3),
+        "objective": obj,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(d, sample, m, n):
+    """The float64 oracle, timed on the host cores, on the leading
+    sample x sample block of the same layer (same grid rows, the leading
+    blocks of A and B), scaled to the full layer by the work ratio
+    mn(m+n) / (ms ns (ms+ns))."""
+    from oracle import recursive as O2
+    from oracle import reference as R
+    ms, ns = min(m, sample), min(n, sample)
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(cores))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    W = d["W"][:ms, :ns]
+    t0 = time.perf_counter()
+    fa, fb = R.factor(d["A"][:ns, :ns]), R.factor(d["B"][:ms, :ms])
+    O2.bakron_recursive(W, fa["P"], fb["P"], d["scale"][:ms], d["zero"][:ms], d["maxq"][:ms])
+    t = time.perf_counter() - t0
+    scale = (float(m) * n * (m + n)) / (float(ms) * ns * (ms + ns))
+    log(f"[bench] cpu oracle on {ms}x{ns}: {t:.2f}s with {threads} threads (x{scale:.1f} to full size)")
+    return {"value": round(t * scale, 3), "unit": "s", "cores": threads, "kind": "oracle",
+            "sample": f"leading {ms}x{ns} block of the same layer (factor + recursive solve, float64), "
+                      f"{t:.2f}s measured, scaled by the cubic work ratio {scale:.2f}"}
+
+
+if __name__ == "__main__":
+    main()

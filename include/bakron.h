@@ -1,0 +1,194 @@
+/*
+ * bakron.h -- C ABI of libbakron.so, the BaKron solver for MI355X (gfx950).
+ *
+ * BaKron rounds a weight matrix W (m x n) onto a per-output-row uniform grid
+ * by GPTQ-style adaptive rounding under a two-sided Kronecker-factored
+ * Hessian A (x) B: A (n x n) describes the input side, B (m x m) the output
+ * side.  Pages cited by title:
+ *   [S] paper summary "FastKron: Efficient Quantization with
+ *       Kronecker-Factored Hessians" (arXiv 2608.06291): setup, derivation
+ *       naive -> antidiagonal -> BaKron, Proposition 3.1, Theorem 3.2,
+ *       Corollary 3.4;
+ *   [A] paper page "BaKron: Efficient Quantization with Kronecker-Factored
+ *       Hessians": abstract (O(m+n) sequential steps, O(mn(m+n)) work,
+ *       modular base quantizer).
+ *
+ * Conventions for every entry point:
+ *   - Matrices are dense, row-major, float32, leading dimension = number of
+ *     columns.  Row i of W is output coordinate i, column j input
+ *     coordinate j.
+ *   - Every pointer is a DEVICE pointer (hipMalloc'd or equivalent), owned by
+ *     the caller.  The library never allocates device memory, never frees
+ *     caller memory and never synchronises: all work is enqueued on `stream`
+ *     in order and the call returns as soon as it is enqueued.
+ *   - Scratch memory is the caller's `workspace` (device, >= 256-byte
+ *     aligned, at least the size the matching *_workspace_bytes call
+ *     returns).  Its contents are undefined after a call.  Two calls that
+ *     share a workspace must be ordered (same stream or synchronised).
+ *   - Return value: BAKRON_SUCCESS (0) when the work was enqueued, or a
+ *     negative BAKRON_ERR_* code for an argument error detected on the
+ *     host, in which case nothing was enqueued.  Numerical failures found on
+ *     the device are reported through `info` (bakron_factor).
+ *   - Inputs are const and are not modified.  Inputs and outputs must not
+ *     overlap.
+ */
+#ifndef BAKRON_H
+#define BAKRON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BAKRON_SUCCESS 0
+#define BAKRON_ERR_NULL_POINTER (-1) /* a required pointer is NULL */
+#define BAKRON_ERR_BAD_SIZE (-2)     /* m or n negative or above BAKRON_MAX_DIM */
+#define BAKRON_ERR_WORKSPACE (-3)    /* workspace NULL, too small or not 256-byte aligned */
+#define BAKRON_ERR_BAD_ARG (-4)      /* damp_frac out of range, or a matrix pointer that
+                                        must be 16-byte aligned is not */
+#define BAKRON_ERR_HIP (-5)          /* a HIP launch call failed */
+
+/* Largest supported m or n. */
+#define BAKRON_MAX_DIM 65536
+
+/* Version of this ABI (major * 10000 + minor * 100 + patch). */
+int bakron_version(void);
+
+/* Human-readable text for a return code (static storage, never NULL). */
+const char* bakron_strerror(int code);
+
+/*
+ * Workspace bytes that bakron_factor needs for an n x n factor
+ * (0 when n == 0).  Deterministic; does not touch the device.
+ */
+size_t bakron_factor_workspace_bytes(int64_t n);
+
+/*
+ * bakron_factor -- damping, reverse Cholesky and normalised inverse of one
+ * Kronecker factor ([S] Corollary 3.4: L = RevCholesky(A)).
+ *
+ *   A_d = A + damp_frac * mean(diag A) * I           (damping; not on the pages,
+ *                                                     GPTQ's usual 1% convention)
+ *   L   lower triangular with A_d = L^T L           (RevCholesky)
+ *   P   = L^-1 diag(L), unit lower triangular        (GPTQ's normalised inverse
+ *                                                     rows for the factor)
+ *
+ * A      [in]  n x n, symmetric; only the lower triangle and the diagonal are
+ *              read.  Not modified.
+ * n      [in]  0 <= n <= BAKRON_MAX_DIM.  n == 0 enqueues nothing.
+ * damp_frac [in] finite, >= 0 (use 0.01 for 1% damping).
+ * L      [out] n x n; zeros above the diagonal.  16-byte aligned.
+ * P      [out] n x n; ones on the diagonal, zeros above it.  16-byte aligned.
+ * info   [out] one device int32: 0 on success, or k + 1 when the pivot of
+ *              row k (0-based; rows are eliminated from the last upward) is
+ *              not positive (A_d not positive definite or not finite), as in
+ *              LAPACK.  Written on the device; read it after synchronising.
+ *              L and P are undefined when info != 0.
+ * workspace, workspace_bytes [in] scratch, >= bakron_factor_workspace_bytes(n).
+ * stream [in]  HIP stream (0 = legacy default stream).
+ */
+int bakron_factor(const float* A, int64_t n, float damp_frac, float* L, float* P,
+                  int32_t* info, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
+/*
+ * Workspace bytes that bakron_solve needs for an m x n weight
+ * (0 when m == 0 or n == 0).  Deterministic; does not touch the device.
+ */
+size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);
+
+/*
+ * bakron_solve -- the BaKron rounding of W under A (x) B ([S] derivation and
+ * Theorem 3.2; [A] abstract).
+ *
+ * Computes the output of GPTQ run on vec(W) (column-major) with Hessian
+ * A_d (x) B_d.  Equivalently: visit the entries in an order where (i, j)
+ * comes after every (i', j') with i' <= i and j' <= j; at each entry take the
+ * current working value w~, round it on the row's grid
+ *     x = w~ / scale_i + zero_i,  c = clamp(rint(x), 0, maxq_i),
+ *     v = scale_i (c - zero_i),   e = w~ - v,
+ * and subtract e * P_B[i', i] * P_A[j', j] from every later entry
+ * (i' >= i, j' >= j).  The solver groups entries into 64 x 64 tiles, sweeps
+ * the tiles of one tile anti-diagonal in parallel (anti-diagonal
+ * parallelism) and propagates the errors of the first half of the
+ * remaining anti-diagonals to the second half with dense products
+ * (recursive divide and conquer): O(m + n) dependent steps, O(mn(m + n))
+ * work.  Arithmetic is float32; the rounding decision x is formed as
+ * float32(w~ / scale) + zero.
+ *
+ * W        [in]  m x n.  Not modified.
+ * m, n     [in]  0 <= m, n <= BAKRON_MAX_DIM; m == 0 or n == 0 enqueues
+ *                nothing.  Any m, n (multiples of 64 avoid padding copies).
+ * L_A, L_B [in]  n x n and m x m from bakron_factor(A), bakron_factor(B).
+ *                Only their diagonals are read, and only when `objective`
+ *                is not NULL (they may be NULL otherwise).
+ * P_A, P_B [in]  n x n and m x m from bakron_factor; must be zero above the
+ *                diagonal and one on it.  16-byte aligned.
+ * scale    [in]  m floats, finite and > 0 (grid step of each output row).
+ * zero     [in]  m floats, finite (zero point, fractional allowed).
+ * maxq     [in]  m int32 in [1, 255] (largest code of each row).
+ *                The grid contract is the caller's to keep; the device does
+ *                not check it.
+ * V        [out] m x n float32, V_ij = scale_i (c_ij - zero_i).
+ * codes    [out] m x n uint8 codes c_ij.
+ * err      [out, nullable] m x n float32 raw errors e_ij = w~_ij - V_ij.
+ * objective [out, nullable] one device double:
+ *                sum_ij (L_B[i,i] L_A[j,j] e_ij)^2, which equals
+ *                ||L_B (V - W) L_A^T||_F^2 ([S] Corollary 3.4's quantity).
+ * workspace, workspace_bytes [in] scratch, >= bakron_solve_workspace_bytes(m, n).
+ * stream   [in]  HIP stream.
+ */
+int bakron_solve(const float* W, int64_t m, int64_t n,
+                 const float* L_A, const float* P_A,
+                 const float* L_B, const float* P_B,
+                 const float* scale, const float* zero, const int32_t* maxq,
+                 float* V, uint8_t* codes, float* err, double* objective,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Profiling.  The *_profiled calls enqueue exactly the work of the plain
+ * call, but launch every kernel with HIP start/stop events recorded around
+ * it, then SYNCHRONISE `stream` and report, per kernel, the number of
+ * launches, the summed kernel time and the summed algorithmic flops and
+ * HBM bytes of those launches (the work the kernel's mathematical operation
+ * needs: nonzero block products, each operand tile read once and each
+ * output tile written once; padding and recomputation not counted).
+ * For profilers and benchmarks; they create and destroy HIP events (host
+ * objects) but allocate no device memory.
+ *
+ * stats     [out] host array of max_stats entries; filled in kernel order.
+ * max_stats [in]  capacity (BAKRON_MAX_KERNEL_KINDS is always enough).
+ * n_stats   [out] host int32: number of entries written (kernels launched).
+ */
+#define BAKRON_MAX_KERNEL_KINDS 16
+
+typedef struct bakron_kernel_stat {
+    const char* name;     /* kernel name (static storage) */
+    int32_t launches;     /* launches of this kernel */
+    double total_ms;      /* summed kernel time, milliseconds */
+    double alg_flops;     /* summed algorithmic flops */
+    double alg_bytes;     /* summed algorithmic HBM bytes */
+} bakron_kernel_stat;
+
+int bakron_factor_profiled(const float* A, int64_t n, float damp_frac, float* L, float* P,
+                           int32_t* info, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, bakron_kernel_stat* stats, int32_t max_stats,
+                           int32_t* n_stats);
+
+int bakron_solve_profiled(const float* W, int64_t m, int64_t n,
+                          const float* L_A, const float* P_A,
+                          const float* L_B, const float* P_B,
+                          const float* scale, const float* zero, const int32_t* maxq,
+                          float* V, uint8_t* codes, float* err, double* objective,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BAKRON_H */

@@ -35,7 +35,7 @@ import numpy as np
 __all__ = [
     "damp", "rev_cholesky", "normalized_inverse", "factor", "quantize",
     "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform",
-    "objective", "objective_from_errors", "implied_errors", "validate",
+    "objective", "objective_from_errors", "implied_errors", "implied_errors_p", "validate",
     "order_colmajor", "order_rowmajor", "order_antidiagonal",
 ]
 
@@ -265,9 +265,19 @@ def implied_errors(W, V, LA, LB) -> np.ndarray:
     return M / (np.diag(LB)[:, None] * np.diag(LA)[None, :])
 
 
+def implied_errors_p(W, V, PA, PB) -> np.ndarray:
+    """Same as ``implied_errors`` but from P_A, P_B directly:
+    E = PB^-1 (W - V) PA^-T by two unit-lower triangular solves."""
+    from scipy.linalg import solve_triangular
+    D = np.asarray(W, np.float64) - np.asarray(V, np.float64)
+    X = solve_triangular(np.asarray(PB, np.float64), D, lower=True, unit_diagonal=True)
+    Et = solve_triangular(np.asarray(PA, np.float64), X.T, lower=True, unit_diagonal=True)
+    return np.ascontiguousarray(Et.T)
+
+
 # ----------------------------------------------------------------- validator
 
-def validate(W, codes, s, z, maxq, LA, LB, tau=1e-4) -> dict:
+def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None) -> dict:
     """Check that ``codes`` is a BaKron output for (W, A (x) B, grid), any size.
 
     For a sequence of rounding decisions, the value entry (i, j) is rounded
@@ -278,6 +288,7 @@ def validate(W, codes, s, z, maxq, LA, LB, tau=1e-4) -> dict:
     in exact arithmetic), so a mismatch is a "tie" when x lies within
     ``tau`` grid steps of the boundary and the codes are adjacent.
 
+    The factors are given either as L_A, L_B or as P_A, P_B.
     Returns counts: entries, mismatches, ties (allowed), bad (outside the
     tie band or more than one step apart), max_step, min_margin.
     """
@@ -285,7 +296,10 @@ def validate(W, codes, s, z, maxq, LA, LB, tau=1e-4) -> dict:
     m, n = W.shape
     codes = np.asarray(codes, np.float64)
     V = _values(codes, s, z)
-    E = implied_errors(W, V, LA, LB)
+    if PA is not None:
+        E = implied_errors_p(W, V, PA, PB)
+    else:
+        E = implied_errors(W, V, LA, LB)
     Wt = V + E
     ss = np.broadcast_to(np.asarray(s)[:, None], (m, n))
     zz = np.broadcast_to(np.asarray(z)[:, None], (m, n))

@@ -1,0 +1,113 @@
+"""The C ABI of libbakron.so, checked on the CPU: the library loads, exports
+every function include/bakron.h declares, and rejects bad arguments on the
+host (these paths return before any device call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bakron.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(bakron_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    import two_sided_hessian_amd as B
+    if not os.path.exists(B.LIB_PATH):
+        from two_sided_hessian_amd import build
+        build.build()
+    return B
+
+
+def test_header_declares_the_api():
+    names = _declared()
+    assert names == sorted(["bakron_version", "bakron_strerror", "bakron_factor_workspace_bytes",
+                            "bakron_factor", "bakron_solve_workspace_bytes", "bakron_solve",
+                            "bakron_factor_profiled", "bakron_solve_profiled"])
+
+
+def test_library_exports_every_declared_symbol(B):
+    L = B.lib()
+    from two_sided_hessian_amd._binding import SIGNATURES
+    for name in _declared():
+        assert hasattr(L, name), name
+        assert name in SIGNATURES, name
+
+
+def test_header_constants_match_binding(B):
+    src = open(HEADER).read()
+    from two_sided_hessian_amd import _binding as bb
+    for k in ("BAKRON_SUCCESS", "BAKRON_ERR_NULL_POINTER", "BAKRON_ERR_BAD_SIZE", "BAKRON_ERR_WORKSPACE",
+              "BAKRON_ERR_BAD_ARG", "BAKRON_ERR_HIP", "BAKRON_MAX_DIM", "BAKRON_MAX_KERNEL_KINDS"):
+        v = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % k, src).group(1)
+        assert int(v) == getattr(bb, k), k
+
+
+def test_host_only_calls(B):
+    assert B.version() == 100
+    assert "workspace" in B.strerror(-3)
+    assert "unknown" in B.strerror(12345)
+    assert B.factor_workspace_bytes(0) == 0
+    assert B.solve_workspace_bytes(0, 5) == 0
+    assert B.solve_workspace_bytes(-1, 5) == 0
+    # three m x n float32 matrices at least, plus padded copies when ragged
+    assert B.solve_workspace_bytes(128, 128) >= 3 * 128 * 128 * 4
+    assert B.solve_workspace_bytes(100, 70) >= 3 * 128 * 128 * 4 + 128 * 128 * 4 + 128 * 128 * 4
+    assert B.factor_workspace_bytes(8192) >= 4096 * 4096 * 4
+    assert B.factor_workspace_bytes(100) >= 2 * 128 * 128 * 4
+
+
+def test_host_side_argument_errors(B):
+    L = B.lib()
+    fake = ctypes.c_void_p(4096)       # never dereferenced: every call below fails its host checks
+    # negative / oversized dimensions
+    assert L.bakron_factor(fake, -1, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None) == -2
+    assert L.bakron_factor(fake, 65537, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None) == -2
+    # bad damping
+    assert L.bakron_factor(fake, 8, ctypes.c_float(float("nan")), fake, fake, fake, fake, 1 << 30, None) == -4
+    assert L.bakron_factor(fake, 8, ctypes.c_float(-1.0), fake, fake, fake, fake, 1 << 30, None) == -4
+    # null pointers
+    assert L.bakron_factor(None, 8, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None) == -1
+    # n == 0 is a no-op success
+    assert L.bakron_factor(None, 0, ctypes.c_float(0.01), None, None, None, None, 0, None) == 0
+    # workspace too small / misaligned
+    assert L.bakron_factor(fake, 8, ctypes.c_float(0.01), fake, fake, fake, fake, 16, None) == -3
+    assert L.bakron_factor(fake, 8, ctypes.c_float(0.01), fake, fake, fake, ctypes.c_void_p(4100), 1 << 30, None) == -3
+    # misaligned output matrix
+    assert L.bakron_factor(fake, 8, ctypes.c_float(0.01), ctypes.c_void_p(4100), fake, fake, fake, 1 << 30, None) == -4
+    args = [fake, 64, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, None, fake, 1 << 30, None]
+    a = list(args); a[0] = None
+    assert L.bakron_solve(*a) == -1
+    a = list(args); a[1] = -3
+    assert L.bakron_solve(*a) == -2
+    a = list(args); a[1] = 0
+    assert L.bakron_solve(*a) == 0
+    a = list(args); a[13] = fake; a[3] = None      # objective requested without L_A
+    assert L.bakron_solve(*a) == -1
+    a = list(args); a[15] = 100
+    assert L.bakron_solve(*a) == -3
+    a = list(args); a[4] = ctypes.c_void_p(4104)   # misaligned P_A
+    assert L.bakron_solve(*a) == -4
+
+
+def test_profiled_calls_reject_bad_arguments_on_host(B):
+    L = B.lib()
+    from two_sided_hessian_amd._binding import KernelStat
+    arr = (KernelStat * 16)()
+    cnt = ctypes.c_int32(-7)
+    fake = ctypes.c_void_p(4096)
+    rc = L.bakron_factor_profiled(fake, -1, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None,
+                                  arr, 16, ctypes.byref(cnt))
+    assert rc == -2 and cnt.value == 0
+    rc = L.bakron_factor_profiled(fake, 8, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None,
+                                  arr, 16, None)
+    assert rc == -1
+    args = [None, 64, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, None, fake, 1 << 30, None]
+    assert L.bakron_solve_profiled(*args, arr, 16, ctypes.byref(cnt)) == -1

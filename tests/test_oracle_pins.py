@@ -277,3 +277,12 @@ def test_validator_flags_planted_arithmetic_mistake(plant):
     c, V, E = R.bakron_naive(d["W"], PA, PB, d["scale"], d["zero"], d["maxq"])
     r = R.validate(d["W"], c, d["scale"], d["zero"], d["maxq"], fa["L"], fb["L"])
     assert r["bad"] > 0
+
+
+def test_validator_from_p_matches_from_l():
+    d = make_problem(40, 72, 12)
+    fa, fb = _factors(d)
+    c, V, E = R.bakron_naive(d["W"], fa["P"], fb["P"], d["scale"], d["zero"], d["maxq"])
+    np.testing.assert_allclose(R.implied_errors_p(d["W"], V, fa["P"], fb["P"]), E, atol=1e-12)
+    r = R.validate(d["W"], c, d["scale"], d["zero"], d["maxq"], PA=fa["P"], PB=fb["P"])
+    assert r["mismatches"] == 0

@@ -1,0 +1,198 @@
+"""ctypes binding of libbakron.so (argument marshalling only).
+
+Names follow include/bakron.h.  Tensors are torch CUDA (HIP) tensors; the
+binding allocates outputs and the workspace with torch, passes raw device
+pointers and the current stream, and checks the return code.  Every
+arithmetic step runs in the library's HIP kernels.  There is no fallback:
+if libbakron.so is missing or cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbakron.so")
+
+BAKRON_SUCCESS = 0
+BAKRON_ERR_NULL_POINTER = -1
+BAKRON_ERR_BAD_SIZE = -2
+BAKRON_ERR_WORKSPACE = -3
+BAKRON_ERR_BAD_ARG = -4
+BAKRON_ERR_HIP = -5
+BAKRON_MAX_DIM = 65536
+
+# name -> (restype, argtypes); mirrors include/bakron.h
+_VP, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = {
+    "bakron_version": (ctypes.c_int, []),
+    "bakron_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "bakron_factor_workspace_bytes": (_SZ, [_I64]),
+    "bakron_factor": (ctypes.c_int, [_VP, _I64, ctypes.c_float, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "bakron_solve_workspace_bytes": (_SZ, [_I64, _I64]),
+    "bakron_solve": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                    _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+}
+
+
+
+class KernelStat(ctypes.Structure):
+    """bakron_kernel_stat (include/bakron.h)."""
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double),
+                ("alg_flops", ctypes.c_double), ("alg_bytes", ctypes.c_double)]
+
+
+BAKRON_MAX_KERNEL_KINDS = 16
+_PSTAT = ctypes.POINTER(KernelStat)
+SIGNATURES["bakron_factor_profiled"] = (ctypes.c_int, SIGNATURES["bakron_factor"][1] + [_PSTAT, ctypes.c_int32, _VP])
+SIGNATURES["bakron_solve_profiled"] = (ctypes.c_int, SIGNATURES["bakron_solve"][1] + [_PSTAT, ctypes.c_int32, _VP])
+
+_lib = None
+
+
+class BakronError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Load libbakron.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "(or python two_sided_hessian_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().bakron_strerror(int(code)).decode()
+
+
+def version() -> int:
+    return lib().bakron_version()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, dtype, shape):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns >= 512-byte aligned blocks
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def factor_workspace_bytes(n: int) -> int:
+    return lib().bakron_factor_workspace_bytes(int(n))
+
+
+def solve_workspace_bytes(m: int, n: int) -> int:
+    return lib().bakron_solve_workspace_bytes(int(m), int(n))
+
+
+def _stats_out():
+    arr = (KernelStat * BAKRON_MAX_KERNEL_KINDS)()
+    cnt = ctypes.c_int32(0)
+    return arr, cnt
+
+
+def _stats_list(arr, cnt):
+    return [{"name": arr[i].name.decode(), "launches": arr[i].launches, "total_ms": arr[i].total_ms,
+             "alg_flops": arr[i].alg_flops, "alg_bytes": arr[i].alg_bytes} for i in range(cnt.value)]
+
+
+def factor(A: torch.Tensor, damp_frac: float = 0.01, *, out=None, ws=None, stream=None, profile=None):
+    """bakron_factor: returns (L, P, info) device tensors; info is int32[1]
+    (0 = success), valid once the stream has been synchronised.  With a list
+    passed as ``profile``, runs bakron_factor_profiled (synchronises) and
+    appends its per-kernel statistics to the list."""
+    n = A.shape[0]
+    _check_dev("A", A, torch.float32, (n, n))
+    dev = A.device
+    if out is None:
+        L = torch.empty((n, n), dtype=torch.float32, device=dev)
+        P = torch.empty((n, n), dtype=torch.float32, device=dev)
+        info = torch.empty((1,), dtype=torch.int32, device=dev)
+    else:
+        L, P, info = out
+    need = factor_workspace_bytes(n)
+    if ws is None:
+        ws = workspace(need, dev)
+    args = [_ptr(A), n, ctypes.c_float(damp_frac), _ptr(L), _ptr(P), _ptr(info), _ptr(ws), ws.numel(),
+            _stream(stream)]
+    if profile is None:
+        rc = lib().bakron_factor(*args)
+    else:
+        arr, cnt = _stats_out()
+        rc = lib().bakron_factor_profiled(*args, arr, BAKRON_MAX_KERNEL_KINDS, ctypes.byref(cnt))
+        profile.extend(_stats_list(arr, cnt))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_factor")
+    return L, P, info
+
+
+def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objective=True,
+          out=None, ws=None, stream=None, profile=None):
+    """bakron_solve: returns dict(V, codes, err?, objective?) of device tensors.
+    ``profile``: as in factor()."""
+    m, n = W.shape
+    _check_dev("W", W, torch.float32, (m, n))
+    _check_dev("P_A", PA, torch.float32, (n, n))
+    _check_dev("P_B", PB, torch.float32, (m, m))
+    _check_dev("scale", scale, torch.float32, (m,))
+    _check_dev("zero", zero, torch.float32, (m,))
+    _check_dev("maxq", maxq, torch.int32, (m,))
+    if want_objective:
+        _check_dev("L_A", LA, torch.float32, (n, n))
+        _check_dev("L_B", LB, torch.float32, (m, m))
+    dev = W.device
+    if out is None:
+        out = {
+            "V": torch.empty((m, n), dtype=torch.float32, device=dev),
+            "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
+        }
+        if want_err:
+            out["err"] = torch.empty((m, n), dtype=torch.float32, device=dev)
+        if want_objective:
+            out["objective"] = torch.empty((1,), dtype=torch.float64, device=dev)
+    need = solve_workspace_bytes(m, n)
+    if ws is None:
+        ws = workspace(need, dev)
+    args = [_ptr(W), m, n, _ptr(LA) if want_objective else None, _ptr(PA),
+            _ptr(LB) if want_objective else None, _ptr(PB), _ptr(scale), _ptr(zero),
+            _ptr(maxq), _ptr(out["V"]), _ptr(out["codes"]), _ptr(out.get("err")),
+            _ptr(out.get("objective")), _ptr(ws), ws.numel(), _stream(stream)]
+    if profile is None:
+        rc = lib().bakron_solve(*args)
+    else:
+        arr, cnt = _stats_out()
+        rc = lib().bakron_solve_profiled(*args, arr, BAKRON_MAX_KERNEL_KINDS, ctypes.byref(cnt))
+        profile.extend(_stats_list(arr, cnt))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_solve")
+    return out

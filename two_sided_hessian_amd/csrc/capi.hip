@@ -1,0 +1,157 @@
+// capi.hip -- extern "C" entry points of libbakron.so (declared in
+// include/bakron.h).  Host-side argument checks only; the work is enqueued
+// by factor.hip and solve.hip.
+#include <math.h>
+
+#include "../../include/bakron.h"
+#include "internal.hpp"
+
+extern "C" {
+
+int bakron_version(void) { return 100; }   // 0.1.0
+
+const char* bakron_strerror(int code)
+{
+    switch (code) {
+    case BAKRON_SUCCESS: return "success";
+    case BAKRON_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case BAKRON_ERR_BAD_SIZE: return "matrix dimension negative or above BAKRON_MAX_DIM";
+    case BAKRON_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
+    case BAKRON_ERR_BAD_ARG: return "scalar argument out of range";
+    case BAKRON_ERR_HIP: return "HIP kernel launch failed";
+    default: return "unknown bakron error code";
+    }
+}
+
+size_t bakron_factor_workspace_bytes(int64_t n)
+{
+    if (n <= 0 || n > BAKRON_MAX_DIM) return 0;
+    return bk::factor_workspace_bytes(n);
+}
+
+size_t bakron_solve_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return 0;
+    return bk::solve_workspace_bytes(m, n);
+}
+
+static int check_ws(const void* ws, size_t have, size_t need)
+{
+    if (need == 0) return BAKRON_SUCCESS;
+    if (!ws || have < need || (reinterpret_cast<uintptr_t>(ws) % bk::kAlign) != 0) return BAKRON_ERR_WORKSPACE;
+    return BAKRON_SUCCESS;
+}
+
+int bakron_factor(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (n < 0 || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (!(damp_frac >= 0.f) || !isfinite(damp_frac)) return BAKRON_ERR_BAD_ARG;
+    if (n == 0) return BAKRON_SUCCESS;
+    if (!A || !L || !P || !info) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(L) || !bk::aligned16(P)) return BAKRON_ERR_BAD_ARG;
+    const int w = check_ws(workspace, workspace_bytes, bk::factor_workspace_bytes(n));
+    if (w) return w;
+    return bk::factor_enqueue(A, n, damp_frac, L, P, info, workspace, stream, nullptr) ? BAKRON_ERR_HIP
+                                                                                        : BAKRON_SUCCESS;
+}
+
+int bakron_factor_profiled(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream,
+                           bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)
+{
+    if (!n_stats || (max_stats > 0 && !stats)) return BAKRON_ERR_NULL_POINTER;
+    *n_stats = 0;
+    if (n < 0 || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (!(damp_frac >= 0.f) || !isfinite(damp_frac)) return BAKRON_ERR_BAD_ARG;
+    if (n == 0) return BAKRON_SUCCESS;
+    if (!A || !L || !P || !info) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(L) || !bk::aligned16(P)) return BAKRON_ERR_BAD_ARG;
+    const int w = check_ws(workspace, workspace_bytes, bk::factor_workspace_bytes(n));
+    if (w) return w;
+    bk::Prof prof;
+    const int rc = bk::factor_enqueue(A, n, damp_frac, L, P, info, workspace, stream, &prof);
+    const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
+    return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
+int bakron_solve(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                 const float* L_B, const float* P_B, const float* scale, const float* zero,
+                 const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !P_A || !P_B || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && (!L_A || !L_B)) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(P_A) || !bk::aligned16(P_B)) return BAKRON_ERR_BAD_ARG;
+    const int w = check_ws(workspace, workspace_bytes, bk::solve_workspace_bytes(m, n));
+    if (w) return w;
+    return bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective,
+                             workspace, stream, nullptr)
+               ? BAKRON_ERR_HIP
+               : BAKRON_SUCCESS;
+}
+
+int bakron_solve_profiled(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                          const float* L_B, const float* P_B, const float* scale, const float* zero,
+                          const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream,
+                          bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)
+{
+    if (!n_stats || (max_stats > 0 && !stats)) return BAKRON_ERR_NULL_POINTER;
+    *n_stats = 0;
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !P_A || !P_B || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && (!L_A || !L_B)) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(P_A) || !bk::aligned16(P_B)) return BAKRON_ERR_BAD_ARG;
+    const int w = check_ws(workspace, workspace_bytes, bk::solve_workspace_bytes(m, n));
+    if (w) return w;
+    bk::Prof prof;
+    const int rc = bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective,
+                                     workspace, stream, &prof);
+    const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
+    return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
+}  // extern "C"
+
+namespace bk {
+
+const char* kernel_name(int kind)
+{
+    static const char* const names[KK_COUNT] = {
+        "k_copy_pad", "k_leaf", "k_prop_rows", "k_prop_cols", "k_obj_reduce", "k_f_prep",
+        "k_base_block", "k_f_panel", "k_f_syrk", "k_f_right", "k_f_left", "k_f_finish"};
+    return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
+}
+
+int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)
+{
+    int rc = (hipStreamSynchronize(s) == hipSuccess && !p.failed) ? 0 : -1;
+    bakron_kernel_stat acc[KK_COUNT];
+    for (int k = 0; k < KK_COUNT; ++k) acc[k] = bakron_kernel_stat{kernel_name(k), 0, 0.0, 0.0, 0.0};
+    for (const LaunchRec& r : p.recs) {
+        float ms = 0.f;
+        if (hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess) rc = -1;
+        acc[r.kind].launches += 1;
+        acc[r.kind].total_ms += ms;
+        acc[r.kind].alg_flops += r.flops;
+        acc[r.kind].alg_bytes += r.bytes;
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    p.recs.clear();
+    int w = 0;
+    for (int k = 0; k < KK_COUNT && w < max_stats; ++k)
+        if (acc[k].launches > 0) stats[w++] = acc[k];
+    *n_stats = w;
+    return rc;
+}
+
+}  // namespace bk
+
+extern "C" {
+
+}  // extern "C"

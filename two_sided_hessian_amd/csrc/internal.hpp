@@ -1,0 +1,82 @@
+// internal.hpp -- shared host-side declarations of libbakron (not part of the ABI).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/bakron.h"
+
+namespace bk {
+
+// ------------------------------------------------------------ launches
+//
+// Every kernel is launched through launch().  With a Prof attached (the
+// *_profiled entry points) each launch carries HIP start/stop events
+// (hipExtLaunchKernelGGL records them around the kernel itself) and the
+// launch's algorithmic flops and bytes; the totals per kernel are read back
+// after the stream drains.
+
+enum KernelKind {
+    KK_COPY_PAD, KK_LEAF, KK_PROP_ROWS, KK_PROP_COLS, KK_OBJ_REDUCE,
+    KK_F_PREP, KK_F_BASE, KK_F_PANEL, KK_F_SYRK, KK_F_RIGHT, KK_F_LEFT, KK_F_FINISH, KK_COUNT
+};
+
+const char* kernel_name(int kind);
+
+struct LaunchRec {
+    int kind;
+    hipEvent_t start, stop;
+    double flops, bytes;
+};
+
+struct Prof {
+    std::vector<LaunchRec> recs;
+    bool failed = false;
+};
+
+template <typename... KArgs, typename... Args>
+inline void launch(Prof* p, int kind, double flops, double bytes, void (*kernel)(KArgs...), dim3 g, dim3 b,
+                   hipStream_t s, Args... args)
+{
+    if (!p) {
+        hipLaunchKernelGGL(kernel, g, b, 0, s, static_cast<KArgs>(args)...);
+        return;
+    }
+    LaunchRec r{kind, nullptr, nullptr, flops, bytes};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+        p->failed = true;
+        hipLaunchKernelGGL(kernel, g, b, 0, s, static_cast<KArgs>(args)...);
+        return;
+    }
+    hipExtLaunchKernelGGL(kernel, g, b, 0, s, r.start, r.stop, 0u, static_cast<KArgs>(args)...);
+    p->recs.push_back(r);
+}
+
+// Drain the stream, sum the per-launch event times per kernel kind into
+// stats (at most max_stats entries, in KernelKind order), release events.
+int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+constexpr int kTile = 64;            // tile edge of the solve and of the factor's base blocks
+constexpr size_t kAlign = 256;       // workspace sub-buffer alignment
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Factor (factor.hip)
+size_t factor_workspace_bytes(int64_t n);
+int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
+                   void* ws, hipStream_t stream, Prof* prof);
+
+// Solve (solve.hip)
+size_t solve_workspace_bytes(int64_t m, int64_t n);
+int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
+                  const float* LB, const float* PB, const float* scale, const float* zero,
+                  const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                  void* ws, hipStream_t stream, Prof* prof);
+
+}  // namespace bk

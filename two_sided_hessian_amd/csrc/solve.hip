@@ -1,0 +1,514 @@
+// solve.hip -- the BaKron rounding of W (m x n) under A (x) B, for gfx950.
+//
+// Method (paper summary "FastKron: Efficient Quantization with
+// Kronecker-Factored Hessians", derivation naive -> antidiagonal -> BaKron,
+// Theorem 3.2): GPTQ on vec(W) with Hessian A (x) B.  Quantizing entry (i, j)
+// with raw error e changes only entries (i', j') with i' >= i and j' >= j, by
+// e * P_B[i', i] * P_A[j', j] (P = L^-1 diag(L), L = RevCholesky).  So all
+// entries of one anti-diagonal can be rounded together, and the anti-diagonal
+// range can be split recursively: solve the first half, push its errors into
+// the second half with dense products, then solve the second half.
+//
+// MI355X layout of that idea:
+//  * 64 x 64 tiles.  Tile (I, J) only depends on tiles (I', J') with I' <= I,
+//    J' <= J, so tile anti-diagonals K = I + J are the recursion's unit.
+//  * Leaf (one launch per tile anti-diagonal, one workgroup per tile): the
+//    tile and its diagonal P_A block sit in LDS; 127 in-tile anti-diagonal
+//    steps quantize up to 64 entries each.  The value of entry (a, b) is
+//        W~in[a,b] - sum_{a'<=a} P_B[a,a'] U[a',b],
+//        U[a',b] = sum_{b'<=b, done} e[a',b'] P_A[b,b'],
+//    two length-64 dot products per entry, split over 4 lanes and reduced
+//    with lane shuffles.
+//  * Internal node (K0, mid, K1): stage 1 forms, per tile row I, the partial
+//    products Y[I, J'] = sum_J E[I, J] P_A[J', J]^T over the source tiles
+//    (K0 <= I + J < mid, J <= J'); stage 2 subtracts
+//    sum_I P_B[I', I] Y[I, J'] from every target tile (mid <= I' + J' < K1).
+//    Both are fp32 MFMA GEMMs whose K range follows the staircase of the
+//    tile band.
+//
+// Workspace (pitch Np = 64 * ceil(n / 64), Mp = 64 * ceil(m / 64)):
+//   Wt  Mp x Np  working weights (W copied in, zero padded)
+//   E   Mp x Np  raw errors of solved tiles
+//   Y   Mp x Np  stage-1 partial products
+//   obj Mt x Nt  per-tile objective partials (double)
+//   PAp Np x Np, PBp Mp x Mp  padded copies, only when n (m) is not a
+//        multiple of 64.
+// Padding entries are forced to zero error, so they never touch real ones.
+#include <algorithm>
+
+#include "gemm.hpp"
+#include "internal.hpp"
+
+namespace bk {
+
+// dst (R x C, pitch ldd) = src (rows x cols, pitch lds) with zeros outside.
+__global__ __launch_bounds__(256) void k_copy_pad(const float* __restrict__ src, int64_t rows, int64_t cols,
+                                                  int64_t lds, float* __restrict__ dst, int64_t R, int64_t C,
+                                                  int64_t ldd)
+{
+    for (int64_t i = blockIdx.y; i < R; i += gridDim.y)
+        for (int64_t j = blockIdx.x * 256 + threadIdx.x; j < C; j += (int64_t)gridDim.x * 256)
+            dst[i * ldd + j] = (i < rows && j < cols) ? src[i * lds + j] : 0.f;
+}
+
+struct LeafArgs {
+    float* Wt;            // Mp x Np working weights (pitch ldw)
+    float* E;             // Mp x Np raw errors (pitch ldw)
+    int64_t ldw;
+    const float* PA;      // P_A (pitch lda)
+    int64_t lda;
+    const float* PB;      // P_B (pitch ldb)
+    int64_t ldb;
+    const float* scale;
+    const float* zero;
+    const int32_t* maxq;
+    int m, n;
+    uint8_t* codes;       // m x n outputs (pitch n)
+    float* V;
+    float* err;           // nullable
+    const float* LA;      // nullable: diag source for the objective (pitch n)
+    const float* LB;      // nullable (pitch m)
+    double* objp;         // nullable: Mt x Nt partials
+    int Nt;
+    int K;                // tile anti-diagonal
+    int I_lo;             // first tile row on it
+    int vec_out;          // outputs may use 16-byte stores
+};
+
+constexpr int kLP = 68;   // LDS pitch (floats) of the P_A, U^T and E tiles
+
+__global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
+{
+    __shared__ float sW[64 * 64];
+    __shared__ __align__(16) float sPA[64 * kLP];
+    __shared__ __align__(16) float sUT[64 * kLP];   // sUT[b][a] = U[a][b]
+    __shared__ __align__(16) float sF[64 * kLP];    // raw errors e[a][b]
+    __shared__ __align__(16) uint8_t sC[64 * 64];
+    __shared__ double sRed[4];
+
+    const int I = g.I_lo + blockIdx.x;
+    const int J = g.K - I;
+    const int t = threadIdx.x;
+    const int a = t >> 2, sg = t & 3;
+    const int64_t r0 = (int64_t)I * 64, c0 = (int64_t)J * 64;
+
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int f = t + 256 * u;
+        const int row = f >> 4, cq = 4 * (f & 15);
+        const f32x4 w = *reinterpret_cast<const f32x4*>(g.Wt + (r0 + row) * g.ldw + c0 + cq);
+        *reinterpret_cast<f32x4*>(sW + row * 64 + cq) = w;
+        const f32x4 p = *reinterpret_cast<const f32x4*>(g.PA + (c0 + row) * g.lda + c0 + cq);
+        *reinterpret_cast<f32x4*>(sPA + row * kLP + cq) = p;
+    }
+    for (int idx = t; idx < 64 * kLP; idx += 256) {
+        sUT[idx] = 0.f;
+        sF[idx] = 0.f;
+    }
+    float pb[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(g.PB + (r0 + a) * g.ldb + r0 + 16 * sg + 4 * q);
+        pb[4 * q + 0] = v.x;
+        pb[4 * q + 1] = v.y;
+        pb[4 * q + 2] = v.z;
+        pb[4 * q + 3] = v.w;
+    }
+    const int64_t grow = r0 + a;
+    const bool row_ok = grow < g.m;
+    const float sc = row_ok ? g.scale[grow] : 1.f;
+    const float zc = row_ok ? g.zero[grow] : 0.f;
+    const float mq = row_ok ? (float)g.maxq[grow] : 0.f;
+    __syncthreads();
+
+    for (int d = 0; d < 127; ++d) {
+        const int b = d - a;
+        const bool act = (unsigned)b < 64u;
+        float pu = 0.f, ps = 0.f;
+        if (act) {
+            if (16 * sg < b) {
+                const f32x4* fr = reinterpret_cast<const f32x4*>(sF + a * kLP + 16 * sg);
+                const f32x4* pr = reinterpret_cast<const f32x4*>(sPA + b * kLP + 16 * sg);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 f4 = fr[q], p4 = pr[q];
+                    pu += f4.x * p4.x + f4.y * p4.y + f4.z * p4.z + f4.w * p4.w;
+                }
+            }
+            if (16 * sg < a) {
+                const f32x4* ur = reinterpret_cast<const f32x4*>(sUT + b * kLP + 16 * sg);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x4 u4 = ur[q];
+                    ps += pb[4 * q] * u4.x + pb[4 * q + 1] * u4.y + pb[4 * q + 2] * u4.z + pb[4 * q + 3] * u4.w;
+                }
+            }
+        }
+        pu += __shfl_xor(pu, 1);
+        pu += __shfl_xor(pu, 2);
+        ps += __shfl_xor(ps, 1);
+        ps += __shfl_xor(ps, 2);
+        if (act && sg == 0) {
+            const float w = sW[a * 64 + b] - pu - ps;
+            const bool ok = row_ok && (c0 + b) < g.n;
+            const float x = w / sc + zc;
+            const float c = fminf(fmaxf(rintf(x), 0.f), mq);
+            const float v = sc * (c - zc);
+            const float e = ok ? (w - v) : 0.f;
+            sF[a * kLP + b] = e;
+            sUT[b * kLP + a] = pu + e;
+            sC[a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
+        }
+        __syncthreads();
+    }
+
+    // Outputs: raw errors to the workspace, codes / values / errors to the
+    // caller, and this tile's objective partial.
+    const int row = t >> 2, cs = 16 * (t & 3);
+    const int64_t orow = r0 + row;
+    double objs = 0.0;
+    const float lb = (g.objp && orow < g.m) ? g.LB[orow * g.m + orow] : 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(g.E + orow * g.ldw + c0 + cs + 4 * q) =
+            *reinterpret_cast<const f32x4*>(sF + row * kLP + cs + 4 * q);
+    if (orow < g.m) {
+        const float so = g.scale[orow], zo = g.zero[orow];
+        if (g.vec_out) {
+            *reinterpret_cast<uint4*>(g.codes + orow * g.n + c0 + cs) =
+                *reinterpret_cast<const uint4*>(sC + row * 64 + cs);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                f32x4 v;
+                v.x = so * ((float)sC[row * 64 + cs + 4 * q + 0] - zo);
+                v.y = so * ((float)sC[row * 64 + cs + 4 * q + 1] - zo);
+                v.z = so * ((float)sC[row * 64 + cs + 4 * q + 2] - zo);
+                v.w = so * ((float)sC[row * 64 + cs + 4 * q + 3] - zo);
+                *reinterpret_cast<f32x4*>(g.V + orow * g.n + c0 + cs + 4 * q) = v;
+                if (g.err)
+                    *reinterpret_cast<f32x4*>(g.err + orow * g.n + c0 + cs + 4 * q) =
+                        *reinterpret_cast<const f32x4*>(sF + row * kLP + cs + 4 * q);
+            }
+        } else {
+            for (int k = 0; k < 16; ++k) {
+                const int64_t col = c0 + cs + k;
+                if (col >= g.n) break;
+                const uint8_t c = sC[row * 64 + cs + k];
+                g.codes[orow * g.n + col] = c;
+                g.V[orow * g.n + col] = so * ((float)c - zo);
+                if (g.err) g.err[orow * g.n + col] = sF[row * kLP + cs + k];
+            }
+        }
+        if (g.objp) {
+            for (int k = 0; k < 16; ++k) {
+                const int64_t col = c0 + cs + k;
+                if (col >= g.n) break;
+                const double q = (double)lb * (double)g.LA[col * g.n + col] * (double)sF[row * kLP + cs + k];
+                objs += q * q;
+            }
+        }
+    }
+    if (g.objp) {
+        for (int off = 32; off > 0; off >>= 1) objs += __shfl_xor(objs, off);
+        if ((t & 63) == 0) sRed[t >> 6] = objs;
+        __syncthreads();
+        if (t == 0) g.objp[(int64_t)I * g.Nt + J] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+    }
+}
+
+// ------------------------------------------------------ propagation
+
+typedef Block<1, 4> RowBlk;   // stage 1: 64 rows (one tile row) x 256 cols
+typedef Block<4, 1> ColBlk;   // stage 2: 256 rows x 64 cols (one tile column)
+
+// Stage 1 of node (K0, mid, K1): for tile row I (blockIdx.y + I_lo) and the
+// four target tile columns J' = j0 .. j0 + 3 of this block,
+//   Y[I, J'] = sum_{J = sl .. min(sh, J')} E[I, J] P_A[J', J]^T.
+// P_A[J', J] is zero for J > J', so the block uses K = sl .. min(sh, j0 + 3).
+__global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
+                                                   float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                   int K0, int mid, int K1, int Nt, int I_lo)
+{
+    __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
+    const int I = I_lo + blockIdx.y;
+    const int sl = max(0, K0 - I), sh = min(Nt - 1, mid - 1 - I), th = min(Nt - 1, K1 - 1 - I);
+    const int j0 = sl + 4 * blockIdx.x;
+    if (j0 > th) return;
+    const int jh = min(th, j0 + 3);
+    const int kb = 64 * sl, ke = 64 * (min(sh, jh) + 1);
+    const int64_t r0 = (int64_t)I * 64;
+    Acc acc;
+    acc_zero(acc);
+    block_gemm<1, 4, RowK, RowK>(E + r0 * ldw, ldw, 64, PA + (int64_t)j0 * 64 * lda, lda,
+                                 64 * (jh - j0 + 1), kb, ke, lds, acc);
+    block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
+}
+
+// Stage 2 of node (K0, mid, K1): for target tile column J (blockIdx.y + J_lo)
+// and the four target tile rows I' = i0 .. i0 + 3 of this block,
+//   Wt[I', J] -= sum_{I = max(0, K0 - J) .. min(I', mid - 1)} P_B[I', I] Y[I, J].
+// Only rows on target anti-diagonals (mid <= I' + J < K1) are written.
+__global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                   float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                   int K0, int mid, int K1, int Mt, int J_lo)
+{
+    __shared__ __align__(16) float lds[ColBlk::LDS_FLOATS];
+    const int J = J_lo + blockIdx.y;
+    const int tl = max(0, mid - J), th = min(Mt - 1, K1 - 1 - J);
+    const int i0 = tl + 4 * blockIdx.x;
+    if (i0 > th) return;
+    const int ih = min(th, i0 + 3);
+    const int kb = 64 * max(0, K0 - J), ke = 64 * (min(mid - 1, ih) + 1);
+    const int64_t c0 = (int64_t)J * 64, rr = (int64_t)i0 * 64;
+    Acc acc;
+    acc_zero(acc);
+    block_gemm<4, 1, RowK, KRow>(PB + rr * ldb, ldb, 64 * (ih - i0 + 1), Y + c0, ldw, 64, kb, ke, lds, acc);
+    block_store<4, 1>(Wt + rr * ldw + c0, ldw, 64 * (ih - i0 + 1), 64, -1.f, 1.f, acc);
+}
+
+__global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t count,
+                                                    double* __restrict__ out)
+{
+    __shared__ double red[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < count; i += 256) s += part[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) out[0] = red[0];
+}
+
+// ------------------------------------------------------------ host side
+
+namespace {
+
+struct SolvePlan {
+    int64_t m, n, Mt, Nt, Mp, Np;
+    bool pad_a, pad_b;
+    size_t off_wt, off_e, off_y, off_obj, off_pa, off_pb, total;
+};
+
+SolvePlan plan_solve(int64_t m, int64_t n)
+{
+    SolvePlan p;
+    p.m = m;
+    p.n = n;
+    p.Mt = ceil_div(m, kTile);
+    p.Nt = ceil_div(n, kTile);
+    p.Mp = p.Mt * kTile;
+    p.Np = p.Nt * kTile;
+    p.pad_a = (n % kTile) != 0;
+    p.pad_b = (m % kTile) != 0;
+    const size_t mat = sizeof(float) * (size_t)(p.Mp * p.Np);
+    size_t off = 0;
+    p.off_wt = off;
+    off = align_up(off + mat);
+    p.off_e = off;
+    off = align_up(off + mat);
+    p.off_y = off;
+    off = align_up(off + mat);
+    p.off_obj = off;
+    off = align_up(off + sizeof(double) * (size_t)(p.Mt * p.Nt));
+    p.off_pa = p.off_pb = 0;
+    if (p.pad_a) {
+        p.off_pa = off;
+        off = align_up(off + sizeof(float) * (size_t)(p.Np * p.Np));
+    }
+    if (p.pad_b) {
+        p.off_pb = off;
+        off = align_up(off + sizeof(float) * (size_t)(p.Mp * p.Mp));
+    }
+    p.total = off;
+    return p;
+}
+
+dim3 copy_grid(int64_t R, int64_t C)
+{
+    return dim3((unsigned)ceil_div(C, 256), (unsigned)std::min<int64_t>(R, 32768));
+}
+
+struct SolveRun {
+    LeafArgs leaf;
+    float* Y;
+    int Mt, Nt;
+    hipStream_t s;
+    Prof* prof;
+};
+
+int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
+
+constexpr double kTileB = 4.0 * 64 * 64;                 // bytes of one fp32 tile
+constexpr double kFull = 64.0 * 64.0 * 64.0;             // multiply-adds of a full block product
+constexpr double kTriB = 64.0 * 64.0 * 65.0 / 2.0;       // ... with a triangular diagonal block
+
+void enqueue_leaf(SolveRun& R, int K)
+{
+    const int I_lo = std::max(0, K - (R.Nt - 1));
+    const int I_hi = std::min(R.Mt - 1, K);
+    const int count = I_hi - I_lo + 1;
+    R.leaf.K = K;
+    R.leaf.I_lo = I_lo;
+    // per tile: the two in-tile triangular products (U = E P_A^T, P_B U);
+    // bytes: W~, P_A and P_B diagonal blocks in; E and V out (+ err), codes
+    const double flops = count * 2.0 * 2.0 * kTriB;
+    const double bytes = count * (5.0 * kTileB + (R.leaf.err ? kTileB : 0.0) + 64.0 * 64.0);
+    launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(256), R.s, R.leaf);
+}
+
+void enqueue_prop(SolveRun& R, int K0, int mid, int K1)
+{
+    const int Mt = R.Mt, Nt = R.Nt;
+    // stage 1 over tile rows with source tiles
+    const int I_lo = std::max(0, K0 - (Nt - 1));
+    const int I_hi = std::min(Mt - 1, mid - 1);
+    int span = 0;
+    double fl = 0.0, by = 0.0;
+    for (int I = I_lo; I <= I_hi; ++I) {
+        const int sl = std::max(0, K0 - I), sh = std::min(Nt - 1, mid - 1 - I);
+        const int th = std::min(Nt - 1, K1 - 1 - I);
+        span = std::max(span, th - sl + 1);
+        if (R.prof) {
+            const double S = sh - sl + 1, T = th - sl + 1;
+            const double pairs = S * (S + 1) / 2 + (T - S) * S;   // (J, J') with J <= J'
+            fl += 2.0 * ((pairs - S) * kFull + S * kTriB);
+            by += (S + T) * kTileB;                              // E read, Y written
+        }
+    }
+    if (R.prof)   // distinct P_A blocks: for source column J, J' runs over [J, th(first row using J)]
+        for (int J = 0; J < Nt; ++J) {
+            const int Ia = std::max(I_lo, K0 - J), Ib = std::min(I_hi, mid - 1 - J);
+            if (Ia > Ib) continue;
+            by += (std::min(Nt - 1, K1 - 1 - Ia) - J + 1) * kTileB;
+        }
+    if (I_hi >= I_lo && span > 0) {
+        dim3 g((unsigned)ceil_div(span, 4), (unsigned)(I_hi - I_lo + 1));
+        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, g, dim3(256), R.s, (const float*)R.leaf.E,
+               R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt, I_lo);
+    }
+    // stage 2 over target tile columns
+    const int J_lo = std::max(0, mid - (Mt - 1));
+    const int J_hi = std::min(Nt - 1, K1 - 1);
+    span = 0;
+    fl = by = 0.0;
+    for (int J = J_lo; J <= J_hi; ++J) {
+        const int tl = std::max(0, mid - J), th = std::min(Mt - 1, K1 - 1 - J);
+        span = std::max(span, th - tl + 1);
+        if (R.prof) {
+            const int slo = std::max(0, K0 - J);
+            for (int Ip = tl; Ip <= th; ++Ip) {
+                const int shi = std::min(mid - 1, Ip);
+                const double cnt = shi - slo + 1;
+                const bool diag = Ip <= mid - 1;
+                fl += 2.0 * ((cnt - (diag ? 1 : 0)) * kFull + (diag ? kTriB : 0.0));
+            }
+            by += (std::min(mid - 1, th) - slo + 1) * kTileB;   // Y read
+            by += 2.0 * (th - tl + 1) * kTileB;                 // W~ read and written
+        }
+    }
+    if (R.prof)   // distinct P_B blocks: for source row I, I' runs over [max(I, tl(J_hi)), th(first column using I)]
+        for (int I = 0; I < Mt; ++I) {
+            const int Ja = std::max(J_lo, K0 - I);
+            if (Ja > J_hi || I > mid - 1) continue;
+            const int hi = std::min(Mt - 1, K1 - 1 - Ja);
+            const int lo = std::max(I, std::max(0, mid - J_hi));
+            if (hi >= lo) by += (hi - lo + 1) * kTileB;
+        }
+    if (J_hi >= J_lo && span > 0) {
+        dim3 g((unsigned)ceil_div(span, 4), (unsigned)(J_hi - J_lo + 1));
+        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, g, dim3(256), R.s, (const float*)R.Y, R.leaf.PB,
+               R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, J_lo);
+    }
+}
+
+void solve_rec(SolveRun& R, int K0, int K1)
+{
+    if (K1 - K0 == 1) {
+        enqueue_leaf(R, K0);
+        return;
+    }
+    const int mid = (K0 + K1) / 2;
+    solve_rec(R, K0, mid);
+    enqueue_prop(R, K0, mid, K1);
+    solve_rec(R, mid, K1);
+}
+
+}  // namespace
+
+size_t solve_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0) return 0;
+    return plan_solve(m, n).total;
+}
+
+int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
+                  const float* LB, const float* PB, const float* scale, const float* zero,
+                  const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                  void* ws, hipStream_t s, Prof* prof)
+{
+    const SolvePlan p = plan_solve(m, n);
+    char* w = static_cast<char*>(ws);
+    SolveRun R;
+    R.prof = prof;
+    R.s = s;
+    LeafArgs& g = R.leaf;
+    g.Wt = reinterpret_cast<float*>(w + p.off_wt);
+    g.E = reinterpret_cast<float*>(w + p.off_e);
+    g.ldw = p.Np;
+    R.Y = reinterpret_cast<float*>(w + p.off_y);
+    const double dm = (double)m, dn = (double)n;
+    if (p.pad_a) {
+        float* pa = reinterpret_cast<float*>(w + p.off_pa);
+        launch(prof, KK_COPY_PAD, 0.0, 4.0 * (dn * dn + (double)(p.Np * p.Np)), k_copy_pad, copy_grid(p.Np, p.Np),
+               dim3(256), s, PA, n, n, n, pa, p.Np, p.Np, p.Np);
+        g.PA = pa;
+        g.lda = p.Np;
+    } else {
+        g.PA = PA;
+        g.lda = n;
+    }
+    if (p.pad_b) {
+        float* pb = reinterpret_cast<float*>(w + p.off_pb);
+        launch(prof, KK_COPY_PAD, 0.0, 4.0 * (dm * dm + (double)(p.Mp * p.Mp)), k_copy_pad, copy_grid(p.Mp, p.Mp),
+               dim3(256), s, PB, m, m, m, pb, p.Mp, p.Mp, p.Mp);
+        g.PB = pb;
+        g.ldb = p.Mp;
+    } else {
+        g.PB = PB;
+        g.ldb = m;
+    }
+    launch(prof, KK_COPY_PAD, 0.0, 4.0 * (dm * dn + (double)(p.Mp * p.Np)), k_copy_pad, copy_grid(p.Mp, p.Np),
+           dim3(256), s, W, m, n, n, g.Wt, p.Mp, p.Np, p.Np);
+    if (launch_ok()) return -1;
+    g.scale = scale;
+    g.zero = zero;
+    g.maxq = maxq;
+    g.m = (int)m;
+    g.n = (int)n;
+    g.codes = codes;
+    g.V = V;
+    g.err = err;
+    g.LA = LA;
+    g.LB = LB;
+    g.objp = objective ? reinterpret_cast<double*>(w + p.off_obj) : nullptr;
+    g.Nt = (int)p.Nt;
+    g.vec_out = (m % kTile == 0 && n % kTile == 0 && (reinterpret_cast<uintptr_t>(codes) & 15u) == 0 &&
+                 aligned16(V) && (err == nullptr || aligned16(err)))
+                    ? 1
+                    : 0;
+    R.Mt = (int)p.Mt;
+    R.Nt = (int)p.Nt;
+    solve_rec(R, 0, R.Mt + R.Nt - 1);
+    if (launch_ok()) return -1;
+    if (objective) {
+        const double cnt = (double)(p.Mt * p.Nt);
+        launch(prof, KK_OBJ_REDUCE, cnt, 8.0 * (cnt + 1.0), k_obj_reduce, dim3(1), dim3(256), s,
+               (const double*)g.objp, p.Mt * p.Nt, objective);
+        if (launch_ok()) return -1;
+    }
+    return 0;
+}
+
+}  // namespace bk
