@@ -151,7 +151,3 @@ int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_
 }
 
 }  // namespace bk
-
-extern "C" {
-
-}  // extern "C"

@@ -192,22 +192,29 @@ __device__ __forceinline__ void block_store(float* __restrict__ C, int64_t ldc, 
 {
     const int wave = threadIdx.x >> 6;
     const int wy = wave / WN, wx = wave % WN;
+    // rlim and clim are multiples of 64, so a wave's 64 x 64 sub-block is
+    // either inside or outside: one wave-uniform test.
+    if (wy * 64 >= rlim || wx * 64 >= clim) return;
+    float* base = C + (int64_t)(wy * 64) * ldc + wx * 64;
+    // all loads first (one wait), then all stores
+    float old[2][2][16];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-            const int col = wx * 64 + acc_col(ni);
-            if (col >= clim) continue;
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                old[mi][ni][r] = (beta != 0.f) ? base[(int64_t)acc_row(mi, r) * ldc + acc_col(ni)] : 0.f;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = wy * 64 + acc_row(mi, r);
-                if (row >= rlim || row - col < diag) continue;
-                float* p = C + (int64_t)row * ldc + col;
-                float v = alpha * acc.c[mi][ni][r];
-                if (beta != 0.f) v += beta * *p;
-                *p = v;
+                const int row = acc_row(mi, r), col = acc_col(ni);
+                if (wy * 64 + row - (wx * 64 + col) < diag) continue;
+                base[(int64_t)row * ldc + col] = alpha * acc.c[mi][ni][r] + beta * old[mi][ni][r];
             }
-        }
 }
 
 }  // namespace bk

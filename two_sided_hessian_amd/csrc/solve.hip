@@ -77,6 +77,27 @@ struct LeafArgs {
 
 constexpr int kLP = 68;   // LDS pitch (floats) of the P_A, U^T and E tiles
 
+// Sum over the 4 lanes of a quad (DPP quad permutes, no LDS round trip).
+__device__ __forceinline__ float quad_sum(float x)
+{
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
+    x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
+    return x;
+}
+
+// One tile (I, J) of tile anti-diagonal K per workgroup; 256 threads = 64
+// rows x 4 lanes (each lane owns 16 of the 64 columns of a dot product).
+//
+// In-tile step d visits entry (a, b = d - a) of every row a.  Its value is
+//   w~ = W~in[a,b] - pu - ps,
+//   pu = sum_{c<b} e[a,c] P_A[b,c]          (own row, earlier columns)
+//   ps = sum_{r<a} P_B[a,r] U[r,b],  U[r,b] = sum_{c<=b} e[r,c] P_A[b,c]
+// (P_A, P_B: the diagonal blocks of this tile).  Only two terms are new at
+// step d: e[a,b-1] in pu and U[a-1,b] in ps; everything else was final one
+// step earlier.  So each step computes, for the NEXT column bn = b + 1, the
+// partial sums without those terms (off the critical path), and the
+// critical path of a step is: barrier, read U[a-1,b], one FMA, quantize,
+// write e[a,b] and U[a,b] = pu + e[a,b], barrier.
 __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
 {
     __shared__ float sW[64 * 64];
@@ -105,7 +126,8 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
         sUT[idx] = 0.f;
         sF[idx] = 0.f;
     }
-    float pb[16];
+    // P_B row a, this lane's 16 columns; pbz drops column a-1 (the fresh term)
+    float pb[16], pbz[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(g.PB + (r0 + a) * g.ldb + r0 + 16 * sg + 4 * q);
@@ -114,6 +136,9 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
         pb[4 * q + 2] = v.z;
         pb[4 * q + 3] = v.w;
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) pbz[j] = (16 * sg + j == a - 1) ? 0.f : pb[j];
+    const float pbm1 = a > 0 ? g.PB[(r0 + a) * g.ldb + r0 + a - 1] : 0.f;   // P_B[a][a-1]
     const int64_t grow = r0 + a;
     const bool row_ok = grow < g.m;
     const float sc = row_ok ? g.scale[grow] : 1.f;
@@ -121,43 +146,67 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
     const float mq = row_ok ? (float)g.maxq[grow] : 0.f;
     __syncthreads();
 
+    float pu = 0.f, psp = 0.f;                      // for the current column
+    float wcur = (a == 0) ? sW[0] : 0.f;
     for (int d = 0; d < 127; ++d) {
-        const int b = d - a;
+        const int b = d - a, bn = b + 1;
         const bool act = (unsigned)b < 64u;
-        float pu = 0.f, ps = 0.f;
-        if (act) {
-            if (16 * sg < b) {
-                const f32x4* fr = reinterpret_cast<const f32x4*>(sF + a * kLP + 16 * sg);
-                const f32x4* pr = reinterpret_cast<const f32x4*>(sPA + b * kLP + 16 * sg);
+        const bool actn = (unsigned)bn < 64u;
+        // fresh term and next-step operands (all final after the last barrier)
+        float fresh = 0.f, pa_sub = 0.f, wnext = 0.f;
+        if (act && a > 0) fresh = sUT[b * kLP + a - 1];
+        f32x4 fr[4], pr[4], ur[4];
+        if (actn) {
+            const f32x4* F4 = reinterpret_cast<const f32x4*>(sF + a * kLP + 16 * sg);
+            const f32x4* P4 = reinterpret_cast<const f32x4*>(sPA + bn * kLP + 16 * sg);
+            const f32x4* U4 = reinterpret_cast<const f32x4*>(sUT + bn * kLP + 16 * sg);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 f4 = fr[q], p4 = pr[q];
-                    pu += f4.x * p4.x + f4.y * p4.y + f4.z * p4.z + f4.w * p4.w;
-                }
+            for (int q = 0; q < 4; ++q) {
+                fr[q] = F4[q];
+                pr[q] = P4[q];
+                ur[q] = U4[q];
             }
-            if (16 * sg < a) {
-                const f32x4* ur = reinterpret_cast<const f32x4*>(sUT + b * kLP + 16 * sg);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const f32x4 u4 = ur[q];
-                    ps += pb[4 * q] * u4.x + pb[4 * q + 1] * u4.y + pb[4 * q + 2] * u4.z + pb[4 * q + 3] * u4.w;
-                }
-            }
+            if (act) pa_sub = sPA[bn * kLP + b];
+            wnext = sW[a * 64 + bn];
         }
-        pu += __shfl_xor(pu, 1);
-        pu += __shfl_xor(pu, 2);
-        ps += __shfl_xor(ps, 1);
-        ps += __shfl_xor(ps, 2);
-        if (act && sg == 0) {
-            const float w = sW[a * 64 + b] - pu - ps;
+        // critical path: this step's entry
+        float e = 0.f;
+        if (act) {
+            const float ps = psp + pbm1 * fresh;
+            const float w = wcur - pu - ps;
             const bool ok = row_ok && (c0 + b) < g.n;
             const float x = w / sc + zc;
             const float c = fminf(fmaxf(rintf(x), 0.f), mq);
             const float v = sc * (c - zc);
-            const float e = ok ? (w - v) : 0.f;
-            sF[a * kLP + b] = e;
-            sUT[b * kLP + a] = pu + e;
-            sC[a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
+            e = ok ? (w - v) : 0.f;
+            if (sg == 0) {
+                sF[a * kLP + b] = e;
+                sUT[b * kLP + a] = pu + e;
+                sC[a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
+            }
+        }
+        // next step's partial sums (e[a][b] is read as 0 above: excluded)
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
+        if (actn) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                s0 += fr[q].x * pr[q].x;
+                s1 += fr[q].y * pr[q].y;
+                s2 += fr[q].z * pr[q].z;
+                s3 += fr[q].w * pr[q].w;
+                u0 += pbz[4 * q + 0] * ur[q].x;
+                u1 += pbz[4 * q + 1] * ur[q].y;
+                u2 += pbz[4 * q + 2] * ur[q].z;
+                u3 += pbz[4 * q + 3] * ur[q].w;
+            }
+        }
+        const float pun = quad_sum((s0 + s1) + (s2 + s3));
+        const float psn = quad_sum((u0 + u1) + (u2 + u3));
+        if (actn) {
+            pu = pun + e * pa_sub;
+            psp = psn;
+            wcur = wnext;
         }
         __syncthreads();
     }
