@@ -70,77 +70,109 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
 
 // ------------------------------------------------- 64 x 64 diagonal block
 
+__device__ __forceinline__ float lane_bcast(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
 // Reverse Cholesky of the 64 x 64 block at offset o of Pbuf (lower part
 // read), then its inverse; writes L to Lbuf and L^-1 to Pbuf (zeros above the
 // diagonal).  A non-positive (or NaN) pivot at block row k records
 // info = o + k + 1 unless an earlier block already recorded one.
-__global__ __launch_bounds__(256) void k_base_block(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
-                                                    int64_t ld, int64_t o, int32_t* __restrict__ info)
+//
+// One wave; lane i keeps row i of the (symmetric) working block in
+// registers, and every loop is unrolled so register indices are constants.
+// Elimination from the last row upward: at step k the pivot row k is
+// broadcast with readlane, lane i (< k) takes its multiplier S[i][k]/S[k][k]
+// from its own register k (symmetry), and updates its row.  Then the inverse
+// X = L^-1 row by row from X L = I: lane i computes
+//   X[i][j] = -(sum_{k=j+1..i} X[i][k] L[k][j]) / L[j][j],  j = i-1 .. 0,
+// all rows in parallel, reading column j of L from LDS (broadcast loads).
+__global__ __launch_bounds__(64) void k_base_block(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
+                                                   int64_t ld, int64_t o, int32_t* __restrict__ info)
 {
-    __shared__ float S[64][65];
-    __shared__ float X[64][65];
-    __shared__ int fail;
-    const int t = threadIdx.x;
-    for (int idx = t; idx < 64 * 64; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
-        S[i][j] = (j <= i) ? Pbuf[(o + i) * ld + o + j] : 0.f;
-        X[i][j] = (i == j) ? 1.f : 0.f;
+    __shared__ __align__(16) float sT[64 * 68];      // staging, then L^T (sT[j][k] = L[k][j])
+    const int i = threadIdx.x;
+    for (int idx = i; idx < 64 * 64; idx += 64) {
+        const int r = idx >> 6, c = idx & 63;
+        sT[r * 68 + c] = (c <= r) ? Pbuf[(o + r) * ld + o + c] : 0.f;
     }
-    if (t == 0) fail = -1;
+    __syncthreads();
+    float s[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) s[j] = (j <= i) ? sT[i * 68 + j] : sT[j * 68 + i];
     __syncthreads();
 
-    // Eliminate from the last row upward: row k of L is row k of the current
-    // block divided by sqrt of its pivot; then the leading k x k block drops
-    // the outer product of that row.
+    int fail = -1;
+#pragma unroll
     for (int k = 63; k >= 0; --k) {
-        const float d = S[k][k];
-        const float lkk = sqrtf(d);
-        __syncthreads();
-        if (t == 0) {
-            if (!(d > 0.f) && fail < 0) fail = k;
-            S[k][k] = lkk;
+        const float piv = lane_bcast(s[k], k);
+        if (!(piv > 0.f) && fail < 0) fail = k;
+        const float lkk = sqrtf(piv);
+        const float inv = 1.f / lkk;
+        // S[i][k] / S[k][k] for the rows still to eliminate, 0 for the others:
+        // the update below is branch-free, so every broadcast of row k is
+        // read before lane k rescales that row
+        const float mul = (i < k) ? s[k] / piv : 0.f;
+#pragma unroll
+        for (int j = 0; j < k; ++j) s[j] = fmaf(-mul, lane_bcast(s[j], k), s[j]);
+        if (i == k) {
+#pragma unroll
+            for (int j = 0; j < k; ++j) s[j] *= inv;
+            s[k] = lkk;
+#pragma unroll
+            for (int j = k + 1; j < 64; ++j) s[j] = 0.f;
         }
-        if (t < k) S[k][t] = S[k][t] / lkk;
-        __syncthreads();
-        for (int idx = t; idx < k * k; idx += 256) {
-            const int i = idx / k, j = idx - i * k;
-            if (j <= i) S[i][j] -= S[k][i] * S[k][j];
+    }
+    // lane i now holds row i of L (zeros above the diagonal); publish L^T
+#pragma unroll
+    for (int j = 0; j < 64; ++j) sT[j * 68 + i] = s[j];
+    __syncthreads();
+    float x[64];
+#pragma unroll
+    for (int j = 0; j < 64; ++j) x[j] = (j == i) ? 1.f / sT[j * 68 + j] : 0.f;
+#pragma unroll
+    for (int j = 62; j >= 0; --j) {
+        const f32x4* col = reinterpret_cast<const f32x4*>(sT + j * 68);
+        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+        for (int q = (j + 1) / 4; q < 16; ++q) {
+            const f32x4 c = col[q];
+            if (4 * q + 0 > j) a0 = fmaf(x[4 * q + 0], c.x, a0);
+            if (4 * q + 1 > j) a1 = fmaf(x[4 * q + 1], c.y, a1);
+            if (4 * q + 2 > j) a2 = fmaf(x[4 * q + 2], c.z, a2);
+            if (4 * q + 3 > j) a3 = fmaf(x[4 * q + 3], c.w, a3);
         }
-        __syncthreads();
+        const float v = -((a0 + a1) + (a2 + a3)) / sT[j * 68 + j];
+        x[j] = (j < i) ? v : x[j];
     }
-
-    // X = L^-1 by forward substitution on the identity, row by row.
-    for (int k = 0; k < 64; ++k) {
-        const float lkk = S[k][k];
-        if (t <= k) X[k][t] = X[k][t] / lkk;
-        __syncthreads();
-        const int w = k + 1, rows = 63 - k;
-        for (int idx = t; idx < rows * w; idx += 256) {
-            const int i = k + 1 + idx / w, j = idx % w;
-            X[i][j] -= S[i][k] * X[k][j];
-        }
-        __syncthreads();
+    // coalesced stores of L (from L^T in LDS) and of X (via LDS)
+    for (int idx = i; idx < 64 * 64; idx += 64) {
+        const int r = idx >> 6, c = idx & 63;
+        Lbuf[(o + r) * ld + o + c] = sT[c * 68 + r];
     }
-
-    for (int idx = t; idx < 64 * 64; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
-        Lbuf[(o + i) * ld + o + j] = (j <= i) ? S[i][j] : 0.f;
-        Pbuf[(o + i) * ld + o + j] = (j <= i) ? X[i][j] : 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 64; ++j) sT[i * 68 + j] = x[j];
+    __syncthreads();
+    for (int idx = i; idx < 64 * 64; idx += 64) {
+        const int r = idx >> 6, c = idx & 63;
+        Pbuf[(o + r) * ld + o + c] = sT[r * 68 + c];
     }
-    if (t == 0 && fail >= 0) atomicCAS(info, 0, (int32_t)(o + fail + 1));
+    if (i == 0 && fail >= 0) atomicCAS(info, 0, (int32_t)(o + fail + 1));
 }
 
 // ------------------------------------------------------ recursive GEMMs
 
-typedef Block<2, 2> FB;   // 128 x 128 output blocks
+constexpr int FBM = 128, FBN = 128;   // 128 x 128 output blocks
 
 // L21 = Li22^T A21 : (n2 x n1); Li22^T is upper triangular, so output rows
 // from r0 need K in [r0, n2).
 __global__ __launch_bounds__(256) void k_f_panel(const float* __restrict__ Pbuf, float* __restrict__ Lbuf,
                                                  int64_t ld, int64_t o1, int64_t o2, int n1, int n2)
 {
-    __shared__ __align__(16) float lds[FB::LDS_FLOATS];
-    const int r0 = blockIdx.y * FB::BM, c0 = blockIdx.x * FB::BN;
+    __shared__ __align__(16) float lds[Gemm<2, 2, KRow, KRow>::LDS_FLOATS];
+    const int r0 = blockIdx.y * FBM, c0 = blockIdx.x * FBN;
     Acc acc;
     acc_zero(acc);
     block_gemm<2, 2, KRow, KRow>(Pbuf + o2 * ld + o2 + r0, ld, n2 - r0,
@@ -154,14 +186,14 @@ __global__ __launch_bounds__(256) void k_f_panel(const float* __restrict__ Pbuf,
 __global__ __launch_bounds__(256) void k_f_syrk(const float* __restrict__ Lbuf, float* __restrict__ Pbuf,
                                                 int64_t ld, int64_t o1, int64_t o2, int n1, int n2)
 {
-    __shared__ __align__(16) float lds[FB::LDS_FLOATS];
+    __shared__ __align__(16) float lds[Gemm<2, 2, KRow, KRow>::LDS_FLOATS];
     // linear block index -> (br, bc) with br >= bc
     const int q = blockIdx.x;
     int br = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
     while ((br + 1) * (br + 2) / 2 <= q) ++br;
     while (br * (br + 1) / 2 > q) --br;
     const int bc = q - br * (br + 1) / 2;
-    const int r0 = br * FB::BM, c0 = bc * FB::BN;
+    const int r0 = br * FBM, c0 = bc * FBN;
     Acc acc;
     acc_zero(acc);
     block_gemm<2, 2, KRow, KRow>(Lbuf + o2 * ld + o1 + r0, ld, n1 - r0,
@@ -175,8 +207,8 @@ __global__ __launch_bounds__(256) void k_f_right(const float* __restrict__ Lbuf,
                                                  float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
                                                  int n1, int n2)
 {
-    __shared__ __align__(16) float lds[FB::LDS_FLOATS];
-    const int r0 = blockIdx.y * FB::BM, c0 = blockIdx.x * FB::BN;
+    __shared__ __align__(16) float lds[Gemm<2, 2, RowK, KRow>::LDS_FLOATS];
+    const int r0 = blockIdx.y * FBM, c0 = blockIdx.x * FBN;
     Acc acc;
     acc_zero(acc);
     block_gemm<2, 2, RowK, KRow>(Lbuf + (o2 + r0) * ld + o1, ld, n2 - r0,
@@ -189,9 +221,9 @@ __global__ __launch_bounds__(256) void k_f_right(const float* __restrict__ Lbuf,
 __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, float* __restrict__ Pbuf,
                                                 int64_t ld, int64_t o1, int64_t o2, int n1, int n2)
 {
-    __shared__ __align__(16) float lds[FB::LDS_FLOATS];
-    const int r0 = blockIdx.y * FB::BM, c0 = blockIdx.x * FB::BN;
-    const int kend = min(r0 + FB::BM, n2);
+    __shared__ __align__(16) float lds[Gemm<2, 2, RowK, KRow>::LDS_FLOATS];
+    const int r0 = blockIdx.y * FBM, c0 = blockIdx.x * FBN;
+    const int kend = min(r0 + FBM, n2);
     Acc acc;
     acc_zero(acc);
     block_gemm<2, 2, RowK, KRow>(Pbuf + (o2 + r0) * ld + o2, ld, n2 - r0,
@@ -278,7 +310,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
 {
     if (nsz == kTile) {
         launch(R.prof, KK_F_BASE, 2.0 * 2.0 * 64.0 * 64.0 * 64.0 / 6.0, 4.0 * (tri(64) + 2 * 64 * 64),
-               k_base_block, dim3(1), dim3(256), R.s, R.Lbuf, R.Pbuf, R.ld, o, R.info);
+               k_base_block, dim3(1), dim3(64), R.s, R.Lbuf, R.Pbuf, R.ld, o, R.info);
         return launch_ok();
     }
     const int64_t nt = nsz / kTile;
@@ -288,19 +320,19 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     const double d1 = n1, d2 = n2;
     if (factor_rec(R, o2, n2)) return -1;
     {
-        dim3 g((unsigned)ceil_div(n1, FB::BN), (unsigned)ceil_div(n2, FB::BM));
+        dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
         launch(R.prof, KK_F_PANEL, 2.0 * d1 * tri(d2), 4.0 * (tri(d2) + 2.0 * d2 * d1), k_f_panel, g, dim3(256),
                R.s, R.Pbuf, R.Lbuf, R.ld, o1, o2, n1, n2);
     }
     {
-        const int64_t tb = ceil_div(n1, FB::BM);
+        const int64_t tb = ceil_div(n1, FBM);
         launch(R.prof, KK_F_SYRK, 2.0 * d2 * tri(d1), 4.0 * (d2 * d1 + 2.0 * tri(d1)), k_f_syrk,
                dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s, R.Lbuf, R.Pbuf, R.ld, o1, o2, n1, n2);
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, o1, n1)) return -1;
     {
-        dim3 g((unsigned)ceil_div(n1, FB::BN), (unsigned)ceil_div(n2, FB::BM));
+        dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
         launch(R.prof, KK_F_RIGHT, 2.0 * d2 * tri(d1), 4.0 * (2.0 * d2 * d1 + tri(d1)), k_f_right, g, dim3(256),
                R.s, R.Lbuf, R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
         launch(R.prof, KK_F_LEFT, 2.0 * d1 * tri(d2), 4.0 * (2.0 * d2 * d1 + tri(d2)), k_f_left, g, dim3(256),

@@ -4,9 +4,10 @@
 // block; each wave owns one 64 x 64 sub-block as 2 x 2 tiles of
 // v_mfma_f32_32x32x2f32 (32 x 32 output, K = 2 per instruction, 16 fp32
 // accumulators per lane).  Operands are staged through LDS in K chunks of
-// kBK, double-buffered, with the next chunk's global loads issued before the
-// current chunk's MFMAs.  LDS holds both operands K-major ([k][row]) so the
-// MFMA fragment reads are unit-stride across lanes.
+// kBK; the next chunk's global loads are issued before the current chunk's
+// MFMAs.  Each operand keeps its global orientation in LDS, so global ->
+// LDS copies are float4 moves, and K-contiguous operands feed four MFMAs
+// per 16-byte LDS read.
 //
 // Every row/column extent used by the callers is a multiple of 64, so
 // per-float4 bounds checks (rows beyond `rlim` read as zero) are exact.
@@ -20,82 +21,97 @@ namespace bk {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 16;   // K chunk staged in LDS
+constexpr int kBK = 32;   // K chunk staged in LDS
 constexpr int kPad = 4;   // LDS row padding in floats (keeps 16-byte alignment)
 
 // How an operand is stored in global memory, for operand element (r, k)
 // where r runs over the output rows (operand A) or output columns (operand B):
-//   RowK: p[r * ld + k]   (K contiguous)
-//   KRow: p[k * ld + r]   (r contiguous)
+//   RowK: p[r * ld + k]   (K contiguous)  -> LDS [r][k], pitch kBK + kPad
+//   KRow: p[k * ld + r]   (r contiguous)  -> LDS [k][r], pitch R + kPad
+// Both copies are straight float4 moves (no transposition).
 enum Layout { RowK = 0, KRow = 1 };
 
-template <int R>
-struct OperandTile {
-    static constexpr int LD = R + kPad;               // LDS row pitch (floats)
+template <int R, int LAYOUT>
+struct Operand {
+    static constexpr int PITCH = (LAYOUT == RowK) ? (kBK + kPad) : (R + kPad);
+    static constexpr int FLOATS = (LAYOUT == RowK) ? R * PITCH : kBK * PITCH;
     static constexpr int F4 = R * kBK / 4;            // float4s per chunk
     static constexpr int PER_THREAD = F4 / 256;       // float4s per thread
     static_assert(F4 % 256 == 0, "tile too small for 256 threads");
+
+    // Global -> registers for one K chunk [k0, k0 + kBK); rows >= rlim read 0.
+    static __device__ __forceinline__ void load(const float* __restrict__ p, int64_t ld, int rlim, int k0,
+                                                f32x4 (&reg)[PER_THREAD])
+    {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER_THREAD; ++u) {
+            const int f = t + 256 * u;
+            int r, k;
+            if (LAYOUT == KRow) {
+                k = f / (R / 4);
+                r = 4 * (f % (R / 4));
+            } else {
+                r = f / (kBK / 4);
+                k = 4 * (f % (kBK / 4));
+            }
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (r < rlim) {
+                const float* src = (LAYOUT == KRow) ? p + (int64_t)(k0 + k) * ld + r
+                                                    : p + (int64_t)r * ld + (k0 + k);
+                v = *reinterpret_cast<const f32x4*>(src);
+            }
+            reg[u] = v;
+        }
+    }
+
+    static __device__ __forceinline__ void store(float* __restrict__ s, const f32x4 (&reg)[PER_THREAD])
+    {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int u = 0; u < PER_THREAD; ++u) {
+            const int f = t + 256 * u;
+            int r, k;
+            if (LAYOUT == KRow) {
+                k = f / (R / 4);
+                r = 4 * (f % (R / 4));
+                *reinterpret_cast<f32x4*>(s + k * PITCH + r) = reg[u];
+            } else {
+                r = f / (kBK / 4);
+                k = 4 * (f % (kBK / 4));
+                *reinterpret_cast<f32x4*>(s + r * PITCH + k) = reg[u];
+            }
+        }
+    }
+
+    // MFMA fragment of row `row` for the 8-wide k group starting at kc:
+    // element q is k = kc + 4 * (lane >> 5) + q (the same k assignment for
+    // both operands, so each v_mfma_f32_32x32x2f32 q contracts k = kc + q
+    // and kc + 4 + q).
+    static __device__ __forceinline__ f32x4 frag(const float* __restrict__ s, int row, int kc)
+    {
+        const int kl = (threadIdx.x & 63) >> 5;
+        if (LAYOUT == RowK) {
+            return *reinterpret_cast<const f32x4*>(s + row * PITCH + kc + 4 * kl);
+        } else {
+            const float* c = s + (kc + 4 * kl) * PITCH + row;
+            f32x4 v;
+            v.x = c[0];
+            v.y = c[PITCH];
+            v.z = c[2 * PITCH];
+            v.w = c[3 * PITCH];
+            return v;
+        }
+    }
 };
 
-// Global -> registers for one K chunk [k0, k0 + kBK) of an R-row operand.
-template <int R, int LAYOUT>
-__device__ __forceinline__ void load_chunk(const float* __restrict__ p, int64_t ld, int rlim,
-                                           int k0, f32x4 (&reg)[OperandTile<R>::PER_THREAD])
-{
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < OperandTile<R>::PER_THREAD; ++u) {
-        const int f = t + 256 * u;
-        int r, k;
-        if (LAYOUT == KRow) {
-            k = f / (R / 4);
-            r = 4 * (f % (R / 4));
-        } else {
-            r = f / (kBK / 4);
-            k = 4 * (f % (kBK / 4));
-        }
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (r < rlim) {
-            const float* src = (LAYOUT == KRow) ? p + (int64_t)(k0 + k) * ld + r
-                                                : p + (int64_t)r * ld + (k0 + k);
-            v = *reinterpret_cast<const f32x4*>(src);
-        }
-        reg[u] = v;
-    }
-}
-
-// Registers -> LDS (K-major [k][r], pitch OperandTile<R>::LD).
-template <int R, int LAYOUT>
-__device__ __forceinline__ void store_chunk(float* __restrict__ s,
-                                            const f32x4 (&reg)[OperandTile<R>::PER_THREAD])
-{
-    constexpr int LD = OperandTile<R>::LD;
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int u = 0; u < OperandTile<R>::PER_THREAD; ++u) {
-        const int f = t + 256 * u;
-        if (LAYOUT == KRow) {
-            const int k = f / (R / 4);
-            const int r = 4 * (f % (R / 4));
-            *reinterpret_cast<f32x4*>(s + k * LD + r) = reg[u];
-        } else {
-            const int r = f / (kBK / 4);
-            const int k = 4 * (f % (kBK / 4));
-            s[(k + 0) * LD + r] = reg[u].x;
-            s[(k + 1) * LD + r] = reg[u].y;
-            s[(k + 2) * LD + r] = reg[u].z;
-            s[(k + 3) * LD + r] = reg[u].w;
-        }
-    }
-}
-
-template <int WM, int WN>
-struct Block {
+template <int WM, int WN, int ALAY, int BLAY>
+struct Gemm {
     static constexpr int BM = 64 * WM;
     static constexpr int BN = 64 * WN;
-    static constexpr int LDS_A = kBK * OperandTile<BM>::LD;   // floats per buffer
-    static constexpr int LDS_B = kBK * OperandTile<BN>::LD;
-    static constexpr int LDS_FLOATS = 2 * (LDS_A + LDS_B);
+    typedef Operand<BM, ALAY> OA;
+    typedef Operand<BN, BLAY> OB;
+    static constexpr int LDS_FLOATS = OA::FLOATS + OB::FLOATS;
     static_assert(WM * WN == 4, "four waves per block");
 };
 
@@ -116,56 +132,61 @@ __device__ __forceinline__ void acc_zero(Acc& a)
 
 // C_block += A[m-rows, k0:k1] * B[k0:k1, n-cols] for this workgroup.
 // A rows beyond `alim` and B columns beyond `blim` read as zero.
-// k0, k1 are multiples of kBK.  `lds` must hold Block<WM,WN>::LDS_FLOATS.
+// k0, k1 are multiples of kBK.  `lds` must hold Gemm<...>::LDS_FLOATS.
+// One LDS buffer; the next chunk is prefetched into registers while the
+// current one feeds the MFMAs.
 template <int WM, int WN, int ALAY, int BLAY>
 __device__ __forceinline__ void block_gemm(const float* __restrict__ A, int64_t lda, int alim,
                                            const float* __restrict__ B, int64_t ldb, int blim,
                                            int k0, int k1, float* lds, Acc& acc)
 {
-    typedef Block<WM, WN> Bk;
-    constexpr int BM = Bk::BM, BN = Bk::BN;
-    constexpr int LDA = OperandTile<BM>::LD, LDB = OperandTile<BN>::LD;
+    typedef Gemm<WM, WN, ALAY, BLAY> G;
+    typedef typename G::OA OA;
+    typedef typename G::OB OB;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int wy = wave / WN, wx = wave % WN;
-    const int kl = lane >> 5, ml = lane & 31;
+    const int ml = lane & 31;
+    float* sa = lds;
+    float* sb = lds + OA::FLOATS;
 
-    f32x4 ra[OperandTile<BM>::PER_THREAD];
-    f32x4 rb[OperandTile<BN>::PER_THREAD];
+    f32x4 ra[OA::PER_THREAD];
+    f32x4 rb[OB::PER_THREAD];
     const int nchunk = (k1 - k0) / kBK;
     if (nchunk <= 0) return;
 
-    load_chunk<BM, ALAY>(A, lda, alim, k0, ra);
-    load_chunk<BN, BLAY>(B, ldb, blim, k0, rb);
-    store_chunk<BM, ALAY>(lds, ra);
-    store_chunk<BN, BLAY>(lds + 2 * Bk::LDS_A, rb);
+    OA::load(A, lda, alim, k0, ra);
+    OB::load(B, ldb, blim, k0, rb);
+    OA::store(sa, ra);
+    OB::store(sb, rb);
     __syncthreads();
 
     for (int c = 0; c < nchunk; ++c) {
-        const int buf = c & 1;
         const bool more = (c + 1) < nchunk;
         if (more) {
-            load_chunk<BM, ALAY>(A, lda, alim, k0 + (c + 1) * kBK, ra);
-            load_chunk<BN, BLAY>(B, ldb, blim, k0 + (c + 1) * kBK, rb);
+            OA::load(A, lda, alim, k0 + (c + 1) * kBK, ra);
+            OB::load(B, ldb, blim, k0 + (c + 1) * kBK, rb);
         }
-        const float* sa = lds + buf * Bk::LDS_A + wy * 64 + ml;
-        const float* sb = lds + 2 * Bk::LDS_A + buf * Bk::LDS_B + wx * 64 + ml;
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 2) {
-            const float a0 = sa[(kk + kl) * LDA];
-            const float a1 = sa[(kk + kl) * LDA + 32];
-            const float b0 = sb[(kk + kl) * LDB];
-            const float b1 = sb[(kk + kl) * LDB + 32];
-            acc.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc.c[0][0], 0, 0, 0);
-            acc.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc.c[0][1], 0, 0, 0);
-            acc.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc.c[1][0], 0, 0, 0);
-            acc.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc.c[1][1], 0, 0, 0);
+        for (int kc = 0; kc < kBK; kc += 8) {
+            const f32x4 a0 = OA::frag(sa, wy * 64 + ml, kc);
+            const f32x4 a1 = OA::frag(sa, wy * 64 + 32 + ml, kc);
+            const f32x4 b0 = OB::frag(sb, wx * 64 + ml, kc);
+            const f32x4 b1 = OB::frag(sb, wx * 64 + 32 + ml, kc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[q], b0[q], acc.c[0][0], 0, 0, 0);
+                acc.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[q], b1[q], acc.c[0][1], 0, 0, 0);
+                acc.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], b0[q], acc.c[1][0], 0, 0, 0);
+                acc.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], b1[q], acc.c[1][1], 0, 0, 0);
+            }
         }
         if (more) {
-            store_chunk<BM, ALAY>(lds + (buf ^ 1) * Bk::LDS_A, ra);
-            store_chunk<BN, BLAY>(lds + 2 * Bk::LDS_A + (buf ^ 1) * Bk::LDS_B, rb);
+            __syncthreads();
+            OA::store(sa, ra);
+            OB::store(sb, rb);
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 

@@ -267,8 +267,8 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
 
 // ------------------------------------------------------ propagation
 
-typedef Block<1, 4> RowBlk;   // stage 1: 64 rows (one tile row) x 256 cols
-typedef Block<4, 1> ColBlk;   // stage 2: 256 rows x 64 cols (one tile column)
+typedef Gemm<1, 4, RowK, RowK> RowBlk;   // stage 1: 64 rows (one tile row) x 256 cols
+typedef Gemm<4, 1, RowK, KRow> ColBlk;   // stage 2: 256 rows x 64 cols (one tile column)
 
 // Stage 1 of node (K0, mid, K1): for tile row I (blockIdx.y + I_lo) and the
 // four target tile columns J' = j0 .. j0 + 3 of this block,
