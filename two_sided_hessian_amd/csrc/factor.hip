@@ -70,11 +70,6 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
 
 // ------------------------------------------------- 64 x 64 diagonal block
 
-__device__ __forceinline__ float lane_bcast(float v, int lane)
-{
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
-}
-
 // Reverse Cholesky of the 64 x 64 block at offset o of Pbuf (lower part
 // read), then its inverse; writes L to Lbuf and L^-1 to Pbuf (zeros above the
 // diagonal).  A non-positive (or NaN) pivot at block row k records
@@ -82,55 +77,75 @@ __device__ __forceinline__ float lane_bcast(float v, int lane)
 //
 // One wave; lane i keeps row i of the (symmetric) working block in
 // registers, and every loop is unrolled so register indices are constants.
-// Elimination from the last row upward: at step k the pivot row k is
-// broadcast with readlane, lane i (< k) takes its multiplier S[i][k]/S[k][k]
-// from its own register k (symmetry), and updates its row.  Then the inverse
-// X = L^-1 row by row from X L = I: lane i computes
-//   X[i][j] = -(sum_{k=j+1..i} X[i][k] L[k][j]) / L[j][j],  j = i-1 .. 0,
-// all rows in parallel, reading column j of L from LDS (broadcast loads).
+// Elimination from the last row upward: at step k lane k publishes row k in
+// LDS, every lane reads it back with 16-byte broadcast loads, lane i (< k)
+// takes its multiplier S[i][k] / S[k][k] from its own register k (symmetry)
+// and updates its row.  The rows stay unscaled during the elimination; each
+// lane scales its own row once at the end, L[i][j] = S[i][j] / sqrt(S[i][i]).
+// Then the inverse X = L^-1 row by row from X L = I: lane i computes
+// X[i][j] = -(sum_{k=j+1..i} X[i][k] L[k][j]) / L[j][j] for j = i-1 .. 0, all
+// rows in parallel, reading column j of L from LDS.  Reciprocals and square
+// roots use the hardware approximations (about one ulp): the factor is
+// judged by its backward error, not by correct rounding.
 __global__ __launch_bounds__(64) void k_base_block(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
                                                    int64_t ld, int64_t o, int32_t* __restrict__ info)
 {
     __shared__ __align__(16) float sT[64 * 68];      // staging, then L^T (sT[j][k] = L[k][j])
+    __shared__ __align__(16) float sRow[64];         // the pivot row being broadcast
     const int i = threadIdx.x;
-    for (int idx = i; idx < 64 * 64; idx += 64) {
-        const int r = idx >> 6, c = idx & 63;
-        sT[r * 68 + c] = (c <= r) ? Pbuf[(o + r) * ld + o + c] : 0.f;
+    {
+        // 64 independent coalesced loads (row u, column i), then the stores
+        float v[64];
+#pragma unroll
+        for (int u = 0; u < 64; ++u) v[u] = Pbuf[(o + u) * ld + o + i];
+#pragma unroll
+        for (int u = 0; u < 64; ++u) sT[u * 68 + i] = (i <= u) ? v[u] : 0.f;
     }
     __syncthreads();
     float s[64];
 #pragma unroll
     for (int j = 0; j < 64; ++j) s[j] = (j <= i) ? sT[i * 68 + j] : sT[j * 68 + i];
-    __syncthreads();
 
     int fail = -1;
+    float my_rs = 0.f;
 #pragma unroll
     for (int k = 63; k >= 0; --k) {
-        const float piv = lane_bcast(s[k], k);
-        if (!(piv > 0.f) && fail < 0) fail = k;
-        const float lkk = sqrtf(piv);
-        const float inv = 1.f / lkk;
-        // S[i][k] / S[k][k] for the rows still to eliminate, 0 for the others:
-        // the update below is branch-free, so every broadcast of row k is
-        // read before lane k rescales that row
-        const float mul = (i < k) ? s[k] / piv : 0.f;
-#pragma unroll
-        for (int j = 0; j < k; ++j) s[j] = fmaf(-mul, lane_bcast(s[j], k), s[j]);
         if (i == k) {
 #pragma unroll
-            for (int j = 0; j < k; ++j) s[j] *= inv;
-            s[k] = lkk;
-#pragma unroll
-            for (int j = k + 1; j < 64; ++j) s[j] = 0.f;
+            for (int q = 0; q <= k / 4; ++q) {
+                f32x4 v;
+                v.x = s[4 * q + 0];
+                v.y = s[4 * q + 1];
+                v.z = s[4 * q + 2];
+                v.w = s[4 * q + 3];
+                *reinterpret_cast<f32x4*>(sRow + 4 * q) = v;
+            }
         }
+        __syncthreads();
+        const float piv = sRow[k];
+        if (!(piv > 0.f) && fail < 0) fail = k;
+        const float rs = __builtin_amdgcn_rsqf(piv);          // 1 / sqrt(piv)
+        my_rs = (i == k) ? rs : my_rs;
+        const float mul = (i < k) ? s[k] * (rs * rs) : 0.f;    // S[i][k] / S[k][k]
+#pragma unroll
+        for (int q = 0; 4 * q < k; ++q) {
+            const f32x4 r = *reinterpret_cast<const f32x4*>(sRow + 4 * q);
+            if (4 * q + 0 < k) s[4 * q + 0] = fmaf(-mul, r.x, s[4 * q + 0]);
+            if (4 * q + 1 < k) s[4 * q + 1] = fmaf(-mul, r.y, s[4 * q + 1]);
+            if (4 * q + 2 < k) s[4 * q + 2] = fmaf(-mul, r.z, s[4 * q + 2]);
+            if (4 * q + 3 < k) s[4 * q + 3] = fmaf(-mul, r.w, s[4 * q + 3]);
+        }
+        __syncthreads();     // sRow is rewritten by the next step
     }
+#pragma unroll
+    for (int j = 0; j < 64; ++j) s[j] = (j <= i) ? s[j] * my_rs : 0.f;
     // lane i now holds row i of L (zeros above the diagonal); publish L^T
 #pragma unroll
     for (int j = 0; j < 64; ++j) sT[j * 68 + i] = s[j];
     __syncthreads();
     float x[64];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) x[j] = (j == i) ? 1.f / sT[j * 68 + j] : 0.f;
+    for (int j = 0; j < 64; ++j) x[j] = (j == i) ? __builtin_amdgcn_rcpf(s[j]) : 0.f;
 #pragma unroll
     for (int j = 62; j >= 0; --j) {
         const f32x4* col = reinterpret_cast<const f32x4*>(sT + j * 68);
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(64) void k_base_block(float* __restrict__ Lbuf, flo
             if (4 * q + 2 > j) a2 = fmaf(x[4 * q + 2], c.z, a2);
             if (4 * q + 3 > j) a3 = fmaf(x[4 * q + 3], c.w, a3);
         }
-        const float v = -((a0 + a1) + (a2 + a3)) / sT[j * 68 + j];
+        const float v = -((a0 + a1) + (a2 + a3)) * __builtin_amdgcn_rcpf(sT[j * 68 + j]);
         x[j] = (j < i) ? v : x[j];
     }
     // coalesced stores of L (from L^T in LDS) and of X (via LDS)

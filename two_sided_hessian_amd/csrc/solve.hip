@@ -148,58 +148,57 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
 
     float pu = 0.f, psp = 0.f;                      // for the current column
     float wcur = (a == 0) ? sW[0] : 0.f;
+    const int am1 = a > 0 ? a - 1 : 0;
     for (int d = 0; d < 127; ++d) {
         const int b = d - a, bn = b + 1;
         const bool act = (unsigned)b < 64u;
         const bool actn = (unsigned)bn < 64u;
-        // fresh term and next-step operands (all final after the last barrier)
-        float fresh = 0.f, pa_sub = 0.f, wnext = 0.f;
-        if (act && a > 0) fresh = sUT[b * kLP + a - 1];
+        // Every LDS read is unconditional (clamped, in-bounds indices; the
+        // results are masked below) so the fresh value, read first, is the
+        // only one the critical path waits for.
+        const int bc = min(max(b, 0), 63), bnc = min(max(bn, 0), 63);
+        const float fresh = sUT[bc * kLP + am1];       // U[a-1][b]
+        const float pa_sub = sPA[bnc * kLP + bc];     // P_A[b+1][b]
+        const float wnext = sW[a * 64 + bnc];
+        __builtin_amdgcn_sched_barrier(0);            // keep those three reads first
         f32x4 fr[4], pr[4], ur[4];
-        if (actn) {
+        {
             const f32x4* F4 = reinterpret_cast<const f32x4*>(sF + a * kLP + 16 * sg);
-            const f32x4* P4 = reinterpret_cast<const f32x4*>(sPA + bn * kLP + 16 * sg);
-            const f32x4* U4 = reinterpret_cast<const f32x4*>(sUT + bn * kLP + 16 * sg);
+            const f32x4* P4 = reinterpret_cast<const f32x4*>(sPA + bnc * kLP + 16 * sg);
+            const f32x4* U4 = reinterpret_cast<const f32x4*>(sUT + bnc * kLP + 16 * sg);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 fr[q] = F4[q];
                 pr[q] = P4[q];
                 ur[q] = U4[q];
             }
-            if (act) pa_sub = sPA[bn * kLP + b];
-            wnext = sW[a * 64 + bn];
         }
         // critical path: this step's entry
-        float e = 0.f;
-        if (act) {
-            const float ps = psp + pbm1 * fresh;
-            const float w = wcur - pu - ps;
-            const bool ok = row_ok && (c0 + b) < g.n;
-            const float x = w / sc + zc;
-            const float c = fminf(fmaxf(rintf(x), 0.f), mq);
-            const float v = sc * (c - zc);
-            e = ok ? (w - v) : 0.f;
-            if (sg == 0) {
-                sF[a * kLP + b] = e;
-                sUT[b * kLP + a] = pu + e;
-                sC[a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
-            }
+        const float ps = psp + pbm1 * fresh;          // pbm1 == 0 on row 0
+        const float w = wcur - pu - ps;
+        const float x = w / sc + zc;
+        const float c = fminf(fmaxf(rintf(x), 0.f), mq);
+        const float v = sc * (c - zc);
+        const bool ok = act && row_ok && (c0 + b) < g.n;
+        const float e = ok ? (w - v) : 0.f;
+        if (act && sg == 0) {
+            sF[a * kLP + b] = e;
+            sUT[b * kLP + a] = pu + e;
+            sC[a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
         }
-        // next step's partial sums (e[a][b] is read as 0 above: excluded)
+        // next step's partial sums (e[a][b] was read as 0 above: excluded)
         float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
         float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
-        if (actn) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                s0 += fr[q].x * pr[q].x;
-                s1 += fr[q].y * pr[q].y;
-                s2 += fr[q].z * pr[q].z;
-                s3 += fr[q].w * pr[q].w;
-                u0 += pbz[4 * q + 0] * ur[q].x;
-                u1 += pbz[4 * q + 1] * ur[q].y;
-                u2 += pbz[4 * q + 2] * ur[q].z;
-                u3 += pbz[4 * q + 3] * ur[q].w;
-            }
+        for (int q = 0; q < 4; ++q) {
+            s0 = fmaf(fr[q].x, pr[q].x, s0);
+            s1 = fmaf(fr[q].y, pr[q].y, s1);
+            s2 = fmaf(fr[q].z, pr[q].z, s2);
+            s3 = fmaf(fr[q].w, pr[q].w, s3);
+            u0 = fmaf(pbz[4 * q + 0], ur[q].x, u0);
+            u1 = fmaf(pbz[4 * q + 1], ur[q].y, u1);
+            u2 = fmaf(pbz[4 * q + 2], ur[q].z, u2);
+            u3 = fmaf(pbz[4 * q + 3], ur[q].w, u3);
         }
         const float pun = quad_sum((s0 + s1) + (s2 + s3));
         const float psn = quad_sum((u0 + u1) + (u2 + u3));
