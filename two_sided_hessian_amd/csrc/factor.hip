@@ -237,7 +237,8 @@ __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, flo
                                                 int64_t ld, int64_t o1, int64_t o2, int n1, int n2)
 {
     __shared__ __align__(16) float lds[Gemm<2, 2, RowK, KRow>::LDS_FLOATS];
-    const int r0 = blockIdx.y * FBM, c0 = blockIdx.x * FBN;
+    // heaviest (largest K, last row blocks) first
+    const int r0 = (int)(gridDim.y - 1 - blockIdx.y) * FBM, c0 = blockIdx.x * FBN;
     const int kend = min(r0 + FBM, n2);
     Acc acc;
     acc_zero(acc);

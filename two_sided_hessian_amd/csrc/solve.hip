@@ -278,9 +278,12 @@ __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, 
                                                    int K0, int mid, int K1, int Nt, int I_lo)
 {
     __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
+    // Heaviest blocks first: within a row the K range grows with the column
+    // block, so columns run from the last block down (a long block started
+    // last would leave the other CUs idle at the end of the launch).
     const int I = I_lo + blockIdx.y;
     const int sl = max(0, K0 - I), sh = min(Nt - 1, mid - 1 - I), th = min(Nt - 1, K1 - 1 - I);
-    const int j0 = sl + 4 * blockIdx.x;
+    const int j0 = sl + 4 * (int)(gridDim.x - 1 - blockIdx.x);
     if (j0 > th) return;
     const int jh = min(th, j0 + 3);
     const int kb = 64 * sl, ke = 64 * (min(sh, jh) + 1);
@@ -301,9 +304,11 @@ __global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, 
                                                    int K0, int mid, int K1, int Mt, int J_lo)
 {
     __shared__ __align__(16) float lds[ColBlk::LDS_FLOATS];
-    const int J = J_lo + blockIdx.y;
+    // Heaviest blocks first: the K range grows with the target row block and
+    // the longest columns come last in J, so both orders are reversed.
+    const int J = J_lo + (int)(gridDim.y - 1 - blockIdx.y);
     const int tl = max(0, mid - J), th = min(Mt - 1, K1 - 1 - J);
-    const int i0 = tl + 4 * blockIdx.x;
+    const int i0 = tl + 4 * (int)(gridDim.x - 1 - blockIdx.x);
     if (i0 > th) return;
     const int ih = min(th, i0 + 3);
     const int kb = 64 * max(0, K0 - J), ke = 64 * (min(mid - 1, ih) + 1);
