@@ -22,7 +22,7 @@ namespace bk {
 
 enum KernelKind {
     KK_COPY_PAD, KK_LEAF, KK_PROP_ROWS, KK_PROP_COLS, KK_OBJ_REDUCE,
-    KK_F_PREP, KK_F_BASE, KK_F_PANEL, KK_F_SYRK, KK_F_RIGHT, KK_F_LEFT, KK_F_FINISH, KK_COUNT
+    KK_F_PREP, KK_F_BASE, KK_F_PANEL, KK_F_SYRK, KK_F_RIGHT, KK_F_LEFT, KK_F_FINISH, KK_SCHED, KK_COUNT
 };
 
 const char* kernel_name(int kind);
@@ -61,6 +61,7 @@ inline void launch(Prof* p, int kind, double flops, double bytes, void (*kernel)
 int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
 
 constexpr int kTile = 64;            // tile edge of the solve and of the factor's base blocks
+constexpr int kMaxDim = BAKRON_MAX_DIM;
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

@@ -33,6 +33,7 @@
 //   obj Mt x Nt  per-tile objective partials (double)
 //   PAp Np x Np, PBp Mp x Mp  padded copies, only when n (m) is not a
 //        multiple of 64.
+//   sched  block lists of the propagation launches (k_sched)
 // Padding entries are forced to zero error, so they never touch real ones.
 #include <algorithm>
 
@@ -269,24 +270,146 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
 typedef Gemm<1, 4, RowK, RowK> RowBlk;   // stage 1: 64 rows (one tile row) x 256 cols
 typedef Gemm<4, 1, RowK, KRow> ColBlk;   // stage 2: 256 rows x 64 cols (one tile column)
 
-// Stage 1 of node (K0, mid, K1): for tile row I (blockIdx.y + I_lo) and the
-// four target tile columns J' = j0 .. j0 + 3 of this block,
+// ------------------------------------------------------ block schedule
+//
+// A propagation block's K extent follows the staircase of the tile band, so
+// the blocks of one launch differ in length by up to two orders of
+// magnitude; started in plain index order, the long ones start late and the
+// launch ends with most CUs idle.  k_sched writes, for every internal node
+// of the recursion and each of its two stages, the node's blocks sorted by
+// decreasing K extent (longest first), and the propagation kernels take
+// their block from that list.  The order only decides which CU computes
+// which block: every block writes its own outputs, so results do not
+// depend on it.
+//
+// Nodes are numbered as in a heap: the root [0, Kt) is (depth 0, pos 0) and
+// node (d, p) = [K0, K1) has children (d + 1, 2p) = [K0, mid) and
+// (d + 1, 2p + 1) = [mid, K1), mid = (K0 + K1) / 2.  A node at depth d is at
+// most w_d = ceil(Kt / 2^d) anti-diagonals wide, so a stage has at most
+// max(Mt, Nt) * ceil(w_d / 4) blocks: that is the list capacity cap[d], and
+// the list of (d, p, stage) starts at base[d] + (2p + stage) * cap[d].
+// An entry packs (tile row or column) << 16 | block index.
+
+constexpr int kMaxDepth = 12;                 // Kt <= 2047 needs 11 levels of internal nodes
+constexpr int kMaxKTiles = kMaxDim / kTile;   // K extent of a block, in tiles
+
+struct SchedGeom {
+    int Mt, Nt, Kt, levels;
+    int64_t base[kMaxDepth];
+    int64_t cap[kMaxDepth];
+};
+
+// Stage 1 block (row I, block b): target columns j0 = sl + 4b .. jh, source
+// columns sl .. min(sh, jh).
+struct RowSpan {
+    int sl, sh, th;
+    __host__ __device__ RowSpan(int I, int K0, int mid, int K1, int Nt)
+        : sl(max(0, K0 - I)), sh(min(Nt - 1, mid - 1 - I)), th(min(Nt - 1, K1 - 1 - I)) {}
+    __host__ __device__ int blocks() const { return (th - sl + 4) / 4; }
+    __host__ __device__ int ktiles(int b) const { return min(sh, min(th, sl + 4 * b + 3)) - sl + 1; }
+};
+
+// Stage 2 block (column J, block b): target rows i0 = tl + 4b .. ih, source
+// rows slo .. min(mid - 1, ih).
+struct ColSpan {
+    int tl, th, slo, mid;
+    __host__ __device__ ColSpan(int J, int K0, int mid_, int K1, int Mt)
+        : tl(max(0, mid_ - J)), th(min(Mt - 1, K1 - 1 - J)), slo(max(0, K0 - J)), mid(mid_) {}
+    __host__ __device__ int blocks() const { return (th - tl + 4) / 4; }
+    __host__ __device__ int ktiles(int b) const { return min(mid - 1, min(th, tl + 4 * b + 3)) - slo + 1; }
+};
+
+__host__ __device__ inline int rows_lo(int K0, int Nt) { return max(0, K0 - (Nt - 1)); }
+__host__ __device__ inline int rows_hi(int mid, int Mt) { return min(Mt - 1, mid - 1); }
+__host__ __device__ inline int cols_lo(int mid, int Mt) { return max(0, mid - (Mt - 1)); }
+__host__ __device__ inline int cols_hi(int K1, int Nt) { return min(Nt - 1, K1 - 1); }
+
+// One workgroup per (heap slot, stage): counting sort of the node's blocks
+// by K extent, descending.
+__global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict__ out)
+{
+    __shared__ int cnt[kMaxKTiles + 1];
+    __shared__ int kmax;
+    const int t = threadIdx.x;
+    const unsigned slot = blockIdx.x + 1u;
+    const int d = 31 - __builtin_clz(slot);
+    const int p = (int)(slot - (1u << d));
+    const int stage = blockIdx.y;
+    int K0 = 0, K1 = g.Kt;
+    for (int l = d - 1; l >= 0; --l) {
+        if (K1 - K0 < 2) return;          // no node at this slot
+        const int mid = (K0 + K1) / 2;
+        if ((p >> l) & 1) K0 = mid; else K1 = mid;
+    }
+    if (K1 - K0 < 2) return;              // a leaf: nothing to propagate
+    const int mid = (K0 + K1) / 2;
+    uint32_t* list = out + g.base[d] + (int64_t)(2 * p + stage) * g.cap[d];
+    const int lo = stage == 0 ? rows_lo(K0, g.Nt) : cols_lo(mid, g.Mt);
+    const int hi = stage == 0 ? rows_hi(mid, g.Mt) : cols_hi(K1, g.Nt);
+
+    for (int k = t; k <= kMaxKTiles; k += 256) cnt[k] = 0;
+    if (t == 0) kmax = 0;
+    __syncthreads();
+    int km = 0;
+    for (int u = lo + t; u <= hi; u += 256) {
+        if (stage == 0) {
+            const RowSpan s(u, K0, mid, K1, g.Nt);
+            for (int b = 0; b < s.blocks(); ++b) {
+                const int k = s.ktiles(b);
+                atomicAdd(&cnt[k], 1);
+                km = max(km, k);
+            }
+        } else {
+            const ColSpan s(u, K0, mid, K1, g.Mt);
+            for (int b = 0; b < s.blocks(); ++b) {
+                const int k = s.ktiles(b);
+                atomicAdd(&cnt[k], 1);
+                km = max(km, k);
+            }
+        }
+    }
+    atomicMax(&kmax, km);
+    __syncthreads();
+    if (t == 0) {   // exclusive prefix sum from the longest extent down
+        int run = 0;
+        for (int k = kmax; k >= 1; --k) {
+            const int c = cnt[k];
+            cnt[k] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int u = lo + t; u <= hi; u += 256) {
+        if (stage == 0) {
+            const RowSpan s(u, K0, mid, K1, g.Nt);
+            for (int b = 0; b < s.blocks(); ++b) list[atomicAdd(&cnt[s.ktiles(b)], 1)] = ((uint32_t)u << 16) | (uint32_t)b;
+        } else {
+            const ColSpan s(u, K0, mid, K1, g.Mt);
+            for (int b = 0; b < s.blocks(); ++b) list[atomicAdd(&cnt[s.ktiles(b)], 1)] = ((uint32_t)u << 16) | (uint32_t)b;
+        }
+    }
+}
+
+// ------------------------------------------------------ propagation
+
+// Stage 1 of node (K0, mid, K1): block (row I, b) from the schedule computes,
+// for the (up to) four target tile columns J' = j0 .. jh,
 //   Y[I, J'] = sum_{J = sl .. min(sh, J')} E[I, J] P_A[J', J]^T.
-// P_A[J', J] is zero for J > J', so the block uses K = sl .. min(sh, j0 + 3).
+// P_A[J', J] is zero for J > J', so the block uses K = sl .. min(sh, jh).
 __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
                                                    float* __restrict__ Y, int64_t ldw, int64_t lda,
-                                                   int K0, int mid, int K1, int Nt, int I_lo)
+                                                   int K0, int mid, int K1, int Mt, int Nt,
+                                                   const uint32_t* __restrict__ list)
 {
     __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
-    // Heaviest blocks first: within a row the K range grows with the column
-    // block, so columns run from the last block down (a long block started
-    // last would leave the other CUs idle at the end of the launch).
-    const int I = I_lo + blockIdx.y;
-    const int sl = max(0, K0 - I), sh = min(Nt - 1, mid - 1 - I), th = min(Nt - 1, K1 - 1 - I);
-    const int j0 = sl + 4 * (int)(gridDim.x - 1 - blockIdx.x);
-    if (j0 > th) return;
-    const int jh = min(th, j0 + 3);
-    const int kb = 64 * sl, ke = 64 * (min(sh, jh) + 1);
+    const uint32_t e = list[blockIdx.x];
+    const int I = (int)(e >> 16), b = (int)(e & 0xffffu);
+    if (I < rows_lo(K0, Nt) || I > rows_hi(mid, Mt)) return;
+    const RowSpan s(I, K0, mid, K1, Nt);
+    const int j0 = s.sl + 4 * b;
+    if (j0 > s.th) return;
+    const int jh = min(s.th, j0 + 3);
+    const int kb = 64 * s.sl, ke = 64 * (min(s.sh, jh) + 1);
     const int64_t r0 = (int64_t)I * 64;
     Acc acc;
     acc_zero(acc);
@@ -295,23 +418,25 @@ __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, 
     block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
 }
 
-// Stage 2 of node (K0, mid, K1): for target tile column J (blockIdx.y + J_lo)
-// and the four target tile rows I' = i0 .. i0 + 3 of this block,
-//   Wt[I', J] -= sum_{I = max(0, K0 - J) .. min(I', mid - 1)} P_B[I', I] Y[I, J].
-// Only rows on target anti-diagonals (mid <= I' + J < K1) are written.
+// Stage 2 of node (K0, mid, K1): block (column J, b) from the schedule
+// updates the (up to) four target tile rows I' = i0 .. ih:
+//   Wt[I', J] -= sum_{I = slo .. min(I', mid - 1)} P_B[I', I] Y[I, J],
+// slo = max(0, K0 - J).  Only rows on target anti-diagonals
+// (mid <= I' + J < K1) are written.
 __global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
                                                    float* __restrict__ Wt, int64_t ldw, int64_t ldb,
-                                                   int K0, int mid, int K1, int Mt, int J_lo)
+                                                   int K0, int mid, int K1, int Mt, int Nt,
+                                                   const uint32_t* __restrict__ list)
 {
     __shared__ __align__(16) float lds[ColBlk::LDS_FLOATS];
-    // Heaviest blocks first: the K range grows with the target row block and
-    // the longest columns come last in J, so both orders are reversed.
-    const int J = J_lo + (int)(gridDim.y - 1 - blockIdx.y);
-    const int tl = max(0, mid - J), th = min(Mt - 1, K1 - 1 - J);
-    const int i0 = tl + 4 * (int)(gridDim.x - 1 - blockIdx.x);
-    if (i0 > th) return;
-    const int ih = min(th, i0 + 3);
-    const int kb = 64 * max(0, K0 - J), ke = 64 * (min(mid - 1, ih) + 1);
+    const uint32_t e = list[blockIdx.x];
+    const int J = (int)(e >> 16), b = (int)(e & 0xffffu);
+    if (J < cols_lo(mid, Mt) || J > cols_hi(K1, Nt)) return;
+    const ColSpan s(J, K0, mid, K1, Mt);
+    const int i0 = s.tl + 4 * b;
+    if (i0 > s.th) return;
+    const int ih = min(s.th, i0 + 3);
+    const int kb = 64 * s.slo, ke = 64 * (min(mid - 1, ih) + 1);
     const int64_t c0 = (int64_t)J * 64, rr = (int64_t)i0 * 64;
     Acc acc;
     acc_zero(acc);
@@ -341,8 +466,29 @@ namespace {
 struct SolvePlan {
     int64_t m, n, Mt, Nt, Mp, Np;
     bool pad_a, pad_b;
-    size_t off_wt, off_e, off_y, off_obj, off_pa, off_pb, total;
+    SchedGeom sg;
+    int64_t sched_entries;
+    size_t off_wt, off_e, off_y, off_obj, off_pa, off_pb, off_sched, total;
 };
+
+// Heap levels holding internal nodes, and the list offsets of k_sched.
+void plan_sched(SchedGeom& g, int64_t& entries, int Mt, int Nt)
+{
+    g.Mt = Mt;
+    g.Nt = Nt;
+    g.Kt = Mt + Nt - 1;
+    g.levels = 0;
+    while ((1 << g.levels) < g.Kt) ++g.levels;   // depth d holds a node of width >= 2 iff 2^d < Kt
+    const int64_t R = std::max(Mt, Nt);
+    int64_t off = 0;
+    for (int d = 0; d < kMaxDepth; ++d) {
+        const int64_t w = ceil_div(g.Kt, (int64_t)1 << d);
+        g.base[d] = off;
+        g.cap[d] = R * ceil_div(w, 4);
+        if (d < g.levels) off += ((int64_t)1 << d) * 2 * g.cap[d];
+    }
+    entries = off;
+}
 
 SolvePlan plan_solve(int64_t m, int64_t n)
 {
@@ -374,6 +520,9 @@ SolvePlan plan_solve(int64_t m, int64_t n)
         p.off_pb = off;
         off = align_up(off + sizeof(float) * (size_t)(p.Mp * p.Mp));
     }
+    plan_sched(p.sg, p.sched_entries, (int)p.Mt, (int)p.Nt);
+    p.off_sched = off;
+    off = align_up(off + sizeof(uint32_t) * (size_t)p.sched_entries);
     p.total = off;
     return p;
 }
@@ -386,6 +535,8 @@ dim3 copy_grid(int64_t R, int64_t C)
 struct SolveRun {
     LeafArgs leaf;
     float* Y;
+    const uint32_t* sched;
+    const SchedGeom* sg;
     int Mt, Nt;
     hipStream_t s;
     Prof* prof;
@@ -411,20 +562,22 @@ void enqueue_leaf(SolveRun& R, int K)
     launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(256), R.s, R.leaf);
 }
 
-void enqueue_prop(SolveRun& R, int K0, int mid, int K1)
+// Node (K0, mid, K1) at heap position (d, p): stage 1 over the tile rows
+// with source tiles, then stage 2 over the target tile columns, each over
+// the block list k_sched wrote for it.
+void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
 {
     const int Mt = R.Mt, Nt = R.Nt;
-    // stage 1 over tile rows with source tiles
-    const int I_lo = std::max(0, K0 - (Nt - 1));
-    const int I_hi = std::min(Mt - 1, mid - 1);
-    int span = 0;
+    const uint32_t* list1 = R.sched + R.sg->base[d] + (int64_t)(2 * p) * R.sg->cap[d];
+    const uint32_t* list2 = list1 + R.sg->cap[d];
+    const int I_lo = rows_lo(K0, Nt), I_hi = rows_hi(mid, Mt);
+    int64_t blocks = 0;
     double fl = 0.0, by = 0.0;
     for (int I = I_lo; I <= I_hi; ++I) {
-        const int sl = std::max(0, K0 - I), sh = std::min(Nt - 1, mid - 1 - I);
-        const int th = std::min(Nt - 1, K1 - 1 - I);
-        span = std::max(span, th - sl + 1);
+        const RowSpan sp(I, K0, mid, K1, Nt);
+        blocks += sp.blocks();
         if (R.prof) {
-            const double S = sh - sl + 1, T = th - sl + 1;
+            const double S = sp.sh - sp.sl + 1, T = sp.th - sp.sl + 1;
             const double pairs = S * (S + 1) / 2 + (T - S) * S;   // (J, J') with J <= J'
             fl += 2.0 * ((pairs - S) * kFull + S * kTriB);
             by += (S + T) * kTileB;                              // E read, Y written
@@ -436,29 +589,25 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1)
             if (Ia > Ib) continue;
             by += (std::min(Nt - 1, K1 - 1 - Ia) - J + 1) * kTileB;
         }
-    if (I_hi >= I_lo && span > 0) {
-        dim3 g((unsigned)ceil_div(span, 4), (unsigned)(I_hi - I_lo + 1));
-        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, g, dim3(256), R.s, (const float*)R.leaf.E,
-               R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt, I_lo);
-    }
-    // stage 2 over target tile columns
-    const int J_lo = std::max(0, mid - (Mt - 1));
-    const int J_hi = std::min(Nt - 1, K1 - 1);
-    span = 0;
+    if (blocks > 0)
+        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3((unsigned)blocks), dim3(256), R.s,
+               (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Mt, Nt, list1);
+
+    const int J_lo = cols_lo(mid, Mt), J_hi = cols_hi(K1, Nt);
+    blocks = 0;
     fl = by = 0.0;
     for (int J = J_lo; J <= J_hi; ++J) {
-        const int tl = std::max(0, mid - J), th = std::min(Mt - 1, K1 - 1 - J);
-        span = std::max(span, th - tl + 1);
+        const ColSpan sp(J, K0, mid, K1, Mt);
+        blocks += sp.blocks();
         if (R.prof) {
-            const int slo = std::max(0, K0 - J);
-            for (int Ip = tl; Ip <= th; ++Ip) {
+            for (int Ip = sp.tl; Ip <= sp.th; ++Ip) {
                 const int shi = std::min(mid - 1, Ip);
-                const double cnt = shi - slo + 1;
+                const double cnt = shi - sp.slo + 1;
                 const bool diag = Ip <= mid - 1;
                 fl += 2.0 * ((cnt - (diag ? 1 : 0)) * kFull + (diag ? kTriB : 0.0));
             }
-            by += (std::min(mid - 1, th) - slo + 1) * kTileB;   // Y read
-            by += 2.0 * (th - tl + 1) * kTileB;                 // W~ read and written
+            by += (std::min(mid - 1, sp.th) - sp.slo + 1) * kTileB;   // Y read
+            by += 2.0 * (sp.th - sp.tl + 1) * kTileB;                 // W~ read and written
         }
     }
     if (R.prof)   // distinct P_B blocks: for source row I, I' runs over [max(I, tl(J_hi)), th(first column using I)]
@@ -469,23 +618,21 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1)
             const int lo = std::max(I, std::max(0, mid - J_hi));
             if (hi >= lo) by += (hi - lo + 1) * kTileB;
         }
-    if (J_hi >= J_lo && span > 0) {
-        dim3 g((unsigned)ceil_div(span, 4), (unsigned)(J_hi - J_lo + 1));
-        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, g, dim3(256), R.s, (const float*)R.Y, R.leaf.PB,
-               R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, J_lo);
-    }
+    if (blocks > 0)
+        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3((unsigned)blocks), dim3(256), R.s,
+               (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, Nt, list2);
 }
 
-void solve_rec(SolveRun& R, int K0, int K1)
+void solve_rec(SolveRun& R, int K0, int K1, int d, int p)
 {
     if (K1 - K0 == 1) {
         enqueue_leaf(R, K0);
         return;
     }
     const int mid = (K0 + K1) / 2;
-    solve_rec(R, K0, mid);
-    enqueue_prop(R, K0, mid, K1);
-    solve_rec(R, mid, K1);
+    solve_rec(R, K0, mid, d + 1, 2 * p);
+    enqueue_prop(R, K0, mid, K1, d, p);
+    solve_rec(R, mid, K1, d + 1, 2 * p + 1);
 }
 
 }  // namespace
@@ -553,7 +700,13 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
                     : 0;
     R.Mt = (int)p.Mt;
     R.Nt = (int)p.Nt;
-    solve_rec(R, 0, R.Mt + R.Nt - 1);
+    R.sg = &p.sg;
+    uint32_t* sched = reinterpret_cast<uint32_t*>(w + p.off_sched);
+    R.sched = sched;
+    if (p.sg.levels > 0)
+        launch(prof, KK_SCHED, 0.0, 4.0 * (double)p.sched_entries, k_sched,
+               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u), dim3(256), s, p.sg, sched);
+    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0);
     if (launch_ok()) return -1;
     if (objective) {
         const double cnt = (double)(p.Mt * p.Nt);
