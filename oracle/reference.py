@@ -277,7 +277,8 @@ def implied_errors_p(W, V, PA, PB) -> np.ndarray:
 
 # ----------------------------------------------------------------- validator
 
-def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None) -> dict:
+def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None,
+             return_errors=False) -> dict:
     """Check that ``codes`` is a BaKron output for (W, A (x) B, grid), any size.
 
     For a sequence of rounding decisions, the value entry (i, j) is rounded
@@ -290,7 +291,9 @@ def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None)
 
     The factors are given either as L_A, L_B or as P_A, P_B.
     Returns counts: entries, mismatches, ties (allowed), bad (outside the
-    tie band or more than one step apart), max_step, min_margin.
+    tie band or more than one step apart), max_step, min_margin; with
+    ``return_errors`` also the implied errors as "E" and the boolean masks
+    "tie_mask" and "bad_mask".
     """
     W = np.asarray(W, np.float64)
     m, n = W.shape
@@ -313,7 +316,7 @@ def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None)
     mism = diff != 0
     ties = mism & (margin < tau) & (np.abs(diff) == 1)
     bad = mism & ~ties
-    return {
+    out = {
         "entries": int(m * n),
         "mismatches": int(mism.sum()),
         "ties": int(ties.sum()),
@@ -322,3 +325,16 @@ def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None)
         "min_margin": float(margin.min()) if m * n else float("inf"),
         "bad_index": [tuple(map(int, t)) for t in np.argwhere(bad)[:8]],
     }
+    if return_errors:
+        out["E"] = E
+        out["tie_mask"] = ties
+        out["bad_mask"] = bad
+    return out
+
+
+def dependency_cone(mask) -> np.ndarray:
+    """Entries (i', j') with some masked (i, j), i <= i' and j <= j': the
+    entries whose rounded-from value depends on a masked decision ([S]
+    derivation: entry (i, j) only updates entries to its bottom-right)."""
+    c = np.logical_or.accumulate(np.asarray(mask, bool), axis=0)
+    return np.logical_or.accumulate(c, axis=1)

@@ -119,14 +119,18 @@ def _check_solve(d, LA, PA, LB, PB, out, label):
     Vexp = s[:, None] * (codes.astype(np.float32) - z[:, None])
     assert np.array_equal(out["V"], Vexp.astype(np.float32)), label
     assert np.all(codes <= mq[:, None])
-    v = R.validate(d["W"], codes, s, z, mq, tau=TAU, PA=PA64, PB=PB64)
+    v = R.validate(d["W"], codes, s, z, mq, tau=TAU, PA=PA64, PB=PB64, return_errors=True)
+    ties = v.pop("tie_mask")
+    v.pop("bad_mask"), v.pop("E")
     c_or, V_or, E_or = O2.bakron_recursive(d["W"], PA64, PB64, s, z, mq)
     diff = int((codes != c_or).sum())
     print(f"{label}: {m}x{n} validator {v}, differing from oracle {diff}", flush=True)
     assert v["bad"] == 0 and v["max_step"] <= 1
     assert v["mismatches"] <= max(1, 1e-4 * m * n)
-    if v["mismatches"] == 0:
-        assert diff == 0
+    # the same codes as the oracle everywhere outside the dependency cones
+    # of the ties (where the two trajectories may part)
+    outside = ~R.dependency_cone(ties)
+    assert np.array_equal(codes[outside], c_or[outside])
     # raw errors: float32 accumulation error, in grid steps
     Eimp = R.implied_errors_p(d["W"], R._values(codes, s, z), PA64, PB64)
     err_steps = np.abs(out["err"] - Eimp) / s[:, None]

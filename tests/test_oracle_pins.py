@@ -286,3 +286,15 @@ def test_validator_from_p_matches_from_l():
     np.testing.assert_allclose(R.implied_errors_p(d["W"], V, fa["P"], fb["P"]), E, atol=1e-12)
     r = R.validate(d["W"], c, d["scale"], d["zero"], d["maxq"], PA=fa["P"], PB=fb["P"])
     assert r["mismatches"] == 0
+
+
+def test_dependency_cone_brute_force():
+    """dependency_cone(mask)[i', j'] is true iff some masked (i, j) has
+    i <= i' and j <= j' (checked entry by entry on random masks)."""
+    rng = np.random.default_rng(3)
+    for m, n, p in ((1, 1, 0.5), (5, 7, 0.05), (9, 4, 0.1), (6, 6, 0.0)):
+        mask = rng.random((m, n)) < p
+        c = R.dependency_cone(mask)
+        for i in range(m):
+            for j in range(n):
+                assert c[i, j] == bool(mask[: i + 1, : j + 1].any())

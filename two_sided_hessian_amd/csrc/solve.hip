@@ -444,6 +444,49 @@ __global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, 
     block_store<4, 1>(Wt + rr * ldw + c0, ldw, 64 * (ih - i0 + 1), 64, -1.f, 1.f, acc);
 }
 
+// Small nodes: the same two stages with one 64 x 64 target tile per
+// workgroup and one 32 x 32 quadrant per wave (operands straight from global
+// memory), so a node with few blocks still spreads over many CUs.
+// Stage 1: workgroup (x, y) computes Y[I, J'] for row I = rows_lo + y and
+// J' = th - x (the K extent grows with J': longest first).
+__global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E, const float* __restrict__ PA,
+                                                     float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                     int K0, int mid, int K1, int Nt)
+{
+    const int I = rows_lo(K0, Nt) + (int)blockIdx.y;
+    const RowSpan s(I, K0, mid, K1, Nt);
+    const int Jp = s.th - (int)blockIdx.x;
+    if (Jp < s.sl) return;
+    const int wave = threadIdx.x >> 6;
+    const int64_t r = (int64_t)I * 64 + 32 * (wave >> 1);
+    const int64_t c = (int64_t)Jp * 64 + 32 * (wave & 1);
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    wave_gemm32<RowK, RowK>(E + r * ldw, ldw, PA + c * lda, lda, 64 * s.sl, 64 * (min(s.sh, Jp) + 1), acc);
+    wave_store32(Y + r * ldw + c, ldw, 1.f, 0.f, acc);
+}
+
+// Stage 2: workgroup (x, y) updates Wt[I', J] for column J = cols_lo + y and
+// I' = th - x.
+__global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                     float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                     int K0, int mid, int K1, int Mt)
+{
+    const int J = cols_lo(mid, Mt) + (int)blockIdx.y;
+    const ColSpan s(J, K0, mid, K1, Mt);
+    const int Ip = s.th - (int)blockIdx.x;
+    if (Ip < s.tl) return;
+    const int wave = threadIdx.x >> 6;
+    const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1);
+    const int64_t c = (int64_t)J * 64 + 32 * (wave & 1);
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    wave_gemm32<RowK, KRow>(PB + r * ldb, ldb, Y + c, ldw, 64 * s.slo, 64 * (min(mid - 1, Ip) + 1), acc);
+    wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
+}
+
 __global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t count,
                                                     double* __restrict__ out)
 {
@@ -562,6 +605,13 @@ void enqueue_leaf(SolveRun& R, int K)
     launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(256), R.s, R.leaf);
 }
 
+// A stage with fewer 64 x 256 blocks than this runs one 64 x 64 tile per
+// workgroup instead (k_prop_rows_t / k_prop_cols_t).
+#ifndef BAKRON_BLOCK_LAUNCH_MIN
+#define BAKRON_BLOCK_LAUNCH_MIN 128
+#endif
+constexpr int64_t kBlockLaunchMin = BAKRON_BLOCK_LAUNCH_MIN;
+
 // Node (K0, mid, K1) at heap position (d, p): stage 1 over the tile rows
 // with source tiles, then stage 2 over the target tile columns, each over
 // the block list k_sched wrote for it.
@@ -572,10 +622,12 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
     const uint32_t* list2 = list1 + R.sg->cap[d];
     const int I_lo = rows_lo(K0, Nt), I_hi = rows_hi(mid, Mt);
     int64_t blocks = 0;
+    int span = 0;   // widest row, in target tiles
     double fl = 0.0, by = 0.0;
     for (int I = I_lo; I <= I_hi; ++I) {
         const RowSpan sp(I, K0, mid, K1, Nt);
         blocks += sp.blocks();
+        span = std::max(span, sp.th - sp.sl + 1);
         if (R.prof) {
             const double S = sp.sh - sp.sl + 1, T = sp.th - sp.sl + 1;
             const double pairs = S * (S + 1) / 2 + (T - S) * S;   // (J, J') with J <= J'
@@ -589,16 +641,21 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
             if (Ia > Ib) continue;
             by += (std::min(Nt - 1, K1 - 1 - Ia) - J + 1) * kTileB;
         }
-    if (blocks > 0)
+    if (blocks >= kBlockLaunchMin)
         launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3((unsigned)blocks), dim3(256), R.s,
                (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Mt, Nt, list1);
+    else if (blocks > 0)
+        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows_t, dim3((unsigned)span, (unsigned)(I_hi - I_lo + 1)),
+               dim3(256), R.s, (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt);
 
     const int J_lo = cols_lo(mid, Mt), J_hi = cols_hi(K1, Nt);
     blocks = 0;
+    span = 0;
     fl = by = 0.0;
     for (int J = J_lo; J <= J_hi; ++J) {
         const ColSpan sp(J, K0, mid, K1, Mt);
         blocks += sp.blocks();
+        span = std::max(span, sp.th - sp.tl + 1);
         if (R.prof) {
             for (int Ip = sp.tl; Ip <= sp.th; ++Ip) {
                 const int shi = std::min(mid - 1, Ip);
@@ -618,9 +675,12 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
             const int lo = std::max(I, std::max(0, mid - J_hi));
             if (hi >= lo) by += (hi - lo + 1) * kTileB;
         }
-    if (blocks > 0)
+    if (blocks >= kBlockLaunchMin)
         launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3((unsigned)blocks), dim3(256), R.s,
                (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, Nt, list2);
+    else if (blocks > 0)
+        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols_t, dim3((unsigned)span, (unsigned)(J_hi - J_lo + 1)),
+               dim3(256), R.s, (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt);
 }
 
 void solve_rec(SolveRun& R, int K0, int K1, int d, int p)
