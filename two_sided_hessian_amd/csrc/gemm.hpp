@@ -238,70 +238,6 @@ __device__ __forceinline__ void block_store(float* __restrict__ C, int64_t ldc, 
             }
 }
 
-// ------------------------------------------------ one wave, one 32 x 32 tile
-//
-// For launches with few output tiles: every wave is an independent GEMM on
-// a 32 x 32 output tile, with its MFMA operand fragments loaded straight
-// from global memory (no LDS, no barriers), so a launch keeps as many waves
-// busy as it has 32 x 32 tiles.  A wave's fp32 MFMA rate is the limit here,
-// not operand reuse.
-//
-// Operand pointers address element (0, 0) of the wave's tile:
-//   A: RowK  a[r * lda + k]   KRow  a[k * lda + r]   (r = output row)
-//   B: RowK  b[c * ldb + k]   KRow  b[k * ldb + c]   (c = output column)
-template <int LAYOUT>
-__device__ __forceinline__ f32x4 gfrag(const float* __restrict__ p, int64_t ld, int r, int k)
-{
-    if (LAYOUT == RowK) return *reinterpret_cast<const f32x4*>(p + (int64_t)r * ld + k);
-    f32x4 v;
-    v.x = p[(int64_t)(k + 0) * ld + r];
-    v.y = p[(int64_t)(k + 1) * ld + r];
-    v.z = p[(int64_t)(k + 2) * ld + r];
-    v.w = p[(int64_t)(k + 3) * ld + r];
-    return v;
-}
-
-// acc += A[0:32, kb:ke] B[kb:ke, 0:32]; ke - kb a multiple of 64.  The next
-// 64-deep chunk's fragments are in flight while the current one's 32 MFMAs
-// run.
-template <int ALAY, int BLAY>
-__device__ __forceinline__ void wave_gemm32(const float* __restrict__ A, int64_t lda,
-                                            const float* __restrict__ B, int64_t ldb, int kb, int ke,
-                                            f32x16& acc)
-{
-    const int lane = threadIdx.x & 63;
-    const int ml = lane & 31, k4 = 4 * (lane >> 5);
-    if (ke <= kb) return;
-    f32x4 fa[8], fb[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-        fa[g] = gfrag<ALAY>(A, lda, ml, kb + 8 * g + k4);
-        fb[g] = gfrag<BLAY>(B, ldb, ml, kb + 8 * g + k4);
-    }
-    for (int k = kb; k < ke; k += 64) {
-        f32x4 na[8], nb[8];
-        const bool more = k + 64 < ke;
-        if (more) {
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                na[g] = gfrag<ALAY>(A, lda, ml, k + 64 + 8 * g + k4);
-                nb[g] = gfrag<BLAY>(B, ldb, ml, k + 64 + 8 * g + k4);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < 8; ++g)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[g][q], fb[g][q], acc, 0, 0, 0);
-        if (more) {
-#pragma unroll
-            for (int g = 0; g < 8; ++g) {
-                fa[g] = na[g];
-                fb[g] = nb[g];
-            }
-        }
-    }
-}
-
 // C[r * ldc + c] = alpha * acc + beta * C over the wave's 32 x 32 tile,
 // only where r - c >= diag.  beta == 0 does not read C.
 __device__ __forceinline__ void wave_store32(float* __restrict__ C, int64_t ldc, float alpha, float beta,
@@ -320,6 +256,59 @@ __device__ __forceinline__ void wave_store32(float* __restrict__ C, int64_t ldc,
         const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row - col < diag) continue;
         C[(int64_t)row * ldc + col] = alpha * acc[r] + beta * old[r];
+    }
+}
+
+// ---------------------------------------- 64 x 64 block, 32 x 32 per wave
+//
+// For launches with few output tiles: a workgroup computes one 64 x 64
+// tile, wave w the 32 x 32 quadrant at rows 32 (w >> 1), columns 32 (w & 1),
+// so a launch keeps four waves busy per output tile.  Operands are staged
+// through LDS in coalesced kBK-deep chunks that the four waves share.
+constexpr int kLds64 = Operand<64, RowK>::FLOATS > Operand<64, KRow>::FLOATS ? 2 * Operand<64, RowK>::FLOATS
+                                                                               : 2 * Operand<64, KRow>::FLOATS;
+
+template <int ALAY, int BLAY>
+__device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_t lda,
+                                             const float* __restrict__ B, int64_t ldb, int k0, int k1,
+                                             float* lds, f32x16& acc)
+{
+    typedef Operand<64, ALAY> OA;
+    typedef Operand<64, BLAY> OB;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int ml = lane & 31;
+    const int ra = 32 * (wave >> 1) + ml, rb = 32 * (wave & 1) + ml;
+    float* sa = lds;
+    float* sb = lds + OA::FLOATS;
+    f32x4 pa[OA::PER_THREAD];
+    f32x4 pb[OB::PER_THREAD];
+    const int nchunk = (k1 - k0) / kBK;
+    if (nchunk <= 0) return;
+    OA::load(A, lda, 64, k0, pa);
+    OB::load(B, ldb, 64, k0, pb);
+    OA::store(sa, pa);
+    OB::store(sb, pb);
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+        const bool more = (c + 1) < nchunk;
+        if (more) {
+            OA::load(A, lda, 64, k0 + (c + 1) * kBK, pa);
+            OB::load(B, ldb, 64, k0 + (c + 1) * kBK, pb);
+        }
+#pragma unroll
+        for (int kc = 0; kc < kBK; kc += 8) {
+            const f32x4 a = OA::frag(sa, ra, kc);
+            const f32x4 b = OB::frag(sb, rb, kc);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
+        }
+        if (more) {
+            __syncthreads();
+            OA::store(sa, pa);
+            OB::store(sb, pb);
+            __syncthreads();
+        }
     }
 }
 

@@ -445,25 +445,27 @@ __global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, 
 }
 
 // Small nodes: the same two stages with one 64 x 64 target tile per
-// workgroup and one 32 x 32 quadrant per wave (operands straight from global
-// memory), so a node with few blocks still spreads over many CUs.
+// workgroup and one 32 x 32 quadrant per wave (block_gemm64), so a node with
+// few 64 x 256 blocks still spreads over many CUs.
 // Stage 1: workgroup (x, y) computes Y[I, J'] for row I = rows_lo + y and
 // J' = th - x (the K extent grows with J': longest first).
 __global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E, const float* __restrict__ PA,
                                                      float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                      int K0, int mid, int K1, int Nt)
 {
+    __shared__ __align__(16) float lds[kLds64];
     const int I = rows_lo(K0, Nt) + (int)blockIdx.y;
     const RowSpan s(I, K0, mid, K1, Nt);
     const int Jp = s.th - (int)blockIdx.x;
     if (Jp < s.sl) return;
     const int wave = threadIdx.x >> 6;
-    const int64_t r = (int64_t)I * 64 + 32 * (wave >> 1);
-    const int64_t c = (int64_t)Jp * 64 + 32 * (wave & 1);
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    wave_gemm32<RowK, RowK>(E + r * ldw, ldw, PA + c * lda, lda, 64 * s.sl, 64 * (min(s.sh, Jp) + 1), acc);
+    block_gemm64<RowK, RowK>(E + (int64_t)I * 64 * ldw, ldw, PA + (int64_t)Jp * 64 * lda, lda, 64 * s.sl,
+                             64 * (min(s.sh, Jp) + 1), lds, acc);
+    const int64_t r = (int64_t)I * 64 + 32 * (wave >> 1);
+    const int64_t c = (int64_t)Jp * 64 + 32 * (wave & 1);
     wave_store32(Y + r * ldw + c, ldw, 1.f, 0.f, acc);
 }
 
@@ -473,17 +475,19 @@ __global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y
                                                      float* __restrict__ Wt, int64_t ldw, int64_t ldb,
                                                      int K0, int mid, int K1, int Mt)
 {
+    __shared__ __align__(16) float lds[kLds64];
     const int J = cols_lo(mid, Mt) + (int)blockIdx.y;
     const ColSpan s(J, K0, mid, K1, Mt);
     const int Ip = s.th - (int)blockIdx.x;
     if (Ip < s.tl) return;
     const int wave = threadIdx.x >> 6;
-    const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1);
-    const int64_t c = (int64_t)J * 64 + 32 * (wave & 1);
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    wave_gemm32<RowK, KRow>(PB + r * ldb, ldb, Y + c, ldw, 64 * s.slo, 64 * (min(mid - 1, Ip) + 1), acc);
+    block_gemm64<RowK, KRow>(PB + (int64_t)Ip * 64 * ldb, ldb, Y + (int64_t)J * 64, ldw, 64 * s.slo,
+                             64 * (min(mid - 1, Ip) + 1), lds, acc);
+    const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1);
+    const int64_t c = (int64_t)J * 64 + 32 * (wave & 1);
     wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
 }
 
@@ -608,7 +612,7 @@ void enqueue_leaf(SolveRun& R, int K)
 // A stage with fewer 64 x 256 blocks than this runs one 64 x 64 tile per
 // workgroup instead (k_prop_rows_t / k_prop_cols_t).
 #ifndef BAKRON_BLOCK_LAUNCH_MIN
-#define BAKRON_BLOCK_LAUNCH_MIN 128
+#define BAKRON_BLOCK_LAUNCH_MIN 512
 #endif
 constexpr int64_t kBlockLaunchMin = BAKRON_BLOCK_LAUNCH_MIN;
 
@@ -645,8 +649,9 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
         launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3((unsigned)blocks), dim3(256), R.s,
                (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Mt, Nt, list1);
     else if (blocks > 0)
-        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows_t, dim3((unsigned)span, (unsigned)(I_hi - I_lo + 1)),
-               dim3(256), R.s, (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt);
+        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows_t,
+               dim3((unsigned)span, (unsigned)(I_hi - I_lo + 1)), dim3(256), R.s, (const float*)R.leaf.E, R.leaf.PA,
+               R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt);
 
     const int J_lo = cols_lo(mid, Mt), J_hi = cols_hi(K1, Nt);
     blocks = 0;
@@ -679,8 +684,9 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
         launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3((unsigned)blocks), dim3(256), R.s,
                (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, Nt, list2);
     else if (blocks > 0)
-        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols_t, dim3((unsigned)span, (unsigned)(J_hi - J_lo + 1)),
-               dim3(256), R.s, (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt);
+        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols_t,
+               dim3((unsigned)span, (unsigned)(J_hi - J_lo + 1)), dim3(256), R.s, (const float*)R.Y, R.leaf.PB,
+               R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt);
 }
 
 void solve_rec(SolveRun& R, int K0, int K1, int d, int p)
