@@ -123,7 +123,7 @@ const char* kernel_name(int kind)
 {
     static const char* const names[KK_COUNT] = {
         "k_copy_pad", "k_leaf", "k_prop_rows", "k_prop_cols", "k_obj_reduce", "k_f_prep",
-        "k_base_block", "k_f_panel", "k_f_syrk", "k_f_right", "k_f_left", "k_f_finish", "k_sched"};
+        "k_f_diag", "k_f_panel", "k_f_syrk", "k_f_right", "k_f_left", "k_f_finish", "k_sched"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 

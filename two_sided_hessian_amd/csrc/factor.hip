@@ -14,8 +14,8 @@
 //   L^-1 = [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]].
 // So: recurse on 2 (gives L22 and Li22 = L22^-1); L21 = Li22^T A21 (GEMM,
 // triangular left operand); A11 -= L21^T L21 (SYRK, lower blocks only);
-// recurse on 1; Li21 = -Li22 (L21 Li11) (two GEMMs).  64 x 64 diagonal blocks
-// are factored and inverted in LDS by one workgroup.  Total 2n^3/3 flops.
+// recurse on 1; Li21 = -Li22 (L21 Li11) (two GEMMs).  Diagonal blocks of 128
+// (or 64) are factored and inverted in LDS by one workgroup.
 //
 // Buffers: Pbuf starts as A_d (lower part used) and ends as Li; Lbuf
 // receives L.  Both are n x n with pitch ld.  The temporary T (n2 x n1) lives
@@ -68,118 +68,245 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
         }
 }
 
-// ------------------------------------------------- 64 x 64 diagonal block
-
-// Reverse Cholesky of the 64 x 64 block at offset o of Pbuf (lower part
-// read), then its inverse; writes L to Lbuf and L^-1 to Pbuf (zeros above the
-// diagonal).  A non-positive (or NaN) pivot at block row k records
-// info = o + k + 1 unless an earlier block already recorded one.
+// --------------------------------------------------- diagonal blocks
 //
-// One wave; lane i keeps row i of the (symmetric) working block in
-// registers, and every loop is unrolled so register indices are constants.
-// Elimination from the last row upward: at step k lane k publishes row k in
-// LDS, every lane reads it back with 16-byte broadcast loads, lane i (< k)
-// takes its multiplier S[i][k] / S[k][k] from its own register k (symmetry)
-// and updates its row.  The rows stay unscaled during the elimination; each
-// lane scales its own row once at the end, L[i][j] = S[i][j] / sqrt(S[i][i]).
-// Then the inverse X = L^-1 row by row from X L = I: lane i computes
-// X[i][j] = -(sum_{k=j+1..i} X[i][k] L[k][j]) / L[j][j] for j = i-1 .. 0, all
-// rows in parallel, reading column j of L from LDS.  Reciprocals and square
-// roots use the hardware approximations (about one ulp): the factor is
-// judged by its backward error, not by correct rounding.
-__global__ __launch_bounds__(64) void k_base_block(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
-                                                   int64_t ld, int64_t o, int32_t* __restrict__ info)
-{
-    __shared__ __align__(16) float sT[64 * 68];      // staging, then L^T (sT[j][k] = L[k][j])
-    __shared__ __align__(16) float sRow[64];         // the pivot row being broadcast
-    const int i = threadIdx.x;
-    {
-        // 64 independent coalesced loads (row u, column i), then the stores
-        float v[64];
-#pragma unroll
-        for (int u = 0; u < 64; ++u) v[u] = Pbuf[(o + u) * ld + o + i];
-#pragma unroll
-        for (int u = 0; u < 64; ++u) sT[u * 68 + i] = (i <= u) ? v[u] : 0.f;
-    }
-    __syncthreads();
-    float s[64];
-#pragma unroll
-    for (int j = 0; j < 64; ++j) s[j] = (j <= i) ? sT[i * 68 + j] : sT[j * 68 + i];
+// k_f_diag factors a whole diagonal block of 64 or 128 in one workgroup,
+// with the block and its inverse resident in LDS (2 x 128 x 132 floats):
+//   size 64:  base64 (reverse Cholesky and inverse) of the block;
+//   size 128: base64 of the trailing 64 (L22, Li22); L21 = Li22^T A21;
+//             A11 -= L21^T L21; base64 of A11 (L11, Li11);
+//             Li21 = -Li22 (L21 Li11)
+// -- the same recursion as the GEMM levels above it, with the four 64^3
+// products on the MFMA units straight from LDS.
 
+constexpr int kDP = 132;   // LDS pitch (floats) of the block and its inverse
+
+// base64: reverse Cholesky S = L^T L of the 64 x 64 block at S (pitch kDP,
+// lower part read), then X = L^-1; L overwrites S and X goes to X (both with
+// zeros above the diagonal).  256 threads: thread t owns row i = t / 4,
+// columns 16 (t % 4) .. + 15, in registers.
+//
+// Elimination from the last row up, on unscaled rows: at step k every row
+// i < k takes S[i][j] -= (S[k][i] / S[k][k]) S[k][j]; row k is read from a
+// double-buffered LDS row that its owners published at the end of the
+// previous step, so a step costs one barrier.  At the end each row is scaled
+// once, L[i][j] = S[i][j] / sqrt(S[i][i]) (S[i][i] taken when row i was the
+// pivot).  The inverse solves L X = I by rows, forward: with
+// R[i] = L[i][i] X[i], R[i] = e_i - sum_{k<i} (L[i][k] / L[k][k]) R[k], the
+// same one-row-per-step broadcast.  Reciprocals and square roots use the
+// hardware approximations (about one ulp): the factor is judged by its
+// backward error, not by correct rounding.
+//
+// Returns the block row of the first non-positive (or NaN) pivot met, or -1.
+__device__ __forceinline__ int base64(float* __restrict__ S, float* __restrict__ X, float* __restrict__ rowbuf)
+{
+    const int t = threadIdx.x;
+    const int i = t >> 2, c0 = 16 * (t & 3);
+    float s[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(S + i * kDP + c0 + 4 * u);
+        s[4 * u + 0] = v.x;
+        s[4 * u + 1] = v.y;
+        s[4 * u + 2] = v.z;
+        s[4 * u + 3] = v.w;
+    }
+    if (i == 63)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<f32x4*>(rowbuf + 64 + c0 + 4 * u) =
+                f32x4{s[4 * u], s[4 * u + 1], s[4 * u + 2], s[4 * u + 3]};
+    __syncthreads();
     int fail = -1;
-    float my_rs = 0.f;
+    float mypiv = 1.f;
 #pragma unroll
     for (int k = 63; k >= 0; --k) {
-        if (i == k) {
+        const float* rk = rowbuf + 64 * (k & 1);
+        const float piv = rk[k];
+        const float ski = rk[i];                          // S[k][i] = S[i][k]
+        f32x4 r[4];
 #pragma unroll
-            for (int q = 0; q <= k / 4; ++q) {
-                f32x4 v;
-                v.x = s[4 * q + 0];
-                v.y = s[4 * q + 1];
-                v.z = s[4 * q + 2];
-                v.w = s[4 * q + 3];
-                *reinterpret_cast<f32x4*>(sRow + 4 * q) = v;
-            }
-        }
-        __syncthreads();
-        const float piv = sRow[k];
+        for (int u = 0; u < 4; ++u) r[u] = *reinterpret_cast<const f32x4*>(rk + c0 + 4 * u);
         if (!(piv > 0.f) && fail < 0) fail = k;
-        const float rs = __builtin_amdgcn_rsqf(piv);          // 1 / sqrt(piv)
-        my_rs = (i == k) ? rs : my_rs;
-        const float mul = (i < k) ? s[k] * (rs * rs) : 0.f;    // S[i][k] / S[k][k]
+        if (i == k) mypiv = piv;
+        const float mul = (i < k) ? ski * __builtin_amdgcn_rcpf(piv) : 0.f;
 #pragma unroll
-        for (int q = 0; 4 * q < k; ++q) {
-            const f32x4 r = *reinterpret_cast<const f32x4*>(sRow + 4 * q);
-            if (4 * q + 0 < k) s[4 * q + 0] = fmaf(-mul, r.x, s[4 * q + 0]);
-            if (4 * q + 1 < k) s[4 * q + 1] = fmaf(-mul, r.y, s[4 * q + 1]);
-            if (4 * q + 2 < k) s[4 * q + 2] = fmaf(-mul, r.z, s[4 * q + 2]);
-            if (4 * q + 3 < k) s[4 * q + 3] = fmaf(-mul, r.w, s[4 * q + 3]);
+        for (int u = 0; u < 4; ++u) {
+            s[4 * u + 0] = fmaf(-mul, r[u].x, s[4 * u + 0]);
+            s[4 * u + 1] = fmaf(-mul, r[u].y, s[4 * u + 1]);
+            s[4 * u + 2] = fmaf(-mul, r[u].z, s[4 * u + 2]);
+            s[4 * u + 3] = fmaf(-mul, r[u].w, s[4 * u + 3]);
         }
-        __syncthreads();     // sRow is rewritten by the next step
+        if (k > 0 && i == k - 1)
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<f32x4*>(rowbuf + 64 * ((k - 1) & 1) + c0 + 4 * u) =
+                    f32x4{s[4 * u], s[4 * u + 1], s[4 * u + 2], s[4 * u + 3]};
+        __syncthreads();
     }
+    const float rs = __builtin_amdgcn_rsqf(mypiv);
 #pragma unroll
-    for (int j = 0; j < 64; ++j) s[j] = (j <= i) ? s[j] * my_rs : 0.f;
-    // lane i now holds row i of L (zeros above the diagonal); publish L^T
+    for (int u = 0; u < 4; ++u) {
+        f32x4 v;
+        v.x = (c0 + 4 * u + 0 <= i) ? s[4 * u + 0] * rs : 0.f;
+        v.y = (c0 + 4 * u + 1 <= i) ? s[4 * u + 1] * rs : 0.f;
+        v.z = (c0 + 4 * u + 2 <= i) ? s[4 * u + 2] * rs : 0.f;
+        v.w = (c0 + 4 * u + 3 <= i) ? s[4 * u + 3] * rs : 0.f;
+        *reinterpret_cast<f32x4*>(S + i * kDP + c0 + 4 * u) = v;
+    }
+    // R = I; row 0 published
+    float r[16];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) sT[j * 68 + i] = s[j];
+    for (int c = 0; c < 16; ++c) r[c] = (c0 + c == i) ? 1.f : 0.f;
+    if (i == 0)
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            *reinterpret_cast<f32x4*>(rowbuf + c0 + 4 * u) = f32x4{r[4 * u], r[4 * u + 1], r[4 * u + 2], r[4 * u + 3]};
     __syncthreads();
-    float x[64];
 #pragma unroll
-    for (int j = 0; j < 64; ++j) x[j] = (j == i) ? __builtin_amdgcn_rcpf(s[j]) : 0.f;
+    for (int k = 0; k < 63; ++k) {
+        const float* rk = rowbuf + 64 * (k & 1);
+        f32x4 v[4];
 #pragma unroll
-    for (int j = 62; j >= 0; --j) {
-        const f32x4* col = reinterpret_cast<const f32x4*>(sT + j * 68);
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(rk + c0 + 4 * u);
+        const float coef = (i > k) ? S[i * kDP + k] * __builtin_amdgcn_rcpf(S[k * kDP + k]) : 0.f;
 #pragma unroll
-        for (int q = (j + 1) / 4; q < 16; ++q) {
-            const f32x4 c = col[q];
-            if (4 * q + 0 > j) a0 = fmaf(x[4 * q + 0], c.x, a0);
-            if (4 * q + 1 > j) a1 = fmaf(x[4 * q + 1], c.y, a1);
-            if (4 * q + 2 > j) a2 = fmaf(x[4 * q + 2], c.z, a2);
-            if (4 * q + 3 > j) a3 = fmaf(x[4 * q + 3], c.w, a3);
+        for (int u = 0; u < 4; ++u) {
+            r[4 * u + 0] = fmaf(-coef, v[u].x, r[4 * u + 0]);
+            r[4 * u + 1] = fmaf(-coef, v[u].y, r[4 * u + 1]);
+            r[4 * u + 2] = fmaf(-coef, v[u].z, r[4 * u + 2]);
+            r[4 * u + 3] = fmaf(-coef, v[u].w, r[4 * u + 3]);
         }
-        const float v = -((a0 + a1) + (a2 + a3)) * __builtin_amdgcn_rcpf(sT[j * 68 + j]);
-        x[j] = (j < i) ? v : x[j];
-    }
-    // coalesced stores of L (from L^T in LDS) and of X (via LDS)
-    for (int idx = i; idx < 64 * 64; idx += 64) {
-        const int r = idx >> 6, c = idx & 63;
-        Lbuf[(o + r) * ld + o + c] = sT[c * 68 + r];
-    }
-    __syncthreads();
+        if (i == k + 1)
 #pragma unroll
-    for (int j = 0; j < 64; ++j) sT[i * 68 + j] = x[j];
-    __syncthreads();
-    for (int idx = i; idx < 64 * 64; idx += 64) {
-        const int r = idx >> 6, c = idx & 63;
-        Pbuf[(o + r) * ld + o + c] = sT[r * 68 + c];
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<f32x4*>(rowbuf + 64 * ((k + 1) & 1) + c0 + 4 * u) =
+                    f32x4{r[4 * u], r[4 * u + 1], r[4 * u + 2], r[4 * u + 3]};
+        __syncthreads();
     }
-    if (i == 0 && fail >= 0) atomicCAS(info, 0, (int32_t)(o + fail + 1));
+    const float inv = __builtin_amdgcn_rcpf(S[i * kDP + i]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4 v;
+        v.x = (c0 + 4 * u + 0 <= i) ? r[4 * u + 0] * inv : 0.f;
+        v.y = (c0 + 4 * u + 1 <= i) ? r[4 * u + 1] * inv : 0.f;
+        v.z = (c0 + 4 * u + 2 <= i) ? r[4 * u + 2] * inv : 0.f;
+        v.w = (c0 + 4 * u + 3 <= i) ? r[4 * u + 3] * inv : 0.f;
+        *reinterpret_cast<f32x4*>(X + i * kDP + c0 + 4 * u) = v;
+    }
+    __syncthreads();
+    return fail;
+}
+
+// MFMA fragment of LDS operand element (r, k .. k + 3) (pitch kDP):
+// RowK p[r * kDP + k], KRow p[k * kDP + r].
+template <int LAYOUT>
+__device__ __forceinline__ f32x4 ldsfrag(const float* p, int r, int k)
+{
+    if (LAYOUT == RowK) return *reinterpret_cast<const f32x4*>(p + r * kDP + k);
+    return f32x4{p[k * kDP + r], p[(k + 1) * kDP + r], p[(k + 2) * kDP + r], p[(k + 3) * kDP + r]};
+}
+
+// 64 x 64 x 64 product from LDS: wave w returns the 32 x 32 quadrant at rows
+// 32 (w >> 1), columns 32 (w & 1) of A B, with A(r, k) and B(k, c) addressed
+// as ldsfrag's (r, k) and (c, k).
+template <int ALAY, int BLAY>
+__device__ __forceinline__ f32x16 lds_mm64(const float* A, const float* B)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ml = lane & 31, k4 = 4 * (lane >> 5);
+    const int ra = 32 * (wave >> 1) + ml, rb = 32 * (wave & 1) + ml;
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+#pragma unroll
+    for (int kc = 0; kc < 64; kc += 8) {
+        const f32x4 a = ldsfrag<ALAY>(A, ra, kc + k4);
+        const f32x4 b = ldsfrag<BLAY>(B, rb, kc + k4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
+    }
+    return acc;
+}
+
+// C (64 x 64 in LDS) = alpha * acc + beta * C over this wave's quadrant.
+__device__ __forceinline__ void lds_put64(float* C, const f32x16& acc, float alpha, float beta)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = 32 * (wave & 1) + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int row = 32 * (wave >> 1) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        float* p = C + row * kDP + col;
+        *p = alpha * acc[r] + (beta != 0.f ? beta * *p : 0.f);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
+                                                int64_t o, int nb, int32_t* __restrict__ info)
+{
+    __shared__ __align__(16) float sA[128 * kDP];   // the block, then L
+    __shared__ __align__(16) float sX[128 * kDP];   // L^-1
+    __shared__ __align__(16) float rowbuf[128];
+    const int t = threadIdx.x;
+    const int nf4 = nb / 4;
+    for (int f = t; f < nb * nf4; f += 256) {
+        const int r = f / nf4, c = 4 * (f % nf4);
+        *reinterpret_cast<f32x4*>(sA + r * kDP + c) =
+            *reinterpret_cast<const f32x4*>(Pbuf + (o + r) * ld + o + c);
+    }
+    __syncthreads();
+    // pass 1 (size 128 only): trailing half and the products it feeds;
+    // pass 0: the leading half (or the whole size-64 block) and, for 128,
+    // the off-diagonal block of the inverse.  One inlined copy of base64.
+    int fail[2] = {-1, -1};
+    float* A21 = sA + 64 * kDP;
+    float* X22 = sX + 64 * kDP + 64;
+    for (int h = (nb == 128) ? 1 : 0; h >= 0; --h) {
+        fail[h] = base64(sA + h * (64 * kDP + 64), sX + h * (64 * kDP + 64), rowbuf);
+        if (nb != 128) break;
+        if (h == 1) {
+            f32x16 acc = lds_mm64<KRow, KRow>(X22, A21);          // L21 = Li22^T A21
+            __syncthreads();
+            lds_put64(A21, acc, 1.f, 0.f);
+            __syncthreads();
+            acc = lds_mm64<KRow, KRow>(A21, A21);                 // A11 -= L21^T L21
+            lds_put64(sA, acc, -1.f, 1.f);
+            __syncthreads();
+        } else {
+            f32x16 acc = lds_mm64<RowK, KRow>(A21, sX);           // T = L21 Li11 (into X's upper block)
+            lds_put64(sX + 64, acc, 1.f, 0.f);
+            __syncthreads();
+            acc = lds_mm64<RowK, KRow>(X22, sX + 64);             // Li21 = -Li22 T
+            lds_put64(sX + 64 * kDP, acc, -1.f, 0.f);
+            __syncthreads();
+        }
+    }
+    for (int f = t; f < nb * nf4; f += 256) {
+        const int r = f / nf4, c = 4 * (f % nf4);
+        f32x4 l = *reinterpret_cast<const f32x4*>(sA + r * kDP + c);
+        f32x4 x = *reinterpret_cast<const f32x4*>(sX + r * kDP + c);
+        if (c + 0 > r) l.x = x.x = 0.f;
+        if (c + 1 > r) l.y = x.y = 0.f;
+        if (c + 2 > r) l.z = x.z = 0.f;
+        if (c + 3 > r) l.w = x.w = 0.f;
+        *reinterpret_cast<f32x4*>(Lbuf + (o + r) * ld + o + c) = l;
+        *reinterpret_cast<f32x4*>(Pbuf + (o + r) * ld + o + c) = x;
+    }
+    if (t == 0) {   // the trailing half is factored first: its failure is met first
+        if (fail[1] >= 0) atomicCAS(info, 0, (int32_t)(o + 64 + fail[1] + 1));
+        if (fail[0] >= 0) atomicCAS(info, 0, (int32_t)(o + fail[0] + 1));
+    }
 }
 
 // ------------------------------------------------------ recursive GEMMs
 
 constexpr int FBM = 128, FBN = 128;   // 128 x 128 output blocks
+// A level with fewer 128 x 128 blocks than this uses 64 x 64 tiles (k_f_tile).
+#ifndef BAKRON_FACTOR_BLOCK_MIN
+#define BAKRON_FACTOR_BLOCK_MIN 1024
+#endif
+constexpr int64_t kFactorBlockMin = BAKRON_FACTOR_BLOCK_MIN;
 
 // L21 = Li22^T A21 : (n2 x n1); Li22^T is upper triangular, so output rows
 // from r0 need K in [r0, n2).
@@ -245,6 +372,50 @@ __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, flo
     block_gemm<2, 2, RowK, KRow>(Pbuf + (o2 + r0) * ld + o2, ld, n2 - r0,
                                  T + c0, n1, n1 - c0, 0, kend, lds, acc);
     block_store<2, 2>(Pbuf + (o2 + r0) * ld + o1 + c0, ld, n2 - r0, n1 - c0, -1.f, 0.f, acc);
+}
+
+// The same four products with one 64 x 64 output tile per workgroup (one
+// 32 x 32 quadrant per wave) for the levels whose 128 x 128 grids are too
+// small to fill the GPU.  MODE: 0 panel, 1 syrk, 2 right, 3 left.
+template <int MODE>
+__global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
+                                                float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
+                                                int n1, int n2)
+{
+    __shared__ __align__(16) float lds[kLds64];
+    int r0, c0;
+    if (MODE == 1) {   // linear index -> lower-triangular tile (br >= bc)
+        const int q = blockIdx.x;
+        int br = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+        while ((br + 1) * (br + 2) / 2 <= q) ++br;
+        while (br * (br + 1) / 2 > q) --br;
+        r0 = 64 * br;
+        c0 = 64 * (q - br * (br + 1) / 2);
+    } else if (MODE == 3) {   // heaviest (largest K) first
+        r0 = 64 * (int)(gridDim.y - 1 - blockIdx.y);
+        c0 = 64 * (int)blockIdx.x;
+    } else {
+        r0 = 64 * (int)blockIdx.y;
+        c0 = 64 * (int)blockIdx.x;
+    }
+    const int wave = threadIdx.x >> 6;
+    const int qr = 32 * (wave >> 1), qc = 32 * (wave & 1);
+    f32x16 acc;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+    if (MODE == 0) {          // L21 = Li22^T A21, K in [r0, n2)
+        block_gemm64<KRow, KRow>(Pbuf + o2 * ld + o2 + r0, ld, Pbuf + o2 * ld + o1 + c0, ld, r0, n2, lds, acc);
+        wave_store32(Lbuf + (o2 + r0 + qr) * ld + o1 + c0 + qc, ld, 1.f, 0.f, acc);
+    } else if (MODE == 1) {   // A11 -= L21^T L21, lower part
+        block_gemm64<KRow, KRow>(Lbuf + o2 * ld + o1 + r0, ld, Lbuf + o2 * ld + o1 + c0, ld, 0, n2, lds, acc);
+        wave_store32(Pbuf + (o1 + r0 + qr) * ld + o1 + c0 + qc, ld, -1.f, 1.f, acc, (c0 + qc) - (r0 + qr));
+    } else if (MODE == 2) {   // T = L21 Li11, K in [c0, n1)
+        block_gemm64<RowK, KRow>(Lbuf + (o2 + r0) * ld + o1, ld, Pbuf + o1 * ld + o1 + c0, ld, c0, n1, lds, acc);
+        wave_store32(T + (int64_t)(r0 + qr) * n1 + c0 + qc, n1, 1.f, 0.f, acc);
+    } else {                  // Li21 = -Li22 T, K in [0, r0 + 64)
+        block_gemm64<RowK, KRow>(Pbuf + (o2 + r0) * ld + o2, ld, T + c0, n1, 0, r0 + 64, lds, acc);
+        wave_store32(Pbuf + (o2 + r0 + qr) * ld + o1 + c0 + qc, ld, -1.f, 0.f, acc);
+    }
 }
 
 // P = Li diag(L) on and below the diagonal, zeros above, for L and P; when
@@ -324,9 +495,11 @@ int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
 
 int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
 {
-    if (nsz == kTile) {
-        launch(R.prof, KK_F_BASE, 2.0 * 2.0 * 64.0 * 64.0 * 64.0 / 6.0, 4.0 * (tri(64) + 2 * 64 * 64),
-               k_base_block, dim3(1), dim3(64), R.s, R.Lbuf, R.Pbuf, R.ld, o, R.info);
+    if (nsz <= 2 * kTile) {
+        // factor (b^3 / 3 multiply-adds) and inverse (b^3 / 6) of the block
+        const double b = (double)nsz;
+        launch(R.prof, KK_F_BASE, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
+               R.Lbuf, R.Pbuf, R.ld, o, (int)nsz, R.info);
         return launch_ok();
     }
     const int64_t nt = nsz / kTile;
@@ -335,24 +508,45 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     const int64_t o1 = o, o2 = o + n1;
     const double d1 = n1, d2 = n2;
     if (factor_rec(R, o2, n2)) return -1;
+    // 128 x 128 blocks while they fill the GPU, else 64 x 64 tiles
+    const bool tiles = ceil_div(n1, FBN) * ceil_div(n2, FBM) < kFactorBlockMin;
+    const dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
+    const dim3 gt((unsigned)(n1 / kTile), (unsigned)(n2 / kTile));
+    const double fl_panel = 2.0 * d1 * tri(d2), by_panel = 4.0 * (tri(d2) + 2.0 * d2 * d1);
+    if (tiles)
+        launch(R.prof, KK_F_PANEL, fl_panel, by_panel, k_f_tile<0>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf,
+               R.T, R.ld, o1, o2, n1, n2);
+    else
+        launch(R.prof, KK_F_PANEL, fl_panel, by_panel, k_f_panel, g, dim3(256), R.s, R.Pbuf, R.Lbuf, R.ld, o1, o2,
+               n1, n2);
     {
-        dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
-        launch(R.prof, KK_F_PANEL, 2.0 * d1 * tri(d2), 4.0 * (tri(d2) + 2.0 * d2 * d1), k_f_panel, g, dim3(256),
-               R.s, R.Pbuf, R.Lbuf, R.ld, o1, o2, n1, n2);
-    }
-    {
-        const int64_t tb = ceil_div(n1, FBM);
-        launch(R.prof, KK_F_SYRK, 2.0 * d2 * tri(d1), 4.0 * (d2 * d1 + 2.0 * tri(d1)), k_f_syrk,
-               dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s, R.Lbuf, R.Pbuf, R.ld, o1, o2, n1, n2);
+        const double fl = 2.0 * d2 * tri(d1), by = 4.0 * (d2 * d1 + 2.0 * tri(d1));
+        if (tiles) {
+            const int64_t tb = n1 / kTile;
+            launch(R.prof, KK_F_SYRK, fl, by, k_f_tile<1>, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s,
+                   R.Lbuf, R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
+        } else {
+            const int64_t tb = ceil_div(n1, FBM);
+            launch(R.prof, KK_F_SYRK, fl, by, k_f_syrk, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s,
+                   (const float*)R.Lbuf, R.Pbuf, R.ld, o1, o2, n1, n2);
+        }
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, o1, n1)) return -1;
     {
-        dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
-        launch(R.prof, KK_F_RIGHT, 2.0 * d2 * tri(d1), 4.0 * (2.0 * d2 * d1 + tri(d1)), k_f_right, g, dim3(256),
-               R.s, R.Lbuf, R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
-        launch(R.prof, KK_F_LEFT, 2.0 * d1 * tri(d2), 4.0 * (2.0 * d2 * d1 + tri(d2)), k_f_left, g, dim3(256),
-               R.s, R.T, R.Pbuf, R.ld, o1, o2, n1, n2);
+        const double fr = 2.0 * d2 * tri(d1), br = 4.0 * (2.0 * d2 * d1 + tri(d1));
+        const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
+        if (tiles) {
+            launch(R.prof, KK_F_RIGHT, fr, br, k_f_tile<2>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
+                   R.ld, o1, o2, n1, n2);
+            launch(R.prof, KK_F_LEFT, fl, bl, k_f_tile<3>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
+                   R.ld, o1, o2, n1, n2);
+        } else {
+            launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, g, dim3(256), R.s, (const float*)R.Lbuf,
+                   (const float*)R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
+            launch(R.prof, KK_F_LEFT, fl, bl, k_f_left, g, dim3(256), R.s, (const float*)R.T, R.Pbuf, R.ld, o1, o2,
+                   n1, n2);
+        }
     }
     return launch_ok();
 }

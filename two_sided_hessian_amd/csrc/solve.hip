@@ -145,39 +145,58 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
     const float sc = row_ok ? g.scale[grow] : 1.f;
     const float zc = row_ok ? g.zero[grow] : 0.f;
     const float mq = row_ok ? (float)g.maxq[grow] : 0.f;
+    const float sinv = 1.f / sc;   // correctly rounded
     __syncthreads();
 
     float pu = 0.f, psp = 0.f;                      // for the current column
+    f32x4 fr[4], pr[4], ur[4];                      // partial-sum operands (loop-carried)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) fr[q] = pr[q] = ur[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float wcur = (a == 0) ? sW[0] : 0.f;
     const int am1 = a > 0 ? a - 1 : 0;
     for (int d = 0; d < 127; ++d) {
         const int b = d - a, bn = b + 1;
         const bool act = (unsigned)b < 64u;
         const bool actn = (unsigned)bn < 64u;
-        // Every LDS read is unconditional (clamped, in-bounds indices; the
-        // results are masked below) so the fresh value, read first, is the
-        // only one the critical path waits for.
+        // These three reads are unconditional (clamped, in-bounds indices;
+        // the results are masked below) and issued first, so the fresh value
+        // is the only one the critical path waits for.
         const int bc = min(max(b, 0), 63), bnc = min(max(bn, 0), 63);
         const float fresh = sUT[bc * kLP + am1];       // U[a-1][b]
         const float pa_sub = sPA[bnc * kLP + bc];     // P_A[b+1][b]
         const float wnext = sW[a * 64 + bnc];
         __builtin_amdgcn_sched_barrier(0);            // keep those three reads first
-        f32x4 fr[4], pr[4], ur[4];
-        {
+        // Partial-sum operands, read only where they can be nonzero (LDS
+        // bandwidth is the leaf's limit): for the next column of an active
+        // row, e[a][c] is zero from c = b on and U[r][bn] enters only for
+        // r < a - 1, so a lane whose 16-wide segment lies past that reads
+        // nothing (its registers keep older values) and its sum is taken as 0.
+        const bool need_pu = actn && 16 * sg < b;
+        const bool need_ps = actn && 16 * sg < a - 1;
+        if (need_pu) {
             const f32x4* F4 = reinterpret_cast<const f32x4*>(sF + a * kLP + 16 * sg);
             const f32x4* P4 = reinterpret_cast<const f32x4*>(sPA + bnc * kLP + 16 * sg);
-            const f32x4* U4 = reinterpret_cast<const f32x4*>(sUT + bnc * kLP + 16 * sg);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 fr[q] = F4[q];
                 pr[q] = P4[q];
-                ur[q] = U4[q];
             }
+        }
+        if (need_ps) {
+            const f32x4* U4 = reinterpret_cast<const f32x4*>(sUT + bnc * kLP + 16 * sg);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ur[q] = U4[q];
         }
         // critical path: this step's entry
         const float ps = psp + pbm1 * fresh;          // pbm1 == 0 on row 0
         const float w = wcur - pu - ps;
-        const float x = w / sc + zc;
+        // w / sc correctly rounded (Markstein: with y = RN(1/sc), q0 = RN(w y)
+        // is within an ulp, the remainder w - sc q0 is exact under fma, and
+        // RN(q0 + r y) is RN(w / sc)); then x = RN(q + zc) as in the oracle.
+        float q0 = w * sinv;
+        const float rem = fmaf(-q0, sc, w);
+        q0 = fmaf(rem, sinv, q0);
+        const float x = q0 + zc;
         const float c = fminf(fmaxf(rintf(x), 0.f), mq);
         const float v = sc * (c - zc);
         const bool ok = act && row_ok && (c0 + b) < g.n;
@@ -201,8 +220,8 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
             u2 = fmaf(pbz[4 * q + 2], ur[q].z, u2);
             u3 = fmaf(pbz[4 * q + 3], ur[q].w, u3);
         }
-        const float pun = quad_sum((s0 + s1) + (s2 + s3));
-        const float psn = quad_sum((u0 + u1) + (u2 + u3));
+        const float pun = quad_sum(need_pu ? (s0 + s1) + (s2 + s3) : 0.f);
+        const float psn = quad_sum(need_ps ? (u0 + u1) + (u2 + u3) : 0.f);
         if (actn) {
             pu = pun + e * pa_sub;
             psp = psn;
