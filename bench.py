@@ -46,7 +46,12 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=3072,
                     help="edge of the leading block the oracle baseline solves (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel roofline pass")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: only --gpus 1 is supported; the BaKron solve of one matrix runs on one GPU "
@@ -85,8 +90,23 @@ def main():
         fork.record(stream)
         sA.wait_event(fork)
         sB.wait_event(fork)
-        B.factor(T["A"], 0.01, out=fa, ws=ws_fa, stream=sA, profile=profile)
-        B.factor(T["B"], 0.01, out=fb, ws=ws_fb, stream=sB, profile=profile)
+        if profile is None:
+            B.factor(T["A"], 0.01, out=fa, ws=ws_fa, stream=sA)
+            B.factor(T["B"], 0.01, out=fb, ws=ws_fb, stream=sB)
+        else:
+            # the profiled entry points drain their stream before returning:
+            # one host thread per factor keeps the two running concurrently
+            import threading
+            pa, pb = [], []
+            th = [threading.Thread(target=B.factor, args=(T["A"], 0.01),
+                                   kwargs=dict(out=fa, ws=ws_fa, stream=sA, profile=pa)),
+                  threading.Thread(target=B.factor, args=(T["B"], 0.01),
+                                   kwargs=dict(out=fb, ws=ws_fb, stream=sB, profile=pb))]
+            for x in th:
+                x.start()
+            for x in th:
+                x.join()
+            profile.extend(pa + pb)
         joinA.record(sA)
         joinB.record(sB)
         stream.wait_event(joinA)
@@ -126,7 +146,7 @@ def main():
     alg_factor = 2.0 * (float(m) ** 3 + float(n) ** 3) / 3.0
     solve_s = float(np.median(solve_ms)) / 1e3
 
-    roofline = None
+    roofline = roofline_mfma = None
     kernels = None
     if not args.no_profile:
         prof = []
@@ -142,20 +162,12 @@ def main():
                        "alg_tflops": round(v["alg_flops"] / (v["total_ms"] * 1e-3) / 1e12, 3) if v["total_ms"] > 0 else None,
                        "alg_gbs": round(v["alg_bytes"] / (v["total_ms"] * 1e-3) / 1e9, 1) if v["total_ms"] > 0 else None}
                    for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"])}
+        traffic = load_traffic(spec.name)
         dom = max(agg.items(), key=lambda kv: kv[1]["total_ms"])
-        name, v = dom
-        mfma = name in ("k_prop_rows", "k_prop_cols", "k_f_panel", "k_f_syrk", "k_f_right", "k_f_left")
-        secs = v["total_ms"] * 1e-3
-        if mfma:
-            ach = v["alg_flops"] / secs / 1e12
-            roofline = {"kernel": name, "bound": "mfma", "achieved": round(ach, 3), "peak": PEAK_FP32_MFMA_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(ach / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
-                        "launches": v["launches"], "avg_launch_us": round(1e6 * secs / v["launches"], 3)}
-        else:
-            ach = v["alg_bytes"] / secs / 1e9
-            roofline = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
-                        "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                        "launches": v["launches"], "avg_launch_us": round(1e6 * secs / v["launches"], 3)}
+        roofline = roofline_entry(*dom, traffic)
+        mf = [kv for kv in agg.items() if kernel_bound(kv[0]) == "mfma"]
+        if mf:
+            roofline_mfma = roofline_entry(*max(mf, key=lambda kv: kv[1]["total_ms"]), traffic)
         log(f"[bench] kernels: {json.dumps(kernels)}")
 
     cpu = None
@@ -185,10 +197,87 @@ def main():
         "factor_alg_tflops": round(alg_factor / (float(np.median(factor_ms)) / 1e3) / 1e12, 3),
         "objective": obj,
         "roofline": roofline,
+        "roofline_mfma": roofline_mfma,
         "kernels": kernels,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+# Which roofline bounds each kernel: the dense contractions run on the fp32
+# MFMA units; the copy, damping and finishing passes stream HBM; the rest
+# (the leaf sweep, the diagonal-block factor, the schedule and the objective
+# reduction) are chains of dependent vector arithmetic and LDS traffic,
+# priced against the fp32 vector peak.
+MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_f_panel", "k_f_right",
+                "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>"}
+HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info"}
+PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector
+
+
+def kernel_bound(name):
+    return "mfma" if name in MFMA_KERNELS else ("hbm" if name in HBM_KERNELS else "alu")
+
+
+def sources_digest():
+    """sha256 over the library's kernel sources and ABI header: the HBM
+    counters in profiles/ are valid only for the sources they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "two_sided_hessian_amd", "csrc")
+    for f in sorted(os.listdir(csrc)) + ["../../include/bakron.h"]:
+        path = os.path.normpath(os.path.join(csrc, f))
+        if path.endswith((".hip", ".hpp", ".h")):
+            with open(path, "rb") as fh:
+                h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def load_traffic(workload):
+    """Per-launch HBM bytes (FETCH_SIZE + WRITE_SIZE, calibrated against a
+    plain copy) from profiles/traffic_<workload>.json, or None when missing or
+    taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("sources_sha256") != sources_digest():
+        log("[bench] profiles traffic counters were taken on other kernel sources: traffic = null")
+        return None
+    return t
+
+
+def roofline_entry(name, v, traffic):
+    bound = kernel_bound(name)
+    secs = v["total_ms"] * 1e-3
+    if bound == "hbm":
+        ach, peak, unit = v["alg_bytes"] / secs / 1e9, PEAK_HBM_GBS, "GB/s"
+    else:
+        ach = v["alg_flops"] / secs / 1e12
+        peak = PEAK_FP32_MFMA_TFLOPS if bound == "mfma" else PEAK_FP32_VECTOR_TFLOPS
+        unit = "TFLOP/s"
+    tr = None
+    if traffic and name in traffic.get("kernels", {}):
+        tr = traffic["kernels"][name]["hbm_bytes_per_launch"]
+    return {"kernel": name, "bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
+            "frac": round(ach / peak, 4), "traffic": tr, "launches": v["launches"],
+            "avg_launch_us": round(1e6 * secs / v["launches"], 3),
+            "alg_flops_per_launch": v["alg_flops"] / v["launches"],
+            "alg_bytes_per_launch": v["alg_bytes"] / v["launches"]}
+
+
+def copy_calibration(nbytes):
+    """A plain device-to-device copy of nbytes, five times: the reference
+    dispatch for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = nbytes // 4
+    a = torch.ones(n, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": 4 * n, "copies": 5}), flush=True)
 
 
 def cpu_baseline(d, sample, m, n):

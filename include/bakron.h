@@ -164,7 +164,7 @@ int bakron_solve(const float* W, int64_t m, int64_t n,
  * max_stats [in]  capacity (BAKRON_MAX_KERNEL_KINDS is always enough).
  * n_stats   [out] host int32: number of entries written (kernels launched).
  */
-#define BAKRON_MAX_KERNEL_KINDS 16
+#define BAKRON_MAX_KERNEL_KINDS 32
 
 typedef struct bakron_kernel_stat {
     const char* name;     /* kernel name (static storage) */

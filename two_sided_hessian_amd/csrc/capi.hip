@@ -122,8 +122,9 @@ namespace bk {
 const char* kernel_name(int kind)
 {
     static const char* const names[KK_COUNT] = {
-        "k_copy_pad", "k_leaf", "k_prop_rows", "k_prop_cols", "k_obj_reduce", "k_f_prep",
-        "k_f_diag", "k_f_panel", "k_f_syrk", "k_f_right", "k_f_left", "k_f_finish", "k_sched"};
+        "k_copy_pad", "k_leaf", "k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_obj_reduce",
+        "k_sched", "k_clear_info", "k_diag_mean", "k_load_damped", "k_f_diag", "k_f_panel", "k_f_tile<0>",
+        "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 

@@ -119,9 +119,8 @@ __device__ __forceinline__ int base64(float* __restrict__ S, float* __restrict__
     __syncthreads();
     int fail = -1;
     float mypiv = 1.f;
-#pragma unroll
-    for (int k = 63; k >= 0; --k) {
-        const float* rk = rowbuf + 64 * (k & 1);
+    // One elimination step with pivot row k in rk; row k - 1 goes to rnext.
+    auto chol_step = [&](const int k, const float* rk, float* rnext) {
         const float piv = rk[k];
         const float ski = rk[i];                          // S[k][i] = S[i][k]
         f32x4 r[4];
@@ -137,12 +136,20 @@ __device__ __forceinline__ int base64(float* __restrict__ S, float* __restrict__
             s[4 * u + 2] = fmaf(-mul, r[u].z, s[4 * u + 2]);
             s[4 * u + 3] = fmaf(-mul, r[u].w, s[4 * u + 3]);
         }
-        if (k > 0 && i == k - 1)
+        if (i == k - 1)
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<f32x4*>(rowbuf + 64 * ((k - 1) & 1) + c0 + 4 * u) =
+                *reinterpret_cast<f32x4*>(rnext + c0 + 4 * u) =
                     f32x4{s[4 * u], s[4 * u + 1], s[4 * u + 2], s[4 * u + 3]};
         __syncthreads();
+    };
+    // The step loops stay loops (two steps per iteration, for the buffer
+    // parity): a fully unrolled base is thousands of straight-line
+    // instructions that run once each, and their fetch would dominate.
+#pragma unroll 1
+    for (int k = 63; k > 0; k -= 2) {
+        chol_step(k, rowbuf + 64, rowbuf);
+        chol_step(k - 1, rowbuf, rowbuf + 64);
     }
     const float rs = __builtin_amdgcn_rsqf(mypiv);
 #pragma unroll
@@ -163,9 +170,9 @@ __device__ __forceinline__ int base64(float* __restrict__ S, float* __restrict__
         for (int u = 0; u < 4; ++u)
             *reinterpret_cast<f32x4*>(rowbuf + c0 + 4 * u) = f32x4{r[4 * u], r[4 * u + 1], r[4 * u + 2], r[4 * u + 3]};
     __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 63; ++k) {
-        const float* rk = rowbuf + 64 * (k & 1);
+    // One substitution step with R[k] in rk; R[k + 1] goes to rnext (k = 63
+    // is a no-op that keeps the trip count even).
+    auto inv_step = [&](const int k, const float* rk, float* rnext) {
         f32x4 v[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(rk + c0 + 4 * u);
@@ -180,9 +187,14 @@ __device__ __forceinline__ int base64(float* __restrict__ S, float* __restrict__
         if (i == k + 1)
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<f32x4*>(rowbuf + 64 * ((k + 1) & 1) + c0 + 4 * u) =
+                *reinterpret_cast<f32x4*>(rnext + c0 + 4 * u) =
                     f32x4{r[4 * u], r[4 * u + 1], r[4 * u + 2], r[4 * u + 3]};
         __syncthreads();
+    };
+#pragma unroll 1
+    for (int k = 0; k < 64; k += 2) {
+        inv_step(k, rowbuf, rowbuf + 64);
+        inv_step(k + 1, rowbuf + 64, rowbuf);
     }
     const float inv = __builtin_amdgcn_rcpf(S[i * kDP + i]);
 #pragma unroll
@@ -322,35 +334,15 @@ __global__ __launch_bounds__(256) void k_f_panel(const float* __restrict__ Pbuf,
     block_store<2, 2>(Lbuf + (o2 + r0) * ld + o1 + c0, ld, n2 - r0, n1 - c0, 1.f, 0.f, acc);
 }
 
-// A11 -= L21^T L21 on lower-triangular 128-blocks of the n1 x n1 block;
-// only entries on or below the diagonal are written, so the strictly upper
-// part of Pbuf stays zero (later products read whole triangular blocks).
-__global__ __launch_bounds__(256) void k_f_syrk(const float* __restrict__ Lbuf, float* __restrict__ Pbuf,
-                                                int64_t ld, int64_t o1, int64_t o2, int n1, int n2)
-{
-    __shared__ __align__(16) float lds[Gemm<2, 2, KRow, KRow>::LDS_FLOATS];
-    // linear block index -> (br, bc) with br >= bc
-    const int q = blockIdx.x;
-    int br = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
-    while ((br + 1) * (br + 2) / 2 <= q) ++br;
-    while (br * (br + 1) / 2 > q) --br;
-    const int bc = q - br * (br + 1) / 2;
-    const int r0 = br * FBM, c0 = bc * FBN;
-    Acc acc;
-    acc_zero(acc);
-    block_gemm<2, 2, KRow, KRow>(Lbuf + o2 * ld + o1 + r0, ld, n1 - r0,
-                                 Lbuf + o2 * ld + o1 + c0, ld, n1 - c0, 0, n2, lds, acc);
-    block_store<2, 2>(Pbuf + (o1 + r0) * ld + o1 + c0, ld, n1 - r0, n1 - c0, -1.f, 1.f, acc, c0 - r0);
-}
-
 // T = L21 Li11 : (n2 x n1); Li11 is lower, so output columns from c0 need
-// K in [c0, n1).
+// K in [c0, n1).  Row blocks run along x (the fast launch dimension), so
+// the longest column blocks start first.
 __global__ __launch_bounds__(256) void k_f_right(const float* __restrict__ Lbuf, const float* __restrict__ Pbuf,
                                                  float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
                                                  int n1, int n2)
 {
     __shared__ __align__(16) float lds[Gemm<2, 2, RowK, KRow>::LDS_FLOATS];
-    const int r0 = blockIdx.y * FBM, c0 = blockIdx.x * FBN;
+    const int r0 = blockIdx.x * FBM, c0 = blockIdx.y * FBN;
     Acc acc;
     acc_zero(acc);
     block_gemm<2, 2, RowK, KRow>(Lbuf + (o2 + r0) * ld + o1, ld, n2 - r0,
@@ -394,6 +386,9 @@ __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float*
     } else if (MODE == 3) {   // heaviest (largest K) first
         r0 = 64 * (int)(gridDim.y - 1 - blockIdx.y);
         c0 = 64 * (int)blockIdx.x;
+    } else if (MODE == 2) {   // rows along x: the longest column tiles first
+        r0 = 64 * (int)blockIdx.x;
+        c0 = 64 * (int)blockIdx.y;
     } else {
         r0 = 64 * (int)blockIdx.y;
         c0 = 64 * (int)blockIdx.x;
@@ -420,27 +415,42 @@ __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float*
 
 // P = Li diag(L) on and below the diagonal, zeros above, for L and P; when
 // the factor ran in padded workspace, also copy the leading n x n out.
+// Each thread owns four adjacent columns for a stripe of rows, so the
+// diagonal entries it scales by are read once.
 __global__ __launch_bounds__(256) void k_f_finish(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
                                                   int64_t Np, int64_t n, float* __restrict__ Lout,
                                                   float* __restrict__ Pout)
 {
-    for (int64_t i = blockIdx.y; i < Np; i += gridDim.y)
-        for (int64_t j = blockIdx.x * 256 + threadIdx.x; j < Np; j += (int64_t)gridDim.x * 256) {
-            float l = 0.f, p = 0.f;
-            if (j <= i) {
-                l = Lbuf[i * ld + j];
-                p = Pbuf[i * ld + j] * Lbuf[j * ld + j];
-            }
-            if (Lout) {
-                if (i < n && j < n) {
-                    Lout[i * n + j] = l;
-                    Pout[i * n + j] = p;
-                }
-            } else {
-                Lbuf[i * ld + j] = l;
-                Pbuf[i * ld + j] = p;
+    const int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (j >= Np) return;
+    float dg[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dg[q] = Lbuf[(j + q) * ld + j + q];
+    for (int64_t i = blockIdx.y; i < Np; i += gridDim.y) {
+        f32x4 l = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
+        if (j <= i) {
+            l = *reinterpret_cast<const f32x4*>(Lbuf + i * ld + j);
+            p = *reinterpret_cast<const f32x4*>(Pbuf + i * ld + j);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool below = j + q <= i;
+                l[q] = below ? l[q] : 0.f;
+                p[q] = below ? p[q] * dg[q] : 0.f;
             }
         }
+        if (Lout) {
+            if (i < n)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (j + q < n) {
+                        Lout[i * n + j + q] = l[q];
+                        Pout[i * n + j + q] = p[q];
+                    }
+        } else {
+            *reinterpret_cast<f32x4*>(Lbuf + i * ld + j) = l;
+            *reinterpret_cast<f32x4*>(Pbuf + i * ld + j) = p;
+        }
+    }
 }
 
 // ------------------------------------------------------------ host side
@@ -498,7 +508,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     if (nsz <= 2 * kTile) {
         // factor (b^3 / 3 multiply-adds) and inverse (b^3 / 6) of the block
         const double b = (double)nsz;
-        launch(R.prof, KK_F_BASE, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
+        launch(R.prof, KK_F_DIAG, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
                R.Lbuf, R.Pbuf, R.ld, o, (int)nsz, R.info);
         return launch_ok();
     }
@@ -514,22 +524,19 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     const dim3 gt((unsigned)(n1 / kTile), (unsigned)(n2 / kTile));
     const double fl_panel = 2.0 * d1 * tri(d2), by_panel = 4.0 * (tri(d2) + 2.0 * d2 * d1);
     if (tiles)
-        launch(R.prof, KK_F_PANEL, fl_panel, by_panel, k_f_tile<0>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf,
+        launch(R.prof, KK_F_PANEL_T, fl_panel, by_panel, k_f_tile<0>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf,
                R.T, R.ld, o1, o2, n1, n2);
     else
         launch(R.prof, KK_F_PANEL, fl_panel, by_panel, k_f_panel, g, dim3(256), R.s, R.Pbuf, R.Lbuf, R.ld, o1, o2,
                n1, n2);
     {
+        // SYRK on 64 x 64 tiles at every level: its K extent is uniform, so
+        // the finer grid only helps (a triangle of 128-blocks quantizes badly
+        // over the CUs, e.g. 528 blocks at n1 = 4096).
         const double fl = 2.0 * d2 * tri(d1), by = 4.0 * (d2 * d1 + 2.0 * tri(d1));
-        if (tiles) {
-            const int64_t tb = n1 / kTile;
-            launch(R.prof, KK_F_SYRK, fl, by, k_f_tile<1>, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s,
-                   R.Lbuf, R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
-        } else {
-            const int64_t tb = ceil_div(n1, FBM);
-            launch(R.prof, KK_F_SYRK, fl, by, k_f_syrk, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s,
-                   (const float*)R.Lbuf, R.Pbuf, R.ld, o1, o2, n1, n2);
-        }
+        const int64_t tb = n1 / kTile;
+        launch(R.prof, KK_F_SYRK_T, fl, by, k_f_tile<1>, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s, R.Lbuf,
+               R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, o1, n1)) return -1;
@@ -537,12 +544,12 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
         const double fr = 2.0 * d2 * tri(d1), br = 4.0 * (2.0 * d2 * d1 + tri(d1));
         const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
         if (tiles) {
-            launch(R.prof, KK_F_RIGHT, fr, br, k_f_tile<2>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
+            launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
                    R.ld, o1, o2, n1, n2);
-            launch(R.prof, KK_F_LEFT, fl, bl, k_f_tile<3>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
+            launch(R.prof, KK_F_LEFT_T, fl, bl, k_f_tile<3>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
                    R.ld, o1, o2, n1, n2);
         } else {
-            launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, g, dim3(256), R.s, (const float*)R.Lbuf,
+            launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, dim3(g.y, g.x), dim3(256), R.s, (const float*)R.Lbuf,
                    (const float*)R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
             launch(R.prof, KK_F_LEFT, fl, bl, k_f_left, g, dim3(256), R.s, (const float*)R.T, R.Pbuf, R.ld, o1, o2,
                    n1, n2);
@@ -575,17 +582,17 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     R.Pbuf = p.padded ? reinterpret_cast<float*>(w + p.off_P) : P;
     const double dn = (double)n, dN = (double)p.Np;
 
-    launch(prof, KK_F_PREP, 0.0, 4.0, k_clear_info, dim3(1), dim3(64), s, info);
-    launch(prof, KK_F_PREP, 0.0, 4.0 * dn, k_diag_mean, dim3(1), dim3(256), s, A, n, mean);
+    launch(prof, KK_F_CLEAR, 0.0, 4.0, k_clear_info, dim3(1), dim3(64), s, info);
+    launch(prof, KK_F_MEAN, 0.0, 4.0 * dn, k_diag_mean, dim3(1), dim3(256), s, A, n, mean);
     {
         dim3 g((unsigned)ceil_div(p.Np, 256), (unsigned)std::min<int64_t>(p.Np, 32768));
-        launch(prof, KK_F_PREP, dn, 4.0 * (tri(dn) + dN * dN), k_load_damped, g, dim3(256), s, A, n, R.Pbuf,
+        launch(prof, KK_F_LOAD, dn, 4.0 * (tri(dn) + dN * dN), k_load_damped, g, dim3(256), s, A, n, R.Pbuf,
                p.Np, p.Np, (const float*)mean, damp_frac);
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, 0, p.Np)) return -1;
     {
-        dim3 g((unsigned)ceil_div(p.Np, 256), (unsigned)std::min<int64_t>(p.Np, 32768));
+        dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 256));
         launch(prof, KK_F_FINISH, dn * dn / 2.0, 4.0 * (2.0 * tri(dN) + 2.0 * dn * dn), k_f_finish, g, dim3(256),
                s, R.Lbuf, R.Pbuf, p.Np, p.Np, n, p.padded ? L : (float*)nullptr, p.padded ? P : (float*)nullptr);
     }

@@ -20,10 +20,14 @@ namespace bk {
 // launch's algorithmic flops and bytes; the totals per kernel are read back
 // after the stream drains.
 
+// One kind per __global__ function (template instances counted apart), so
+// the per-kind statistics line up with a profiler's per-kernel summary.
 enum KernelKind {
-    KK_COPY_PAD, KK_LEAF, KK_PROP_ROWS, KK_PROP_COLS, KK_OBJ_REDUCE,
-    KK_F_PREP, KK_F_BASE, KK_F_PANEL, KK_F_SYRK, KK_F_RIGHT, KK_F_LEFT, KK_F_FINISH, KK_SCHED, KK_COUNT
+    KK_COPY_PAD, KK_LEAF, KK_PROP_ROWS, KK_PROP_ROWS_T, KK_PROP_COLS, KK_PROP_COLS_T, KK_OBJ_REDUCE, KK_SCHED,
+    KK_F_CLEAR, KK_F_MEAN, KK_F_LOAD, KK_F_DIAG, KK_F_PANEL, KK_F_PANEL_T, KK_F_SYRK_T, KK_F_RIGHT, KK_F_RIGHT_T,
+    KK_F_LEFT, KK_F_LEFT_T, KK_F_FINISH, KK_COUNT
 };
+static_assert(KK_COUNT <= BAKRON_MAX_KERNEL_KINDS, "kernel kinds exceed the ABI's statistics capacity");
 
 const char* kernel_name(int kind);
 

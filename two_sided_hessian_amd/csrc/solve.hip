@@ -668,7 +668,7 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
         launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3((unsigned)blocks), dim3(256), R.s,
                (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Mt, Nt, list1);
     else if (blocks > 0)
-        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows_t,
+        launch(R.prof, KK_PROP_ROWS_T, fl, by, k_prop_rows_t,
                dim3((unsigned)span, (unsigned)(I_hi - I_lo + 1)), dim3(256), R.s, (const float*)R.leaf.E, R.leaf.PA,
                R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt);
 
@@ -703,7 +703,7 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
         launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3((unsigned)blocks), dim3(256), R.s,
                (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, Nt, list2);
     else if (blocks > 0)
-        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols_t,
+        launch(R.prof, KK_PROP_COLS_T, fl, by, k_prop_cols_t,
                dim3((unsigned)span, (unsigned)(J_hi - J_lo + 1)), dim3(256), R.s, (const float*)R.Y, R.leaf.PB,
                R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt);
 }
