@@ -71,142 +71,138 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
 // --------------------------------------------------- diagonal blocks
 //
 // k_f_diag factors a whole diagonal block of 64 or 128 in one workgroup,
-// with the block and its inverse resident in LDS (2 x 128 x 132 floats):
-//   size 64:  base64 (reverse Cholesky and inverse) of the block;
-//   size 128: base64 of the trailing 64 (L22, Li22); L21 = Li22^T A21;
-//             A11 -= L21^T L21; base64 of A11 (L11, Li11);
-//             Li21 = -Li22 (L21 Li11)
-// -- the same recursion as the GEMM levels above it, with the four 64^3
-// products on the MFMA units straight from LDS.
+// with the block and its inverse resident in LDS (2 x 128 x 132 floats).
+//
+// Factor: right-looking over 16 x 16 diagonal blocks, last first.  For
+// block b: one wave factors and inverts it (base16: L_bb, X_bb = L_bb^-1);
+// then all four waves form the panel L[b][0:16b] = X_bb^T A[b][0:16b] and
+// update the leading part, A[0:16b][0:16b] -= L[b]^T L[b] (lower triangle).
+// This is A = L^T L eliminated from the last row up, 16 rows at a time.
+//
+// Inverse: the diagonal 16-blocks come from base16; the off-diagonal part
+// by the block rule L^-1 = [[X11, 0], [-X22 L21 X11, X22]] applied to 2 x 16,
+// then 2 x 32, then 2 x 64 blocks (the last two on the MFMA units).  Each
+// level parks T = L21 X11 in the upper block of its pair and clears it
+// after use, since the next level multiplies whole (lower-triangular)
+// blocks of X.
 
 constexpr int kDP = 132;   // LDS pitch (floats) of the block and its inverse
 
-// base64: reverse Cholesky S = L^T L of the 64 x 64 block at S (pitch kDP,
-// lower part read), then X = L^-1; L overwrites S and X goes to X (both with
-// zeros above the diagonal).  256 threads: thread t owns row i = t / 4,
-// columns 16 (t % 4) .. + 15, in registers.
-//
-// Elimination from the last row up, on unscaled rows: at step k every row
-// i < k takes S[i][j] -= (S[k][i] / S[k][k]) S[k][j]; row k is read from a
-// double-buffered LDS row that its owners published at the end of the
-// previous step, so a step costs one barrier.  At the end each row is scaled
-// once, L[i][j] = S[i][j] / sqrt(S[i][i]) (S[i][i] taken when row i was the
-// pivot).  The inverse solves L X = I by rows, forward: with
-// R[i] = L[i][i] X[i], R[i] = e_i - sum_{k<i} (L[i][k] / L[k][k]) R[k], the
-// same one-row-per-step broadcast.  Reciprocals and square roots use the
-// hardware approximations (about one ulp): the factor is judged by its
-// backward error, not by correct rounding.
-//
-// Returns the block row of the first non-positive (or NaN) pivot met, or -1.
-__device__ __forceinline__ int base64(float* __restrict__ S, float* __restrict__ X, float* __restrict__ rowbuf)
+// Value of v in lane `src` (any lane of the wave).
+__device__ __forceinline__ float lane_get(float v, int src)
 {
-    const int t = threadIdx.x;
-    const int i = t >> 2, c0 = 16 * (t & 3);
-    float s[16];
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, v)));
+}
+
+__device__ __forceinline__ float wave_get(float v, int lane)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// base16: reverse Cholesky S = L^T L of the 16 x 16 block at S (pitch kDP,
+// lower part read) and X = L^-1, by one wave with no LDS traffic between
+// steps.  Lane 4i + q holds row i, columns 4q .. 4q + 3, of the symmetric
+// working matrix (both triangles, so S[i][k] is in the lane's own quad).
+// Step k (15 .. 0) takes row k from lanes 4k + q (ds_bpermute) and
+// S[i][k] from the quad (DPP), and eliminates: S[i][j] -= S[i][k] S[k][j] /
+// S[k][k] for i < k; rows stay unscaled and are scaled once at the end,
+// L[i][j] = S[i][j] / sqrt(S[i][i]) (S[i][i] taken when row i was the pivot).
+// The inverse solves L X = I by rows, forward: with R[i] = L[i][i] X[i],
+// R[i] = e_i - sum_{k<i} (L[i][k] / L[k][k]) R[k], one row broadcast a step.
+// Reciprocals and square roots use the hardware approximations (about one
+// ulp): the factor is judged by its backward error, not by correct
+// rounding.  L overwrites S, X is written to X (zeros above both
+// diagonals).  Returns the block row of the first non-positive (or NaN)
+// pivot met, or -1.
+__device__ __forceinline__ int base16(float* __restrict__ S, float* __restrict__ X)
+{
+    const int lane = threadIdx.x & 63;
+    const int i = lane >> 2, q = lane & 3, c0 = 4 * q;
+    float s[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(S + i * kDP + c0 + 4 * u);
-        s[4 * u + 0] = v.x;
-        s[4 * u + 1] = v.y;
-        s[4 * u + 2] = v.z;
-        s[4 * u + 3] = v.w;
+        const int j = c0 + u;
+        s[u] = (j <= i) ? S[i * kDP + j] : S[j * kDP + i];
     }
-    if (i == 63)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<f32x4*>(rowbuf + 64 + c0 + 4 * u) =
-                f32x4{s[4 * u], s[4 * u + 1], s[4 * u + 2], s[4 * u + 3]};
-    __syncthreads();
     int fail = -1;
     float mypiv = 1.f;
-    // One elimination step with pivot row k in rk; row k - 1 goes to rnext.
-    auto chol_step = [&](const int k, const float* rk, float* rnext) {
-        const float piv = rk[k];
-        const float ski = rk[i];                          // S[k][i] = S[i][k]
-        f32x4 r[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) r[u] = *reinterpret_cast<const f32x4*>(rk + c0 + 4 * u);
-        if (!(piv > 0.f) && fail < 0) fail = k;
-        if (i == k) mypiv = piv;
-        const float mul = (i < k) ? ski * __builtin_amdgcn_rcpf(piv) : 0.f;
+    // Two pivots (k, k - 1) per step: rows k and k - 1 arrive together, and
+    // each lane applies pivot k to row k - 1 itself (rk1' = rk1 - (S[k][k-1] /
+    // S[k][k]) rk) before eliminating both, which halves the dependent chain.
+    // Column k lives in register k % 4 of the quad's lane k / 4.
+    auto chol2 = [&](const int k, const int ru, const int ru1) {   // ru = k % 4, ru1 = (k - 1) % 4
+        float rk[4], rk1[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            s[4 * u + 0] = fmaf(-mul, r[u].x, s[4 * u + 0]);
-            s[4 * u + 1] = fmaf(-mul, r[u].y, s[4 * u + 1]);
-            s[4 * u + 2] = fmaf(-mul, r[u].z, s[4 * u + 2]);
-            s[4 * u + 3] = fmaf(-mul, r[u].w, s[4 * u + 3]);
+            rk[u] = lane_get(s[u], 4 * k + q);
+            rk1[u] = lane_get(s[u], 4 * (k - 1) + q);
         }
-        if (i == k - 1)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<f32x4*>(rnext + c0 + 4 * u) =
-                    f32x4{s[4 * u], s[4 * u + 1], s[4 * u + 2], s[4 * u + 3]};
-        __syncthreads();
-    };
-    // The step loops stay loops (two steps per iteration, for the buffer
-    // parity): a fully unrolled base is thousands of straight-line
-    // instructions that run once each, and their fetch would dominate.
-#pragma unroll 1
-    for (int k = 63; k > 0; k -= 2) {
-        chol_step(k, rowbuf + 64, rowbuf);
-        chol_step(k - 1, rowbuf, rowbuf + 64);
-    }
-    const float rs = __builtin_amdgcn_rsqf(mypiv);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        f32x4 v;
-        v.x = (c0 + 4 * u + 0 <= i) ? s[4 * u + 0] * rs : 0.f;
-        v.y = (c0 + 4 * u + 1 <= i) ? s[4 * u + 1] * rs : 0.f;
-        v.z = (c0 + 4 * u + 2 <= i) ? s[4 * u + 2] * rs : 0.f;
-        v.w = (c0 + 4 * u + 3 <= i) ? s[4 * u + 3] * rs : 0.f;
-        *reinterpret_cast<f32x4*>(S + i * kDP + c0 + 4 * u) = v;
-    }
-    // R = I; row 0 published
-    float r[16];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) r[c] = (c0 + c == i) ? 1.f : 0.f;
-    if (i == 0)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-            *reinterpret_cast<f32x4*>(rowbuf + c0 + 4 * u) = f32x4{r[4 * u], r[4 * u + 1], r[4 * u + 2], r[4 * u + 3]};
-    __syncthreads();
-    // One substitution step with R[k] in rk; R[k + 1] goes to rnext (k = 63
-    // is a no-op that keeps the trip count even).
-    auto inv_step = [&](const int k, const float* rk, float* rnext) {
-        f32x4 v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(rk + c0 + 4 * u);
-        const float coef = (i > k) ? S[i * kDP + k] * __builtin_amdgcn_rcpf(S[k * kDP + k]) : 0.f;
+        const int g = k >> 2;                                        // k and k - 1 share the quad lane
+        const float a = wave_get(s[ru], 4 * k + g);                  // S[k][k]
+        const float bk = wave_get(s[ru1], 4 * k + g);                // S[k][k-1]
+        const float c = wave_get(s[ru1], 4 * (k - 1) + g);           // S[k-1][k-1]
+        const float sik = lane_get(s[ru], (lane & ~3) + g);          // S[i][k]
+        const float sik1 = lane_get(s[ru1], (lane & ~3) + g);        // S[i][k-1]
+        const float ia = __builtin_amdgcn_rcpf(a);
+        const float cp = c - bk * bk * ia;                           // pivot k - 1 after pivot k
+        if (!(a > 0.f) && fail < 0) fail = k;
+        if (!(cp > 0.f) && fail < 0) fail = k - 1;
+        if (i == k) mypiv = a;
+        if (i == k - 1) mypiv = cp;
+        const float m1 = (i < k) ? sik * ia : 0.f;
+        const float m2 = (i < k - 1) ? (sik1 - sik * bk * ia) * __builtin_amdgcn_rcpf(cp) : 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            r[4 * u + 0] = fmaf(-coef, v[u].x, r[4 * u + 0]);
-            r[4 * u + 1] = fmaf(-coef, v[u].y, r[4 * u + 1]);
-            r[4 * u + 2] = fmaf(-coef, v[u].z, r[4 * u + 2]);
-            r[4 * u + 3] = fmaf(-coef, v[u].w, r[4 * u + 3]);
+            const float r1p = fmaf(-bk * ia, rk[u], rk1[u]);
+            s[u] = fmaf(-m2, r1p, fmaf(-m1, rk[u], s[u]));
         }
-        if (i == k + 1)
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                *reinterpret_cast<f32x4*>(rnext + c0 + 4 * u) =
-                    f32x4{r[4 * u], r[4 * u + 1], r[4 * u + 2], r[4 * u + 3]};
-        __syncthreads();
     };
 #pragma unroll 1
-    for (int k = 0; k < 64; k += 2) {
-        inv_step(k, rowbuf, rowbuf + 64);
-        inv_step(k + 1, rowbuf + 64, rowbuf);
+    for (int g = 3; g >= 0; --g) {
+        chol2(4 * g + 3, 3, 2);
+        chol2(4 * g + 1, 1, 0);
     }
-    const float inv = __builtin_amdgcn_rcpf(S[i * kDP + i]);
+    const float rs = __builtin_amdgcn_rsqf(mypiv);   // 1 / L[i][i]
+    float l[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) l[u] = (c0 + u <= i) ? s[u] * rs : 0.f;
+    float r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = (c0 + u == i) ? 1.f : 0.f;
+    // Two rows (k, k + 1) per step: R[k + 1] takes R[k]'s contribution
+    // locally first.
+    auto inv2 = [&](const int k, const int ru, const int ru1) {    // ru = k % 4, ru1 = (k + 1) % 4
+        float rk[4], rk1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            rk[u] = lane_get(r[u], 4 * k + q);
+            rk1[u] = lane_get(r[u], 4 * (k + 1) + q);
+        }
+        const int g = k >> 2;
+        const float lkk = wave_get(l[ru], 4 * k + g);                // L[k][k]
+        const float lk1k = wave_get(l[ru], 4 * (k + 1) + g);         // L[k+1][k]
+        const float lk1k1 = wave_get(l[ru1], 4 * (k + 1) + g);       // L[k+1][k+1]
+        const float lik = lane_get(l[ru], (lane & ~3) + g);          // L[i][k]
+        const float lik1 = lane_get(l[ru1], (lane & ~3) + g);        // L[i][k+1]
+        const float ik = __builtin_amdgcn_rcpf(lkk);
+        const float c1 = (i > k) ? lik * ik : 0.f;
+        const float c2 = (i > k + 1) ? lik1 * __builtin_amdgcn_rcpf(lk1k1) : 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float r1p = fmaf(-lk1k * ik, rk[u], rk1[u]);
+            r[u] = fmaf(-c2, r1p, fmaf(-c1, rk[u], r[u]));
+        }
+    };
+#pragma unroll 1
+    for (int g = 0; g < 4; ++g) {
+        inv2(4 * g, 0, 1);
+        inv2(4 * g + 2, 2, 3);
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        f32x4 v;
-        v.x = (c0 + 4 * u + 0 <= i) ? r[4 * u + 0] * inv : 0.f;
-        v.y = (c0 + 4 * u + 1 <= i) ? r[4 * u + 1] * inv : 0.f;
-        v.z = (c0 + 4 * u + 2 <= i) ? r[4 * u + 2] * inv : 0.f;
-        v.w = (c0 + 4 * u + 3 <= i) ? r[4 * u + 3] * inv : 0.f;
-        *reinterpret_cast<f32x4*>(X + i * kDP + c0 + 4 * u) = v;
+        S[i * kDP + c0 + u] = l[u];
+        X[i * kDP + c0 + u] = (c0 + u <= i) ? r[u] * rs : 0.f;
     }
-    __syncthreads();
     return fail;
 }
 
@@ -219,39 +215,93 @@ __device__ __forceinline__ f32x4 ldsfrag(const float* p, int r, int k)
     return f32x4{p[k * kDP + r], p[(k + 1) * kDP + r], p[(k + 2) * kDP + r], p[(k + 3) * kDP + r]};
 }
 
-// 64 x 64 x 64 product from LDS: wave w returns the 32 x 32 quadrant at rows
-// 32 (w >> 1), columns 32 (w & 1) of A B, with A(r, k) and B(k, c) addressed
-// as ldsfrag's (r, k) and (c, k).
+// One wave: the 32 x 32 tile of A B over K (a multiple of 8), A(r, k) and
+// B(k, c) addressed as ldsfrag's (r, k) and (c, k).
 template <int ALAY, int BLAY>
-__device__ __forceinline__ f32x16 lds_mm64(const float* A, const float* B)
+__device__ __forceinline__ f32x16 lds_mm32(const float* A, const float* B, int K)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int ml = lane & 31, k4 = 4 * (lane >> 5);
-    const int ra = 32 * (wave >> 1) + ml, rb = 32 * (wave & 1) + ml;
     f32x16 acc;
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-#pragma unroll
-    for (int kc = 0; kc < 64; kc += 8) {
-        const f32x4 a = ldsfrag<ALAY>(A, ra, kc + k4);
-        const f32x4 b = ldsfrag<BLAY>(B, rb, kc + k4);
+    for (int kc = 0; kc < K; kc += 8) {
+        const f32x4 a = ldsfrag<ALAY>(A, ml, kc + k4);
+        const f32x4 b = ldsfrag<BLAY>(B, ml, kc + k4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
     }
     return acc;
 }
 
-// C (64 x 64 in LDS) = alpha * acc + beta * C over this wave's quadrant.
-__device__ __forceinline__ void lds_put64(float* C, const f32x16& acc, float alpha, float beta)
+// C (32 x 32 in LDS) = alpha * acc, one wave.
+__device__ __forceinline__ void lds_put32(float* C, const f32x16& acc, float alpha)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = 32 * (wave & 1) + (lane & 31);
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 31;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 32 * (wave >> 1) + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float* p = C + row * kDP + col;
-        *p = alpha * acc[r] + (beta != 0.f ? beta * *p : 0.f);
+    for (int r = 0; r < 16; ++r) C[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDP + col] = alpha * acc[r];
+}
+
+// 64 x 64 x 64 product from LDS: wave w returns the 32 x 32 quadrant at rows
+// 32 (w >> 1), columns 32 (w & 1) of A B.
+template <int ALAY, int BLAY>
+__device__ __forceinline__ f32x16 lds_mm64(const float* A, const float* B)
+{
+    const int wave = threadIdx.x >> 6;
+    const int ro = 32 * (wave >> 1), co = 32 * (wave & 1);
+    const float* Aw = (ALAY == RowK) ? A + ro * kDP : A + ro;
+    const float* Bw = (BLAY == RowK) ? B + co * kDP : B + co;
+    return lds_mm32<ALAY, BLAY>(Aw, Bw, 64);
+}
+
+__device__ __forceinline__ void lds_put64(float* C, const f32x16& acc, float alpha)
+{
+    const int wave = threadIdx.x >> 6;
+    lds_put32(C + 32 * (wave >> 1) * kDP + 32 * (wave & 1), acc, alpha);
+}
+
+// One wave: X21 = -X22 (L21 X11) for 16 x 16 blocks at diagonal offset d
+// (block rows d .. d + 31 of the 32-block); T goes to X's upper block.
+__device__ __forceinline__ void inv_merge16(const float* sA, float* sX, int d)
+{
+    const int lane = threadIdx.x & 63;
+    const int r = lane >> 2, c0 = 4 * (lane & 3);
+    const float* L21 = sA + (d + 16) * kDP + d;
+    const float* X11 = sX + d * kDP + d;
+    const float* X22 = sX + (d + 16) * kDP + d + 16;
+    float* T = sX + d * kDP + d + 16;          // upper block, unused by the result
+    float* X21 = sX + (d + 16) * kDP + d;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float a = L21[r * kDP + k];
+        const f32x4 b = *reinterpret_cast<const f32x4*>(X11 + k * kDP + c0);
+        acc[0] = fmaf(a, b.x, acc[0]);
+        acc[1] = fmaf(a, b.y, acc[1]);
+        acc[2] = fmaf(a, b.z, acc[2]);
+        acc[3] = fmaf(a, b.w, acc[3]);
     }
+    *reinterpret_cast<f32x4*>(T + r * kDP + c0) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    acc[0] = acc[1] = acc[2] = acc[3] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const float a = X22[r * kDP + k];
+        const f32x4 b = *reinterpret_cast<const f32x4*>(T + k * kDP + c0);
+        acc[0] = fmaf(a, b.x, acc[0]);
+        acc[1] = fmaf(a, b.y, acc[1]);
+        acc[2] = fmaf(a, b.z, acc[2]);
+        acc[3] = fmaf(a, b.w, acc[3]);
+    }
+    *reinterpret_cast<f32x4*>(X21 + r * kDP + c0) = f32x4{-acc[0], -acc[1], -acc[2], -acc[3]};
+    // the next level multiplies whole blocks of X: its upper part must be zero
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    *reinterpret_cast<f32x4*>(T + r * kDP + c0) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
@@ -259,41 +309,125 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
 {
     __shared__ __align__(16) float sA[128 * kDP];   // the block, then L
     __shared__ __align__(16) float sX[128 * kDP];   // L^-1
-    __shared__ __align__(16) float rowbuf[128];
-    const int t = threadIdx.x;
+    __shared__ int sfail;
+    const int t = threadIdx.x, wave = t >> 6;
     const int nf4 = nb / 4;
-    for (int f = t; f < nb * nf4; f += 256) {
-        const int r = f / nf4, c = 4 * (f % nf4);
-        *reinterpret_cast<f32x4*>(sA + r * kDP + c) =
-            *reinterpret_cast<const f32x4*>(Pbuf + (o + r) * ld + o + c);
+    {   // all global loads in flight before the LDS stores
+        f32x4 v[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int f = t + 256 * u;
+            if (f < nb * nf4) v[u] = *reinterpret_cast<const f32x4*>(Pbuf + (o + f / nf4) * ld + o + 4 * (f % nf4));
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int f = t + 256 * u;
+            if (f < nb * nf4) *reinterpret_cast<f32x4*>(sA + (f / nf4) * kDP + 4 * (f % nf4)) = v[u];
+        }
     }
+    if (t == 0) sfail = -1;
     __syncthreads();
-    // pass 1 (size 128 only): trailing half and the products it feeds;
-    // pass 0: the leading half (or the whole size-64 block) and, for 128,
-    // the off-diagonal block of the inverse.  One inlined copy of base64.
-    int fail[2] = {-1, -1};
-    float* A21 = sA + 64 * kDP;
-    float* X22 = sX + 64 * kDP + 64;
-    for (int h = (nb == 128) ? 1 : 0; h >= 0; --h) {
-        fail[h] = base64(sA + h * (64 * kDP + 64), sX + h * (64 * kDP + 64), rowbuf);
-        if (nb != 128) break;
-        if (h == 1) {
-            f32x16 acc = lds_mm64<KRow, KRow>(X22, A21);          // L21 = Li22^T A21
+
+    // factor, 16 rows at a time from the bottom
+    for (int b = nb / 16 - 1; b >= 0; --b) {
+        if (wave == 0) {
+            const int f = base16(sA + 16 * b * (kDP + 1), sX + 16 * b * (kDP + 1));
+            if (t == 0 && f >= 0 && sfail < 0) sfail = 16 * b + f;
+        }
+        __syncthreads();
+        if (b == 0) break;
+        const int W = 16 * b;
+        float* Pr = sA + W * kDP;                    // rows of block b
+        {   // panel: Pr[r][c] = sum_t Xbb[t][r] Pr[t][c], c < W; thread (r, cg)
+            // takes columns cg, cg + 16, ... (one 16-deep dot each)
+            const float* Xbb = sX + W * (kDP + 1);
+            const int r = t & 15, cg = t >> 4;
+            float xr[16];
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt) xr[tt] = Xbb[tt * kDP + r];
+            float acc[7];
+#pragma unroll 1
+            for (int j = 0; j < b; ++j) {
+                float a = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < 16; ++tt) a = fmaf(xr[tt], Pr[tt * kDP + cg + 16 * j], a);
+                acc[j] = a;
+            }
             __syncthreads();
-            lds_put64(A21, acc, 1.f, 0.f);
+#pragma unroll 1
+            for (int j = 0; j < b; ++j) Pr[r * kDP + cg + 16 * j] = acc[j];
             __syncthreads();
-            acc = lds_mm64<KRow, KRow>(A21, A21);                 // A11 -= L21^T L21
-            lds_put64(sA, acc, -1.f, 1.f);
-            __syncthreads();
-        } else {
-            f32x16 acc = lds_mm64<RowK, KRow>(A21, sX);           // T = L21 Li11 (into X's upper block)
-            lds_put64(sX + 64, acc, 1.f, 0.f);
-            __syncthreads();
-            acc = lds_mm64<RowK, KRow>(X22, sX + 64);             // Li21 = -Li22 T
-            lds_put64(sX + 64 * kDP, acc, -1.f, 0.f);
+        }
+        {   // A[0:W][0:W] -= Pr^T Pr on the 4 x 4 tiles of the lower triangle
+            const int n4 = W / 4, ntile = n4 * (n4 + 1) / 2;
+            for (int idx = t; idx < ntile; idx += 256) {
+                int br = (int)((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
+                while ((br + 1) * (br + 2) / 2 <= idx) ++br;
+                while (br * (br + 1) / 2 > idx) --br;
+                const int r0 = 4 * br, cc = 4 * (idx - br * (br + 1) / 2);
+                float acc[4][4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) acc[u][v] = 0.f;
+#pragma unroll
+                for (int tt = 0; tt < 16; ++tt) {
+                    const f32x4 a = *reinterpret_cast<const f32x4*>(Pr + tt * kDP + r0);
+                    const f32x4 c = *reinterpret_cast<const f32x4*>(Pr + tt * kDP + cc);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        acc[0][v] = fmaf(a.x, c[v], acc[0][v]);
+                        acc[1][v] = fmaf(a.y, c[v], acc[1][v]);
+                        acc[2][v] = fmaf(a.z, c[v], acc[2][v]);
+                        acc[3][v] = fmaf(a.w, c[v], acc[3][v]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    f32x4* p = reinterpret_cast<f32x4*>(sA + (r0 + u) * kDP + cc);
+                    f32x4 v = *p;
+                    v.x -= acc[u][0];
+                    v.y -= acc[u][1];
+                    v.z -= acc[u][2];
+                    v.w -= acc[u][3];
+                    *p = v;
+                }
+            }
             __syncthreads();
         }
     }
+
+    // inverse: 2 x 16 blocks (one wave each), 2 x 32 (MFMA, one wave each),
+    // 2 x 64 (MFMA, four waves); T goes to the upper block of each pair
+    if (wave < nb / 32) inv_merge16(sA, sX, 32 * wave);
+    __syncthreads();
+    if (wave < nb / 64) {
+        const int d = 64 * wave;
+        const f32x16 acc = lds_mm32<RowK, KRow>(sA + (d + 32) * kDP + d, sX + d * kDP + d, 32);   // L21 X11
+        lds_put32(sX + d * kDP + d + 32, acc, 1.f);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const f32x16 acc2 = lds_mm32<RowK, KRow>(sX + (d + 32) * (kDP + 1), sX + d * kDP + d + 32, 32);
+        lds_put32(sX + (d + 32) * kDP + d, acc2, -1.f);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x16 z;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) z[q] = 0.f;
+        lds_put32(sX + d * kDP + d + 32, z, 1.f);   // clear T: X's upper part must be zero for the next level
+    }
+    __syncthreads();
+    if (nb == 128) {
+        const f32x16 acc = lds_mm64<RowK, KRow>(sA + 64 * kDP, sX);                  // T = L21 X11
+        lds_put64(sX + 64, acc, 1.f);
+        __syncthreads();
+        const f32x16 acc2 = lds_mm64<RowK, KRow>(sX + 64 * (kDP + 1), sX + 64);       // X21 = -X22 T
+        lds_put64(sX + 64 * kDP, acc2, -1.f);
+        __syncthreads();
+    }
+
     for (int f = t; f < nb * nf4; f += 256) {
         const int r = f / nf4, c = 4 * (f % nf4);
         f32x4 l = *reinterpret_cast<const f32x4*>(sA + r * kDP + c);
@@ -305,10 +439,7 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
         *reinterpret_cast<f32x4*>(Lbuf + (o + r) * ld + o + c) = l;
         *reinterpret_cast<f32x4*>(Pbuf + (o + r) * ld + o + c) = x;
     }
-    if (t == 0) {   // the trailing half is factored first: its failure is met first
-        if (fail[1] >= 0) atomicCAS(info, 0, (int32_t)(o + 64 + fail[1] + 1));
-        if (fail[0] >= 0) atomicCAS(info, 0, (int32_t)(o + fail[0] + 1));
-    }
+    if (t == 0 && sfail >= 0) atomicCAS(info, 0, (int32_t)(o + sfail + 1));
 }
 
 // ------------------------------------------------------ recursive GEMMs

@@ -286,6 +286,22 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
 
 // ------------------------------------------------------ propagation
 
+// Workgroups are dealt to the eight XCDs round-robin (workgroup p runs on
+// XCD p % 8), each XCD with its own L2.  Consecutive list entries share
+// most of their operands (the same block column of neighbouring rows), so
+// groups of kXcdGroup consecutive entries are sent to one XCD: within each
+// run of 8 * kXcdGroup workgroups, p -> entry (p % 8) * kXcdGroup + p / 8.
+// The longest-first order survives at the granularity of a run.
+constexpr int kXcdGroup = 4;
+
+__device__ __forceinline__ unsigned xcd_entry(unsigned p, unsigned n)
+{
+    constexpr unsigned run = 8u * kXcdGroup;
+    if (p >= n / run * run) return p;   // ragged last run: identity
+    const unsigned r = p % run;
+    return p - r + (r % 8u) * kXcdGroup + r / 8u;
+}
+
 typedef Gemm<1, 4, RowK, RowK> RowBlk;   // stage 1: 64 rows (one tile row) x 256 cols
 typedef Gemm<4, 1, RowK, KRow> ColBlk;   // stage 2: 256 rows x 64 cols (one tile column)
 
@@ -421,7 +437,7 @@ __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, 
                                                    const uint32_t* __restrict__ list)
 {
     __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
-    const uint32_t e = list[blockIdx.x];
+    const uint32_t e = list[xcd_entry(blockIdx.x, gridDim.x)];
     const int I = (int)(e >> 16), b = (int)(e & 0xffffu);
     if (I < rows_lo(K0, Nt) || I > rows_hi(mid, Mt)) return;
     const RowSpan s(I, K0, mid, K1, Nt);
@@ -448,7 +464,7 @@ __global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, 
                                                    const uint32_t* __restrict__ list)
 {
     __shared__ __align__(16) float lds[ColBlk::LDS_FLOATS];
-    const uint32_t e = list[blockIdx.x];
+    const uint32_t e = list[xcd_entry(blockIdx.x, gridDim.x)];
     const int J = (int)(e >> 16), b = (int)(e & 0xffffu);
     if (J < cols_lo(mid, Mt) || J > cols_hi(K1, Nt)) return;
     const ColSpan s(J, K0, mid, K1, Mt);
