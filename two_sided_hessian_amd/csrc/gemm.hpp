@@ -21,7 +21,10 @@ namespace bk {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBK = 32;   // K chunk staged in LDS
+#ifndef BAKRON_KBK
+#define BAKRON_KBK 32
+#endif
+constexpr int kBK = BAKRON_KBK;   // K chunk staged in LDS
 constexpr int kPad = 4;   // LDS row padding in floats (keeps 16-byte alignment)
 
 // How an operand is stored in global memory, for operand element (r, k)
