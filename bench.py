@@ -43,7 +43,7 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="sq8192_mixed")
-    ap.add_argument("--cpu-sample", type=int, default=3072,
+    ap.add_argument("--cpu-sample", type=int, default=4608,
                     help="edge of the leading block the oracle baseline solves (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel roofline pass")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
