@@ -150,6 +150,43 @@ int bakron_solve(const float* W, int64_t m, int64_t n,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Workspace bytes that bakron_gptq needs for an m x n weight
+ * (0 when m == 0 or n == 0).  Deterministic; does not touch the device.
+ */
+size_t bakron_gptq_workspace_bytes(int64_t m, int64_t n);
+
+/*
+ * bakron_gptq -- the one-sided case B = I of bakron_solve, i.e. GPTQ with the
+ * input-side Hessian A ([S] setup: GPTQ's Hessian is A (x) I; [N5]: GPTQ as
+ * the one-sided comparison point).
+ *
+ * Returns what bakron_solve returns when P_B is the identity: with B = I an
+ * error e at (i, j) only changes later columns of the same row i, by
+ * -e P_A[j', j], so rows are independent and column j of every row is
+ * rounded at step j (n dependent steps, O(m n^2) work).  The rounding rule,
+ * the float32 arithmetic and the grid contract are those of bakron_solve.
+ *
+ * W        [in]  m x n.  Not modified.
+ * m, n     [in]  0 <= m, n <= BAKRON_MAX_DIM; m == 0 or n == 0 enqueues
+ *                nothing.  Any m, n.
+ * L_A      [in]  n x n from bakron_factor(A); only its diagonal is read, and
+ *                only when `objective` is not NULL (may be NULL otherwise).
+ * P_A      [in]  n x n from bakron_factor(A); zero above the diagonal, one on
+ *                it.  16-byte aligned.
+ * scale, zero, maxq [in] as in bakron_solve (m entries each).
+ * V, codes [out] m x n, as in bakron_solve.
+ * err      [out, nullable] m x n raw errors.
+ * objective [out, nullable] one device double: sum_ij (L_A[j,j] e_ij)^2,
+ *                the objective of bakron_solve with L_B = I.
+ * workspace, workspace_bytes [in] scratch, >= bakron_gptq_workspace_bytes(m, n).
+ * stream   [in]  HIP stream.
+ */
+int bakron_gptq(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                const float* scale, const float* zero, const int32_t* maxq,
+                float* V, uint8_t* codes, float* err, double* objective,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Profiling.  The *_profiled calls enqueue exactly the work of the plain
  * call, but launch every kernel with HIP start/stop events recorded around
  * it, then SYNCHRONISE `stream` and report, per kernel, the number of
@@ -186,6 +223,12 @@ int bakron_solve_profiled(const float* W, int64_t m, int64_t n,
                           float* V, uint8_t* codes, float* err, double* objective,
                           void* workspace, size_t workspace_bytes, hipStream_t stream,
                           bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+int bakron_gptq_profiled(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                         const float* scale, const float* zero, const int32_t* maxq,
+                         float* V, uint8_t* codes, float* err, double* objective,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
 
 #ifdef __cplusplus
 }

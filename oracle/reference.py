@@ -34,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "damp", "rev_cholesky", "normalized_inverse", "factor", "quantize",
-    "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform",
+    "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform", "gptq_columns",
     "objective", "objective_from_errors", "implied_errors", "implied_errors_p", "validate",
     "order_colmajor", "order_rowmajor", "order_antidiagonal",
 ]
@@ -175,6 +175,37 @@ def bakron_naive(W, PA, PB, s, z, maxq, order=None):
         e = Wt[i, j] - v
         C[i, j], V[i, j], E[i, j] = c, v, e
         Wt[i:, j:] -= e * np.outer(PB[i:, i], PA[j:, j])
+    return C, V, E
+
+
+# ------------------------------------- one-sided case B = I (GPTQ), by column
+
+def gptq_columns(W, PA, s, z, maxq, rows=None):
+    """The one-sided case B = I of the rounding ([S] setup: GPTQ's Hessian is
+    A (x) I; [N5]).  With P_B = I the update of BaKron-naive,
+    W~[i', j'] -= e P_B[i', i] P_A[j', j], only reaches later columns of the
+    same row, so every row is rounded column by column independently:
+    for j = 0 .. n-1, round column j of all rows, then
+    W~[:, j'] -= e P_A[j', j] for j' > j.
+    ``rows`` selects a subset of the rows (each row depends on nothing else).
+    Returns (codes, V, E) for the selected rows.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    PA = np.asarray(PA, np.float64)
+    s, z, maxq = np.asarray(s), np.asarray(z), np.asarray(maxq)
+    if rows is not None:
+        rows = np.asarray(rows)
+        W, s, z, maxq = W[rows], s[rows], z[rows], maxq[rows]
+    m, n = W.shape
+    Wt = W.copy()
+    C = np.zeros((m, n))
+    V = np.zeros((m, n))
+    E = np.zeros((m, n))
+    for j in range(n):
+        c, v = quantize(Wt[:, j], s, z, maxq)
+        e = Wt[:, j] - v
+        C[:, j], V[:, j], E[:, j] = c, v, e
+        Wt[:, j + 1:] -= np.outer(e, PA[j + 1:, j])
     return C, V, E
 
 

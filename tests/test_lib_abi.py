@@ -30,7 +30,8 @@ def test_header_declares_the_api():
     names = _declared()
     assert names == sorted(["bakron_version", "bakron_strerror", "bakron_factor_workspace_bytes",
                             "bakron_factor", "bakron_solve_workspace_bytes", "bakron_solve",
-                            "bakron_factor_profiled", "bakron_solve_profiled"])
+                            "bakron_factor_profiled", "bakron_solve_profiled",
+                            "bakron_gptq_workspace_bytes", "bakron_gptq", "bakron_gptq_profiled"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -62,6 +63,10 @@ def test_host_only_calls(B):
     assert B.solve_workspace_bytes(100, 70) >= 3 * 128 * 128 * 4 + 128 * 128 * 4 + 128 * 128 * 4
     assert B.factor_workspace_bytes(8192) >= 4096 * 4096 * 4
     assert B.factor_workspace_bytes(100) >= 2 * 128 * 128 * 4
+    # the one-sided path: working weights and errors, padded copy of P_A when ragged
+    assert B.gptq_workspace_bytes(0, 64) == 0
+    assert B.gptq_workspace_bytes(128, 128) >= 2 * 128 * 128 * 4
+    assert B.gptq_workspace_bytes(100, 70) >= 2 * 128 * 128 * 4 + 128 * 128 * 4
 
 
 def test_host_side_argument_errors(B):
@@ -95,6 +100,20 @@ def test_host_side_argument_errors(B):
     assert L.bakron_solve(*a) == -3
     a = list(args); a[4] = ctypes.c_void_p(4104)   # misaligned P_A
     assert L.bakron_solve(*a) == -4
+    # bakron_gptq(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, err, objective, ws, bytes, stream)
+    g = [fake, 64, 64, fake, fake, fake, fake, fake, fake, fake, None, None, fake, 1 << 30, None]
+    a = list(g); a[4] = None
+    assert L.bakron_gptq(*a) == -1
+    a = list(g); a[2] = 65537
+    assert L.bakron_gptq(*a) == -2
+    a = list(g); a[1] = 0
+    assert L.bakron_gptq(*a) == 0
+    a = list(g); a[11] = fake; a[3] = None          # objective requested without L_A
+    assert L.bakron_gptq(*a) == -1
+    a = list(g); a[13] = 100
+    assert L.bakron_gptq(*a) == -3
+    a = list(g); a[4] = ctypes.c_void_p(4104)
+    assert L.bakron_gptq(*a) == -4
 
 
 def test_profiled_calls_reject_bad_arguments_on_host(B):

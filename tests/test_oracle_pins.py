@@ -202,6 +202,39 @@ def test_special_case_B_identity_is_gptq():
     assert np.array_equal(c, g)
 
 
+def test_gptq_columns_is_textbook_gptq():
+    # the column-by-column form of the case B = I against textbook GPTQ
+    # (Cholesky of the inverse Hessian), an independent formula path
+    d = make_problem(24, 80, 13)
+    fa = R.factor(d["A"])
+    c, V, E = R.gptq_columns(d["W"], fa["P"], d["scale"], d["zero"], d["maxq"])
+    g = _textbook_gptq_rows(d["W"], fa["Ad"], d["scale"], d["zero"], d["maxq"])
+    assert np.array_equal(c, g)
+    np.testing.assert_allclose(V, R._values(c, d["scale"], d["zero"]), rtol=0, atol=1e-15)
+
+
+def test_gptq_columns_is_bakron_with_identity_b():
+    # same codes, values and errors as BaKron-naive with P_B = I, in the
+    # anti-diagonal order (Theorem 3.2: any linear extension)
+    d = make_problem(18, 40, 14)
+    fa = R.factor(d["A"])
+    PB = np.eye(18)
+    c1, V1, E1 = R.gptq_columns(d["W"], fa["P"], d["scale"], d["zero"], d["maxq"])
+    c2, V2, E2 = R.bakron_naive(d["W"], fa["P"], PB, d["scale"], d["zero"], d["maxq"],
+                                order=R.order_antidiagonal(18, 40))
+    assert np.array_equal(c1, c2)
+    np.testing.assert_allclose(E1, E2, rtol=0, atol=1e-12)
+
+
+def test_gptq_columns_rows_are_independent():
+    d = make_problem(30, 50, 15)
+    fa = R.factor(d["A"])
+    c, V, E = R.gptq_columns(d["W"], fa["P"], d["scale"], d["zero"], d["maxq"])
+    rows = np.array([29, 3, 17])
+    cs, Vs, Es = R.gptq_columns(d["W"], fa["P"], d["scale"], d["zero"], d["maxq"], rows=rows)
+    assert np.array_equal(cs, c[rows]) and np.array_equal(Es, E[rows])
+
+
 def test_special_case_A_identity_is_columnwise_gptq():
     d = make_problem(48, 20, 4, global_grid=True)
     fb = R.factor(d["B"])

@@ -34,6 +34,8 @@ SIGNATURES = {
     "bakron_solve_workspace_bytes": (_SZ, [_I64, _I64]),
     "bakron_solve": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                     _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "bakron_gptq_workspace_bytes": (_SZ, [_I64, _I64]),
+    "bakron_gptq": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
 }
 
 
@@ -48,6 +50,7 @@ BAKRON_MAX_KERNEL_KINDS = 32
 _PSTAT = ctypes.POINTER(KernelStat)
 SIGNATURES["bakron_factor_profiled"] = (ctypes.c_int, SIGNATURES["bakron_factor"][1] + [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_solve_profiled"] = (ctypes.c_int, SIGNATURES["bakron_solve"][1] + [_PSTAT, ctypes.c_int32, _VP])
+SIGNATURES["bakron_gptq_profiled"] = (ctypes.c_int, SIGNATURES["bakron_gptq"][1] + [_PSTAT, ctypes.c_int32, _VP])
 
 _lib = None
 
@@ -113,6 +116,10 @@ def factor_workspace_bytes(n: int) -> int:
 
 def solve_workspace_bytes(m: int, n: int) -> int:
     return lib().bakron_solve_workspace_bytes(int(m), int(n))
+
+
+def gptq_workspace_bytes(m: int, n: int) -> int:
+    return lib().bakron_gptq_workspace_bytes(int(m), int(n))
 
 
 def _stats_out():
@@ -195,4 +202,43 @@ def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objectiv
         profile.extend(_stats_list(arr, cnt))
     if rc != BAKRON_SUCCESS:
         raise BakronError(rc, "bakron_solve")
+    return out
+
+
+def gptq(W, LA, PA, scale, zero, maxq, *, want_err=False, want_objective=True, out=None, ws=None, stream=None,
+         profile=None):
+    """bakron_gptq (the one-sided case B = I): returns dict(V, codes, err?,
+    objective?) of device tensors.  ``profile``: as in factor()."""
+    m, n = W.shape
+    _check_dev("W", W, torch.float32, (m, n))
+    _check_dev("P_A", PA, torch.float32, (n, n))
+    _check_dev("scale", scale, torch.float32, (m,))
+    _check_dev("zero", zero, torch.float32, (m,))
+    _check_dev("maxq", maxq, torch.int32, (m,))
+    if want_objective:
+        _check_dev("L_A", LA, torch.float32, (n, n))
+    dev = W.device
+    if out is None:
+        out = {
+            "V": torch.empty((m, n), dtype=torch.float32, device=dev),
+            "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
+        }
+        if want_err:
+            out["err"] = torch.empty((m, n), dtype=torch.float32, device=dev)
+        if want_objective:
+            out["objective"] = torch.empty((1,), dtype=torch.float64, device=dev)
+    need = gptq_workspace_bytes(m, n)
+    if ws is None:
+        ws = workspace(need, dev)
+    args = [_ptr(W), m, n, _ptr(LA) if want_objective else None, _ptr(PA), _ptr(scale), _ptr(zero), _ptr(maxq),
+            _ptr(out["V"]), _ptr(out["codes"]), _ptr(out.get("err")), _ptr(out.get("objective")), _ptr(ws),
+            ws.numel(), _stream(stream)]
+    if profile is None:
+        rc = lib().bakron_gptq(*args)
+    else:
+        arr, cnt = _stats_out()
+        rc = lib().bakron_gptq_profiled(*args, arr, BAKRON_MAX_KERNEL_KINDS, ctypes.byref(cnt))
+        profile.extend(_stats_list(arr, cnt))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_gptq")
     return out

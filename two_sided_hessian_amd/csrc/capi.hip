@@ -115,6 +115,54 @@ int bakron_solve_profiled(const float* W, int64_t m, int64_t n, const float* L_A
     return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
 }
 
+size_t bakron_gptq_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return 0;
+    return bk::gptq_workspace_bytes(m, n);
+}
+
+static int check_gptq(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A, const float* scale,
+                      const float* zero, const int32_t* maxq, float* V, uint8_t* codes, double* objective,
+                      void* workspace, size_t workspace_bytes)
+{
+    if (!W || !P_A || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && !L_A) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(P_A)) return BAKRON_ERR_BAD_ARG;
+    return check_ws(workspace, workspace_bytes, bk::gptq_workspace_bytes(m, n));
+}
+
+int bakron_gptq(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A, const float* scale,
+                const float* zero, const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    const int c = check_gptq(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, objective, workspace, workspace_bytes);
+    if (c) return c;
+    return bk::gptq_enqueue(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, err, objective, workspace, stream,
+                            nullptr)
+               ? BAKRON_ERR_HIP
+               : BAKRON_SUCCESS;
+}
+
+int bakron_gptq_profiled(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                         const float* scale, const float* zero, const int32_t* maxq, float* V, uint8_t* codes,
+                         float* err, double* objective, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                         bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)
+{
+    if (!n_stats || (max_stats > 0 && !stats)) return BAKRON_ERR_NULL_POINTER;
+    *n_stats = 0;
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    const int c = check_gptq(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, objective, workspace, workspace_bytes);
+    if (c) return c;
+    bk::Prof prof;
+    const int rc = bk::gptq_enqueue(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, err, objective, workspace,
+                                    stream, &prof);
+    const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
+    return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
 }  // extern "C"
 
 namespace bk {
@@ -124,7 +172,8 @@ const char* kernel_name(int kind)
     static const char* const names[KK_COUNT] = {
         "k_copy_pad", "k_leaf", "k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_obj_reduce",
         "k_sched", "k_clear_info", "k_diag_mean", "k_load_damped", "k_f_diag", "k_f_panel", "k_f_tile<0>",
-        "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish"};
+        "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish", "k_gptq_load",
+        "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 
