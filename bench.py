@@ -31,6 +31,7 @@ import numpy as np  # noqa: E402
 PEAK_FP32_MFMA_TFLOPS = 157.3     # MI355X dense fp32 matrix peak
 PEAK_HBM_GBS = 8000.0             # MI355X HBM3E
 PAGES_8192_SECONDS = 1.839        # the pages' BaKron time at 8192 x 8192 (another GPU): context
+PAGES_GPTQ_8192_SECONDS = 0.059   # the pages' GPTQ time on the same matrix and GPU: context
 
 
 def log(msg):
@@ -46,6 +47,8 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=4608,
                     help="edge of the leading block the oracle baseline solves (0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel roofline pass")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the secondary paths (the one-sided case B = I) measured beside the step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
     args = ap.parse_args()
@@ -170,6 +173,12 @@ def main():
             roofline_mfma = roofline_entry(*max(mf, key=lambda kv: kv[1]["total_ms"]), traffic)
         log(f"[bench] kernels: {json.dumps(kernels)}")
 
+    nxt = None
+    if not args.no_next:
+        traffic = None if args.no_profile else load_traffic(spec.name)
+        nxt = {"gptq": bench_gptq(B, T, fa, m, n, args, traffic)}
+        nxt.update(bench_factors(B, WL, spec, dev, args, traffic))
+
     cpu = None
     if args.cpu_sample > 0:
         cpu = cpu_baseline(d, args.cpu_sample, m, n)
@@ -199,9 +208,111 @@ def main():
         "roofline": roofline,
         "roofline_mfma": roofline_mfma,
         "kernels": kernels,
+        "next": nxt,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def bench_gptq(B, T, fa, m, n, args, traffic):
+    """The one-sided case B = I (bakron_gptq) on the same layer and the same
+    factor of A, inputs resident: mean time over args.steps calls after
+    args.warmup, its algorithmic rate (m n^2 flops: the triangular product
+    E P_A^T), and the roofline object of its dominant kernel."""
+    import torch
+    dev = T["W"].device
+    ws = B._binding.workspace(B.gptq_workspace_bytes(m, n), dev)
+    out = {"V": torch.empty((m, n), device=dev), "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
+           "objective": torch.empty(1, dtype=torch.float64, device=dev)}
+    stream = torch.cuda.current_stream()
+
+    def call(profile=None):
+        B.gptq(T["W"], fa[0], fa[1], T["scale"], T["zero"], T["maxq"], out=out, ws=ws, stream=stream,
+               profile=profile)
+
+    for _ in range(args.warmup):
+        call()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        call()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    alg = float(m) * n * n
+    res = {"entry": "bakron_gptq", "ms": round(ms, 4), "alg_tflops": round(alg / (ms * 1e-3) / 1e12, 3),
+           "vs_pages": round(ms * 1e-3 / PAGES_GPTQ_8192_SECONDS, 5) if (m, n) == (8192, 8192) else None,
+           "objective": float(out["objective"].item()), "roofline": None, "kernels": None}
+    log(f"[bench] one-sided (B = I): {ms:.3f} ms per call")
+    if not args.no_profile:
+        prof = []
+        call(profile=prof)
+        agg = {r["name"]: r for r in prof}
+        res["kernels"] = {k: {"launches": v["launches"], "total_ms": round(v["total_ms"], 4),
+                              "avg_us": round(1e3 * v["total_ms"] / v["launches"], 3)} for k, v in agg.items()}
+        dom = max(agg.items(), key=lambda kv: kv[1]["total_ms"])
+        res["roofline"] = roofline_entry(*dom, traffic)
+    return res
+
+
+def bench_factors(B, WL, spec, dev, args, traffic):
+    """Kronecker-factor construction from the layer's per-sample inputs
+    (X: N x n activations, G: N x m output gradients, sample-major, resident):
+    K-FAC A = E[a a^T], B = E[b b^T], and one-step Shampoo A = E[|b|^2 a a^T],
+    B = E[|a|^2 b b^T].  Mean time over args.steps after args.warmup; the
+    algorithmic rate counts the lower triangles, N n (n + 1) flops per factor
+    (plus the weights and the norms for Shampoo)."""
+    import torch
+    S = WL.samples(spec)
+    X = torch.from_numpy(S["X"]).to(dev)
+    G = torch.from_numpy(S["G"]).to(dev)
+    del S
+    N, n = X.shape
+    m = G.shape[1]
+    A = torch.zeros((n, n), device=dev)
+    Bm = torch.zeros((m, m), device=dev)
+    wa = torch.empty(N, device=dev)
+    wb = torch.empty(N, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def kfac(profile=None):
+        B.moment(X, out=A, stream=stream, profile=profile)
+        B.moment(G, out=Bm, stream=stream, profile=profile)
+
+    def shampoo(profile=None):
+        B.row_sqnorms(X, out=wa, stream=stream)
+        B.row_sqnorms(G, out=wb, stream=stream)
+        B.moment(X, wb, out=A, stream=stream, profile=profile)
+        B.moment(G, wa, out=Bm, stream=stream, profile=profile)
+
+    fl = float(N) * (n * (n + 1.0) + m * (m + 1.0))
+    res = {}
+    for name, fn, extra in (("kfac", kfac, 0.0), ("shampoo", shampoo, 4.0 * N * (n + m))):
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        r = {"entry": "bakron_moment" + (" + bakron_row_sqnorms" if extra else ""), "N": N, "n": n, "m": m,
+             "ms": round(ms, 4), "alg_tflops": round((fl + extra) / (ms * 1e-3) / 1e12, 3), "roofline": None}
+        log(f"[bench] {name} factors: {ms:.3f} ms")
+        if not args.no_profile:
+            prof = []
+            fn(profile=prof)
+            agg = {}
+            for x in prof:
+                a = agg.setdefault(x["name"], {"launches": 0, "total_ms": 0.0, "alg_flops": 0.0, "alg_bytes": 0.0})
+                for k in ("launches", "total_ms", "alg_flops", "alg_bytes"):
+                    a[k] += x[k]
+            r["roofline"] = roofline_entry(*max(agg.items(), key=lambda kv: kv[1]["total_ms"]), traffic)
+        res[name] = r
+    return res
 
 
 # Which roofline bounds each kernel: the dense contractions run on the fp32
@@ -210,8 +321,10 @@ def main():
 # reduction) are chains of dependent vector arithmetic and LDS traffic,
 # priced against the fp32 vector peak.
 MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_f_panel", "k_f_right",
-                "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>"}
-HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info"}
+                "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_gptq_update",
+                "k_gptq_update_t", "k_moment<false>", "k_moment<true>"}
+HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info", "k_gptq_load",
+               "k_row_sqnorms"}
 PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector
 
 

@@ -187,6 +187,45 @@ int bakron_gptq(const float* W, int64_t m, int64_t n, const float* L_A, const fl
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Kronecker factors from per-sample inputs ([S], Hessian choices): with
+ * input activations a_t (n) and output gradients b_t (m) of N samples,
+ *   K-FAC-style independence:          A = E[a a^T],        B = E[b b^T];
+ *   Shampoo-style, one power-iteration step of the nearest Kronecker
+ *   product from the identity:         A = E[|b|^2 a a^T],  B = E[|a|^2 b b^T].
+ * Both are weighted second moments of a sample-major matrix, built from the
+ * two calls below (the weights |y_t|^2 come from bakron_row_sqnorms of the
+ * other side's samples; scale = 1 / N).
+ */
+
+/*
+ * bakron_row_sqnorms -- out[t] = sum_i X[t, i]^2 for t < N.
+ *
+ * X      [in]  N x n, row-major (row t = sample t); 16-byte aligned.
+ * N, n   [in]  N >= 0, 0 <= n <= BAKRON_MAX_DIM, n a multiple of 4
+ *              (BAKRON_ERR_BAD_ARG otherwise); N == 0 or n == 0 enqueues
+ *              nothing.
+ * out    [out] N floats.
+ * stream [in]  HIP stream.
+ */
+int bakron_row_sqnorms(const float* X, int64_t N, int64_t n, float* out, hipStream_t stream);
+
+/*
+ * bakron_moment -- M = scale * sum_t w_t x_t x_t^T  (x_t = row t of X).
+ *
+ * X      [in]  N x n, row-major (row t = sample t); 16-byte aligned.
+ * N, n   [in]  as in bakron_row_sqnorms; n == 0 enqueues nothing, N == 0
+ *              writes zeros.
+ * w      [in, nullable] N per-sample weights; NULL means w_t = 1 (K-FAC).
+ * scale  [in]  finite (1 / N for an expectation).
+ * M      [out] n x n.  The lower triangle and the diagonal are written, the
+ *              strict upper triangle is not touched (bakron_factor reads
+ *              only the lower triangle and the diagonal).
+ * stream [in]  HIP stream.
+ */
+int bakron_moment(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M,
+                  hipStream_t stream);
+
+/*
  * Profiling.  The *_profiled calls enqueue exactly the work of the plain
  * call, but launch every kernel with HIP start/stop events recorded around
  * it, then SYNCHRONISE `stream` and report, per kernel, the number of
@@ -229,6 +268,10 @@ int bakron_gptq_profiled(const float* W, int64_t m, int64_t n, const float* L_A,
                          float* V, uint8_t* codes, float* err, double* objective,
                          void* workspace, size_t workspace_bytes, hipStream_t stream,
                          bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+int bakron_moment_profiled(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M,
+                           hipStream_t stream, bakron_kernel_stat* stats, int32_t max_stats,
+                           int32_t* n_stats);
 
 #ifdef __cplusplus
 }

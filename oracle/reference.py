@@ -35,11 +35,47 @@ import numpy as np
 __all__ = [
     "damp", "rev_cholesky", "normalized_inverse", "factor", "quantize",
     "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform", "gptq_columns",
+    "kron_moment", "row_sqnorms", "kfac_factors", "shampoo_factors",
     "objective", "objective_from_errors", "implied_errors", "implied_errors_p", "validate",
     "order_colmajor", "order_rowmajor", "order_antidiagonal",
 ]
 
 _f32 = np.float32
+
+
+# ------------------------------------------- Kronecker factors from samples
+
+def row_sqnorms(X) -> np.ndarray:
+    """|x_t|^2 for every row x_t of the sample-major matrix X (float64)."""
+    X = np.asarray(X, np.float64)
+    return np.sum(X * X, axis=1)
+
+
+def kron_moment(X, w=None, scale=None) -> np.ndarray:
+    """M = scale * sum_t w_t x_t x_t^T, x_t = row t of X, in float64
+    (scale defaults to 1 / N: an expectation over the samples)."""
+    X = np.asarray(X, np.float64)
+    N = X.shape[0]
+    if scale is None:
+        scale = 1.0 / N
+    Xw = X if w is None else X * np.asarray(w, np.float64)[:, None]
+    return scale * (Xw.T @ X)
+
+
+def kfac_factors(Xa, Xb):
+    """K-FAC-style independence ([S], Hessian choices): the Hessian of the
+    layer, E[(a (x) b)(a (x) b)^T] = E[a a^T (x) b b^T], is replaced by
+    E[a a^T] (x) E[b b^T].  Xa (N x n) holds the input activations a_t,
+    Xb (N x m) the output gradients b_t, one sample per row."""
+    return kron_moment(Xa), kron_moment(Xb)
+
+
+def shampoo_factors(Xa, Xb):
+    """Shampoo-style ([S], Hessian choices): one power-iteration step of the
+    nearest Kronecker product A (x) B to E[a a^T (x) b b^T], started from the
+    identity on the other side, gives A = E[|b|^2 a a^T] and
+    B = E[|a|^2 b b^T]."""
+    return kron_moment(Xa, row_sqnorms(Xb)), kron_moment(Xb, row_sqnorms(Xa))
 
 
 # ---------------------------------------------------------------- factor step

@@ -31,7 +31,8 @@ def test_header_declares_the_api():
     assert names == sorted(["bakron_version", "bakron_strerror", "bakron_factor_workspace_bytes",
                             "bakron_factor", "bakron_solve_workspace_bytes", "bakron_solve",
                             "bakron_factor_profiled", "bakron_solve_profiled",
-                            "bakron_gptq_workspace_bytes", "bakron_gptq", "bakron_gptq_profiled"])
+                            "bakron_gptq_workspace_bytes", "bakron_gptq", "bakron_gptq_profiled",
+                            "bakron_row_sqnorms", "bakron_moment", "bakron_moment_profiled"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -114,6 +115,19 @@ def test_host_side_argument_errors(B):
     assert L.bakron_gptq(*a) == -3
     a = list(g); a[4] = ctypes.c_void_p(4104)
     assert L.bakron_gptq(*a) == -4
+    # bakron_moment(X, N, n, w, scale, M, stream) / bakron_row_sqnorms(X, N, n, out, stream)
+    one = ctypes.c_float(1.0)
+    assert L.bakron_moment(fake, 16, 6, None, one, fake, None) == -4            # n not a multiple of 4
+    assert L.bakron_moment(ctypes.c_void_p(4100), 16, 8, None, one, fake, None) == -4   # misaligned X
+    assert L.bakron_moment(fake, -1, 8, None, one, fake, None) == -2
+    assert L.bakron_moment(fake, 16, 65540, None, one, fake, None) == -2
+    assert L.bakron_moment(None, 16, 8, None, one, fake, None) == -1
+    assert L.bakron_moment(fake, 16, 8, None, one, None, None) == -1
+    assert L.bakron_moment(fake, 16, 8, None, ctypes.c_float(float("nan")), fake, None) == -4
+    assert L.bakron_moment(None, 16, 0, None, one, None, None) == 0
+    assert L.bakron_row_sqnorms(fake, 16, 10, fake, None) == -4
+    assert L.bakron_row_sqnorms(fake, 16, 8, None, None) == -1
+    assert L.bakron_row_sqnorms(None, 0, 0, None, None) == 0
 
 
 def test_profiled_calls_reject_bad_arguments_on_host(B):

@@ -36,6 +36,8 @@ SIGNATURES = {
                                     _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "bakron_gptq_workspace_bytes": (_SZ, [_I64, _I64]),
     "bakron_gptq": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "bakron_row_sqnorms": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP]),
+    "bakron_moment": (ctypes.c_int, [_VP, _I64, _I64, _VP, ctypes.c_float, _VP, _VP]),
 }
 
 
@@ -51,6 +53,7 @@ _PSTAT = ctypes.POINTER(KernelStat)
 SIGNATURES["bakron_factor_profiled"] = (ctypes.c_int, SIGNATURES["bakron_factor"][1] + [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_solve_profiled"] = (ctypes.c_int, SIGNATURES["bakron_solve"][1] + [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_gptq_profiled"] = (ctypes.c_int, SIGNATURES["bakron_gptq"][1] + [_PSTAT, ctypes.c_int32, _VP])
+SIGNATURES["bakron_moment_profiled"] = (ctypes.c_int, SIGNATURES["bakron_moment"][1] + [_PSTAT, ctypes.c_int32, _VP])
 
 _lib = None
 
@@ -242,3 +245,52 @@ def gptq(W, LA, PA, scale, zero, maxq, *, want_err=False, want_objective=True, o
     if rc != BAKRON_SUCCESS:
         raise BakronError(rc, "bakron_gptq")
     return out
+
+
+def row_sqnorms(X, *, out=None, stream=None):
+    """bakron_row_sqnorms: out[t] = |X[t, :]|^2 (device float32, N)."""
+    N, n = X.shape
+    _check_dev("X", X, torch.float32, (N, n))
+    if out is None:
+        out = torch.empty((N,), dtype=torch.float32, device=X.device)
+    rc = lib().bakron_row_sqnorms(_ptr(X), N, n, _ptr(out), _stream(stream))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_row_sqnorms")
+    return out
+
+
+def moment(X, w=None, scale=None, *, out=None, stream=None, profile=None):
+    """bakron_moment: M = scale * sum_t w_t x_t x_t^T (lower triangle and
+    diagonal written; scale defaults to 1 / N).  ``profile``: as in factor()."""
+    N, n = X.shape
+    _check_dev("X", X, torch.float32, (N, n))
+    if w is not None:
+        _check_dev("w", w, torch.float32, (N,))
+    if scale is None:
+        scale = 1.0 / N if N else 0.0
+    if out is None:
+        out = torch.zeros((n, n), dtype=torch.float32, device=X.device)
+    args = [_ptr(X), N, n, _ptr(w), ctypes.c_float(scale), _ptr(out), _stream(stream)]
+    if profile is None:
+        rc = lib().bakron_moment(*args)
+    else:
+        arr, cnt = _stats_out()
+        rc = lib().bakron_moment_profiled(*args, arr, BAKRON_MAX_KERNEL_KINDS, ctypes.byref(cnt))
+        profile.extend(_stats_list(arr, cnt))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_moment")
+    return out
+
+
+def kfac_factors(Xa, Xb, *, stream=None):
+    """K-FAC-style factors from sample-major activations Xa (N x n) and
+    output gradients Xb (N x m): A = E[a a^T], B = E[b b^T] (lower
+    triangles)."""
+    return moment(Xa, stream=stream), moment(Xb, stream=stream)
+
+
+def shampoo_factors(Xa, Xb, *, stream=None):
+    """Shampoo-style factors after one power-iteration step from the
+    identity: A = E[|b|^2 a a^T], B = E[|a|^2 b b^T] (lower triangles)."""
+    wa, wb = row_sqnorms(Xa, stream=stream), row_sqnorms(Xb, stream=stream)
+    return moment(Xa, wb, stream=stream), moment(Xb, wa, stream=stream)

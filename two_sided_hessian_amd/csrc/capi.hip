@@ -163,6 +163,47 @@ int bakron_gptq_profiled(const float* W, int64_t m, int64_t n, const float* L_A,
     return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
 }
 
+static int check_samples(const float* X, int64_t N, int64_t n)
+{
+    if (N < 0 || n < 0 || n > BAKRON_MAX_DIM || N > ((int64_t)1 << 40)) return BAKRON_ERR_BAD_SIZE;
+    if (n == 0) return BAKRON_SUCCESS;
+    if (!X) return BAKRON_ERR_NULL_POINTER;
+    if (n % 4 != 0 || !bk::aligned16(X)) return BAKRON_ERR_BAD_ARG;
+    return BAKRON_SUCCESS;
+}
+
+int bakron_row_sqnorms(const float* X, int64_t N, int64_t n, float* out, hipStream_t stream)
+{
+    const int c = check_samples(X, N, n);
+    if (c || n == 0 || N == 0) return c;
+    if (!out) return BAKRON_ERR_NULL_POINTER;
+    return bk::sqnorms_enqueue(X, N, n, out, stream, nullptr) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
+int bakron_moment(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M, hipStream_t stream)
+{
+    const int c = check_samples(X, N, n);
+    if (c || n == 0) return c;
+    if (!M) return BAKRON_ERR_NULL_POINTER;
+    if (!isfinite(scale)) return BAKRON_ERR_BAD_ARG;
+    return bk::moment_enqueue(X, N, n, w, scale, M, stream, nullptr) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
+int bakron_moment_profiled(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M,
+                           hipStream_t stream, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)
+{
+    if (!n_stats || (max_stats > 0 && !stats)) return BAKRON_ERR_NULL_POINTER;
+    *n_stats = 0;
+    const int c = check_samples(X, N, n);
+    if (c || n == 0) return c;
+    if (!M) return BAKRON_ERR_NULL_POINTER;
+    if (!isfinite(scale)) return BAKRON_ERR_BAD_ARG;
+    bk::Prof prof;
+    const int rc = bk::moment_enqueue(X, N, n, w, scale, M, stream, &prof);
+    const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
+    return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
 }  // extern "C"
 
 namespace bk {
@@ -173,7 +214,8 @@ const char* kernel_name(int kind)
         "k_copy_pad", "k_leaf", "k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_obj_reduce",
         "k_sched", "k_clear_info", "k_diag_mean", "k_load_damped", "k_f_diag", "k_f_panel", "k_f_tile<0>",
         "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish", "k_gptq_load",
-        "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj"};
+        "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj", "k_row_sqnorms", "k_moment<false>",
+        "k_moment<true>"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 

@@ -25,7 +25,8 @@ namespace bk {
 enum KernelKind {
     KK_COPY_PAD, KK_LEAF, KK_PROP_ROWS, KK_PROP_ROWS_T, KK_PROP_COLS, KK_PROP_COLS_T, KK_OBJ_REDUCE, KK_SCHED,
     KK_F_CLEAR, KK_F_MEAN, KK_F_LOAD, KK_F_DIAG, KK_F_PANEL, KK_F_PANEL_T, KK_F_SYRK_T, KK_F_RIGHT, KK_F_RIGHT_T,
-    KK_F_LEFT, KK_F_LEFT_T, KK_F_FINISH, KK_G_LOAD, KK_G_SWEEP, KK_G_UPDATE, KK_G_UPDATE_T, KK_G_OBJ, KK_COUNT
+    KK_F_LEFT, KK_F_LEFT_T, KK_F_FINISH, KK_G_LOAD, KK_G_SWEEP, KK_G_UPDATE, KK_G_UPDATE_T, KK_G_OBJ,
+    KK_K_SQNORM, KK_K_MOMENT, KK_K_MOMENT_W, KK_COUNT
 };
 static_assert(KK_COUNT <= BAKRON_MAX_KERNEL_KINDS, "kernel kinds exceed the ABI's statistics capacity");
 
@@ -89,5 +90,10 @@ size_t gptq_workspace_bytes(int64_t m, int64_t n);
 int gptq_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA, const float* scale,
                  const float* zero, const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
                  void* ws, hipStream_t stream, Prof* prof);
+
+// Kronecker factors from per-sample inputs (kfac.hip)
+int sqnorms_enqueue(const float* X, int64_t N, int64_t n, float* out, hipStream_t s, Prof* prof);
+int moment_enqueue(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M, hipStream_t s,
+                   Prof* prof);
 
 }  // namespace bk

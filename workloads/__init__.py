@@ -36,7 +36,7 @@ import hashlib
 
 import numpy as np
 
-__all__ = ["Spec", "CONFIGS", "by_name", "generate", "make_problem", "grid_minmax", "digest"]
+__all__ = ["Spec", "CONFIGS", "by_name", "generate", "samples", "make_problem", "grid_minmax", "digest"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -90,13 +90,23 @@ def grid_minmax(W: np.ndarray, maxq: np.ndarray):
     return s.astype(np.float32), z.astype(np.float32)
 
 
-def _factor_input(rng, dim, samples, lognormal):
+def _draw_samples(rng, dim, samples, lognormal):
+    """dim x samples draws (feature-major), with log-normal channel scales."""
     if lognormal:
         sc = np.exp(rng.standard_normal(dim))
     X = rng.standard_normal((dim, samples))
     if lognormal:
         X *= sc[:, None]
-    return X @ X.T / samples
+    return X
+
+
+def _draw_w(rng, spec):
+    m, n = spec.m, spec.n
+    if spec.w_dist == "normal":
+        return rng.standard_normal((m, n)) * spec.w_scale
+    if spec.w_dist == "student5":
+        return rng.standard_t(5, size=(m, n)) * spec.w_scale
+    raise ValueError(spec.w_dist)
 
 
 def generate(spec: Spec, seed: int | None = None, global_grid: bool = False) -> dict:
@@ -106,14 +116,13 @@ def generate(spec: Spec, seed: int | None = None, global_grid: bool = False) -> 
     matrix (same step and zero point on every row; needed when n == 1)."""
     rng = np.random.default_rng(spec.seed if seed is None else seed)
     m, n = spec.m, spec.n
-    if spec.w_dist == "normal":
-        W = rng.standard_normal((m, n)) * spec.w_scale
-    elif spec.w_dist == "student5":
-        W = rng.standard_t(5, size=(m, n)) * spec.w_scale
-    else:
-        raise ValueError(spec.w_dist)
-    A = _factor_input(rng, n, spec.samples, spec.lognormal)
-    B = _factor_input(rng, m, spec.samples, spec.lognormal)
+    W = _draw_w(rng, spec)
+    X = _draw_samples(rng, n, spec.samples, spec.lognormal)
+    A = X @ X.T / spec.samples
+    del X
+    G = _draw_samples(rng, m, spec.samples, spec.lognormal)
+    B = G @ G.T / spec.samples
+    del G
     maxq = np.full(m, 2 ** spec.bits - 1, dtype=np.int32)
     if spec.mixed_low_rows:
         rows = rng.permutation(m)[: spec.mixed_low_rows]
@@ -134,6 +143,21 @@ def generate(spec: Spec, seed: int | None = None, global_grid: bool = False) -> 
         "maxq": maxq,
         "name": spec.name,
     }
+
+
+def samples(spec: Spec, seed: int | None = None) -> dict:
+    """The per-sample inputs behind A and B of ``generate`` (same draws):
+    X (N x n) input activations and G (N x m) output gradients, sample-major
+    (row t is sample t), float32.  ``generate`` forms A = X^T X / N and
+    B = G^T G / N from the float64 draws; these are the float32 samples."""
+    rng = np.random.default_rng(spec.seed if seed is None else seed)
+    _draw_w(rng, spec)
+    X = _draw_samples(rng, spec.n, spec.samples, spec.lognormal)
+    Xs = np.ascontiguousarray(X.T, dtype=np.float32)
+    del X
+    G = _draw_samples(rng, spec.m, spec.samples, spec.lognormal)
+    Gs = np.ascontiguousarray(G.T, dtype=np.float32)
+    return {"X": Xs, "G": Gs, "name": spec.name}
 
 
 def make_problem(m: int, n: int, seed: int, bits: int = 3, samples: int | None = None,
