@@ -178,6 +178,7 @@ def main():
         traffic = None if args.no_profile else load_traffic(spec.name)
         nxt = {"gptq": bench_gptq(B, T, fa, m, n, args, traffic)}
         nxt.update(bench_factors(B, WL, spec, dev, args, traffic))
+        nxt["batch"] = bench_batch(B, WL, dev, args)
 
     cpu = None
     if args.cpu_sample > 0:
@@ -312,6 +313,54 @@ def bench_factors(B, WL, spec, dev, args, traffic):
                     a[k] += x[k]
             r["roofline"] = roofline_entry(*max(agg.items(), key=lambda kv: kv[1]["total_ms"]), traffic)
         res[name] = r
+    return res
+
+
+def bench_batch(B, WL, dev, args, layers=16, name="sq1024"):
+    """Batched solves of independent layers (bakron_solve_batch): `layers`
+    layers of the 1024 x 1024 recipe (seeds 0 ..), factors from
+    bakron_factor, inputs resident; the batch on one stream against the
+    batch spread over four streams (the hardware queues of a process).
+    Reports layers per second and algorithmic TFLOP/s (mn(m+n) per layer)."""
+    import torch
+    spec = WL.by_name(name)
+    probs = []
+    for k in range(layers):
+        d = WL.generate(spec, seed=k)
+        T = {key: torch.from_numpy(np.ascontiguousarray(d[key])).to(dev) for key in ("W", "A", "B", "scale", "zero", "maxq")}
+        LA, PA, _ = B.factor(T["A"], 0.01)
+        LB, PB, _ = B.factor(T["B"], 0.01)
+        probs.append({"W": T["W"], "LA": LA, "PA": PA, "LB": LB, "PB": PB, "scale": T["scale"],
+                      "zero": T["zero"], "maxq": T["maxq"]})
+    torch.cuda.synchronize()
+    main = torch.cuda.current_stream()
+    res = {"entry": "bakron_solve_batch", "layers": layers, "shape": [spec.m, spec.n]}
+    alg = layers * float(spec.m) * spec.n * (spec.m + spec.n)
+    for ns in (1, 4):
+        streams = [main] if ns == 1 else [torch.cuda.Stream() for _ in range(ns)]
+
+        def run():
+            for s in streams:
+                if s is not main:
+                    s.wait_stream(main)
+            B.solve_batch(probs, streams)
+            for s in streams:
+                if s is not main:
+                    main.wait_stream(s)
+
+        for _ in range(args.warmup):
+            run()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(main)
+        for _ in range(args.steps):
+            run()
+        ev[1].record(main)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        res[f"streams{ns}"] = {"ms": round(ms, 4), "layers_per_s": round(layers / (ms * 1e-3), 1),
+                               "alg_tflops": round(alg / (ms * 1e-3) / 1e12, 3)}
+        log(f"[bench] batch of {layers} {spec.m}x{spec.n} layers on {ns} stream(s): {ms:.3f} ms")
     return res
 
 

@@ -150,6 +150,54 @@ int bakron_solve(const float* W, int64_t m, int64_t n,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Batched solves of independent layers ([S]: every linear layer has its own
+ * W, A and B, so layers share nothing).  One descriptor per layer; the
+ * fields mean what the arguments of bakron_solve mean.
+ */
+typedef struct bakron_layer {
+    const float* W;
+    int64_t m, n;
+    const float* L_A;
+    const float* P_A;
+    const float* L_B;
+    const float* P_B;
+    const float* scale;
+    const float* zero;
+    const int32_t* maxq;
+    float* V;
+    uint8_t* codes;
+    float* err;          /* nullable */
+    double* objective;   /* nullable */
+} bakron_layer;
+
+/*
+ * Workspace bytes for bakron_solve_batch with these layers on n_streams
+ * streams: one slice per stream, each as large as the largest
+ * bakron_solve_workspace_bytes of the layers that stream runs (layer k runs
+ * on stream k % n_streams), every slice 256-byte aligned.  0 when count or
+ * n_streams is not positive.  Host only.
+ */
+size_t bakron_solve_batch_workspace_bytes(const bakron_layer* layers, int32_t count, int32_t n_streams);
+
+/*
+ * bakron_solve_batch -- bakron_solve for `count` independent layers, spread
+ * over the caller's streams: layer k is enqueued on streams[k % n_streams]
+ * with that stream's workspace slice, so layers on one stream run in order
+ * and layers on different streams may run concurrently.  Each layer's
+ * results are those of bakron_solve on the same inputs (the same kernels).
+ *
+ * layers    [in]  host array of `count` descriptors (device pointers inside).
+ * count     [in]  >= 0; 0 enqueues nothing.
+ * workspace, workspace_bytes [in] scratch,
+ *                 >= bakron_solve_batch_workspace_bytes(layers, count, n_streams).
+ * streams   [in]  host array of n_streams HIP streams (1 <= n_streams <= 64).
+ * Every descriptor is checked before anything is enqueued: a bad layer
+ * returns the error bakron_solve would return for it, and nothing runs.
+ */
+int bakron_solve_batch(const bakron_layer* layers, int32_t count, void* workspace, size_t workspace_bytes,
+                       const hipStream_t* streams, int32_t n_streams);
+
+/*
  * Workspace bytes that bakron_gptq needs for an m x n weight
  * (0 when m == 0 or n == 0).  Deterministic; does not touch the device.
  */

@@ -32,7 +32,8 @@ def test_header_declares_the_api():
                             "bakron_factor", "bakron_solve_workspace_bytes", "bakron_solve",
                             "bakron_factor_profiled", "bakron_solve_profiled",
                             "bakron_gptq_workspace_bytes", "bakron_gptq", "bakron_gptq_profiled",
-                            "bakron_row_sqnorms", "bakron_moment", "bakron_moment_profiled"])
+                            "bakron_row_sqnorms", "bakron_moment", "bakron_moment_profiled",
+                            "bakron_solve_batch_workspace_bytes", "bakron_solve_batch"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -128,6 +129,23 @@ def test_host_side_argument_errors(B):
     assert L.bakron_row_sqnorms(fake, 16, 10, fake, None) == -4
     assert L.bakron_row_sqnorms(fake, 16, 8, None, None) == -1
     assert L.bakron_row_sqnorms(None, 0, 0, None, None) == 0
+    # batches: every layer is checked before anything is enqueued
+    from two_sided_hessian_amd._binding import Layer
+    f = 4096
+    good = Layer(f, 64, 64, f, f, f, f, f, f, f, f, f, None, None)
+    bad = Layer(f, 64, 64, f, None, f, f, f, f, f, f, f, None, None)       # no P_A
+    ragged = Layer(f, 100, 70, f, f, f, f, f, f, f, f, f, None, None)
+    arr = (Layer * 3)(good, ragged, bad)
+    st = (ctypes.c_void_p * 2)(None, None)
+    assert L.bakron_solve_batch(arr, 3, fake, 1 << 40, st, 2) == -1
+    assert L.bakron_solve_batch(arr, 2, fake, 100, st, 2) == -3
+    assert L.bakron_solve_batch(arr, 2, fake, 1 << 40, st, 0) == -4
+    assert L.bakron_solve_batch(arr, 0, None, 0, None, 0) == 0
+    # one slice per stream, each sized for its largest layer
+    one = L.bakron_solve_batch_workspace_bytes(arr, 2, 1)
+    two = L.bakron_solve_batch_workspace_bytes(arr, 2, 2)
+    assert one == L.bakron_solve_workspace_bytes(100, 70)
+    assert two == L.bakron_solve_workspace_bytes(64, 64) + L.bakron_solve_workspace_bytes(100, 70)
 
 
 def test_profiled_calls_reject_bad_arguments_on_host(B):

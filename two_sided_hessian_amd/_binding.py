@@ -42,6 +42,18 @@ SIGNATURES = {
 
 
 
+class Layer(ctypes.Structure):
+    """bakron_layer (include/bakron.h)."""
+    _fields_ = [("W", _VP), ("m", _I64), ("n", _I64), ("L_A", _VP), ("P_A", _VP), ("L_B", _VP), ("P_B", _VP),
+                ("scale", _VP), ("zero", _VP), ("maxq", _VP), ("V", _VP), ("codes", _VP), ("err", _VP),
+                ("objective", _VP)]
+
+
+SIGNATURES["bakron_solve_batch_workspace_bytes"] = (_SZ, [ctypes.POINTER(Layer), ctypes.c_int32, ctypes.c_int32])
+SIGNATURES["bakron_solve_batch"] = (ctypes.c_int, [ctypes.POINTER(Layer), ctypes.c_int32, _VP, _SZ,
+                                                   ctypes.POINTER(_VP), ctypes.c_int32])
+
+
 class KernelStat(ctypes.Structure):
     """bakron_kernel_stat (include/bakron.h)."""
     _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double),
@@ -294,3 +306,47 @@ def shampoo_factors(Xa, Xb, *, stream=None):
     identity: A = E[|b|^2 a a^T], B = E[|a|^2 b b^T] (lower triangles)."""
     wa, wb = row_sqnorms(Xa, stream=stream), row_sqnorms(Xb, stream=stream)
     return moment(Xa, wb, stream=stream), moment(Xb, wa, stream=stream)
+
+
+def solve_batch(problems, streams=None, *, want_err=False, want_objective=True, ws=None):
+    """bakron_solve_batch: ``problems`` is a list of dicts with device
+    tensors W, LA, PA, LB, PB, scale, zero, maxq (one per layer); layer k runs
+    on streams[k % len(streams)] (default: the current stream only).
+    Returns one output dict per layer, as solve() does."""
+    if streams is None:
+        streams = [torch.cuda.current_stream()]
+    outs, descs = [], []
+    for p in problems:
+        W = p["W"]
+        m, n = W.shape
+        _check_dev("W", W, torch.float32, (m, n))
+        _check_dev("P_A", p["PA"], torch.float32, (n, n))
+        _check_dev("P_B", p["PB"], torch.float32, (m, m))
+        _check_dev("scale", p["scale"], torch.float32, (m,))
+        _check_dev("zero", p["zero"], torch.float32, (m,))
+        _check_dev("maxq", p["maxq"], torch.int32, (m,))
+        if want_objective:
+            _check_dev("L_A", p["LA"], torch.float32, (n, n))
+            _check_dev("L_B", p["LB"], torch.float32, (m, m))
+        dev = W.device
+        o = {"V": torch.empty((m, n), dtype=torch.float32, device=dev),
+             "codes": torch.empty((m, n), dtype=torch.uint8, device=dev)}
+        if want_err:
+            o["err"] = torch.empty((m, n), dtype=torch.float32, device=dev)
+        if want_objective:
+            o["objective"] = torch.empty((1,), dtype=torch.float64, device=dev)
+        outs.append(o)
+        descs.append(Layer(W.data_ptr(), m, n, p["LA"].data_ptr() if want_objective else None, p["PA"].data_ptr(),
+                           p["LB"].data_ptr() if want_objective else None, p["PB"].data_ptr(),
+                           p["scale"].data_ptr(), p["zero"].data_ptr(), p["maxq"].data_ptr(), o["V"].data_ptr(),
+                           o["codes"].data_ptr(), o["err"].data_ptr() if want_err else None,
+                           o["objective"].data_ptr() if want_objective else None))
+    arr = (Layer * max(1, len(descs)))(*descs)
+    sarr = (_VP * len(streams))(*[s.cuda_stream for s in streams])
+    need = lib().bakron_solve_batch_workspace_bytes(arr, len(descs), len(streams))
+    if ws is None:
+        ws = workspace(need, problems[0]["W"].device if problems else "cuda")
+    rc = lib().bakron_solve_batch(arr, len(descs), _ptr(ws), ws.numel(), sarr, len(streams))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_solve_batch")
+    return outs

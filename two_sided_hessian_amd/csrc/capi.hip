@@ -3,6 +3,8 @@
 // by factor.hip and solve.hip.
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/bakron.h"
 #include "internal.hpp"
 
@@ -113,6 +115,72 @@ int bakron_solve_profiled(const float* W, int64_t m, int64_t n, const float* L_A
                                      workspace, stream, &prof);
     const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
     return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
+static int check_solve_args(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                            const float* L_B, const float* P_B, const float* scale, const float* zero,
+                            const int32_t* maxq, float* V, uint8_t* codes, double* objective)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !P_A || !P_B || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && (!L_A || !L_B)) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(P_A) || !bk::aligned16(P_B)) return BAKRON_ERR_BAD_ARG;
+    return BAKRON_SUCCESS;
+}
+
+constexpr int32_t kMaxBatchStreams = 64;
+
+size_t bakron_solve_batch_workspace_bytes(const bakron_layer* layers, int32_t count, int32_t n_streams)
+{
+    if (!layers || count <= 0 || n_streams <= 0 || n_streams > kMaxBatchStreams) return 0;
+    size_t total = 0;
+    for (int32_t s = 0; s < n_streams; ++s) {
+        size_t need = 0;
+        for (int32_t k = s; k < count; k += n_streams) {
+            const bakron_layer& L = layers[k];
+            if (L.m > 0 && L.n > 0 && L.m <= BAKRON_MAX_DIM && L.n <= BAKRON_MAX_DIM)
+                need = std::max(need, bk::solve_workspace_bytes(L.m, L.n));
+        }
+        total += bk::align_up(need);
+    }
+    return total;
+}
+
+int bakron_solve_batch(const bakron_layer* layers, int32_t count, void* workspace, size_t workspace_bytes,
+                       const hipStream_t* streams, int32_t n_streams)
+{
+    if (count < 0) return BAKRON_ERR_BAD_SIZE;
+    if (count == 0) return BAKRON_SUCCESS;
+    if (!layers || !streams) return BAKRON_ERR_NULL_POINTER;
+    if (n_streams <= 0 || n_streams > kMaxBatchStreams) return BAKRON_ERR_BAD_ARG;
+    for (int32_t k = 0; k < count; ++k) {
+        const bakron_layer& L = layers[k];
+        const int c = check_solve_args(L.W, L.m, L.n, L.L_A, L.P_A, L.L_B, L.P_B, L.scale, L.zero, L.maxq, L.V,
+                                       L.codes, L.objective);
+        if (c) return c;
+    }
+    const size_t need = bakron_solve_batch_workspace_bytes(layers, count, n_streams);
+    const int w = check_ws(workspace, workspace_bytes, need);
+    if (w) return w;
+    // slice s starts after the slices of streams 0 .. s-1
+    char* base = static_cast<char*>(workspace);
+    for (int32_t s = 0; s < n_streams && s < count; ++s) {
+        size_t slice = 0;
+        for (int32_t k = s; k < count; k += n_streams) {
+            const bakron_layer& L = layers[k];
+            if (L.m > 0 && L.n > 0) slice = std::max(slice, bk::solve_workspace_bytes(L.m, L.n));
+        }
+        for (int32_t k = s; k < count; k += n_streams) {
+            const bakron_layer& L = layers[k];
+            if (L.m == 0 || L.n == 0) continue;
+            if (bk::solve_enqueue(L.W, L.m, L.n, L.L_A, L.P_A, L.L_B, L.P_B, L.scale, L.zero, L.maxq, L.V, L.codes,
+                                  L.err, L.objective, base, streams[s], nullptr))
+                return BAKRON_ERR_HIP;
+        }
+        base += bk::align_up(slice);
+    }
+    return BAKRON_SUCCESS;
 }
 
 size_t bakron_gptq_workspace_bytes(int64_t m, int64_t n)
