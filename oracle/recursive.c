@@ -25,6 +25,17 @@
  * clamp(rint(x), 0, maxq) (round half to even), the value is s (c - z) in
  * float64, and the raw error is e = w~ - value.
  *
+ * Tie-following mode (for comparing against another implementation): given
+ * that implementation's codes `follow`, at an entry whose float32 decision x
+ * lies within `tau` grid steps of a rounding boundary (x = k + 1/2) and whose
+ * followed code is the neighbouring one (one step away), the oracle takes the
+ * followed code and counts an adoption.  Near such a boundary float32 and
+ * float64 arithmetic may legitimately round either way (Theorem 3.2's
+ * equality is exact only in exact arithmetic), and one flip changes every
+ * later entry below and to the right; following keeps the two trajectories
+ * together so that every other decision can be compared exactly.  Elsewhere
+ * the oracle keeps its own decision.
+ *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared.  OpenMP only
  * splits the rows of the dense propagation products; the summation order of
  * each dot product is fixed by `omp simd` lanes, so results may differ from a
@@ -47,9 +58,13 @@ typedef struct {
     int32_t* codes;     /* m x n */
     double* V;          /* m x n */
     double* T;          /* scratch: rows x cols of the largest pushed block */
+    const int32_t* follow;   /* NULL, or codes to follow at near-ties */
+    double tau;
+    int64_t adoptions;
 } ctx_t;
 
-static void quant(double w, float s, float z, int32_t maxq, int32_t* code, double* val)
+/* Returns the float32 decision x; sets the code and value. */
+static float quant(double w, float s, float z, int32_t maxq, int32_t* code, double* val)
 {
     float wf = (float)w;
     float x = wf / s;
@@ -59,6 +74,17 @@ static void quant(double w, float s, float z, int32_t maxq, int32_t* code, doubl
     if (c > (float)maxq) c = (float)maxq;
     *code = (int32_t)c;
     *val = (double)s * ((double)c - (double)z);
+    return x;
+}
+
+/* Distance (in grid steps) of x from the nearest rounding boundary k + 1/2
+ * with 0 <= k < maxq (beyond them the clamp decides). */
+static double margin_of(float x, int32_t maxq)
+{
+    double b = floor((double)x) + 0.5;
+    if (b < 0.5) b = 0.5;
+    if (b > (double)maxq - 0.5) b = (double)maxq - 0.5;
+    return fabs((double)x - b);
 }
 
 /* Naive rule on rows [r0,r1) x cols [c0,c1), column-major visiting order. */
@@ -76,7 +102,15 @@ static void leaf_solve(ctx_t* X, int64_t r0, int64_t r1, int64_t c0, int64_t c1)
             int32_t c;
             double v;
             double w = X->Wt[i * n + j];
-            quant(w, X->s[i], X->z[i], X->maxq[i], &c, &v);
+            const float x = quant(w, X->s[i], X->z[i], X->maxq[i], &c, &v);
+            if (X->follow) {
+                const int32_t g = X->follow[i * n + j];
+                if ((g == c + 1 || g == c - 1) && margin_of(x, X->maxq[i]) < X->tau) {
+                    c = g;
+                    v = (double)X->s[i] * ((double)c - (double)X->z[i]);
+                    X->adoptions += 1;
+                }
+            }
             double e = w - v;
             X->codes[i * n + j] = c;
             X->V[i * n + j] = v;
@@ -166,12 +200,16 @@ static void solve_block(ctx_t* X, int64_t r0, int64_t r1, int64_t c0, int64_t c1
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
  * W, PA, PB: float64 row-major; s, z: float32 grid; maxq: int32.
  * Outputs codes (int32), V and E (float64), all m x n row-major.
+ * follow (nullable, m x n int32) and tau select the tie-following mode;
+ * *adoptions (nullable) receives the number of codes taken over.
  */
-int oracle_bakron_recursive(int64_t m, int64_t n, const double* W, const double* PA,
-                            const double* PB, const float* s, const float* z,
-                            const int32_t* maxq, int64_t leaf, int32_t* codes,
-                            double* V, double* E)
+int oracle_bakron_recursive_follow(int64_t m, int64_t n, const double* W, const double* PA,
+                                   const double* PB, const float* s, const float* z,
+                                   const int32_t* maxq, int64_t leaf, int32_t* codes,
+                                   double* V, double* E, const int32_t* follow, double tau,
+                                   int64_t* adoptions)
 {
+    if (adoptions) *adoptions = 0;
     if (m < 0 || n < 0 || leaf < 1) return -1;
     if (m == 0 || n == 0) return 0;
     if (!W || !PA || !PB || !s || !z || !maxq || !codes || !V || !E) return -1;
@@ -179,6 +217,7 @@ int oracle_bakron_recursive(int64_t m, int64_t n, const double* W, const double*
     X.m = m; X.n = n; X.leaf = leaf;
     X.PA = PA; X.PB = PB; X.s = s; X.z = z; X.maxq = maxq;
     X.codes = codes; X.V = V; X.E = E;
+    X.follow = follow; X.tau = tau; X.adoptions = 0;
     X.Wt = (double*)malloc(sizeof(double) * (size_t)(m * n));
     /* largest pushed block: half the rows times all the columns */
     X.T = (double*)malloc(sizeof(double) * (size_t)(((m + 1) / 2 + leaf) * n + 1));
@@ -188,5 +227,14 @@ int oracle_bakron_recursive(int64_t m, int64_t n, const double* W, const double*
     solve_block(&X, 0, m, 0, n);
     free(X.Wt);
     free(X.T);
+    if (adoptions) *adoptions = X.adoptions;
     return 0;
+}
+
+int oracle_bakron_recursive(int64_t m, int64_t n, const double* W, const double* PA,
+                            const double* PB, const float* s, const float* z,
+                            const int32_t* maxq, int64_t leaf, int32_t* codes,
+                            double* V, double* E)
+{
+    return oracle_bakron_recursive_follow(m, n, W, PA, PB, s, z, maxq, leaf, codes, V, E, NULL, 0.0, NULL);
 }

@@ -38,12 +38,20 @@ def _load():
         f.restype = ctypes.c_int
         f.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 6 + \
                      [ctypes.c_int64] + [ctypes.c_void_p] * 3
+        g = lib.oracle_bakron_recursive_follow
+        g.restype = ctypes.c_int
+        g.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 6 + \
+                     [ctypes.c_int64] + [ctypes.c_void_p] * 4 + [ctypes.c_double, ctypes.c_void_p]
         _lib = lib
     return _lib
 
 
-def bakron_recursive(W, PA, PB, s, z, maxq, leaf: int = 32, threads: int | None = None):
-    """Returns (codes int32, V float64, E float64), all m x n."""
+def bakron_recursive(W, PA, PB, s, z, maxq, leaf: int = 32, threads: int | None = None, follow=None,
+                     tau: float = 1e-4):
+    """Returns (codes int32, V float64, E float64), all m x n.
+
+    With ``follow`` (m x n codes of another implementation) the oracle runs in
+    tie-following mode (see recursive.c) and returns (codes, V, E, adoptions)."""
     lib = _load()
     W = np.ascontiguousarray(W, dtype=np.float64)
     PA = np.ascontiguousarray(PA, dtype=np.float64)
@@ -59,9 +67,21 @@ def bakron_recursive(W, PA, PB, s, z, maxq, leaf: int = 32, threads: int | None 
     E = np.zeros((m, n))
     if threads is not None:
         os.environ["OMP_NUM_THREADS"] = str(int(threads))
-    rc = lib.oracle_bakron_recursive(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
-                                     s.ctypes.data, z.ctypes.data, maxq.ctypes.data, int(leaf),
-                                     codes.ctypes.data, V.ctypes.data, E.ctypes.data)
+    if follow is None:
+        rc = lib.oracle_bakron_recursive(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
+                                         s.ctypes.data, z.ctypes.data, maxq.ctypes.data, int(leaf),
+                                         codes.ctypes.data, V.ctypes.data, E.ctypes.data)
+        if rc != 0:
+            raise RuntimeError("oracle_bakron_recursive failed with %d" % rc)
+        return codes, V, E
+    fol = np.ascontiguousarray(follow, dtype=np.int32)
+    if fol.shape != (m, n):
+        raise ValueError("follow must be m x n")
+    adopt = ctypes.c_int64(0)
+    rc = lib.oracle_bakron_recursive_follow(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
+                                            s.ctypes.data, z.ctypes.data, maxq.ctypes.data, int(leaf),
+                                            codes.ctypes.data, V.ctypes.data, E.ctypes.data, fol.ctypes.data,
+                                            float(tau), ctypes.byref(adopt))
     if rc != 0:
-        raise RuntimeError("oracle_bakron_recursive failed with %d" % rc)
-    return codes, V, E
+        raise RuntimeError("oracle_bakron_recursive_follow failed with %d" % rc)
+    return codes, V, E, int(adopt.value)

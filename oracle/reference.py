@@ -216,7 +216,7 @@ def bakron_naive(W, PA, PB, s, z, maxq, order=None):
 
 # ------------------------------------- one-sided case B = I (GPTQ), by column
 
-def gptq_columns(W, PA, s, z, maxq, rows=None):
+def gptq_columns(W, PA, s, z, maxq, rows=None, follow=None, tau=1e-4):
     """The one-sided case B = I of the rounding ([S] setup: GPTQ's Hessian is
     A (x) I; [N5]).  With P_B = I the update of BaKron-naive,
     W~[i', j'] -= e P_B[i', i] P_A[j', j], only reaches later columns of the
@@ -224,7 +224,12 @@ def gptq_columns(W, PA, s, z, maxq, rows=None):
     for j = 0 .. n-1, round column j of all rows, then
     W~[:, j'] -= e P_A[j', j] for j' > j.
     ``rows`` selects a subset of the rows (each row depends on nothing else).
-    Returns (codes, V, E) for the selected rows.
+    ``follow`` (codes of another implementation, for the selected rows) turns
+    on tie following as in recursive.c: where the float32 decision lies
+    within ``tau`` grid steps of a rounding boundary and the followed code is
+    the neighbouring one, it is taken over.
+    Returns (codes, V, E) for the selected rows, and with ``follow`` also the
+    number of codes taken over.
     """
     W = np.asarray(W, dtype=np.float64)
     PA = np.asarray(PA, np.float64)
@@ -237,11 +242,24 @@ def gptq_columns(W, PA, s, z, maxq, rows=None):
     C = np.zeros((m, n))
     V = np.zeros((m, n))
     E = np.zeros((m, n))
+    adopted = 0
     for j in range(n):
         c, v = quantize(Wt[:, j], s, z, maxq)
+        if follow is not None:
+            x = (Wt[:, j].astype(_f32) / s.astype(_f32)).astype(_f32) + z.astype(_f32)
+            x = x.astype(np.float64)
+            bnd = np.clip(np.floor(x) + 0.5, 0.5, maxq - 0.5)
+            g = np.asarray(follow)[:, j].astype(np.float64)
+            take = (np.abs(g - c) == 1) & (np.abs(x - bnd) < tau)
+            if take.any():
+                c = np.where(take, g, c)
+                v = s.astype(np.float64) * (c - z.astype(np.float64))
+                adopted += int(take.sum())
         e = Wt[:, j] - v
         C[:, j], V[:, j], E[:, j] = c, v, e
         Wt[:, j + 1:] -= np.outer(e, PA[j + 1:, j])
+    if follow is not None:
+        return C, V, E, adopted
     return C, V, E
 
 

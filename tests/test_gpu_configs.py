@@ -19,10 +19,11 @@ streams, then the solve.  The checks:
   objective equals sum (L_B,ii e_ij L_A,jj)^2 of the returned errors (1e-6)
   and of the implied errors (1e-3, the objective bar);
 * where the float64 oracle finishes in seconds (up to 4096 x 4096):
-  - same factors: the oracle's own solve with the GPU factors (float64) gives
-    the same code at every entry outside the dependency cone (the entries
-    below and to the right) of the validator's ties, where the trajectories
-    may part;
+  - same factors: the oracle's solve with the GPU factors (float64), following
+    the GPU's code wherever its own decision lies within TAU grid steps of a
+    rounding boundary (both roundings are valid there, and the trajectories
+    would part), gives the same code at every entry, with at most 1e-4 of the
+    entries followed;
   - end to end: against the oracle's solve with its float64 factors, the
     objective within max(1e-3, 5 x the spread recorded in
     tests/golden/trajectory_spread.json), the relative objective gap of two
@@ -128,13 +129,14 @@ def test_config_end_to_end(name):
     assert obj == pytest.approx(R.objective_from_errors(E, LA, LB), rel=1e-3)
 
     if name in FULL_ORACLE:
-        # same factors: identical codes outside the cones of the ties
-        c_same, _, _ = O2.bakron_recursive(d["W"], PA.astype(np.float64), PB.astype(np.float64), s, z, mq)
-        cone = R.dependency_cone(ties)
-        outside = ~cone
-        print(f"{name}: tie cones cover {cone.mean():.4f} of the entries; outside them "
-              f"{int((codes != c_same)[outside].sum())} codes differ", flush=True)
-        assert np.array_equal(codes[outside], c_same[outside])
+        # same factors, following the GPU at near-ties: identical codes
+        c_same, _, _, adopted = O2.bakron_recursive(d["W"], PA.astype(np.float64), PB.astype(np.float64), s, z, mq,
+                                                    follow=codes, tau=TAU)
+        same_diff = int((codes != c_same).sum())
+        print(f"{name}: oracle on the same factors adopted {adopted} near-tie codes; {same_diff} codes differ",
+              flush=True)
+        assert adopted <= max(1, 1e-4 * m * n)
+        assert same_diff == 0
         # end to end against the float64 factors
         fa, fb = R.factor(d["A"]), R.factor(d["B"])
         c_or, V_or, _ = O2.bakron_recursive(d["W"], fa["P"], fb["P"], s, z, mq)

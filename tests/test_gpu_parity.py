@@ -122,15 +122,16 @@ def _check_solve(d, LA, PA, LB, PB, out, label):
     v = R.validate(d["W"], codes, s, z, mq, tau=TAU, PA=PA64, PB=PB64, return_errors=True)
     ties = v.pop("tie_mask")
     v.pop("bad_mask"), v.pop("E")
-    c_or, V_or, E_or = O2.bakron_recursive(d["W"], PA64, PB64, s, z, mq)
+    # the oracle on the same factors, following the GPU's code where its own
+    # decision lies within TAU of a rounding boundary (there both roundings
+    # are valid and the trajectories would part): every other code is equal
+    c_or, V_or, E_or, adopted = O2.bakron_recursive(d["W"], PA64, PB64, s, z, mq, follow=codes, tau=TAU)
     diff = int((codes != c_or).sum())
-    print(f"{label}: {m}x{n} validator {v}, differing from oracle {diff}", flush=True)
+    print(f"{label}: {m}x{n} validator {v}, oracle adopted {adopted}, differing from it {diff}", flush=True)
     assert v["bad"] == 0 and v["max_step"] <= 1
     assert v["mismatches"] <= max(1, 1e-4 * m * n)
-    # the same codes as the oracle everywhere outside the dependency cones
-    # of the ties (where the two trajectories may part)
-    outside = ~R.dependency_cone(ties)
-    assert np.array_equal(codes[outside], c_or[outside])
+    assert adopted <= max(1, 1e-4 * m * n)
+    assert diff == 0
     # raw errors: float32 accumulation error, in grid steps
     Eimp = R.implied_errors_p(d["W"], R._values(codes, s, z), PA64, PB64)
     err_steps = np.abs(out["err"] - Eimp) / s[:, None]

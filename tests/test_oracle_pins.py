@@ -331,3 +331,64 @@ def test_dependency_cone_brute_force():
         for i in range(m):
             for j in range(n):
                 assert c[i, j] == bool(mask[: i + 1, : j + 1].any())
+
+
+# Tie-following mode of the C oracle (the comparison protocol for several
+# valid outputs): following its own codes changes nothing; a code planted on
+# the other side of the nearest-to-a-boundary decision is adopted when that
+# decision lies within tau of the boundary, and a planted code away from any
+# boundary is not.
+def _margins(V, E, s, z, maxq):
+    w = (V + E).astype(np.float32)
+    x = (w / s[:, None].astype(np.float32)).astype(np.float32) + z[:, None].astype(np.float32)
+    x = x.astype(np.float64)
+    b = np.clip(np.floor(x) + 0.5, 0.5, maxq[:, None] - 0.5)
+    return np.abs(x - b), x
+
+
+def test_recursive_follow_mode():
+    d = make_problem(48, 40, 23)
+    fa, fb = R.factor(d["A"]), R.factor(d["B"])
+    args = (d["W"], fa["P"], fb["P"], d["scale"], d["zero"], d["maxq"])
+    c, V, E = O2.bakron_recursive(*args, leaf=8)
+    c2, V2, E2, k = O2.bakron_recursive(*args, leaf=8, follow=c, tau=0.5)
+    assert k == 0 and np.array_equal(c2, c) and np.array_equal(E2, E)
+    mg, x = _margins(V, E, d["scale"], d["zero"], d["maxq"])
+    inner = (np.floor(x) >= 0) & (np.floor(x) < d["maxq"][:, None] - 1)   # both neighbours on the grid
+    i, j = np.unravel_index(np.argmin(np.where(inner, mg, np.inf)), mg.shape)
+    other = int(np.floor(x[i, j])) + (1 if c[i, j] == np.floor(x[i, j]) else 0)
+    assert abs(other - c[i, j]) == 1
+    plant = c.copy()
+    plant[i, j] = other
+    tau = 2 * mg[i, j] + 1e-12
+    c3, V3, E3, k3 = O2.bakron_recursive(*args, leaf=8, follow=plant, tau=tau)
+    assert c3[i, j] == other and k3 >= 1
+    v = R.validate(d["W"], c3, d["scale"], d["zero"], d["maxq"], tau=tau, PA=fa["P"], PB=fb["P"])
+    assert v["bad"] == 0 and v["ties"] >= 1
+    # a plant far from any boundary is ignored
+    i2, j2 = np.unravel_index(np.argmax(np.where(inner, mg, -1)), mg.shape)
+    plant2 = c.copy()
+    plant2[i2, j2] = c[i2, j2] + (1 if c[i2, j2] < d["maxq"][i2] else -1)
+    c4, _, _, k4 = O2.bakron_recursive(*args, leaf=8, follow=plant2, tau=1e-4)
+    assert k4 == 0 and np.array_equal(c4, c)
+
+
+def test_gptq_columns_follow_mode():
+    d = make_problem(30, 50, 16)
+    fa = R.factor(d["A"])
+    args = (d["W"], fa["P"], d["scale"], d["zero"], d["maxq"])
+    c, V, E = R.gptq_columns(*args)
+    c2, _, _, k = R.gptq_columns(*args, follow=c, tau=0.5)
+    assert k == 0 and np.array_equal(c2, c)
+    mg, x = _margins(V, E, d["scale"], d["zero"], d["maxq"])
+    inner = (np.floor(x) >= 0) & (np.floor(x) < d["maxq"][:, None] - 1)
+    i, j = np.unravel_index(np.argmin(np.where(inner, mg, np.inf)), mg.shape)
+    other = int(np.floor(x[i, j])) + (1 if c[i, j] == np.floor(x[i, j]) else 0)
+    plant = c.copy()
+    plant[i, j] = other
+    c3, _, _, k3 = R.gptq_columns(*args, follow=plant, tau=2 * mg[i, j] + 1e-12)
+    assert c3[i, j] == other and k3 >= 1
+    # the adopted flip only changes row i (rows are independent)
+    same = np.ones(c.shape[0], bool)
+    same[i] = False
+    assert np.array_equal(c3[same], c[same])

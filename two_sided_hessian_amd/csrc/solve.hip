@@ -87,22 +87,115 @@ __device__ __forceinline__ float quad_sum(float x)
 }
 
 // One tile (I, J) of tile anti-diagonal K per workgroup; 256 threads = 64
-// rows x 4 lanes (each lane owns 16 of the 64 columns of a dot product).
+// rows x 4 lanes (each lane owns 16 of the 64 columns of a row).
 //
 // In-tile step d visits entry (a, b = d - a) of every row a.  Its value is
 //   w~ = W~in[a,b] - pu - ps,
 //   pu = sum_{c<b} e[a,c] P_A[b,c]          (own row, earlier columns)
 //   ps = sum_{r<a} P_B[a,r] U[r,b],  U[r,b] = sum_{c<=b} e[r,c] P_A[b,c]
-// (P_A, P_B: the diagonal blocks of this tile).  Only two terms are new at
-// step d: e[a,b-1] in pu and U[a-1,b] in ps; everything else was final one
-// step earlier.  So each step computes, for the NEXT column bn = b + 1, the
-// partial sums without those terms (off the critical path), and the
-// critical path of a step is: barrier, read U[a-1,b], one FMA, quantize,
-// write e[a,b] and U[a,b] = pu + e[a,b], barrier.
+// (P_A, P_B: the diagonal blocks of this tile).
+//  * pu is accumulated forward: each row keeps U[a, b .. b+63] (only the
+//    errors found so far) in registers, 16 columns per lane, in a window that
+//    starts at the row's current column b.  After rounding (a, b) the row adds
+//    e[a,b] P_A[c,b] to every column c of the window, reading P_A[b .. b+63, b]
+//    from the skewed copy S[b][j] = P_A[b+j, b] (four 16-byte reads per lane);
+//    the window then moves on by one column.  The loop is unrolled 16 times
+//    so that the move is a renaming of registers, plus one lane shuffle for
+//    the column passed between neighbouring lanes.  The window's first
+//    column is pu for the next step, and at the diagonal P_A[b,b] = 1 makes
+//    it U[a,b] = pu + e[a,b].
+//  * ps is gathered from U^T in LDS: each step reads column b+1 of U^T
+//    (rows r < a-1, final one step earlier) for the next step, and the one
+//    new term, U[a-1,b], is read at the start of the step.
+// The critical path of a step is: barrier, read U[a-1,b], one FMA, round,
+// write e[a,b] and U[a,b], barrier.
+
+struct LeafRow {
+    const float* sW;
+    const float* sS;
+    float* sUT;
+    float* sF;
+    uint8_t* sC;
+    int a, sg, am1;
+    float sc, sinv, zc, mq, pbm1;
+    bool row_ok;
+    int64_t c0;
+    int n;
+};
+
+template <int U>
+__device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[16], const float (&pbz)[16], float& pu,
+                                          float& psp, float& wcur)
+{
+    const int d = d0 + U;
+    const int b = d - L.a, bn = b + 1;
+    const bool act = (unsigned)b < 64u;
+    const bool actn = (unsigned)bn < 64u;
+    // clamped, in-bounds indices; what inactive rows read is masked below
+    const int bc = min(max(b, 0), 63), bnc = min(max(bn, 0), 63);
+    const float fresh = L.sUT[bc * kLP + L.am1];   // U[a-1][b]
+    const float wnext = L.sW[L.a * 64 + bnc];
+    __builtin_amdgcn_sched_barrier(0);             // the fresh value first
+    f32x4 s4[4], u4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        s4[q] = *reinterpret_cast<const f32x4*>(L.sS + bc * kLP + 16 * L.sg + 4 * q);    // P_A[b + 16 sg + 4q + i][b]
+        u4[q] = *reinterpret_cast<const f32x4*>(L.sUT + bnc * kLP + 16 * L.sg + 4 * q);  // U[16 sg + 4q + i][b + 1]
+    }
+    // critical path: this step's entry
+    const float ps = psp + L.pbm1 * fresh;         // pbm1 == 0 on row 0
+    const float w = wcur - pu - ps;
+    // w / sc correctly rounded (Markstein: with y = RN(1/sc), q0 = RN(w y)
+    // is within an ulp, the remainder w - sc q0 is exact under fma, and
+    // RN(q0 + r y) is RN(w / sc)); then x = RN(q + zc) as in the oracle.
+    float q0 = w * L.sinv;
+    const float rem = fmaf(-q0, L.sc, w);
+    q0 = fmaf(rem, L.sinv, q0);
+    const float x = q0 + L.zc;
+    const float c = fminf(fmaxf(rintf(x), 0.f), L.mq);
+    const float v = L.sc * (c - L.zc);
+    const bool ok = act && L.row_ok && (L.c0 + b) < L.n;
+    const float e = ok ? (w - v) : 0.f;
+    if (act && L.sg == 0) {
+        L.sF[L.a * kLP + b] = e;
+        L.sUT[b * kLP + L.a] = pu + e;
+        L.sC[L.a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
+    }
+    // window update: logical column k (= b + 16 sg + k) lives in R[(k + U) & 15]
+#pragma unroll
+    for (int k = 0; k < 16; ++k) R[(k + U) & 15] = fmaf(e, s4[k >> 2][k & 3], R[(k + U) & 15]);
+    // next step's ps without the fresh term (P_B[a][a-1] is zero in pbz)
+    const bool need_ps = actn && 16 * L.sg < L.a - 1;
+    float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        u0 = fmaf(pbz[4 * q + 0], u4[q].x, u0);
+        u1 = fmaf(pbz[4 * q + 1], u4[q].y, u1);
+        u2 = fmaf(pbz[4 * q + 2], u4[q].z, u2);
+        u3 = fmaf(pbz[4 * q + 3], u4[q].w, u3);
+    }
+    const float psn = quad_sum(need_ps ? (u0 + u1) + (u2 + u3) : 0.f);
+    // move the window one column on: logical 0 (column b, done) becomes
+    // logical 15 and takes the next lane's logical 0 (column b + 16 (sg + 1);
+    // nothing past the tile for the last lane)
+    constexpr int P0 = U & 15;
+    const int nb = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, R[P0]), 0xF9, 0xF, 0xF, false);   // quad_perm [1,2,3,3]
+    R[P0] = L.sg == 3 ? 0.f : __builtin_bit_cast(float, nb);
+    // pu of the next step: logical 0 of lane 0 of the quad
+    const float pun = __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, R[(U + 1) & 15]), 0x00, 0xF, 0xF, false));
+    if (actn) {
+        pu = pun;
+        psp = psn;
+        wcur = wnext;
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
 {
     __shared__ float sW[64 * 64];
-    __shared__ __align__(16) float sPA[64 * kLP];
+    __shared__ __align__(16) float sS[64 * kLP];    // sS[b][j] = P_A[b + j][b], zero past the tile
     __shared__ __align__(16) float sUT[64 * kLP];   // sUT[b][a] = U[a][b]
     __shared__ __align__(16) float sF[64 * kLP];    // raw errors e[a][b]
     __shared__ __align__(16) uint8_t sC[64 * 64];
@@ -114,120 +207,80 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
     const int a = t >> 2, sg = t & 3;
     const int64_t r0 = (int64_t)I * 64, c0 = (int64_t)J * 64;
 
+    for (int idx = t; idx < 64 * kLP; idx += 256) {
+        sS[idx] = 0.f;
+        sUT[idx] = 0.f;
+        sF[idx] = 0.f;
+    }
+    f32x4 pa[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int f = t + 256 * u;
         const int row = f >> 4, cq = 4 * (f & 15);
         const f32x4 w = *reinterpret_cast<const f32x4*>(g.Wt + (r0 + row) * g.ldw + c0 + cq);
         *reinterpret_cast<f32x4*>(sW + row * 64 + cq) = w;
-        const f32x4 p = *reinterpret_cast<const f32x4*>(g.PA + (c0 + row) * g.lda + c0 + cq);
-        *reinterpret_cast<f32x4*>(sPA + row * kLP + cq) = p;
+        pa[u] = *reinterpret_cast<const f32x4*>(g.PA + (c0 + row) * g.lda + c0 + cq);
     }
-    for (int idx = t; idx < 64 * kLP; idx += 256) {
-        sUT[idx] = 0.f;
-        sF[idx] = 0.f;
+    __syncthreads();   // zeroing done before the skewed scatter
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int f = t + 256 * u;
+        const int row = f >> 4, cq = 4 * (f & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (row >= cq + i) sS[(cq + i) * kLP + (row - cq - i)] = pa[u][i];   // P_A[row][col], col <= row
     }
     // P_B row a, this lane's 16 columns; pbz drops column a-1 (the fresh term)
-    float pb[16], pbz[16];
+    float pbz[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const f32x4 v = *reinterpret_cast<const f32x4*>(g.PB + (r0 + a) * g.ldb + r0 + 16 * sg + 4 * q);
-        pb[4 * q + 0] = v.x;
-        pb[4 * q + 1] = v.y;
-        pb[4 * q + 2] = v.z;
-        pb[4 * q + 3] = v.w;
-    }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) pbz[j] = (16 * sg + j == a - 1) ? 0.f : pb[j];
-    const float pbm1 = a > 0 ? g.PB[(r0 + a) * g.ldb + r0 + a - 1] : 0.f;   // P_B[a][a-1]
+        for (int i = 0; i < 4; ++i) pbz[4 * q + i] = (16 * sg + 4 * q + i == a - 1) ? 0.f : v[i];
+    }
     const int64_t grow = r0 + a;
-    const bool row_ok = grow < g.m;
-    const float sc = row_ok ? g.scale[grow] : 1.f;
-    const float zc = row_ok ? g.zero[grow] : 0.f;
-    const float mq = row_ok ? (float)g.maxq[grow] : 0.f;
-    const float sinv = 1.f / sc;   // correctly rounded
+    LeafRow L;
+    L.sW = sW;
+    L.sS = sS;
+    L.sUT = sUT;
+    L.sF = sF;
+    L.sC = sC;
+    L.a = a;
+    L.sg = sg;
+    L.am1 = a > 0 ? a - 1 : 0;
+    L.pbm1 = a > 0 ? g.PB[(r0 + a) * g.ldb + r0 + a - 1] : 0.f;   // P_B[a][a-1]
+    L.row_ok = grow < g.m;
+    L.sc = L.row_ok ? g.scale[grow] : 1.f;
+    L.zc = L.row_ok ? g.zero[grow] : 0.f;
+    L.mq = L.row_ok ? (float)g.maxq[grow] : 0.f;
+    L.sinv = 1.f / L.sc;   // correctly rounded
+    L.c0 = c0;
+    L.n = g.n;
     __syncthreads();
 
-    float pu = 0.f, psp = 0.f;                      // for the current column
-    f32x4 fr[4], pr[4], ur[4];                      // partial-sum operands (loop-carried)
+    float R[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) fr[q] = pr[q] = ur[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 16; ++k) R[k] = 0.f;
+    float pu = 0.f, psp = 0.f;
     float wcur = (a == 0) ? sW[0] : 0.f;
-    const int am1 = a > 0 ? a - 1 : 0;
-    for (int d = 0; d < 127; ++d) {
-        const int b = d - a, bn = b + 1;
-        const bool act = (unsigned)b < 64u;
-        const bool actn = (unsigned)bn < 64u;
-        // These three reads are unconditional (clamped, in-bounds indices;
-        // the results are masked below) and issued first, so the fresh value
-        // is the only one the critical path waits for.
-        const int bc = min(max(b, 0), 63), bnc = min(max(bn, 0), 63);
-        const float fresh = sUT[bc * kLP + am1];       // U[a-1][b]
-        const float pa_sub = sPA[bnc * kLP + bc];     // P_A[b+1][b]
-        const float wnext = sW[a * 64 + bnc];
-        __builtin_amdgcn_sched_barrier(0);            // keep those three reads first
-        // Partial-sum operands, read only where they can be nonzero (LDS
-        // bandwidth is the leaf's limit): for the next column of an active
-        // row, e[a][c] is zero from c = b on and U[r][bn] enters only for
-        // r < a - 1, so a lane whose 16-wide segment lies past that reads
-        // nothing (its registers keep older values) and its sum is taken as 0.
-        const bool need_pu = actn && 16 * sg < b;
-        const bool need_ps = actn && 16 * sg < a - 1;
-        if (need_pu) {
-            const f32x4* F4 = reinterpret_cast<const f32x4*>(sF + a * kLP + 16 * sg);
-            const f32x4* P4 = reinterpret_cast<const f32x4*>(sPA + bnc * kLP + 16 * sg);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                fr[q] = F4[q];
-                pr[q] = P4[q];
-            }
-        }
-        if (need_ps) {
-            const f32x4* U4 = reinterpret_cast<const f32x4*>(sUT + bnc * kLP + 16 * sg);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) ur[q] = U4[q];
-        }
-        // critical path: this step's entry
-        const float ps = psp + pbm1 * fresh;          // pbm1 == 0 on row 0
-        const float w = wcur - pu - ps;
-        // w / sc correctly rounded (Markstein: with y = RN(1/sc), q0 = RN(w y)
-        // is within an ulp, the remainder w - sc q0 is exact under fma, and
-        // RN(q0 + r y) is RN(w / sc)); then x = RN(q + zc) as in the oracle.
-        float q0 = w * sinv;
-        const float rem = fmaf(-q0, sc, w);
-        q0 = fmaf(rem, sinv, q0);
-        const float x = q0 + zc;
-        const float c = fminf(fmaxf(rintf(x), 0.f), mq);
-        const float v = sc * (c - zc);
-        const bool ok = act && row_ok && (c0 + b) < g.n;
-        const float e = ok ? (w - v) : 0.f;
-        if (act && sg == 0) {
-            sF[a * kLP + b] = e;
-            sUT[b * kLP + a] = pu + e;
-            sC[a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
-        }
-        // next step's partial sums (e[a][b] was read as 0 above: excluded)
-        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
-        float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            s0 = fmaf(fr[q].x, pr[q].x, s0);
-            s1 = fmaf(fr[q].y, pr[q].y, s1);
-            s2 = fmaf(fr[q].z, pr[q].z, s2);
-            s3 = fmaf(fr[q].w, pr[q].w, s3);
-            u0 = fmaf(pbz[4 * q + 0], ur[q].x, u0);
-            u1 = fmaf(pbz[4 * q + 1], ur[q].y, u1);
-            u2 = fmaf(pbz[4 * q + 2], ur[q].z, u2);
-            u3 = fmaf(pbz[4 * q + 3], ur[q].w, u3);
-        }
-        const float pun = quad_sum(need_pu ? (s0 + s1) + (s2 + s3) : 0.f);
-        const float psn = quad_sum(need_ps ? (u0 + u1) + (u2 + u3) : 0.f);
-        if (actn) {
-            pu = pun + e * pa_sub;
-            psp = psn;
-            wcur = wnext;
-        }
-        __syncthreads();
+    // 127 steps, in 8 unrolled groups of 16 (the 128th step is idle for every row)
+    for (int d0 = 0; d0 < 128; d0 += 16) {
+        leaf_step<0>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<1>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<2>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<3>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<4>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<5>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<6>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<7>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<8>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<9>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<10>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<11>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<12>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<13>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<14>(L, d0, R, pbz, pu, psp, wcur);
+        leaf_step<15>(L, d0, R, pbz, pu, psp, wcur);
     }
 
     // Outputs: raw errors to the workspace, codes / values / errors to the
