@@ -304,6 +304,38 @@ __device__ __forceinline__ void inv_merge16(const float* sA, float* sX, int d)
     *reinterpret_cast<f32x4*>(T + r * kDP + c0) = f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
+// A[r0 .. r0+3][cc .. cc+3] -= sum over the 16 panel rows t of Pr[t][r] Pr[t][c].
+__device__ __forceinline__ void syrk_tile4(float* __restrict__ sA, const float* __restrict__ Pr, int r0, int cc)
+{
+    float acc[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 16; ++tt) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(Pr + tt * kDP + r0);
+        const f32x4 c = *reinterpret_cast<const f32x4*>(Pr + tt * kDP + cc);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            acc[0][v] = fmaf(a.x, c[v], acc[0][v]);
+            acc[1][v] = fmaf(a.y, c[v], acc[1][v]);
+            acc[2][v] = fmaf(a.z, c[v], acc[2][v]);
+            acc[3][v] = fmaf(a.w, c[v], acc[3][v]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        f32x4* p = reinterpret_cast<f32x4*>(sA + (r0 + u) * kDP + cc);
+        f32x4 v = *p;
+        v.x -= acc[u][0];
+        v.y -= acc[u][1];
+        v.z -= acc[u][2];
+        v.w -= acc[u][3];
+        *p = v;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
                                                 int64_t o, int nb, int32_t* __restrict__ info)
 {
@@ -328,14 +360,17 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
     if (t == 0) sfail = -1;
     __syncthreads();
 
-    // factor, 16 rows at a time from the bottom
-    for (int b = nb / 16 - 1; b >= 0; --b) {
-        if (wave == 0) {
-            const int f = base16(sA + 16 * b * (kDP + 1), sX + 16 * b * (kDP + 1));
-            if (t == 0 && f >= 0 && sfail < 0) sfail = 16 * b + f;
-        }
-        __syncthreads();
-        if (b == 0) break;
+    // factor, 16 rows at a time from the bottom, with a one-block lookahead:
+    // once the panel of block b is formed, wave 0 updates only the diagonal
+    // block b - 1 and factors it (base16) while waves 1 - 3 apply the rest of
+    // block b's update to the remaining upper-left part.
+    if (wave == 0) {
+        const int b = nb / 16 - 1;
+        const int f = base16(sA + 16 * b * (kDP + 1), sX + 16 * b * (kDP + 1));
+        if (t == 0 && f >= 0) sfail = 16 * b + f;
+    }
+    __syncthreads();
+    for (int b = nb / 16 - 1; b >= 1; --b) {
         const int W = 16 * b;
         float* Pr = sA + W * kDP;                    // rows of block b
         {   // panel: Pr[r][c] = sum_t Xbb[t][r] Pr[t][c], c < W; thread (r, cg)
@@ -358,43 +393,35 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
             for (int j = 0; j < b; ++j) Pr[r * kDP + cg + 16 * j] = acc[j];
             __syncthreads();
         }
-        {   // A[0:W][0:W] -= Pr^T Pr on the 4 x 4 tiles of the lower triangle
-            const int n4 = W / 4, ntile = n4 * (n4 + 1) / 2;
-            for (int idx = t; idx < ntile; idx += 256) {
+        // A[0:W][0:W] -= Pr^T Pr on the 4 x 4 tiles of the lower triangle;
+        // the tiles of diagonal block b - 1 (rows and columns W - 16 .. W - 1)
+        // go to wave 0, which then factors that block
+        const int n4 = W / 4, ntile = n4 * (n4 + 1) / 2;
+        const int d4 = n4 - 4;                       // first 4-row of block b - 1
+        if (wave == 0) {
+            const int l = t;                         // 10 tiles of the diagonal block's lower triangle
+            if (l < 10) {
+                int br = 0;
+                while ((br + 1) * (br + 2) / 2 <= l) ++br;
+                const int r0 = 4 * (d4 + br), cc = 4 * (d4 + l - br * (br + 1) / 2);
+                syrk_tile4(sA, Pr, r0, cc);
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int f = base16(sA + 16 * (b - 1) * (kDP + 1), sX + 16 * (b - 1) * (kDP + 1));
+            if (t == 0 && f >= 0 && sfail < 0) sfail = 16 * (b - 1) + f;
+        } else {
+            for (int idx = t - 64; idx < ntile; idx += 192) {
                 int br = (int)((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
                 while ((br + 1) * (br + 2) / 2 <= idx) ++br;
                 while (br * (br + 1) / 2 > idx) --br;
-                const int r0 = 4 * br, cc = 4 * (idx - br * (br + 1) / 2);
-                float acc[4][4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) acc[u][v] = 0.f;
-#pragma unroll
-                for (int tt = 0; tt < 16; ++tt) {
-                    const f32x4 a = *reinterpret_cast<const f32x4*>(Pr + tt * kDP + r0);
-                    const f32x4 c = *reinterpret_cast<const f32x4*>(Pr + tt * kDP + cc);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        acc[0][v] = fmaf(a.x, c[v], acc[0][v]);
-                        acc[1][v] = fmaf(a.y, c[v], acc[1][v]);
-                        acc[2][v] = fmaf(a.z, c[v], acc[2][v]);
-                        acc[3][v] = fmaf(a.w, c[v], acc[3][v]);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    f32x4* p = reinterpret_cast<f32x4*>(sA + (r0 + u) * kDP + cc);
-                    f32x4 v = *p;
-                    v.x -= acc[u][0];
-                    v.y -= acc[u][1];
-                    v.z -= acc[u][2];
-                    v.w -= acc[u][3];
-                    *p = v;
-                }
+                const int bc = idx - br * (br + 1) / 2;
+                if (br >= d4 && bc >= d4) continue;  // wave 0's
+                syrk_tile4(sA, Pr, 4 * br, 4 * bc);
             }
-            __syncthreads();
         }
+        __syncthreads();
     }
 
     // inverse: 2 x 16 blocks (one wave each), 2 x 32 (MFMA, one wave each),
