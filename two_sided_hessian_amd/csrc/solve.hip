@@ -78,16 +78,29 @@ struct LeafArgs {
 
 constexpr int kLP = 68;   // LDS pitch (floats) of the P_A, U^T and E tiles
 
-// Sum over the 4 lanes of a quad (DPP quad permutes, no LDS round trip).
-__device__ __forceinline__ float quad_sum(float x)
+// Lane shuffles inside a row's group of 8 lanes (two quads of a 16-lane DPP
+// row), all DPP moves (no LDS round trip).
+// value of lane 0 of the group, in every lane of the group
+__device__ __forceinline__ float bcast8_lane0(float x)
+{
+    const int b = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x00, 0xF, 0xF, false);   // quad_perm [0,0,0,0]
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(b, b, 0x114, 0xF, 0xA, false));  // quads 1, 3 <- 0, 2
+}
+
+// sum over the 8 lanes of the group, in every lane
+__device__ __forceinline__ float sum8(float x)
 {
     x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, true));
     x += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
-    return x;
+    const int xi = __builtin_bit_cast(int, x);
+    int y = __builtin_amdgcn_update_dpp(0, xi, 0x104, 0xF, 0x5, false);   // quads 0, 2 <- 1, 3 (row_shl:4)
+    y = __builtin_amdgcn_update_dpp(y, xi, 0x114, 0xF, 0xA, false);       // quads 1, 3 <- 0, 2 (row_shr:4)
+    return x + __builtin_bit_cast(float, y);
 }
 
-// One tile (I, J) of tile anti-diagonal K per workgroup; 256 threads = 64
-// rows x 4 lanes (each lane owns 16 of the 64 columns of a row).
+// One tile (I, J) of tile anti-diagonal K per workgroup; 512 threads = 64
+// rows x 8 lanes (each lane owns 8 of the 64 columns of a row), so that two
+// waves share each SIMD and hide each other's latencies.
 //
 // In-tile step d visits entry (a, b = d - a) of every row a.  Its value is
 //   w~ = W~in[a,b] - pu - ps,
@@ -95,12 +108,12 @@ __device__ __forceinline__ float quad_sum(float x)
 //   ps = sum_{r<a} P_B[a,r] U[r,b],  U[r,b] = sum_{c<=b} e[r,c] P_A[b,c]
 // (P_A, P_B: the diagonal blocks of this tile).
 //  * pu is accumulated forward: each row keeps U[a, b .. b+63] (only the
-//    errors found so far) in registers, 16 columns per lane, in a window that
+//    errors found so far) in registers, 8 columns per lane, in a window that
 //    starts at the row's current column b.  After rounding (a, b) the row adds
 //    e[a,b] P_A[c,b] to every column c of the window, reading P_A[b .. b+63, b]
-//    from the skewed copy S[b][j] = P_A[b+j, b] (four 16-byte reads per lane);
-//    the window then moves on by one column.  The loop is unrolled 16 times
-//    so that the move is a renaming of registers, plus one lane shuffle for
+//    from the skewed copy S[b][j] = P_A[b+j, b] (two 16-byte reads per lane);
+//    the window then moves on by one column.  The loop is unrolled 8 times
+//    so that the move is a renaming of registers, plus one lane shift for
 //    the column passed between neighbouring lanes.  The window's first
 //    column is pu for the next step, and at the diagonal P_A[b,b] = 1 makes
 //    it U[a,b] = pu + e[a,b].
@@ -112,6 +125,7 @@ __device__ __forceinline__ float quad_sum(float x)
 
 struct LeafRow {
     const float* sW;
+    const float* sZ;   // 8 zeros: the operand of lanes whose reads could only return zeros
     const float* sS;
     float* sUT;
     float* sF;
@@ -124,7 +138,7 @@ struct LeafRow {
 };
 
 template <int U>
-__device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[16], const float (&pbz)[16], float& pu,
+__device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[8], const float (&pbz)[8], float& pu,
                                           float& psp, float& wcur)
 {
     const int d = d0 + U;
@@ -136,12 +150,16 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[1
     const float fresh = L.sUT[bc * kLP + L.am1];   // U[a-1][b]
     const float wnext = L.sW[L.a * 64 + bnc];
     __builtin_amdgcn_sched_barrier(0);             // the fresh value first
-    f32x4 s4[4], u4[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        s4[q] = *reinterpret_cast<const f32x4*>(L.sS + bc * kLP + 16 * L.sg + 4 * q);    // P_A[b + 16 sg + 4q + i][b]
-        u4[q] = *reinterpret_cast<const f32x4*>(L.sUT + bnc * kLP + 16 * L.sg + 4 * q);  // U[16 sg + 4q + i][b + 1]
-    }
+    // S[b][8 sg ..] is zero past the tile (8 sg > 63 - b) and U[8 sg ..][b + 1]
+    // only enters for rows below a - 1: such lanes read the shared zeros
+    // instead, which the LDS serves as one broadcast
+    const bool need_ps = actn && 8 * L.sg < L.a - 1;
+    const float* sp = (act && 8 * L.sg <= 63 - b) ? L.sS + bc * kLP + 8 * L.sg : L.sZ;   // P_A[b + 8 sg + i][b]
+    const float* up = need_ps ? L.sUT + bnc * kLP + 8 * L.sg : L.sZ;                    // U[8 sg + i][b + 1]
+    const f32x4 s0 = *reinterpret_cast<const f32x4*>(sp);
+    const f32x4 s1 = *reinterpret_cast<const f32x4*>(sp + 4);
+    const f32x4 u0 = *reinterpret_cast<const f32x4*>(up);
+    const f32x4 u1 = *reinterpret_cast<const f32x4*>(up + 4);
     // critical path: this step's entry
     const float ps = psp + L.pbm1 * fresh;         // pbm1 == 0 on row 0
     const float w = wcur - pu - ps;
@@ -161,29 +179,29 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[1
         L.sUT[b * kLP + L.a] = pu + e;
         L.sC[L.a * 64 + b] = ok ? (uint8_t)c : (uint8_t)0;
     }
-    // window update: logical column k (= b + 16 sg + k) lives in R[(k + U) & 15]
+    // window update: logical column k (= b + 8 sg + k) lives in R[(k + U) & 7]
 #pragma unroll
-    for (int k = 0; k < 16; ++k) R[(k + U) & 15] = fmaf(e, s4[k >> 2][k & 3], R[(k + U) & 15]);
-    // next step's ps without the fresh term (P_B[a][a-1] is zero in pbz)
-    const bool need_ps = actn && 16 * L.sg < L.a - 1;
-    float u0 = 0.f, u1 = 0.f, u2 = 0.f, u3 = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        u0 = fmaf(pbz[4 * q + 0], u4[q].x, u0);
-        u1 = fmaf(pbz[4 * q + 1], u4[q].y, u1);
-        u2 = fmaf(pbz[4 * q + 2], u4[q].z, u2);
-        u3 = fmaf(pbz[4 * q + 3], u4[q].w, u3);
+    for (int k = 0; k < 4; ++k) {
+        R[(k + U) & 7] = fmaf(e, s0[k], R[(k + U) & 7]);
+        R[(k + 4 + U) & 7] = fmaf(e, s1[k], R[(k + 4 + U) & 7]);
     }
-    const float psn = quad_sum(need_ps ? (u0 + u1) + (u2 + u3) : 0.f);
+    // next step's ps without the fresh term (P_B[a][a-1] is zero in pbz)
+    float t0 = pbz[0] * u0.x, t1 = pbz[1] * u0.y;
+    t0 = fmaf(pbz[2], u0.z, t0);
+    t1 = fmaf(pbz[3], u0.w, t1);
+    t0 = fmaf(pbz[4], u1.x, t0);
+    t1 = fmaf(pbz[5], u1.y, t1);
+    t0 = fmaf(pbz[6], u1.z, t0);
+    t1 = fmaf(pbz[7], u1.w, t1);
+    const float psn = sum8(need_ps ? t0 + t1 : 0.f);
     // move the window one column on: logical 0 (column b, done) becomes
-    // logical 15 and takes the next lane's logical 0 (column b + 16 (sg + 1);
-    // nothing past the tile for the last lane)
-    constexpr int P0 = U & 15;
-    const int nb = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, R[P0]), 0xF9, 0xF, 0xF, false);   // quad_perm [1,2,3,3]
-    R[P0] = L.sg == 3 ? 0.f : __builtin_bit_cast(float, nb);
-    // pu of the next step: logical 0 of lane 0 of the quad
-    const float pun = __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, R[(U + 1) & 15]), 0x00, 0xF, 0xF, false));
+    // logical 7 and takes the next lane's logical 0 (column b + 8 (sg + 1);
+    // nothing past the tile for the last lane of the row)
+    constexpr int P0 = U & 7;
+    const int nb = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, R[P0]), 0x101, 0xF, 0xF, false);   // row_shl:1
+    R[P0] = L.sg == 7 ? 0.f : __builtin_bit_cast(float, nb);
+    // pu of the next step: logical 0 of lane 0 of the row's group
+    const float pun = bcast8_lane0(R[(U + 1) & 7]);
     if (actn) {
         pu = pun;
         psp = psn;
@@ -192,30 +210,32 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[1
     __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
+__global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
 {
     __shared__ float sW[64 * 64];
     __shared__ __align__(16) float sS[64 * kLP];    // sS[b][j] = P_A[b + j][b], zero past the tile
     __shared__ __align__(16) float sUT[64 * kLP];   // sUT[b][a] = U[a][b]
     __shared__ __align__(16) float sF[64 * kLP];    // raw errors e[a][b]
     __shared__ __align__(16) uint8_t sC[64 * 64];
-    __shared__ double sRed[4];
+    __shared__ __align__(16) float sZ[8];
+    __shared__ double sRed[8];
 
     const int I = g.I_lo + blockIdx.x;
     const int J = g.K - I;
     const int t = threadIdx.x;
-    const int a = t >> 2, sg = t & 3;
+    const int a = t >> 3, sg = t & 7;
+    if (t < 8) sZ[t] = 0.f;
     const int64_t r0 = (int64_t)I * 64, c0 = (int64_t)J * 64;
 
-    for (int idx = t; idx < 64 * kLP; idx += 256) {
+    for (int idx = t; idx < 64 * kLP; idx += 512) {
         sS[idx] = 0.f;
         sUT[idx] = 0.f;
         sF[idx] = 0.f;
     }
-    f32x4 pa[4];
+    f32x4 pa[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int f = t + 256 * u;
+    for (int u = 0; u < 2; ++u) {
+        const int f = t + 512 * u;
         const int row = f >> 4, cq = 4 * (f & 15);
         const f32x4 w = *reinterpret_cast<const f32x4*>(g.Wt + (r0 + row) * g.ldw + c0 + cq);
         *reinterpret_cast<f32x4*>(sW + row * 64 + cq) = w;
@@ -223,24 +243,25 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
     }
     __syncthreads();   // zeroing done before the skewed scatter
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int f = t + 256 * u;
+    for (int u = 0; u < 2; ++u) {
+        const int f = t + 512 * u;
         const int row = f >> 4, cq = 4 * (f & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             if (row >= cq + i) sS[(cq + i) * kLP + (row - cq - i)] = pa[u][i];   // P_A[row][col], col <= row
     }
-    // P_B row a, this lane's 16 columns; pbz drops column a-1 (the fresh term)
-    float pbz[16];
+    // P_B row a, this lane's 8 columns; pbz drops column a-1 (the fresh term)
+    float pbz[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(g.PB + (r0 + a) * g.ldb + r0 + 16 * sg + 4 * q);
+    for (int q = 0; q < 2; ++q) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(g.PB + (r0 + a) * g.ldb + r0 + 8 * sg + 4 * q);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pbz[4 * q + i] = (16 * sg + 4 * q + i == a - 1) ? 0.f : v[i];
+        for (int i = 0; i < 4; ++i) pbz[4 * q + i] = (8 * sg + 4 * q + i == a - 1) ? 0.f : v[i];
     }
     const int64_t grow = r0 + a;
     LeafRow L;
     L.sW = sW;
+    L.sZ = sZ;
     L.sS = sS;
     L.sUT = sUT;
     L.sF = sF;
@@ -258,13 +279,13 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
     L.n = g.n;
     __syncthreads();
 
-    float R[16];
+    float R[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) R[k] = 0.f;
+    for (int k = 0; k < 8; ++k) R[k] = 0.f;
     float pu = 0.f, psp = 0.f;
     float wcur = (a == 0) ? sW[0] : 0.f;
-    // 127 steps, in 8 unrolled groups of 16 (the 128th step is idle for every row)
-    for (int d0 = 0; d0 < 128; d0 += 16) {
+    // 127 steps, in 16 unrolled groups of 8 (the 128th step is idle for every row)
+    for (int d0 = 0; d0 < 128; d0 += 8) {
         leaf_step<0>(L, d0, R, pbz, pu, psp, wcur);
         leaf_step<1>(L, d0, R, pbz, pu, psp, wcur);
         leaf_step<2>(L, d0, R, pbz, pu, psp, wcur);
@@ -273,33 +294,25 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
         leaf_step<5>(L, d0, R, pbz, pu, psp, wcur);
         leaf_step<6>(L, d0, R, pbz, pu, psp, wcur);
         leaf_step<7>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<8>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<9>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<10>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<11>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<12>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<13>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<14>(L, d0, R, pbz, pu, psp, wcur);
-        leaf_step<15>(L, d0, R, pbz, pu, psp, wcur);
     }
 
     // Outputs: raw errors to the workspace, codes / values / errors to the
-    // caller, and this tile's objective partial.
-    const int row = t >> 2, cs = 16 * (t & 3);
+    // caller, and this tile's objective partial.  Thread (row, 8 columns).
+    const int row = t >> 3, cs = 8 * (t & 7);
     const int64_t orow = r0 + row;
     double objs = 0.0;
     const float lb = (g.objp && orow < g.m) ? g.LB[orow * g.m + orow] : 0.f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 2; ++q)
         *reinterpret_cast<f32x4*>(g.E + orow * g.ldw + c0 + cs + 4 * q) =
             *reinterpret_cast<const f32x4*>(sF + row * kLP + cs + 4 * q);
     if (orow < g.m) {
         const float so = g.scale[orow], zo = g.zero[orow];
         if (g.vec_out) {
-            *reinterpret_cast<uint4*>(g.codes + orow * g.n + c0 + cs) =
-                *reinterpret_cast<const uint4*>(sC + row * 64 + cs);
+            *reinterpret_cast<uint2*>(g.codes + orow * g.n + c0 + cs) =
+                *reinterpret_cast<const uint2*>(sC + row * 64 + cs);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
+            for (int q = 0; q < 2; ++q) {
                 f32x4 v;
                 v.x = so * ((float)sC[row * 64 + cs + 4 * q + 0] - zo);
                 v.y = so * ((float)sC[row * 64 + cs + 4 * q + 1] - zo);
@@ -311,7 +324,7 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
                         *reinterpret_cast<const f32x4*>(sF + row * kLP + cs + 4 * q);
             }
         } else {
-            for (int k = 0; k < 16; ++k) {
+            for (int k = 0; k < 8; ++k) {
                 const int64_t col = c0 + cs + k;
                 if (col >= g.n) break;
                 const uint8_t c = sC[row * 64 + cs + k];
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
             }
         }
         if (g.objp) {
-            for (int k = 0; k < 16; ++k) {
+            for (int k = 0; k < 8; ++k) {
                 const int64_t col = c0 + cs + k;
                 if (col >= g.n) break;
                 const double q = (double)lb * (double)g.LA[col * g.n + col] * (double)sF[row * kLP + cs + k];
@@ -333,7 +346,11 @@ __global__ __launch_bounds__(256) void k_leaf(LeafArgs g)
         for (int off = 32; off > 0; off >>= 1) objs += __shfl_xor(objs, off);
         if ((t & 63) == 0) sRed[t >> 6] = objs;
         __syncthreads();
-        if (t == 0) g.objp[(int64_t)I * g.Nt + J] = sRed[0] + sRed[1] + sRed[2] + sRed[3];
+        if (t == 0) {
+            double sum = 0.0;
+            for (int w = 0; w < 8; ++w) sum += sRed[w];
+            g.objp[(int64_t)I * g.Nt + J] = sum;
+        }
     }
 }
 
@@ -694,7 +711,7 @@ void enqueue_leaf(SolveRun& R, int K)
     // bytes: W~, P_A and P_B diagonal blocks in; E and V out (+ err), codes
     const double flops = count * 2.0 * 2.0 * kTriB;
     const double bytes = count * (5.0 * kTileB + (R.leaf.err ? kTileB : 0.0) + 64.0 * 64.0);
-    launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(256), R.s, R.leaf);
+    launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(512), R.s, R.leaf);
 }
 
 // A stage with fewer 64 x 256 blocks than this runs one 64 x 64 tile per
