@@ -34,15 +34,15 @@ constexpr int kPad = 4;   // LDS row padding in floats (keeps 16-byte alignment)
 // Both copies are straight float4 moves (no transposition).
 enum Layout { RowK = 0, KRow = 1 };
 
-template <int R, int LAYOUT>
+template <int R, int LAYOUT, int BK = kBK>
 struct Operand {
-    static constexpr int PITCH = (LAYOUT == RowK) ? (kBK + kPad) : (R + kPad);
-    static constexpr int FLOATS = (LAYOUT == RowK) ? R * PITCH : kBK * PITCH;
-    static constexpr int F4 = R * kBK / 4;            // float4s per chunk
+    static constexpr int PITCH = (LAYOUT == RowK) ? (BK + kPad) : (R + kPad);
+    static constexpr int FLOATS = (LAYOUT == RowK) ? R * PITCH : BK * PITCH;
+    static constexpr int F4 = R * BK / 4;             // float4s per chunk
     static constexpr int PER_THREAD = F4 / 256;       // float4s per thread
     static_assert(F4 % 256 == 0, "tile too small for 256 threads");
 
-    // Global -> registers for one K chunk [k0, k0 + kBK); rows >= rlim read 0.
+    // Global -> registers for one K chunk [k0, k0 + BK); rows >= rlim read 0.
     static __device__ __forceinline__ void load(const float* __restrict__ p, int64_t ld, int rlim, int k0,
                                                 f32x4 (&reg)[PER_THREAD])
     {
@@ -55,8 +55,8 @@ struct Operand {
                 k = f / (R / 4);
                 r = 4 * (f % (R / 4));
             } else {
-                r = f / (kBK / 4);
-                k = 4 * (f % (kBK / 4));
+                r = f / (BK / 4);
+                k = 4 * (f % (BK / 4));
             }
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (r < rlim) {
@@ -80,8 +80,8 @@ struct Operand {
                 r = 4 * (f % (R / 4));
                 *reinterpret_cast<f32x4*>(s + k * PITCH + r) = reg[u];
             } else {
-                r = f / (kBK / 4);
-                k = 4 * (f % (kBK / 4));
+                r = f / (BK / 4);
+                k = 4 * (f % (BK / 4));
                 *reinterpret_cast<f32x4*>(s + r * PITCH + k) = reg[u];
             }
         }
@@ -267,17 +267,25 @@ __device__ __forceinline__ void wave_store32(float* __restrict__ C, int64_t ldc,
 // For launches with few output tiles: a workgroup computes one 64 x 64
 // tile, wave w the 32 x 32 quadrant at rows 32 (w >> 1), columns 32 (w & 1),
 // so a launch keeps four waves busy per output tile.  Operands are staged
-// through LDS in coalesced kBK-deep chunks that the four waves share.
-constexpr int kLds64 = Operand<64, RowK>::FLOATS > Operand<64, KRow>::FLOATS ? 2 * Operand<64, RowK>::FLOATS
-                                                                               : 2 * Operand<64, KRow>::FLOATS;
+// through LDS in coalesced chunks of kBK64 that the four waves share; a
+// quadrant does only 4 MFMAs per 8 k, so the chunk is deeper than the block
+// core's to spread the two barriers of a chunk over more MFMAs.
+#ifndef BAKRON_KBK64
+#define BAKRON_KBK64 64
+#endif
+constexpr int kBK64 = BAKRON_KBK64;
+constexpr int kLds64 = Operand<64, RowK, kBK64>::FLOATS > Operand<64, KRow, kBK64>::FLOATS
+                           ? 2 * Operand<64, RowK, kBK64>::FLOATS
+                           : 2 * Operand<64, KRow, kBK64>::FLOATS;
 
+// k0, k1 are multiples of kBK64.
 template <int ALAY, int BLAY>
 __device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_t lda,
                                              const float* __restrict__ B, int64_t ldb, int k0, int k1,
                                              float* lds, f32x16& acc)
 {
-    typedef Operand<64, ALAY> OA;
-    typedef Operand<64, BLAY> OB;
+    typedef Operand<64, ALAY, kBK64> OA;
+    typedef Operand<64, BLAY, kBK64> OB;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int ml = lane & 31;
@@ -286,7 +294,7 @@ __device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_
     float* sb = lds + OA::FLOATS;
     f32x4 pa[OA::PER_THREAD];
     f32x4 pb[OB::PER_THREAD];
-    const int nchunk = (k1 - k0) / kBK;
+    const int nchunk = (k1 - k0) / kBK64;
     if (nchunk <= 0) return;
     OA::load(A, lda, 64, k0, pa);
     OB::load(B, ldb, 64, k0, pb);
@@ -296,11 +304,11 @@ __device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_
     for (int c = 0; c < nchunk; ++c) {
         const bool more = (c + 1) < nchunk;
         if (more) {
-            OA::load(A, lda, 64, k0 + (c + 1) * kBK, pa);
-            OB::load(B, ldb, 64, k0 + (c + 1) * kBK, pb);
+            OA::load(A, lda, 64, k0 + (c + 1) * kBK64, pa);
+            OB::load(B, ldb, 64, k0 + (c + 1) * kBK64, pb);
         }
 #pragma unroll
-        for (int kc = 0; kc < kBK; kc += 8) {
+        for (int kc = 0; kc < kBK64; kc += 8) {
             const f32x4 a = OA::frag(sa, ra, kc);
             const f32x4 b = OB::frag(sb, rb, kc);
 #pragma unroll
