@@ -4,13 +4,15 @@
 // block; each wave owns one 64 x 64 sub-block as 2 x 2 tiles of
 // v_mfma_f32_32x32x2f32 (32 x 32 output, K = 2 per instruction, 16 fp32
 // accumulators per lane).  Operands are staged through LDS in K chunks of
-// kBK; the next chunk's global loads are issued before the current chunk's
-// MFMAs.  Each operand keeps its global orientation in LDS, so global ->
-// LDS copies are float4 moves, and K-contiguous operands feed four MFMAs
-// per 16-byte LDS read.
+// kBK with gfx950's direct global -> LDS loads (global_load_lds_dwordx4:
+// each lane's 16 bytes go straight to LDS, no register round trip) into two
+// LDS buffers, so the next chunk streams in while the current one feeds the
+// MFMAs and a chunk costs one barrier.  Each operand keeps its global
+// orientation in LDS; K-contiguous operands feed four MFMAs per 16-byte LDS
+// read.
 //
 // Every row/column extent used by the callers is a multiple of 64, so
-// per-float4 bounds checks (rows beyond `rlim` read as zero) are exact.
+// limits (rows beyond `rlim` are not needed) are handled per 64 rows.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -108,13 +110,78 @@ struct Operand {
     }
 };
 
+typedef __attribute__((address_space(1))) const void* global_cptr;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Direct staging of one kBK chunk: one wave instruction fills 1 KB of LDS,
+// lane L the 16 bytes at 16 L, so the LDS image is fixed by which global
+// float4 each lane fetches.
+//   RowK: an instruction covers 8 rows x 32 k (rows 128 bytes apart, no
+//         padding); row r's k-quad u sits in 16-byte slot u ^ (r & 7), so
+//         the eight rows of a fragment read hit eight different slots.
+//   KRow: an instruction covers 256 / R k-rows of R floats, pitch R.
+// Rows >= rlim are not needed by the caller (they only reach outputs it
+// does not store): RowK skips their instructions (rlim is a multiple of 64,
+// so the test is wave-uniform); KRow fetches an in-range column in their
+// place.  Either way every global address stays inside the operand.
+template <int R, int LAYOUT>
+struct Direct {
+    static constexpr int FLOATS = R * kBK;
+    static constexpr int INSTR = FLOATS / 256;     // wave instructions per chunk
+    static constexpr int PER_WAVE = INSTR / 4;
+    static_assert(kBK == 32 && INSTR % 4 == 0, "direct staging assumes 32-deep chunks, R >= 32");
+
+    static __device__ __forceinline__ void issue(const float* __restrict__ p, int64_t ld, int rlim, int k0, float* s)
+    {
+        const int lane = threadIdx.x & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+        for (int i = 0; i < PER_WAVE; ++i) {
+            const int q = wave + 4 * i;
+            const float* src;
+            if (LAYOUT == RowK) {
+                if (8 * q >= rlim) continue;
+                const int r = 8 * q + (lane >> 3);
+                src = p + (int64_t)r * ld + k0 + 4 * ((lane & 7) ^ (r & 7));
+            } else {
+                const int f = 64 * q + lane;
+                int r = 4 * (f % (R / 4));
+                if (R > 64) r = min(r, rlim - 4);
+                src = p + (int64_t)(k0 + f / (R / 4)) * ld + r;
+            }
+            __builtin_amdgcn_global_load_lds((global_cptr)src, (lds_ptr)(s + 256 * q), 16, 0, 0);
+        }
+    }
+
+    // Same fragment as Operand::frag: element q is k = kc + 4 (lane >> 5) + q.
+    static __device__ __forceinline__ f32x4 frag(const float* __restrict__ s, int row, int kc)
+    {
+        const int kl = (threadIdx.x & 63) >> 5;
+        if (LAYOUT == RowK) {
+            return *reinterpret_cast<const f32x4*>(s + row * kBK + 4 * (((kc >> 2) + kl) ^ (row & 7)));
+        } else {
+            const float* c = s + (kc + 4 * kl) * R + row;
+            f32x4 v;
+            v.x = c[0];
+            v.y = c[R];
+            v.z = c[2 * R];
+            v.w = c[3 * R];
+            return v;
+        }
+    }
+};
+
+// Direct loads count against vmcnt until their data is in LDS.
+__device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int WM, int WN, int ALAY, int BLAY>
 struct Gemm {
     static constexpr int BM = 64 * WM;
     static constexpr int BN = 64 * WN;
-    typedef Operand<BM, ALAY> OA;
-    typedef Operand<BN, BLAY> OB;
-    static constexpr int LDS_FLOATS = OA::FLOATS + OB::FLOATS;
+    typedef Direct<BM, ALAY> OA;
+    typedef Direct<BN, BLAY> OB;
+    static constexpr int BUF = OA::FLOATS + OB::FLOATS;
+    static constexpr int LDS_FLOATS = 2 * BUF;   // two chunk buffers
     static_assert(WM * WN == 4, "four waves per block");
 };
 
@@ -134,10 +201,10 @@ __device__ __forceinline__ void acc_zero(Acc& a)
 }
 
 // C_block += A[m-rows, k0:k1] * B[k0:k1, n-cols] for this workgroup.
-// A rows beyond `alim` and B columns beyond `blim` read as zero.
-// k0, k1 are multiples of kBK.  `lds` must hold Gemm<...>::LDS_FLOATS.
-// One LDS buffer; the next chunk is prefetched into registers while the
-// current one feeds the MFMAs.
+// A rows beyond `alim` and B columns beyond `blim` are not needed (their
+// outputs are garbage: store with the same limits).  k0, k1 are multiples
+// of kBK.  `lds` must hold Gemm<...>::LDS_FLOATS; it is free again when
+// this returns.
 template <int WM, int WN, int ALAY, int BLAY>
 __device__ __forceinline__ void block_gemm(const float* __restrict__ A, int64_t lda, int alim,
                                            const float* __restrict__ B, int64_t ldb, int blim,
@@ -150,26 +217,23 @@ __device__ __forceinline__ void block_gemm(const float* __restrict__ A, int64_t 
     const int wave = threadIdx.x >> 6;
     const int wy = wave / WN, wx = wave % WN;
     const int ml = lane & 31;
-    float* sa = lds;
-    float* sb = lds + OA::FLOATS;
-
-    f32x4 ra[OA::PER_THREAD];
-    f32x4 rb[OB::PER_THREAD];
     const int nchunk = (k1 - k0) / kBK;
     if (nchunk <= 0) return;
 
-    OA::load(A, lda, alim, k0, ra);
-    OB::load(B, ldb, blim, k0, rb);
-    OA::store(sa, ra);
-    OB::store(sb, rb);
-    __syncthreads();
-
+    OA::issue(A, lda, alim, k0, lds);
+    OB::issue(B, ldb, blim, k0, lds + OA::FLOATS);
     for (int c = 0; c < nchunk; ++c) {
-        const bool more = (c + 1) < nchunk;
-        if (more) {
-            OA::load(A, lda, alim, k0 + (c + 1) * kBK, ra);
-            OB::load(B, ldb, blim, k0 + (c + 1) * kBK, rb);
+        // chunk c is in LDS for every wave, and every wave is done with
+        // chunk c - 1, whose buffer the next issue overwrites
+        wait_direct_loads();
+        __syncthreads();
+        if (c + 1 < nchunk) {
+            float* nb = lds + ((c + 1) & 1) * G::BUF;
+            OA::issue(A, lda, alim, k0 + (c + 1) * kBK, nb);
+            OB::issue(B, ldb, blim, k0 + (c + 1) * kBK, nb + OA::FLOATS);
         }
+        const float* sa = lds + (c & 1) * G::BUF;
+        const float* sb = sa + OA::FLOATS;
 #pragma unroll
         for (int kc = 0; kc < kBK; kc += 8) {
             const f32x4 a0 = OA::frag(sa, wy * 64 + ml, kc);
@@ -184,13 +248,8 @@ __device__ __forceinline__ void block_gemm(const float* __restrict__ A, int64_t 
                 acc.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], b1[q], acc.c[1][1], 0, 0, 0);
             }
         }
-        if (more) {
-            __syncthreads();
-            OA::store(sa, ra);
-            OB::store(sb, rb);
-            __syncthreads();
-        }
     }
+    __syncthreads();
 }
 
 // Row / column (within the block) of accumulator element r of tile (mi, ni)
@@ -214,31 +273,30 @@ template <int WM, int WN>
 __device__ __forceinline__ void block_store(float* __restrict__ C, int64_t ldc, int rlim, int clim,
                                             float alpha, float beta, const Acc& acc, int diag = kNoDiag)
 {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wy = wave / WN, wx = wave % WN;
     // rlim and clim are multiples of 64, so a wave's 64 x 64 sub-block is
     // either inside or outside: one wave-uniform test.
     if (wy * 64 >= rlim || wx * 64 >= clim) return;
-    float* base = C + (int64_t)(wy * 64) * ldc + wx * 64;
-    // all loads first (one wait), then all stores
-    float old[2][2][16];
+    float* base = C + (int64_t)(wy * 64) * ldc + wx * 64;   // wave-uniform
+    const uint32_t ld32 = (uint32_t)ldc;                      // 64 ldc < 2^32
+    // one 32 x 32 tile at a time: its 16 loads, one wait, its 16 stores
+    // (keeps the epilogue's registers below the main loop's)
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < 2; ++ni) {
+            float old[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                old[mi][ni][r] = (beta != 0.f) ? base[(int64_t)acc_row(mi, r) * ldc + acc_col(ni)] : 0.f;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+                old[r] = (beta != 0.f) ? base[(uint32_t)acc_row(mi, r) * ld32 + (uint32_t)acc_col(ni)] : 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = acc_row(mi, r), col = acc_col(ni);
                 if (wy * 64 + row - (wx * 64 + col) < diag) continue;
-                base[(int64_t)row * ldc + col] = alpha * acc.c[mi][ni][r] + beta * old[mi][ni][r];
+                base[(uint32_t)row * ld32 + (uint32_t)col] = alpha * acc.c[mi][ni][r] + beta * old[r];
             }
+        }
 }
 
 // C[r * ldc + c] = alpha * acc + beta * C over the wave's 32 x 32 tile,
@@ -266,30 +324,63 @@ __device__ __forceinline__ void wave_store32(float* __restrict__ C, int64_t ldc,
 //
 // For launches with few output tiles: a workgroup computes one 64 x 64
 // tile, wave w the 32 x 32 quadrant at rows 32 (w >> 1), columns 32 (w & 1),
-// so a launch keeps four waves busy per output tile.  Operands are staged
-// through LDS in coalesced chunks of kBK64 that the four waves share; a
-// quadrant does only 4 MFMAs per 8 k, so the chunk is deeper than the block
-// core's to spread the two barriers of a chunk over more MFMAs.
+// so a launch keeps four waves busy per output tile.  A quadrant does only
+// 4 MFMAs per 8 k.  With a K-contiguous A operand the chunks are staged by
+// direct loads into two buffers (one barrier per kBK chunk); with both
+// operands K-major (four scalar LDS reads per fragment on each side) the
+// register-staged copy in deeper chunks of kBK64 measured faster.
 #ifndef BAKRON_KBK64
 #define BAKRON_KBK64 64
 #endif
 constexpr int kBK64 = BAKRON_KBK64;
-constexpr int kLds64 = Operand<64, RowK, kBK64>::FLOATS > Operand<64, KRow, kBK64>::FLOATS
-                           ? 2 * Operand<64, RowK, kBK64>::FLOATS
-                           : 2 * Operand<64, KRow, kBK64>::FLOATS;
+constexpr int kLdsStaged64 = Operand<64, RowK, kBK64>::FLOATS > Operand<64, KRow, kBK64>::FLOATS
+                                 ? 2 * Operand<64, RowK, kBK64>::FLOATS
+                                 : 2 * Operand<64, KRow, kBK64>::FLOATS;
+constexpr int kLdsDirect64 = 2 * 2 * Direct<64, RowK>::FLOATS;
+constexpr int kLds64 = kLdsStaged64 > kLdsDirect64 ? kLdsStaged64 : kLdsDirect64;
 
-// k0, k1 are multiples of kBK64.
+// k0, k1 are multiples of kBK64; `lds` holds kLds64 floats and is free
+// again when this returns.
 template <int ALAY, int BLAY>
 __device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_t lda,
                                              const float* __restrict__ B, int64_t ldb, int k0, int k1,
                                              float* lds, f32x16& acc)
 {
-    typedef Operand<64, ALAY, kBK64> OA;
-    typedef Operand<64, BLAY, kBK64> OB;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int ml = lane & 31;
     const int ra = 32 * (wave >> 1) + ml, rb = 32 * (wave & 1) + ml;
+    if (ALAY == RowK) {
+        typedef Direct<64, ALAY> OA;
+        typedef Direct<64, BLAY> OB;
+        constexpr int BUF = OA::FLOATS + OB::FLOATS;
+        const int nchunk = (k1 - k0) / kBK;
+        if (nchunk <= 0) return;
+        OA::issue(A, lda, 64, k0, lds);
+        OB::issue(B, ldb, 64, k0, lds + OA::FLOATS);
+        for (int c = 0; c < nchunk; ++c) {
+            wait_direct_loads();
+            __syncthreads();
+            if (c + 1 < nchunk) {
+                float* nb = lds + ((c + 1) & 1) * BUF;
+                OA::issue(A, lda, 64, k0 + (c + 1) * kBK, nb);
+                OB::issue(B, ldb, 64, k0 + (c + 1) * kBK, nb + OA::FLOATS);
+            }
+            const float* sa = lds + (c & 1) * BUF;
+            const float* sb = sa + OA::FLOATS;
+#pragma unroll
+            for (int kc = 0; kc < kBK; kc += 8) {
+                const f32x4 a = OA::frag(sa, ra, kc);
+                const f32x4 b = OB::frag(sb, rb, kc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
+            }
+        }
+        __syncthreads();
+        return;
+    }
+    typedef Operand<64, ALAY, kBK64> OA;
+    typedef Operand<64, BLAY, kBK64> OB;
     float* sa = lds;
     float* sb = lds + OA::FLOATS;
     f32x4 pa[OA::PER_THREAD];
@@ -314,8 +405,8 @@ __device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[q], b[q], acc, 0, 0, 0);
         }
+        __syncthreads();
         if (more) {
-            __syncthreads();
             OA::store(sa, pa);
             OB::store(sb, pb);
             __syncthreads();

@@ -278,7 +278,7 @@ __device__ __forceinline__ unsigned xcd_group4(unsigned p, unsigned n)
     return p - r + (r % 8u) * 4u + r / 8u;
 }
 
-__global__ __launch_bounds__(256) void k_gptq_update(const float* __restrict__ E, const float* __restrict__ PA,
+__global__ __launch_bounds__(256, 2) void k_gptq_update(const float* __restrict__ E, const float* __restrict__ PA,
                                                      float* __restrict__ Wt, int64_t ldw, int64_t lda, int rows,
                                                      int s0, int s1, int t0, int t1)
 {

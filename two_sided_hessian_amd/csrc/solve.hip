@@ -528,7 +528,7 @@ __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, 
 //   Wt[I', J] -= sum_{I = slo .. min(I', mid - 1)} P_B[I', I] Y[I, J],
 // slo = max(0, K0 - J).  Only rows on target anti-diagonals
 // (mid <= I' + J < K1) are written.
-__global__ __launch_bounds__(256) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
+__global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
                                                    float* __restrict__ Wt, int64_t ldw, int64_t ldb,
                                                    int K0, int mid, int K1, int Mt, int Nt,
                                                    const uint32_t* __restrict__ list)
