@@ -170,7 +170,8 @@ def main():
         roofline = roofline_entry(*dom, traffic)
         mf = [kv for kv in agg.items() if kernel_bound(kv[0]) == "mfma"]
         if mf:
-            roofline_mfma = roofline_entry(*max(mf, key=lambda kv: kv[1]["total_ms"]), traffic)
+            # the MFMA kernel that carries the most algorithmic work
+            roofline_mfma = roofline_entry(*max(mf, key=lambda kv: kv[1]["alg_flops"]), traffic)
         log(f"[bench] kernels: {json.dumps(kernels)}")
 
     nxt = None
@@ -382,16 +383,16 @@ def kernel_bound(name):
 
 
 def sources_digest():
-    """sha256 over the library's kernel sources and ABI header: the HBM
-    counters in profiles/ are valid only for the sources they were taken on."""
+    """sha256 over the library's device and host sources (csrc/): the HBM
+    counters in profiles/ are valid only for the code they were taken on."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "two_sided_hessian_amd", "csrc")
-    for f in sorted(os.listdir(csrc)) + ["../../include/bakron.h"]:
-        path = os.path.normpath(os.path.join(csrc, f))
-        if path.endswith((".hip", ".hpp", ".h")):
+    for f in sorted(os.listdir(csrc)):
+        path = os.path.join(csrc, f)
+        if path.endswith((".hip", ".hpp")):
             with open(path, "rb") as fh:
-                h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+                h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
 
 

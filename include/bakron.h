@@ -140,7 +140,14 @@ size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);
  *                sum_ij (L_B[i,i] L_A[j,j] e_ij)^2, which equals
  *                ||L_B (V - W) L_A^T||_F^2 ([S] Corollary 3.4's quantity).
  * workspace, workspace_bytes [in] scratch, >= bakron_solve_workspace_bytes(m, n).
- * stream   [in]  HIP stream.
+ * stream   [in]  HIP stream of the current device.  All work is ordered on
+ *                it: part of the propagation of the upper recursion levels
+ *                runs on library-owned streams of the same device (created
+ *                on first use, default priority, kept until the process
+ *                ends), forked from and joined back into `stream` with
+ *                events before the call's last kernel, so later work on
+ *                `stream` sees every result.  Two calls that share one
+ *                workspace must be ordered on one stream.
  */
 int bakron_solve(const float* W, int64_t m, int64_t n,
                  const float* L_A, const float* P_A,
@@ -172,10 +179,12 @@ typedef struct bakron_layer {
 
 /*
  * Workspace bytes for bakron_solve_batch with these layers on n_streams
- * streams: one slice per stream, each as large as the largest
- * bakron_solve_workspace_bytes of the layers that stream runs (layer k runs
- * on stream k % n_streams), every slice 256-byte aligned.  0 when count or
- * n_streams is not positive.  Host only.
+ * streams: one slice per stream, each as large as the largest workspace a
+ * layer of that stream needs (layer k runs on stream k % n_streams), every
+ * slice 256-byte aligned.  A batch layer runs entirely on its stream (no
+ * library-owned streams), so its slice can be smaller than
+ * bakron_solve_workspace_bytes.  0 when count or n_streams is not positive.
+ * Host only.
  */
 size_t bakron_solve_batch_workspace_bytes(const bakron_layer* layers, int32_t count, int32_t n_streams);
 
@@ -184,7 +193,8 @@ size_t bakron_solve_batch_workspace_bytes(const bakron_layer* layers, int32_t co
  * over the caller's streams: layer k is enqueued on streams[k % n_streams]
  * with that stream's workspace slice, so layers on one stream run in order
  * and layers on different streams may run concurrently.  Each layer's
- * results are those of bakron_solve on the same inputs (the same kernels).
+ * results are those of bakron_solve on the same inputs (the same kernels,
+ * all on the layer's stream).
  *
  * layers    [in]  host array of `count` descriptors (device pointers inside).
  * count     [in]  >= 0; 0 enqueues nothing.

@@ -140,7 +140,7 @@ size_t bakron_solve_batch_workspace_bytes(const bakron_layer* layers, int32_t co
         for (int32_t k = s; k < count; k += n_streams) {
             const bakron_layer& L = layers[k];
             if (L.m > 0 && L.n > 0 && L.m <= BAKRON_MAX_DIM && L.n <= BAKRON_MAX_DIM)
-                need = std::max(need, bk::solve_workspace_bytes(L.m, L.n));
+                need = std::max(need, bk::solve_workspace_bytes(L.m, L.n, false));
         }
         total += bk::align_up(need);
     }
@@ -169,13 +169,13 @@ int bakron_solve_batch(const bakron_layer* layers, int32_t count, void* workspac
         size_t slice = 0;
         for (int32_t k = s; k < count; k += n_streams) {
             const bakron_layer& L = layers[k];
-            if (L.m > 0 && L.n > 0) slice = std::max(slice, bk::solve_workspace_bytes(L.m, L.n));
+            if (L.m > 0 && L.n > 0) slice = std::max(slice, bk::solve_workspace_bytes(L.m, L.n, false));
         }
         for (int32_t k = s; k < count; k += n_streams) {
             const bakron_layer& L = layers[k];
             if (L.m == 0 || L.n == 0) continue;
             if (bk::solve_enqueue(L.W, L.m, L.n, L.L_A, L.P_A, L.L_B, L.P_B, L.scale, L.zero, L.maxq, L.V, L.codes,
-                                  L.err, L.objective, base, streams[s], nullptr))
+                                  L.err, L.objective, base, streams[s], nullptr, false))
                 return BAKRON_ERR_HIP;
         }
         base += bk::align_up(slice);

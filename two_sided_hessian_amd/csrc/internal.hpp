@@ -61,6 +61,25 @@ inline void launch(Prof* p, int kind, double flops, double bytes, void (*kernel)
     p->recs.push_back(r);
 }
 
+// The same with `shmem` bytes of dynamic LDS reserved for the launch.
+template <typename... KArgs, typename... Args>
+inline void launch_shm(Prof* p, int kind, double flops, double bytes, void (*kernel)(KArgs...), dim3 g, dim3 b,
+                       size_t shmem, hipStream_t s, Args... args)
+{
+    if (!p) {
+        hipLaunchKernelGGL(kernel, g, b, shmem, s, static_cast<KArgs>(args)...);
+        return;
+    }
+    LaunchRec r{kind, nullptr, nullptr, flops, bytes};
+    if (hipEventCreate(&r.start) != hipSuccess || hipEventCreate(&r.stop) != hipSuccess) {
+        p->failed = true;
+        hipLaunchKernelGGL(kernel, g, b, shmem, s, static_cast<KArgs>(args)...);
+        return;
+    }
+    hipExtLaunchKernelGGL(kernel, g, b, shmem, s, r.start, r.stop, 0u, static_cast<KArgs>(args)...);
+    p->recs.push_back(r);
+}
+
 // Drain the stream, sum the per-launch event times per kernel kind into
 // stats (at most max_stats entries, in KernelKind order), release events.
 int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
@@ -78,12 +97,13 @@ size_t factor_workspace_bytes(int64_t n);
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
                    void* ws, hipStream_t stream, Prof* prof);
 
-// Solve (solve.hip)
-size_t solve_workspace_bytes(int64_t m, int64_t n);
+// Solve (solve.hip).  With `split`, the far parts of the upper nodes run on
+// library-owned streams, ordered against `stream` by events.
+size_t solve_workspace_bytes(int64_t m, int64_t n, bool split = true);
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,
                   const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                  void* ws, hipStream_t stream, Prof* prof);
+                  void* ws, hipStream_t stream, Prof* prof, bool split = true);
 
 // One-sided case B = I (gptq.hip)
 size_t gptq_workspace_bytes(int64_t m, int64_t n);

@@ -36,6 +36,9 @@
 //   sched  block lists of the propagation launches (k_sched)
 // Padding entries are forced to zero error, so they never touch real ones.
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <vector>
 
 #include "gemm.hpp"
 #include "internal.hpp"
@@ -381,56 +384,100 @@ typedef Gemm<4, 1, RowK, KRow> ColBlk;   // stage 2: 256 rows x 64 cols (one til
 // the blocks of one launch differ in length by up to two orders of
 // magnitude; started in plain index order, the long ones start late and the
 // launch ends with most CUs idle.  k_sched writes, for every internal node
-// of the recursion and each of its two stages, the node's blocks sorted by
-// decreasing K extent (longest first), and the propagation kernels take
-// their block from that list.  The order only decides which CU computes
-// which block: every block writes its own outputs, so results do not
-// depend on it.
+// of the recursion, each of its two stages and each part (below), the
+// blocks sorted by decreasing K extent (longest first), and the propagation
+// kernels take their block from that list.  The order only decides which CU
+// computes which block: every block writes its own outputs, so results do
+// not depend on it.
 //
 // Nodes are numbered as in a heap: the root [0, Kt) is (depth 0, pos 0) and
 // node (d, p) = [K0, K1) has children (d + 1, 2p) = [K0, mid) and
 // (d + 1, 2p + 1) = [mid, K1), mid = (K0 + K1) / 2.  A node at depth d is at
 // most w_d = ceil(Kt / 2^d) anti-diagonals wide, so a stage has at most
 // max(Mt, Nt) * ceil(w_d / 4) blocks: that is the list capacity cap[d], and
-// the list of (d, p, stage) starts at base[d] + (2p + stage) * cap[d].
+// the list of (d, p, stage, part) starts at
+// base[d] + (4p + 2 stage + part) * cap[d].
 // An entry packs (tile row or column) << 16 | block index.
+//
+// Parts.  The right child [mid, K1) of a node first solves [mid, m2),
+// m2 = (mid + K1) / 2, which needs only the node's updates of the target
+// anti-diagonals [mid, m2) (the near part).  The updates of [m2, K1) (the
+// far part) are not needed before the right child's own propagation, so on
+// the upper levels (depth < split_depth, K1 - mid >= kSplitMin) the far
+// part runs on a second stream while [mid, m2) is being solved.  Stage 1 of
+// the near part forms Y[I, J'] for J' < m2 - I (what near targets read),
+// the far part the remaining columns J' < K1 - I; far targets read both.
+// An unsplit node is one part: targets [mid, K1), Y columns J' < K1 - I.
 
 constexpr int kMaxDepth = 12;                 // Kt <= 2047 needs 11 levels of internal nodes
 constexpr int kMaxKTiles = kMaxDim / kTile;   // K extent of a block, in tiles
+#ifndef BAKRON_SPLIT_DEPTH
+#define BAKRON_SPLIT_DEPTH 4
+#endif
+constexpr int kSplitDepth = BAKRON_SPLIT_DEPTH;   // nodes above this depth may be split
+#ifndef BAKRON_SPLIT_MIN
+#define BAKRON_SPLIT_MIN 8
+#endif
+constexpr int kSplitMin = BAKRON_SPLIT_MIN;       // ... when the right child is at least this wide
 
 struct SchedGeom {
     int Mt, Nt, Kt, levels;
+    int split_depth;   // 0: no node is split
     int64_t base[kMaxDepth];
     int64_t cap[kMaxDepth];
 };
 
-// Stage 1 block (row I, block b): target columns j0 = sl + 4b .. jh, source
-// columns sl .. min(sh, jh).
-struct RowSpan {
-    int sl, sh, th;
-    __host__ __device__ RowSpan(int I, int K0, int mid, int K1, int Nt)
-        : sl(max(0, K0 - I)), sh(min(Nt - 1, mid - 1 - I)), th(min(Nt - 1, K1 - 1 - I)) {}
-    __host__ __device__ int blocks() const { return (th - sl + 4) / 4; }
-    __host__ __device__ int ktiles(int b) const { return min(sh, min(th, sl + 4 * b + 3)) - sl + 1; }
+__host__ __device__ inline bool node_split(const SchedGeom& g, int d, int mid, int K1)
+{
+    return d < g.split_depth && K1 - mid >= kSplitMin;
+}
+
+// Target range of a part: stage-1 Y columns J' < y1 - I (from the first
+// source column), stage-2 target anti-diagonals [t0, t1).
+struct PartRange {
+    int y1, t0, t1;
+    __host__ __device__ PartRange(bool split, int part, int mid, int K1)
+    {
+        const int m2 = (mid + K1) / 2;
+        if (!split) {
+            y1 = K1; t0 = mid; t1 = K1;
+        } else if (part == 0) {
+            y1 = m2; t0 = mid; t1 = m2;
+        } else {
+            y1 = K1; t0 = m2; t1 = K1;
+        }
+    }
 };
 
-// Stage 2 block (column J, block b): target rows i0 = tl + 4b .. ih, source
-// rows slo .. min(mid - 1, ih).
+// Stage 1 block (row I, block b): target columns j0 = tl + 4b .. jh, source
+// columns sl .. min(sh, jh).  y0 is where this part's Y columns start
+// (a far part skips the columns its near part formed).
+struct RowSpan {
+    int sl, sh, tl, th;
+    __host__ __device__ RowSpan(int I, int K0, int mid, int y0, int y1, int Nt)
+        : sl(max(0, K0 - I)), sh(min(Nt - 1, mid - 1 - I)), tl(max(max(0, K0 - I), y0 - I)),
+          th(min(Nt - 1, y1 - 1 - I)) {}
+    __host__ __device__ int blocks() const { return max(0, (th - tl + 4) / 4); }
+    __host__ __device__ int ktiles(int b) const { return min(sh, min(th, tl + 4 * b + 3)) - sl + 1; }
+};
+
+// Stage 2 block (column J, block b): target rows i0 = tl + 4b .. ih on the
+// target anti-diagonals [t0, t1), source rows slo .. min(mid - 1, ih).
 struct ColSpan {
     int tl, th, slo, mid;
-    __host__ __device__ ColSpan(int J, int K0, int mid_, int K1, int Mt)
-        : tl(max(0, mid_ - J)), th(min(Mt - 1, K1 - 1 - J)), slo(max(0, K0 - J)), mid(mid_) {}
-    __host__ __device__ int blocks() const { return (th - tl + 4) / 4; }
+    __host__ __device__ ColSpan(int J, int K0, int mid_, int t0, int t1, int Mt)
+        : tl(max(0, t0 - J)), th(min(Mt - 1, t1 - 1 - J)), slo(max(0, K0 - J)), mid(mid_) {}
+    __host__ __device__ int blocks() const { return max(0, (th - tl + 4) / 4); }
     __host__ __device__ int ktiles(int b) const { return min(mid - 1, min(th, tl + 4 * b + 3)) - slo + 1; }
 };
 
 __host__ __device__ inline int rows_lo(int K0, int Nt) { return max(0, K0 - (Nt - 1)); }
 __host__ __device__ inline int rows_hi(int mid, int Mt) { return min(Mt - 1, mid - 1); }
-__host__ __device__ inline int cols_lo(int mid, int Mt) { return max(0, mid - (Mt - 1)); }
-__host__ __device__ inline int cols_hi(int K1, int Nt) { return min(Nt - 1, K1 - 1); }
+__host__ __device__ inline int cols_lo(int t0, int Mt) { return max(0, t0 - (Mt - 1)); }
+__host__ __device__ inline int cols_hi(int t1, int Nt) { return min(Nt - 1, t1 - 1); }
 
-// One workgroup per (heap slot, stage): counting sort of the node's blocks
-// by K extent, descending.
+// One workgroup per (heap slot, stage, part): counting sort of the part's
+// blocks by K extent, descending.
 __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict__ out)
 {
     __shared__ int cnt[kMaxKTiles + 1];
@@ -439,7 +486,7 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     const unsigned slot = blockIdx.x + 1u;
     const int d = 31 - __builtin_clz(slot);
     const int p = (int)(slot - (1u << d));
-    const int stage = blockIdx.y;
+    const int stage = blockIdx.y, part = blockIdx.z;
     int K0 = 0, K1 = g.Kt;
     for (int l = d - 1; l >= 0; --l) {
         if (K1 - K0 < 2) return;          // no node at this slot
@@ -448,9 +495,13 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     }
     if (K1 - K0 < 2) return;              // a leaf: nothing to propagate
     const int mid = (K0 + K1) / 2;
-    uint32_t* list = out + g.base[d] + (int64_t)(2 * p + stage) * g.cap[d];
-    const int lo = stage == 0 ? rows_lo(K0, g.Nt) : cols_lo(mid, g.Mt);
-    const int hi = stage == 0 ? rows_hi(mid, g.Mt) : cols_hi(K1, g.Nt);
+    const bool split = node_split(g, d, mid, K1);
+    if (part == 1 && !split) return;
+    const PartRange pr(split, part, mid, K1);
+    const int y0 = part == 1 ? (mid + K1) / 2 : K0;
+    uint32_t* list = out + g.base[d] + (int64_t)(4 * p + 2 * stage + part) * g.cap[d];
+    const int lo = stage == 0 ? rows_lo(K0, g.Nt) : cols_lo(pr.t0, g.Mt);
+    const int hi = stage == 0 ? rows_hi(mid, g.Mt) : cols_hi(pr.t1, g.Nt);
 
     for (int k = t; k <= kMaxKTiles; k += 256) cnt[k] = 0;
     if (t == 0) kmax = 0;
@@ -458,14 +509,14 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     int km = 0;
     for (int u = lo + t; u <= hi; u += 256) {
         if (stage == 0) {
-            const RowSpan s(u, K0, mid, K1, g.Nt);
+            const RowSpan s(u, K0, mid, y0, pr.y1, g.Nt);
             for (int b = 0; b < s.blocks(); ++b) {
                 const int k = s.ktiles(b);
                 atomicAdd(&cnt[k], 1);
                 km = max(km, k);
             }
         } else {
-            const ColSpan s(u, K0, mid, K1, g.Mt);
+            const ColSpan s(u, K0, mid, pr.t0, pr.t1, g.Mt);
             for (int b = 0; b < s.blocks(); ++b) {
                 const int k = s.ktiles(b);
                 atomicAdd(&cnt[k], 1);
@@ -486,10 +537,10 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     __syncthreads();
     for (int u = lo + t; u <= hi; u += 256) {
         if (stage == 0) {
-            const RowSpan s(u, K0, mid, K1, g.Nt);
+            const RowSpan s(u, K0, mid, y0, pr.y1, g.Nt);
             for (int b = 0; b < s.blocks(); ++b) list[atomicAdd(&cnt[s.ktiles(b)], 1)] = ((uint32_t)u << 16) | (uint32_t)b;
         } else {
-            const ColSpan s(u, K0, mid, K1, g.Mt);
+            const ColSpan s(u, K0, mid, pr.t0, pr.t1, g.Mt);
             for (int b = 0; b < s.blocks(); ++b) list[atomicAdd(&cnt[s.ktiles(b)], 1)] = ((uint32_t)u << 16) | (uint32_t)b;
         }
     }
@@ -497,103 +548,120 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
 
 // ------------------------------------------------------ propagation
 
-// Stage 1 of node (K0, mid, K1): block (row I, b) from the schedule computes,
-// for the (up to) four target tile columns J' = j0 .. jh,
+// Stage 1 of node (K0, mid, K1), one part: block (row I, b) from the
+// schedule computes, for the (up to) four target tile columns J' = j0 .. jh
+// of its part,
 //   Y[I, J'] = sum_{J = sl .. min(sh, J')} E[I, J] P_A[J', J]^T.
 // P_A[J', J] is zero for J > J', so the block uses K = sl .. min(sh, jh).
+//
+// A launch covers `count` list entries with gridDim.x <= count workgroups,
+// each taking entries blockIdx.x, blockIdx.x + gridDim.x, ... (a far part
+// runs on a capped grid, next to the leaves; see enqueue_prop).
 __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
                                                    float* __restrict__ Y, int64_t ldw, int64_t lda,
-                                                   int K0, int mid, int K1, int Mt, int Nt,
-                                                   const uint32_t* __restrict__ list)
+                                                   int K0, int mid, int y0, int y1, int Mt, int Nt,
+                                                   const uint32_t* __restrict__ list, unsigned count)
 {
     __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
-    const uint32_t e = list[xcd_entry(blockIdx.x, gridDim.x)];
-    const int I = (int)(e >> 16), b = (int)(e & 0xffffu);
-    if (I < rows_lo(K0, Nt) || I > rows_hi(mid, Mt)) return;
-    const RowSpan s(I, K0, mid, K1, Nt);
-    const int j0 = s.sl + 4 * b;
-    if (j0 > s.th) return;
-    const int jh = min(s.th, j0 + 3);
-    const int kb = 64 * s.sl, ke = 64 * (min(s.sh, jh) + 1);
-    const int64_t r0 = (int64_t)I * 64;
-    Acc acc;
-    acc_zero(acc);
-    block_gemm<1, 4, RowK, RowK>(E + r0 * ldw, ldw, 64, PA + (int64_t)j0 * 64 * lda, lda,
-                                 64 * (jh - j0 + 1), kb, ke, lds, acc);
-    block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
+    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+        const uint32_t e = list[xcd_entry(q, count)];
+        const int I = (int)(e >> 16), b = (int)(e & 0xffffu);
+        if (I < rows_lo(K0, Nt) || I > rows_hi(mid, Mt)) continue;
+        const RowSpan s(I, K0, mid, y0, y1, Nt);
+        const int j0 = s.tl + 4 * b;
+        if (j0 > s.th) continue;
+        const int jh = min(s.th, j0 + 3);
+        const int kb = 64 * s.sl, ke = 64 * (min(s.sh, jh) + 1);
+        const int64_t r0 = (int64_t)I * 64;
+        Acc acc;
+        acc_zero(acc);
+        block_gemm<1, 4, RowK, RowK>(E + r0 * ldw, ldw, 64, PA + (int64_t)j0 * 64 * lda, lda,
+                                     64 * (jh - j0 + 1), kb, ke, lds, acc);
+        block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
+    }
 }
 
-// Stage 2 of node (K0, mid, K1): block (column J, b) from the schedule
-// updates the (up to) four target tile rows I' = i0 .. ih:
+// Stage 2 of node (K0, mid, K1), one part: block (column J, b) from the
+// schedule updates the (up to) four target tile rows I' = i0 .. ih on the
+// part's target anti-diagonals [t0, t1):
 //   Wt[I', J] -= sum_{I = slo .. min(I', mid - 1)} P_B[I', I] Y[I, J],
-// slo = max(0, K0 - J).  Only rows on target anti-diagonals
-// (mid <= I' + J < K1) are written.
+// slo = max(0, K0 - J).
 __global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
-                                                   float* __restrict__ Wt, int64_t ldw, int64_t ldb,
-                                                   int K0, int mid, int K1, int Mt, int Nt,
-                                                   const uint32_t* __restrict__ list)
+                                                      float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                      int K0, int mid, int t0, int t1, int Mt, int Nt,
+                                                      const uint32_t* __restrict__ list, unsigned count)
 {
     __shared__ __align__(16) float lds[ColBlk::LDS_FLOATS];
-    const uint32_t e = list[xcd_entry(blockIdx.x, gridDim.x)];
-    const int J = (int)(e >> 16), b = (int)(e & 0xffffu);
-    if (J < cols_lo(mid, Mt) || J > cols_hi(K1, Nt)) return;
-    const ColSpan s(J, K0, mid, K1, Mt);
-    const int i0 = s.tl + 4 * b;
-    if (i0 > s.th) return;
-    const int ih = min(s.th, i0 + 3);
-    const int kb = 64 * s.slo, ke = 64 * (min(mid - 1, ih) + 1);
-    const int64_t c0 = (int64_t)J * 64, rr = (int64_t)i0 * 64;
-    Acc acc;
-    acc_zero(acc);
-    block_gemm<4, 1, RowK, KRow>(PB + rr * ldb, ldb, 64 * (ih - i0 + 1), Y + c0, ldw, 64, kb, ke, lds, acc);
-    block_store<4, 1>(Wt + rr * ldw + c0, ldw, 64 * (ih - i0 + 1), 64, -1.f, 1.f, acc);
+    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+        const uint32_t e = list[xcd_entry(q, count)];
+        const int J = (int)(e >> 16), b = (int)(e & 0xffffu);
+        if (J < cols_lo(t0, Mt) || J > cols_hi(t1, Nt)) continue;
+        const ColSpan s(J, K0, mid, t0, t1, Mt);
+        const int i0 = s.tl + 4 * b;
+        if (i0 > s.th) continue;
+        const int ih = min(s.th, i0 + 3);
+        const int kb = 64 * s.slo, ke = 64 * (min(mid - 1, ih) + 1);
+        const int64_t c0 = (int64_t)J * 64, rr = (int64_t)i0 * 64;
+        Acc acc;
+        acc_zero(acc);
+        block_gemm<4, 1, RowK, KRow>(PB + rr * ldb, ldb, 64 * (ih - i0 + 1), Y + c0, ldw, 64, kb, ke, lds, acc);
+        block_store<4, 1>(Wt + rr * ldw + c0, ldw, 64 * (ih - i0 + 1), 64, -1.f, 1.f, acc);
+    }
 }
 
-// Small nodes: the same two stages with one 64 x 64 target tile per
-// workgroup and one 32 x 32 quadrant per wave (block_gemm64), so a node with
+// Small parts: the same two stages with one 64 x 64 target tile per
+// workgroup and one 32 x 32 quadrant per wave (block_gemm64), so a part with
 // few 64 x 256 blocks still spreads over many CUs.
-// Stage 1: workgroup (x, y) computes Y[I, J'] for row I = rows_lo + y and
+// Work item q = y * span + x (x fastest), taken by workgroups blockIdx.x,
+// blockIdx.x + gridDim.x, ... as in the block kernels.
+// Stage 1: item (x, y) computes Y[I, J'] for row I = rows_lo + y and
 // J' = th - x (the K extent grows with J': longest first).
 __global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E, const float* __restrict__ PA,
                                                      float* __restrict__ Y, int64_t ldw, int64_t lda,
-                                                     int K0, int mid, int K1, int Nt)
+                                                     int K0, int mid, int y0, int y1, int Nt, unsigned span,
+                                                     unsigned count)
 {
     __shared__ __align__(16) float lds[kLds64];
-    const int I = rows_lo(K0, Nt) + (int)blockIdx.y;
-    const RowSpan s(I, K0, mid, K1, Nt);
-    const int Jp = s.th - (int)blockIdx.x;
-    if (Jp < s.sl) return;
     const int wave = threadIdx.x >> 6;
-    f32x16 acc;
+    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+        const int I = rows_lo(K0, Nt) + (int)(q / span);
+        const RowSpan s(I, K0, mid, y0, y1, Nt);
+        const int Jp = s.th - (int)(q % span);
+        if (Jp < s.tl) continue;
+        f32x16 acc;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    block_gemm64<RowK, RowK>(E + (int64_t)I * 64 * ldw, ldw, PA + (int64_t)Jp * 64 * lda, lda, 64 * s.sl,
-                             64 * (min(s.sh, Jp) + 1), lds, acc);
-    const int64_t r = (int64_t)I * 64 + 32 * (wave >> 1);
-    const int64_t c = (int64_t)Jp * 64 + 32 * (wave & 1);
-    wave_store32(Y + r * ldw + c, ldw, 1.f, 0.f, acc);
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        block_gemm64<RowK, RowK>(E + (int64_t)I * 64 * ldw, ldw, PA + (int64_t)Jp * 64 * lda, lda, 64 * s.sl,
+                                 64 * (min(s.sh, Jp) + 1), lds, acc);
+        const int64_t r = (int64_t)I * 64 + 32 * (wave >> 1);
+        const int64_t c = (int64_t)Jp * 64 + 32 * (wave & 1);
+        wave_store32(Y + r * ldw + c, ldw, 1.f, 0.f, acc);
+    }
 }
 
-// Stage 2: workgroup (x, y) updates Wt[I', J] for column J = cols_lo + y and
+// Stage 2: item (x, y) updates Wt[I', J] for column J = cols_lo + y and
 // I' = th - x.
 __global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y, const float* __restrict__ PB,
                                                      float* __restrict__ Wt, int64_t ldw, int64_t ldb,
-                                                     int K0, int mid, int K1, int Mt)
+                                                     int K0, int mid, int t0, int t1, int Mt, unsigned span,
+                                                     unsigned count)
 {
     __shared__ __align__(16) float lds[kLds64];
-    const int J = cols_lo(mid, Mt) + (int)blockIdx.y;
-    const ColSpan s(J, K0, mid, K1, Mt);
-    const int Ip = s.th - (int)blockIdx.x;
-    if (Ip < s.tl) return;
     const int wave = threadIdx.x >> 6;
-    f32x16 acc;
+    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+        const int J = cols_lo(t0, Mt) + (int)(q / span);
+        const ColSpan s(J, K0, mid, t0, t1, Mt);
+        const int Ip = s.th - (int)(q % span);
+        if (Ip < s.tl) continue;
+        f32x16 acc;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.f;
-    block_gemm64<RowK, KRow>(PB + (int64_t)Ip * 64 * ldb, ldb, Y + (int64_t)J * 64, ldw, 64 * s.slo,
-                             64 * (min(mid - 1, Ip) + 1), lds, acc);
-    const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1);
-    const int64_t c = (int64_t)J * 64 + 32 * (wave & 1);
-    wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        block_gemm64<RowK, KRow>(PB + (int64_t)Ip * 64 * ldb, ldb, Y + (int64_t)J * 64, ldw, 64 * s.slo,
+                                 64 * (min(mid - 1, Ip) + 1), lds, acc);
+        const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1);
+        const int64_t c = (int64_t)J * 64 + 32 * (wave & 1);
+        wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
+    }
 }
 
 __global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t count,
@@ -620,7 +688,9 @@ struct SolvePlan {
     bool pad_a, pad_b;
     SchedGeom sg;
     int64_t sched_entries;
+    int split_levels;   // depths 0 .. split_levels - 1 may hold split nodes
     size_t off_wt, off_e, off_y, off_obj, off_pa, off_pb, off_sched, total;
+    size_t off_ysplit[kSplitDepth];   // one stage-1 buffer per depth with split nodes
 };
 
 // Heap levels holding internal nodes, and the list offsets of k_sched.
@@ -631,18 +701,24 @@ void plan_sched(SchedGeom& g, int64_t& entries, int Mt, int Nt)
     g.Kt = Mt + Nt - 1;
     g.levels = 0;
     while ((1 << g.levels) < g.Kt) ++g.levels;   // depth d holds a node of width >= 2 iff 2^d < Kt
+    // the widest node at depth d is ceil(Kt / 2^d) wide, its right child
+    // half of that (rounded up)
+    g.split_depth = 0;
+    while (g.split_depth < std::min(kSplitDepth, g.levels) &&
+           ceil_div(ceil_div(g.Kt, (int64_t)1 << g.split_depth), 2) >= kSplitMin)
+        ++g.split_depth;
     const int64_t R = std::max(Mt, Nt);
     int64_t off = 0;
     for (int d = 0; d < kMaxDepth; ++d) {
         const int64_t w = ceil_div(g.Kt, (int64_t)1 << d);
         g.base[d] = off;
         g.cap[d] = R * ceil_div(w, 4);
-        if (d < g.levels) off += ((int64_t)1 << d) * 2 * g.cap[d];
+        if (d < g.levels) off += ((int64_t)1 << d) * 4 * g.cap[d];   // 2 stages x 2 parts per node
     }
     entries = off;
 }
 
-SolvePlan plan_solve(int64_t m, int64_t n)
+SolvePlan plan_solve(int64_t m, int64_t n, bool split)
 {
     SolvePlan p;
     p.m = m;
@@ -653,6 +729,9 @@ SolvePlan plan_solve(int64_t m, int64_t n)
     p.Np = p.Nt * kTile;
     p.pad_a = (n % kTile) != 0;
     p.pad_b = (m % kTile) != 0;
+    plan_sched(p.sg, p.sched_entries, (int)p.Mt, (int)p.Nt);
+    if (!split) p.sg.split_depth = 0;
+    p.split_levels = p.sg.split_depth;
     const size_t mat = sizeof(float) * (size_t)(p.Mp * p.Np);
     size_t off = 0;
     p.off_wt = off;
@@ -661,6 +740,10 @@ SolvePlan plan_solve(int64_t m, int64_t n)
     off = align_up(off + mat);
     p.off_y = off;
     off = align_up(off + mat);
+    for (int d = 0; d < kSplitDepth; ++d) {
+        p.off_ysplit[d] = off;
+        if (d < p.split_levels) off = align_up(off + mat);
+    }
     p.off_obj = off;
     off = align_up(off + sizeof(double) * (size_t)(p.Mt * p.Nt));
     p.off_pa = p.off_pb = 0;
@@ -672,7 +755,6 @@ SolvePlan plan_solve(int64_t m, int64_t n)
         p.off_pb = off;
         off = align_up(off + sizeof(float) * (size_t)(p.Mp * p.Mp));
     }
-    plan_sched(p.sg, p.sched_entries, (int)p.Mt, (int)p.Nt);
     p.off_sched = off;
     off = align_up(off + sizeof(uint32_t) * (size_t)p.sched_entries);
     p.total = off;
@@ -686,13 +768,46 @@ dim3 copy_grid(int64_t R, int64_t C)
 
 struct SolveRun {
     LeafArgs leaf;
-    float* Y;
+    float* Y;                      // stage-1 buffer of unsplit nodes
+    float* Ysplit[kSplitDepth];    // ... of the split nodes at each depth
     const uint32_t* sched;
     const SchedGeom* sg;
     int Mt, Nt;
-    hipStream_t s;
+    hipStream_t s;                 // the caller's stream: leaves, unsplit nodes, near parts
+    hipStream_t far[kSplitDepth];  // far parts of split nodes, one stream per depth
+    std::vector<hipEvent_t> events;
+    bool failed;
     Prof* prof;
 };
+
+// Library-owned streams for far parts (default priority, non-blocking),
+// created on first use per device and kept for the life of the process.
+hipStream_t far_stream(int d)
+{
+    static std::mutex mu;
+    static std::map<int, std::vector<hipStream_t>> table;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    std::vector<hipStream_t>& v = table[dev];
+    while ((int)v.size() <= d) {
+        hipStream_t st = nullptr;
+        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        v.push_back(st);
+    }
+    return v[d];
+}
+
+hipEvent_t new_event(SolveRun& R)
+{
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+        R.failed = true;
+        return nullptr;
+    }
+    R.events.push_back(e);
+    return e;
+}
 
 int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
 
@@ -721,109 +836,189 @@ void enqueue_leaf(SolveRun& R, int K)
 #endif
 constexpr int64_t kBlockLaunchMin = BAKRON_BLOCK_LAUNCH_MIN;
 
-// Node (K0, mid, K1) at heap position (d, p): stage 1 over the tile rows
-// with source tiles, then stage 2 over the target tile columns, each over
-// the block list k_sched wrote for it.
-void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
+// A far part runs beside the leaves and small nodes of the caller's stream,
+// which are latency-bound: a leaf sharing a CU with a propagation workgroup
+// runs about three times slower.  So a far launch takes at most kFarGrid
+// workgroups (looping over its blocks) and reserves enough extra LDS that no
+// leaf fits next to one of them: leaves then run on CUs of their own.
+#ifndef BAKRON_FAR_GRID
+#define BAKRON_FAR_GRID 192
+#endif
+constexpr unsigned kFarGrid = BAKRON_FAR_GRID;
+#ifndef BAKRON_FAR_BLOCK_MIN
+#define BAKRON_FAR_BLOCK_MIN BAKRON_BLOCK_LAUNCH_MIN
+#endif
+constexpr int64_t kFarBlockMin = BAKRON_FAR_BLOCK_MIN;   // the block kernel from this many blocks
+constexpr size_t kLdsPerCU = 160 * 1024;
+constexpr size_t kLeafLds = sizeof(float) * (64 * 64 + 3 * 64 * kLP + 8) + 64 * 64 + 8 * sizeof(double);   // k_leaf's arrays
+constexpr size_t pad_to_exclude(size_t static_lds)
+{
+    return static_lds + kLeafLds > kLdsPerCU ? 0 : kLdsPerCU - kLeafLds - static_lds + 1024;
+}
+constexpr size_t kFarPadBlock = pad_to_exclude(sizeof(float) * RowBlk::LDS_FLOATS);
+#ifndef BAKRON_FAR_PAD_TILE
+#define BAKRON_FAR_PAD_TILE 1
+#endif
+constexpr size_t kFarPadTile = BAKRON_FAR_PAD_TILE ? pad_to_exclude(sizeof(float) * kLds64) : 0;
+static_assert(sizeof(float) * RowBlk::LDS_FLOATS == sizeof(float) * ColBlk::LDS_FLOATS, "one pad for both stages");
+
+// Stage 1 of one part of node (K0, mid, K1) on stream st into Y.
+void enqueue_stage1(SolveRun& R, int K0, int mid, int y0, int y1, const uint32_t* list, float* Y, hipStream_t st,
+                    bool far)
 {
     const int Mt = R.Mt, Nt = R.Nt;
-    const uint32_t* list1 = R.sched + R.sg->base[d] + (int64_t)(2 * p) * R.sg->cap[d];
-    const uint32_t* list2 = list1 + R.sg->cap[d];
     const int I_lo = rows_lo(K0, Nt), I_hi = rows_hi(mid, Mt);
     int64_t blocks = 0;
     int span = 0;   // widest row, in target tiles
     double fl = 0.0, by = 0.0;
+    std::vector<uint8_t> pa_used;
+    if (R.prof) pa_used.assign((size_t)Nt * Nt, 0);
     for (int I = I_lo; I <= I_hi; ++I) {
-        const RowSpan sp(I, K0, mid, K1, Nt);
-        blocks += sp.blocks();
-        span = std::max(span, sp.th - sp.sl + 1);
-        if (R.prof) {
-            const double S = sp.sh - sp.sl + 1, T = sp.th - sp.sl + 1;
-            const double pairs = S * (S + 1) / 2 + (T - S) * S;   // (J, J') with J <= J'
-            fl += 2.0 * ((pairs - S) * kFull + S * kTriB);
-            by += (S + T) * kTileB;                              // E read, Y written
-        }
-    }
-    if (R.prof)   // distinct P_A blocks: for source column J, J' runs over [J, th(first row using J)]
-        for (int J = 0; J < Nt; ++J) {
-            const int Ia = std::max(I_lo, K0 - J), Ib = std::min(I_hi, mid - 1 - J);
-            if (Ia > Ib) continue;
-            by += (std::min(Nt - 1, K1 - 1 - Ia) - J + 1) * kTileB;
-        }
-    if (blocks >= kBlockLaunchMin)
-        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3((unsigned)blocks), dim3(256), R.s,
-               (const float*)R.leaf.E, R.leaf.PA, R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Mt, Nt, list1);
-    else if (blocks > 0)
-        launch(R.prof, KK_PROP_ROWS_T, fl, by, k_prop_rows_t,
-               dim3((unsigned)span, (unsigned)(I_hi - I_lo + 1)), dim3(256), R.s, (const float*)R.leaf.E, R.leaf.PA,
-               R.Y, R.leaf.ldw, R.leaf.lda, K0, mid, K1, Nt);
-
-    const int J_lo = cols_lo(mid, Mt), J_hi = cols_hi(K1, Nt);
-    blocks = 0;
-    span = 0;
-    fl = by = 0.0;
-    for (int J = J_lo; J <= J_hi; ++J) {
-        const ColSpan sp(J, K0, mid, K1, Mt);
+        const RowSpan sp(I, K0, mid, y0, y1, Nt);
         blocks += sp.blocks();
         span = std::max(span, sp.th - sp.tl + 1);
-        if (R.prof) {
+        if (R.prof && sp.th >= sp.tl) {
+            // pairs (J, J') with sl <= J <= min(sh, J'); the diagonal block is triangular
+            for (int Jp = sp.tl; Jp <= sp.th; ++Jp) {
+                const int hi = std::min(sp.sh, Jp);
+                const double cnt = hi - sp.sl + 1;
+                const bool diag = Jp <= sp.sh;
+                fl += 2.0 * ((cnt - (diag ? 1 : 0)) * kFull + (diag ? kTriB : 0.0));
+                for (int J = sp.sl; J <= hi; ++J) pa_used[(size_t)Jp * Nt + J] = 1;
+            }
+            by += ((sp.sh - sp.sl + 1) + (sp.th - sp.tl + 1)) * kTileB;   // E read, Y written
+        }
+    }
+    if (R.prof)   // distinct P_A blocks
+        for (uint8_t u : pa_used) by += u ? kTileB : 0.0;
+    if (blocks >= (far ? kFarBlockMin : kBlockLaunchMin)) {
+        const unsigned n = (unsigned)blocks;
+        launch_shm(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+                   far ? kFarPadBlock : 0, st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid,
+                   y0, y1, Mt, Nt, list, n);
+    } else if (blocks > 0) {
+        const unsigned n = (unsigned)span * (unsigned)(I_hi - I_lo + 1);
+        launch_shm(R.prof, KK_PROP_ROWS_T, fl, by, k_prop_rows_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+                   far ? kFarPadTile : 0, st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid,
+                   y0, y1, Nt, (unsigned)span, n);
+    }
+}
+
+// Stage 2 of one part of node (K0, mid, K1) (targets [t0, t1)) on stream st from Y.
+void enqueue_stage2(SolveRun& R, int K0, int mid, int t0, int t1, const uint32_t* list, const float* Y,
+                    hipStream_t st, bool far)
+{
+    const int Mt = R.Mt, Nt = R.Nt;
+    const int J_lo = cols_lo(t0, Mt), J_hi = cols_hi(t1, Nt);
+    int64_t blocks = 0;
+    int span = 0;
+    double fl = 0.0, by = 0.0;
+    std::vector<uint8_t> pb_used;
+    if (R.prof) pb_used.assign((size_t)Mt * Mt, 0);
+    for (int J = J_lo; J <= J_hi; ++J) {
+        const ColSpan sp(J, K0, mid, t0, t1, Mt);
+        blocks += sp.blocks();
+        span = std::max(span, sp.th - sp.tl + 1);
+        if (R.prof && sp.th >= sp.tl) {
             for (int Ip = sp.tl; Ip <= sp.th; ++Ip) {
                 const int shi = std::min(mid - 1, Ip);
                 const double cnt = shi - sp.slo + 1;
                 const bool diag = Ip <= mid - 1;
                 fl += 2.0 * ((cnt - (diag ? 1 : 0)) * kFull + (diag ? kTriB : 0.0));
+                for (int I = sp.slo; I <= shi; ++I) pb_used[(size_t)Ip * Mt + I] = 1;
             }
             by += (std::min(mid - 1, sp.th) - sp.slo + 1) * kTileB;   // Y read
             by += 2.0 * (sp.th - sp.tl + 1) * kTileB;                 // W~ read and written
         }
     }
-    if (R.prof)   // distinct P_B blocks: for source row I, I' runs over [max(I, tl(J_hi)), th(first column using I)]
-        for (int I = 0; I < Mt; ++I) {
-            const int Ja = std::max(J_lo, K0 - I);
-            if (Ja > J_hi || I > mid - 1) continue;
-            const int hi = std::min(Mt - 1, K1 - 1 - Ja);
-            const int lo = std::max(I, std::max(0, mid - J_hi));
-            if (hi >= lo) by += (hi - lo + 1) * kTileB;
-        }
-    if (blocks >= kBlockLaunchMin)
-        launch(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3((unsigned)blocks), dim3(256), R.s,
-               (const float*)R.Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt, Nt, list2);
-    else if (blocks > 0)
-        launch(R.prof, KK_PROP_COLS_T, fl, by, k_prop_cols_t,
-               dim3((unsigned)span, (unsigned)(J_hi - J_lo + 1)), dim3(256), R.s, (const float*)R.Y, R.leaf.PB,
-               R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, K1, Mt);
+    if (R.prof)   // distinct P_B blocks
+        for (uint8_t u : pb_used) by += u ? kTileB : 0.0;
+    if (blocks >= (far ? kFarBlockMin : kBlockLaunchMin)) {
+        const unsigned n = (unsigned)blocks;
+        launch_shm(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+                   far ? kFarPadBlock : 0, st, Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, t0, t1, Mt,
+                   Nt, list, n);
+    } else if (blocks > 0) {
+        const unsigned n = (unsigned)span * (unsigned)(J_hi - J_lo + 1);
+        launch_shm(R.prof, KK_PROP_COLS_T, fl, by, k_prop_cols_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+                   far ? kFarPadTile : 0, st, Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, t0, t1, Mt,
+                   (unsigned)span, n);
+    }
 }
 
-void solve_rec(SolveRun& R, int K0, int K1, int d, int p)
+// Node (K0, mid, K1) at heap position (d, p).  Unsplit: both stages on the
+// caller's stream; returns nullptr.  Split: the near part on the caller's
+// stream, the far part on the depth's own stream once the near stage 1 is
+// done (far targets read those Y columns too); returns the event that marks
+// the far part done, which the right child waits for before its own
+// propagation (the first work that touches [m2, K1)).
+hipEvent_t enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
 {
-    if (K1 - K0 == 1) {
+    const SchedGeom& g = *R.sg;
+    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(4 * p) * g.cap[d];   // (stage, part) at (2 stage + part) cap
+    const bool split = node_split(g, d, mid, K1);
+    const PartRange near(split, 0, mid, K1);
+    float* Y = split ? R.Ysplit[d] : R.Y;
+    enqueue_stage1(R, K0, mid, K0, near.y1, lists, Y, R.s, false);
+    if (!split) {
+        enqueue_stage2(R, K0, mid, near.t0, near.t1, lists + 2 * g.cap[d], Y, R.s, false);
+        return nullptr;
+    }
+    const PartRange far(true, 1, mid, K1);
+    hipEvent_t ev1 = new_event(R), ev2 = new_event(R);
+    if (!ev1 || !ev2) return nullptr;
+    if (hipEventRecord(ev1, R.s) != hipSuccess || hipStreamWaitEvent(R.far[d], ev1, 0) != hipSuccess) {
+        R.failed = true;
+        return nullptr;
+    }
+    enqueue_stage2(R, K0, mid, near.t0, near.t1, lists + 2 * g.cap[d], Y, R.s, false);
+    enqueue_stage1(R, K0, mid, (mid + K1) / 2, far.y1, lists + g.cap[d], Y, R.far[d], true);
+    enqueue_stage2(R, K0, mid, far.t0, far.t1, lists + 3 * g.cap[d], Y, R.far[d], true);
+    if (hipEventRecord(ev2, R.far[d]) != hipSuccess) {
+        R.failed = true;
+        return nullptr;
+    }
+    return ev2;
+}
+
+// `wait`: the far part of the parent, which updated [mid, K1) of this node.
+void solve_rec(SolveRun& R, int K0, int K1, int d, int p, hipEvent_t wait)
+{
+    if (K1 - K0 == 1) {   // (a split parent's right child is never a leaf)
         enqueue_leaf(R, K0);
         return;
     }
     const int mid = (K0 + K1) / 2;
-    solve_rec(R, K0, mid, d + 1, 2 * p);
-    enqueue_prop(R, K0, mid, K1, d, p);
-    solve_rec(R, mid, K1, d + 1, 2 * p + 1);
+    solve_rec(R, K0, mid, d + 1, 2 * p, nullptr);
+    if (wait && hipStreamWaitEvent(R.s, wait, 0) != hipSuccess) R.failed = true;
+    hipEvent_t far_done = enqueue_prop(R, K0, mid, K1, d, p);
+    solve_rec(R, mid, K1, d + 1, 2 * p + 1, far_done);
 }
 
 }  // namespace
 
-size_t solve_workspace_bytes(int64_t m, int64_t n)
+size_t solve_workspace_bytes(int64_t m, int64_t n, bool split)
 {
     if (m <= 0 || n <= 0) return 0;
-    return plan_solve(m, n).total;
+    return plan_solve(m, n, split).total;
 }
 
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,
                   const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                  void* ws, hipStream_t s, Prof* prof)
+                  void* ws, hipStream_t s, Prof* prof, bool split)
 {
-    const SolvePlan p = plan_solve(m, n);
+    SolvePlan p = plan_solve(m, n, split);
     char* w = static_cast<char*>(ws);
     SolveRun R;
     R.prof = prof;
     R.s = s;
+    R.failed = false;
+    for (int d = 0; d < kSplitDepth; ++d) {
+        R.Ysplit[d] = d < p.sg.split_depth ? reinterpret_cast<float*>(w + p.off_ysplit[d]) : nullptr;
+        R.far[d] = d < p.sg.split_depth ? far_stream(d) : nullptr;
+        if (d < p.sg.split_depth && !R.far[d]) p.sg.split_depth = 0;   // no stream: nothing is split
+    }
     LeafArgs& g = R.leaf;
     g.Wt = reinterpret_cast<float*>(w + p.off_wt);
     g.E = reinterpret_cast<float*>(w + p.off_e);
@@ -876,9 +1071,25 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.sched = sched;
     if (p.sg.levels > 0)
         launch(prof, KK_SCHED, 0.0, 4.0 * (double)p.sched_entries, k_sched,
-               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u), dim3(256), s, p.sg, sched);
-    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0);
-    if (launch_ok()) return -1;
+               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u, 2u), dim3(256), s, p.sg, sched);
+    if (p.sg.split_depth > 0) {
+        static std::once_flag attrs;
+        std::call_once(attrs, [] {
+            (void)hipFuncSetAttribute((const void*)k_prop_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFarPadBlock);
+            (void)hipFuncSetAttribute((const void*)k_prop_cols, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFarPadBlock);
+            if (kFarPadTile) {
+                (void)hipFuncSetAttribute((const void*)k_prop_rows_t, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)kFarPadTile);
+                (void)hipFuncSetAttribute((const void*)k_prop_cols_t, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)kFarPadTile);
+            }
+        });
+    }
+    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, nullptr);
+    // every far part is waited for by the right child of its node, so all
+    // of them are ordered before the rest of the work on s
+    for (hipEvent_t e : R.events) (void)hipEventDestroy(e);
+    if (R.failed || launch_ok()) return -1;
     if (objective) {
         const double cnt = (double)(p.Mt * p.Nt);
         launch(prof, KK_OBJ_REDUCE, cnt, 8.0 * (cnt + 1.0), k_obj_reduce, dim3(1), dim3(256), s,
