@@ -166,9 +166,14 @@ def main():
                        "alg_gbs": round(v["alg_bytes"] / (v["total_ms"] * 1e-3) / 1e9, 1) if v["total_ms"] > 0 else None}
                    for k, v in sorted(agg.items(), key=lambda kv: -kv[1]["total_ms"])}
         traffic = load_traffic(spec.name)
-        dom = max(agg.items(), key=lambda kv: kv[1]["total_ms"])
+        # The far parts of the solve run beside the caller's stream on a
+        # capped grid (their launches are the *_far kernels): their summed
+        # durations overlap the rest of the step, so the dominant kernel is
+        # chosen among the kernels of the step's own stream order.
+        main = [kv for kv in agg.items() if not kv[0].endswith("_far")]
+        dom = max(main, key=lambda kv: kv[1]["total_ms"])
         roofline = roofline_entry(*dom, traffic)
-        mf = [kv for kv in agg.items() if kernel_bound(kv[0]) == "mfma"]
+        mf = [kv for kv in main if kernel_bound(kv[0]) == "mfma"]
         if mf:
             # the MFMA kernel that carries the most algorithmic work
             roofline_mfma = roofline_entry(*max(mf, key=lambda kv: kv[1]["alg_flops"]), traffic)
@@ -370,7 +375,8 @@ def bench_batch(B, WL, dev, args, layers=16, name="sq1024"):
 # (the leaf sweep, the diagonal-block factor, the schedule and the objective
 # reduction) are chains of dependent vector arithmetic and LDS traffic,
 # priced against the fp32 vector peak.
-MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_f_panel", "k_f_right",
+MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_prop_rows_far", "k_prop_rows_t_far",
+                "k_prop_cols_far", "k_prop_cols_t_far", "k_f_panel", "k_f_right",
                 "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_gptq_update",
                 "k_gptq_update_t", "k_moment<false>", "k_moment<true>"}
 HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info", "k_gptq_load",

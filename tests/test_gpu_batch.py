@@ -1,7 +1,10 @@
 """Batched solves of independent layers (bakron_solve_batch, through the C
 ABI): every layer's outputs equal bakron_solve's on the same inputs, bit for
 bit, whatever the stream a layer lands on, and pass the float64 oracle's
-validator.
+validator.  A batch layer runs all its work on its own stream, while
+bakron_solve runs the far parts of its upper recursion nodes on separate
+streams (shapes with at least 16 tile anti-diagonals), so the comparison
+also pins the split schedule to the unsplit one, padded shapes included.
 
 Pages: [S] paper summary "FastKron: Efficient Quantization with
 Kronecker-Factored Hessians" (every linear layer has its own W, A and B).
@@ -16,7 +19,8 @@ from workloads import make_problem
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SHAPES = [(64, 64), (130, 70), (256, 192), (1024, 1024), (96, 300), (1, 64), (512, 512)]
+SHAPES = [(64, 64), (130, 70), (256, 192), (1024, 1024), (96, 300), (1, 64), (512, 512), (1000, 1500),
+          (2048, 640)]
 
 
 def to_dev(a):

@@ -415,6 +415,10 @@ constexpr int kMaxKTiles = kMaxDim / kTile;   // K extent of a block, in tiles
 #define BAKRON_SPLIT_DEPTH 4
 #endif
 constexpr int kSplitDepth = BAKRON_SPLIT_DEPTH;   // nodes above this depth may be split
+#ifndef BAKRON_SPLIT3_DEPTH
+#define BAKRON_SPLIT3_DEPTH 3
+#endif
+constexpr int kSplit3Depth = BAKRON_SPLIT3_DEPTH;  // nodes above this depth may be cut in three
 #ifndef BAKRON_SPLIT_MIN
 #define BAKRON_SPLIT_MIN 8
 #endif
@@ -422,30 +426,35 @@ constexpr int kSplitMin = BAKRON_SPLIT_MIN;       // ... when the right child is
 
 struct SchedGeom {
     int Mt, Nt, Kt, levels;
-    int split_depth;   // 0: no node is split
+    int split_depth;    // nodes above this depth may be cut in parts (0: none)
+    int split3_depth;   // ... and in three parts above this one
     int64_t base[kMaxDepth];
     int64_t cap[kMaxDepth];
 };
 
-__host__ __device__ inline bool node_split(const SchedGeom& g, int d, int mid, int K1)
+// Parts of node (d, [K0, K1)): 1 (unsplit), 2 (targets [mid, m2) and
+// [m2, K1)) or 3 (the first of those cut again at m3 = (mid + m2) / 2, the
+// split point of the right child's left child).
+__host__ __device__ inline int node_parts(const SchedGeom& g, int d, int mid, int K1)
 {
-    return d < g.split_depth && K1 - mid >= kSplitMin;
+    if (d >= g.split_depth || K1 - mid < kSplitMin) return 1;
+    const int m2 = (mid + K1) / 2;
+    return (d < g.split3_depth && m2 - mid >= kSplitMin) ? 3 : 2;
 }
 
-// Target range of a part: stage-1 Y columns J' < y1 - I (from the first
-// source column), stage-2 target anti-diagonals [t0, t1).
+// Part `part` of a node cut into `parts`: it forms the stage-1 Y columns
+// y0 - I <= J' < y1 - I (the first part from the first source column) and
+// updates the target anti-diagonals [t0, t1).
 struct PartRange {
-    int y1, t0, t1;
-    __host__ __device__ PartRange(bool split, int part, int mid, int K1)
+    int y0, y1, t0, t1;
+    __host__ __device__ PartRange(int parts, int part, int K0, int mid, int K1)
     {
-        const int m2 = (mid + K1) / 2;
-        if (!split) {
-            y1 = K1; t0 = mid; t1 = K1;
-        } else if (part == 0) {
-            y1 = m2; t0 = mid; t1 = m2;
-        } else {
-            y1 = K1; t0 = m2; t1 = K1;
-        }
+        const int m2 = (mid + K1) / 2, m3 = (mid + m2) / 2;
+        const int cut[4] = {mid, parts == 3 ? m3 : (parts == 2 ? m2 : K1), parts == 3 ? m2 : K1, K1};
+        t0 = cut[part];
+        t1 = cut[part + 1];
+        y0 = part == 0 ? K0 : t0;
+        y1 = t1;
     }
 };
 
@@ -495,11 +504,11 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     }
     if (K1 - K0 < 2) return;              // a leaf: nothing to propagate
     const int mid = (K0 + K1) / 2;
-    const bool split = node_split(g, d, mid, K1);
-    if (part == 1 && !split) return;
-    const PartRange pr(split, part, mid, K1);
-    const int y0 = part == 1 ? (mid + K1) / 2 : K0;
-    uint32_t* list = out + g.base[d] + (int64_t)(4 * p + 2 * stage + part) * g.cap[d];
+    const int parts = node_parts(g, d, mid, K1);
+    if (part >= parts) return;
+    const PartRange pr(parts, part, K0, mid, K1);
+    const int y0 = pr.y0;
+    uint32_t* list = out + g.base[d] + (int64_t)(6 * p + 3 * stage + part) * g.cap[d];
     const int lo = stage == 0 ? rows_lo(K0, g.Nt) : cols_lo(pr.t0, g.Mt);
     const int hi = stage == 0 ? rows_hi(mid, g.Mt) : cols_hi(pr.t1, g.Nt);
 
@@ -556,11 +565,13 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
 //
 // A launch covers `count` list entries with gridDim.x <= count workgroups,
 // each taking entries blockIdx.x, blockIdx.x + gridDim.x, ... (a far part
-// runs on a capped grid, next to the leaves; see enqueue_prop).
-__global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
-                                                   float* __restrict__ Y, int64_t ldw, int64_t lda,
-                                                   int K0, int mid, int y0, int y1, int Mt, int Nt,
-                                                   const uint32_t* __restrict__ list, unsigned count)
+// runs on a capped grid, next to the leaves; see enqueue_prop).  Every
+// kernel has a `_far` twin with the same body, used for the far parts, so
+// that timings of the two kinds of launch are told apart.
+__device__ __forceinline__ void prop_rows_body(const float* __restrict__ E, const float* __restrict__ PA,
+                                               float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                               int K0, int mid, int y0, int y1, int Mt, int Nt,
+                                               const uint32_t* __restrict__ list, unsigned count)
 {
     __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
     for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
@@ -580,16 +591,30 @@ __global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, 
         block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
     }
 }
+__global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
+                                                   float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                   int K0, int mid, int y0, int y1, int Mt, int Nt,
+                                                   const uint32_t* __restrict__ list, unsigned count)
+{
+    prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count);
+}
+__global__ __launch_bounds__(256) void k_prop_rows_far(const float* __restrict__ E, const float* __restrict__ PA,
+                                                       float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                       int K0, int mid, int y0, int y1, int Mt, int Nt,
+                                                       const uint32_t* __restrict__ list, unsigned count)
+{
+    prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count);
+}
 
 // Stage 2 of node (K0, mid, K1), one part: block (column J, b) from the
 // schedule updates the (up to) four target tile rows I' = i0 .. ih on the
 // part's target anti-diagonals [t0, t1):
 //   Wt[I', J] -= sum_{I = slo .. min(I', mid - 1)} P_B[I', I] Y[I, J],
 // slo = max(0, K0 - J).
-__global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
-                                                      float* __restrict__ Wt, int64_t ldw, int64_t ldb,
-                                                      int K0, int mid, int t0, int t1, int Mt, int Nt,
-                                                      const uint32_t* __restrict__ list, unsigned count)
+__device__ __forceinline__ void prop_cols_body(const float* __restrict__ Y, const float* __restrict__ PB,
+                                               float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                               int K0, int mid, int t0, int t1, int Mt, int Nt,
+                                               const uint32_t* __restrict__ list, unsigned count)
 {
     __shared__ __align__(16) float lds[ColBlk::LDS_FLOATS];
     for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
@@ -608,6 +633,20 @@ __global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ 
         block_store<4, 1>(Wt + rr * ldw + c0, ldw, 64 * (ih - i0 + 1), 64, -1.f, 1.f, acc);
     }
 }
+__global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                      float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                      int K0, int mid, int t0, int t1, int Mt, int Nt,
+                                                      const uint32_t* __restrict__ list, unsigned count)
+{
+    prop_cols_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, Nt, list, count);
+}
+__global__ __launch_bounds__(256, 2) void k_prop_cols_far(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                          float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                          int K0, int mid, int t0, int t1, int Mt, int Nt,
+                                                          const uint32_t* __restrict__ list, unsigned count)
+{
+    prop_cols_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, Nt, list, count);
+}
 
 // Small parts: the same two stages with one 64 x 64 target tile per
 // workgroup and one 32 x 32 quadrant per wave (block_gemm64), so a part with
@@ -616,10 +655,10 @@ __global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ 
 // blockIdx.x + gridDim.x, ... as in the block kernels.
 // Stage 1: item (x, y) computes Y[I, J'] for row I = rows_lo + y and
 // J' = th - x (the K extent grows with J': longest first).
-__global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E, const float* __restrict__ PA,
-                                                     float* __restrict__ Y, int64_t ldw, int64_t lda,
-                                                     int K0, int mid, int y0, int y1, int Nt, unsigned span,
-                                                     unsigned count)
+__device__ __forceinline__ void prop_rows_t_body(const float* __restrict__ E, const float* __restrict__ PA,
+                                                 float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                 int K0, int mid, int y0, int y1, int Nt, unsigned span,
+                                                 unsigned count)
 {
     __shared__ __align__(16) float lds[kLds64];
     const int wave = threadIdx.x >> 6;
@@ -638,13 +677,27 @@ __global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E
         wave_store32(Y + r * ldw + c, ldw, 1.f, 0.f, acc);
     }
 }
+__global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E, const float* __restrict__ PA,
+                                                     float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                     int K0, int mid, int y0, int y1, int Nt, unsigned span,
+                                                     unsigned count)
+{
+    prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count);
+}
+__global__ __launch_bounds__(256) void k_prop_rows_t_far(const float* __restrict__ E, const float* __restrict__ PA,
+                                                         float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                         int K0, int mid, int y0, int y1, int Nt, unsigned span,
+                                                         unsigned count)
+{
+    prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count);
+}
 
 // Stage 2: item (x, y) updates Wt[I', J] for column J = cols_lo + y and
 // I' = th - x.
-__global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y, const float* __restrict__ PB,
-                                                     float* __restrict__ Wt, int64_t ldw, int64_t ldb,
-                                                     int K0, int mid, int t0, int t1, int Mt, unsigned span,
-                                                     unsigned count)
+__device__ __forceinline__ void prop_cols_t_body(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                 float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                 int K0, int mid, int t0, int t1, int Mt, unsigned span,
+                                                 unsigned count)
 {
     __shared__ __align__(16) float lds[kLds64];
     const int wave = threadIdx.x >> 6;
@@ -662,6 +715,20 @@ __global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y
         const int64_t c = (int64_t)J * 64 + 32 * (wave & 1);
         wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
     }
+}
+__global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                     float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                     int K0, int mid, int t0, int t1, int Mt, unsigned span,
+                                                     unsigned count)
+{
+    prop_cols_t_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, span, count);
+}
+__global__ __launch_bounds__(256) void k_prop_cols_t_far(const float* __restrict__ Y, const float* __restrict__ PB,
+                                                         float* __restrict__ Wt, int64_t ldw, int64_t ldb,
+                                                         int K0, int mid, int t0, int t1, int Mt, unsigned span,
+                                                         unsigned count)
+{
+    prop_cols_t_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, span, count);
 }
 
 __global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t count,
@@ -707,13 +774,14 @@ void plan_sched(SchedGeom& g, int64_t& entries, int Mt, int Nt)
     while (g.split_depth < std::min(kSplitDepth, g.levels) &&
            ceil_div(ceil_div(g.Kt, (int64_t)1 << g.split_depth), 2) >= kSplitMin)
         ++g.split_depth;
+    g.split3_depth = std::min(kSplit3Depth, g.split_depth);
     const int64_t R = std::max(Mt, Nt);
     int64_t off = 0;
     for (int d = 0; d < kMaxDepth; ++d) {
         const int64_t w = ceil_div(g.Kt, (int64_t)1 << d);
         g.base[d] = off;
         g.cap[d] = R * ceil_div(w, 4);
-        if (d < g.levels) off += ((int64_t)1 << d) * 4 * g.cap[d];   // 2 stages x 2 parts per node
+        if (d < g.levels) off += ((int64_t)1 << d) * 6 * g.cap[d];   // 2 stages x 3 parts per node
     }
     entries = off;
 }
@@ -730,7 +798,7 @@ SolvePlan plan_solve(int64_t m, int64_t n, bool split)
     p.pad_a = (n % kTile) != 0;
     p.pad_b = (m % kTile) != 0;
     plan_sched(p.sg, p.sched_entries, (int)p.Mt, (int)p.Nt);
-    if (!split) p.sg.split_depth = 0;
+    if (!split) p.sg.split_depth = p.sg.split3_depth = 0;
     p.split_levels = p.sg.split_depth;
     const size_t mat = sizeof(float) * (size_t)(p.Mp * p.Np);
     size_t off = 0;
@@ -893,12 +961,12 @@ void enqueue_stage1(SolveRun& R, int K0, int mid, int y0, int y1, const uint32_t
         for (uint8_t u : pa_used) by += u ? kTileB : 0.0;
     if (blocks >= (far ? kFarBlockMin : kBlockLaunchMin)) {
         const unsigned n = (unsigned)blocks;
-        launch_shm(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+        launch_shm(R.prof, far ? KK_PROP_ROWS_FAR : KK_PROP_ROWS, fl, by, far ? k_prop_rows_far : k_prop_rows, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
                    far ? kFarPadBlock : 0, st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid,
                    y0, y1, Mt, Nt, list, n);
     } else if (blocks > 0) {
         const unsigned n = (unsigned)span * (unsigned)(I_hi - I_lo + 1);
-        launch_shm(R.prof, KK_PROP_ROWS_T, fl, by, k_prop_rows_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+        launch_shm(R.prof, far ? KK_PROP_ROWS_T_FAR : KK_PROP_ROWS_T, fl, by, far ? k_prop_rows_t_far : k_prop_rows_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
                    far ? kFarPadTile : 0, st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid,
                    y0, y1, Nt, (unsigned)span, n);
     }
@@ -935,64 +1003,74 @@ void enqueue_stage2(SolveRun& R, int K0, int mid, int t0, int t1, const uint32_t
         for (uint8_t u : pb_used) by += u ? kTileB : 0.0;
     if (blocks >= (far ? kFarBlockMin : kBlockLaunchMin)) {
         const unsigned n = (unsigned)blocks;
-        launch_shm(R.prof, KK_PROP_COLS, fl, by, k_prop_cols, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+        launch_shm(R.prof, far ? KK_PROP_COLS_FAR : KK_PROP_COLS, fl, by, far ? k_prop_cols_far : k_prop_cols, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
                    far ? kFarPadBlock : 0, st, Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, t0, t1, Mt,
                    Nt, list, n);
     } else if (blocks > 0) {
         const unsigned n = (unsigned)span * (unsigned)(J_hi - J_lo + 1);
-        launch_shm(R.prof, KK_PROP_COLS_T, fl, by, k_prop_cols_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+        launch_shm(R.prof, far ? KK_PROP_COLS_T_FAR : KK_PROP_COLS_T, fl, by, far ? k_prop_cols_t_far : k_prop_cols_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
                    far ? kFarPadTile : 0, st, Y, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.ldb, K0, mid, t0, t1, Mt,
                    (unsigned)span, n);
     }
 }
 
 // Node (K0, mid, K1) at heap position (d, p).  Unsplit: both stages on the
-// caller's stream; returns nullptr.  Split: the near part on the caller's
-// stream, the far part on the depth's own stream once the near stage 1 is
-// done (far targets read those Y columns too); returns the event that marks
-// the far part done, which the right child waits for before its own
-// propagation (the first work that touches [m2, K1)).
-hipEvent_t enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p)
+// caller's stream.  Cut in parts: the first part on the caller's stream,
+// the others in order on the depth's own stream once the first part's
+// stage 1 is done (later parts read its Y columns too).  Events mark the
+// later parts done: `done_left` for [m3, m2) (three parts), which the right
+// child's left child waits for before its own propagation, and `done_right`
+// for [m2, K1), which the right child waits for before its propagation
+// (the first work on the caller's stream that touches those targets).
+void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, hipEvent_t& done_left,
+                  hipEvent_t& done_right)
 {
+    done_left = done_right = nullptr;
     const SchedGeom& g = *R.sg;
-    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(4 * p) * g.cap[d];   // (stage, part) at (2 stage + part) cap
-    const bool split = node_split(g, d, mid, K1);
-    const PartRange near(split, 0, mid, K1);
-    float* Y = split ? R.Ysplit[d] : R.Y;
-    enqueue_stage1(R, K0, mid, K0, near.y1, lists, Y, R.s, false);
-    if (!split) {
-        enqueue_stage2(R, K0, mid, near.t0, near.t1, lists + 2 * g.cap[d], Y, R.s, false);
-        return nullptr;
+    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(6 * p) * g.cap[d];   // (stage, part) at (3 stage + part) cap
+    const int parts = node_parts(g, d, mid, K1);
+    float* Y = parts > 1 ? R.Ysplit[d] : R.Y;
+    const PartRange p0(parts, 0, K0, mid, K1);
+    enqueue_stage1(R, K0, mid, p0.y0, p0.y1, lists, Y, R.s, false);
+    if (parts == 1) {
+        enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + 3 * g.cap[d], Y, R.s, false);
+        return;
     }
-    const PartRange far(true, 1, mid, K1);
-    hipEvent_t ev1 = new_event(R), ev2 = new_event(R);
-    if (!ev1 || !ev2) return nullptr;
-    if (hipEventRecord(ev1, R.s) != hipSuccess || hipStreamWaitEvent(R.far[d], ev1, 0) != hipSuccess) {
+    hipEvent_t ev0 = new_event(R);
+    if (!ev0) return;
+    if (hipEventRecord(ev0, R.s) != hipSuccess || hipStreamWaitEvent(R.far[d], ev0, 0) != hipSuccess) {
         R.failed = true;
-        return nullptr;
+        return;
     }
-    enqueue_stage2(R, K0, mid, near.t0, near.t1, lists + 2 * g.cap[d], Y, R.s, false);
-    enqueue_stage1(R, K0, mid, (mid + K1) / 2, far.y1, lists + g.cap[d], Y, R.far[d], true);
-    enqueue_stage2(R, K0, mid, far.t0, far.t1, lists + 3 * g.cap[d], Y, R.far[d], true);
-    if (hipEventRecord(ev2, R.far[d]) != hipSuccess) {
-        R.failed = true;
-        return nullptr;
+    enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + 3 * g.cap[d], Y, R.s, false);
+    for (int part = 1; part < parts; ++part) {
+        const PartRange pr(parts, part, K0, mid, K1);
+        enqueue_stage1(R, K0, mid, pr.y0, pr.y1, lists + part * g.cap[d], Y, R.far[d], true);
+        enqueue_stage2(R, K0, mid, pr.t0, pr.t1, lists + (3 + part) * g.cap[d], Y, R.far[d], true);
+        hipEvent_t ev = new_event(R);
+        if (!ev || hipEventRecord(ev, R.far[d]) != hipSuccess) {
+            R.failed = true;
+            return;
+        }
+        (part + 1 == parts ? done_right : done_left) = ev;
     }
-    return ev2;
 }
 
-// `wait`: the far part of the parent, which updated [mid, K1) of this node.
-void solve_rec(SolveRun& R, int K0, int K1, int d, int p, hipEvent_t wait)
+// `wait`: a far part of an ancestor that updates [mid, K1) of this node,
+// due before this node's propagation; `wait_left`: the same for this
+// node's left child.
+void solve_rec(SolveRun& R, int K0, int K1, int d, int p, hipEvent_t wait, hipEvent_t wait_left)
 {
-    if (K1 - K0 == 1) {   // (a split parent's right child is never a leaf)
+    if (K1 - K0 == 1) {   // (the nodes that carry waits are never leaves)
         enqueue_leaf(R, K0);
         return;
     }
     const int mid = (K0 + K1) / 2;
-    solve_rec(R, K0, mid, d + 1, 2 * p, nullptr);
+    solve_rec(R, K0, mid, d + 1, 2 * p, wait_left, nullptr);
     if (wait && hipStreamWaitEvent(R.s, wait, 0) != hipSuccess) R.failed = true;
-    hipEvent_t far_done = enqueue_prop(R, K0, mid, K1, d, p);
-    solve_rec(R, mid, K1, d + 1, 2 * p + 1, far_done);
+    hipEvent_t done_left, done_right;
+    enqueue_prop(R, K0, mid, K1, d, p, done_left, done_right);
+    solve_rec(R, mid, K1, d + 1, 2 * p + 1, done_right, done_left);
 }
 
 }  // namespace
@@ -1017,7 +1095,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     for (int d = 0; d < kSplitDepth; ++d) {
         R.Ysplit[d] = d < p.sg.split_depth ? reinterpret_cast<float*>(w + p.off_ysplit[d]) : nullptr;
         R.far[d] = d < p.sg.split_depth ? far_stream(d) : nullptr;
-        if (d < p.sg.split_depth && !R.far[d]) p.sg.split_depth = 0;   // no stream: nothing is split
+        if (d < p.sg.split_depth && !R.far[d]) p.sg.split_depth = p.sg.split3_depth = 0;   // no stream: nothing is split
     }
     LeafArgs& g = R.leaf;
     g.Wt = reinterpret_cast<float*>(w + p.off_wt);
@@ -1071,21 +1149,23 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.sched = sched;
     if (p.sg.levels > 0)
         launch(prof, KK_SCHED, 0.0, 4.0 * (double)p.sched_entries, k_sched,
-               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u, 2u), dim3(256), s, p.sg, sched);
+               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u, 3u), dim3(256), s, p.sg, sched);
     if (p.sg.split_depth > 0) {
         static std::once_flag attrs;
         std::call_once(attrs, [] {
-            (void)hipFuncSetAttribute((const void*)k_prop_rows, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFarPadBlock);
-            (void)hipFuncSetAttribute((const void*)k_prop_cols, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFarPadBlock);
+            (void)hipFuncSetAttribute((const void*)k_prop_rows_far, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)kFarPadBlock);
+            (void)hipFuncSetAttribute((const void*)k_prop_cols_far, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)kFarPadBlock);
             if (kFarPadTile) {
-                (void)hipFuncSetAttribute((const void*)k_prop_rows_t, hipFuncAttributeMaxDynamicSharedMemorySize,
+                (void)hipFuncSetAttribute((const void*)k_prop_rows_t_far, hipFuncAttributeMaxDynamicSharedMemorySize,
                                           (int)kFarPadTile);
-                (void)hipFuncSetAttribute((const void*)k_prop_cols_t, hipFuncAttributeMaxDynamicSharedMemorySize,
+                (void)hipFuncSetAttribute((const void*)k_prop_cols_t_far, hipFuncAttributeMaxDynamicSharedMemorySize,
                                           (int)kFarPadTile);
             }
         });
     }
-    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, nullptr);
+    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, nullptr, nullptr);
     // every far part is waited for by the right child of its node, so all
     // of them are ordered before the rest of the work on s
     for (hipEvent_t e : R.events) (void)hipEventDestroy(e);
