@@ -418,7 +418,11 @@ constexpr int kSplitDepth = BAKRON_SPLIT_DEPTH;   // nodes above this depth may 
 #ifndef BAKRON_SPLIT3_DEPTH
 #define BAKRON_SPLIT3_DEPTH 3
 #endif
-constexpr int kSplit3Depth = BAKRON_SPLIT3_DEPTH;  // nodes above this depth may be cut in three
+constexpr int kSplit3Depth = BAKRON_SPLIT3_DEPTH;  // nodes above this depth may be cut in more than two
+#ifndef BAKRON_MAX_PARTS
+#define BAKRON_MAX_PARTS 3
+#endif
+constexpr int kMaxParts = BAKRON_MAX_PARTS;
 #ifndef BAKRON_SPLIT_MIN
 #define BAKRON_SPLIT_MIN 8
 #endif
@@ -427,7 +431,7 @@ constexpr int kSplitMin = BAKRON_SPLIT_MIN;       // ... when the right child is
 struct SchedGeom {
     int Mt, Nt, Kt, levels;
     int split_depth;    // nodes above this depth may be cut in parts (0: none)
-    int split3_depth;   // ... and in three parts above this one
+    int split3_depth;   // ... and in up to kMaxParts parts above this one
     int64_t base[kMaxDepth];
     int64_t cap[kMaxDepth];
 };
@@ -438,21 +442,30 @@ struct SchedGeom {
 __host__ __device__ inline int node_parts(const SchedGeom& g, int d, int mid, int K1)
 {
     if (d >= g.split_depth || K1 - mid < kSplitMin) return 1;
-    const int m2 = (mid + K1) / 2;
-    return (d < g.split3_depth && m2 - mid >= kSplitMin) ? 3 : 2;
+    int parts = 2, b = (mid + K1) / 2;
+    while (parts < kMaxParts && d < g.split3_depth && b - mid >= kSplitMin) {
+        b = (mid + b) / 2;
+        ++parts;
+    }
+    return parts;
 }
 
 // Part `part` of a node cut into `parts`: it forms the stage-1 Y columns
 // y0 - I <= J' < y1 - I (the first part from the first source column) and
-// updates the target anti-diagonals [t0, t1).
+// updates the target anti-diagonals [t0, t1).  The cuts are the split
+// points down the left spine of the right child: K1, m2 = (mid + K1) / 2,
+// (mid + m2) / 2, ...
 struct PartRange {
     int y0, y1, t0, t1;
     __host__ __device__ PartRange(int parts, int part, int K0, int mid, int K1)
     {
-        const int m2 = (mid + K1) / 2, m3 = (mid + m2) / 2;
-        const int cut[4] = {mid, parts == 3 ? m3 : (parts == 2 ? m2 : K1), parts == 3 ? m2 : K1, K1};
-        t0 = cut[part];
-        t1 = cut[part + 1];
+        int hi = K1, lo = parts > 1 ? (mid + K1) / 2 : mid;   // part parts - 1 is [lo, hi)
+        for (int k = parts - 1; k > part; --k) {
+            hi = lo;
+            lo = k - 1 > 0 ? (mid + lo) / 2 : mid;
+        }
+        t0 = lo;
+        t1 = hi;
         y0 = part == 0 ? K0 : t0;
         y1 = t1;
     }
@@ -508,7 +521,7 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     if (part >= parts) return;
     const PartRange pr(parts, part, K0, mid, K1);
     const int y0 = pr.y0;
-    uint32_t* list = out + g.base[d] + (int64_t)(6 * p + 3 * stage + part) * g.cap[d];
+    uint32_t* list = out + g.base[d] + (int64_t)(2 * kMaxParts * p + kMaxParts * stage + part) * g.cap[d];
     const int lo = stage == 0 ? rows_lo(K0, g.Nt) : cols_lo(pr.t0, g.Mt);
     const int hi = stage == 0 ? rows_hi(mid, g.Mt) : cols_hi(pr.t1, g.Nt);
 
@@ -781,7 +794,7 @@ void plan_sched(SchedGeom& g, int64_t& entries, int Mt, int Nt)
         const int64_t w = ceil_div(g.Kt, (int64_t)1 << d);
         g.base[d] = off;
         g.cap[d] = R * ceil_div(w, 4);
-        if (d < g.levels) off += ((int64_t)1 << d) * 6 * g.cap[d];   // 2 stages x 3 parts per node
+        if (d < g.levels) off += ((int64_t)1 << d) * 2 * kMaxParts * g.cap[d];   // 2 stages x kMaxParts parts per node
     }
     entries = off;
 }
@@ -1014,26 +1027,30 @@ void enqueue_stage2(SolveRun& R, int K0, int mid, int t0, int t1, const uint32_t
     }
 }
 
+// Events due before the propagation of the nodes down a left spine:
+// e[j] for the node j levels below (e[0]: the node itself).
+struct SpineWaits {
+    hipEvent_t e[kMaxParts];
+};
+
 // Node (K0, mid, K1) at heap position (d, p).  Unsplit: both stages on the
 // caller's stream.  Cut in parts: the first part on the caller's stream,
 // the others in order on the depth's own stream once the first part's
-// stage 1 is done (later parts read its Y columns too).  Events mark the
-// later parts done: `done_left` for [m3, m2) (three parts), which the right
-// child's left child waits for before its own propagation, and `done_right`
-// for [m2, K1), which the right child waits for before its propagation
-// (the first work on the caller's stream that touches those targets).
-void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, hipEvent_t& done_left,
-                  hipEvent_t& done_right)
+// stage 1 is done (later parts read its Y columns too).  Part k >= 1 ends
+// with an event, due before the propagation of the node parts - 1 - k
+// levels down the left spine of the right child (the first work on the
+// caller's stream that touches the part's targets): returned in `done`.
+void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits& done)
 {
-    done_left = done_right = nullptr;
+    for (hipEvent_t& e : done.e) e = nullptr;
     const SchedGeom& g = *R.sg;
-    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(6 * p) * g.cap[d];   // (stage, part) at (3 stage + part) cap
+    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(2 * kMaxParts * p) * g.cap[d];   // (stage, part) at (kMaxParts stage + part) cap
     const int parts = node_parts(g, d, mid, K1);
     float* Y = parts > 1 ? R.Ysplit[d] : R.Y;
     const PartRange p0(parts, 0, K0, mid, K1);
     enqueue_stage1(R, K0, mid, p0.y0, p0.y1, lists, Y, R.s, false);
     if (parts == 1) {
-        enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + 3 * g.cap[d], Y, R.s, false);
+        enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + kMaxParts * g.cap[d], Y, R.s, false);
         return;
     }
     hipEvent_t ev0 = new_event(R);
@@ -1042,35 +1059,36 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, hipEvent_t
         R.failed = true;
         return;
     }
-    enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + 3 * g.cap[d], Y, R.s, false);
+    enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + kMaxParts * g.cap[d], Y, R.s, false);
     for (int part = 1; part < parts; ++part) {
         const PartRange pr(parts, part, K0, mid, K1);
         enqueue_stage1(R, K0, mid, pr.y0, pr.y1, lists + part * g.cap[d], Y, R.far[d], true);
-        enqueue_stage2(R, K0, mid, pr.t0, pr.t1, lists + (3 + part) * g.cap[d], Y, R.far[d], true);
+        enqueue_stage2(R, K0, mid, pr.t0, pr.t1, lists + (kMaxParts + part) * g.cap[d], Y, R.far[d], true);
         hipEvent_t ev = new_event(R);
         if (!ev || hipEventRecord(ev, R.far[d]) != hipSuccess) {
             R.failed = true;
             return;
         }
-        (part + 1 == parts ? done_right : done_left) = ev;
+        done.e[parts - 1 - part] = ev;
     }
 }
 
-// `wait`: a far part of an ancestor that updates [mid, K1) of this node,
-// due before this node's propagation; `wait_left`: the same for this
-// node's left child.
-void solve_rec(SolveRun& R, int K0, int K1, int d, int p, hipEvent_t wait, hipEvent_t wait_left)
+// `waits`: far parts of ancestors due before the propagation of this node
+// and of the nodes down its left spine.
+void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits)
 {
     if (K1 - K0 == 1) {   // (the nodes that carry waits are never leaves)
         enqueue_leaf(R, K0);
         return;
     }
     const int mid = (K0 + K1) / 2;
-    solve_rec(R, K0, mid, d + 1, 2 * p, wait_left, nullptr);
-    if (wait && hipStreamWaitEvent(R.s, wait, 0) != hipSuccess) R.failed = true;
-    hipEvent_t done_left, done_right;
-    enqueue_prop(R, K0, mid, K1, d, p, done_left, done_right);
-    solve_rec(R, mid, K1, d + 1, 2 * p + 1, done_right, done_left);
+    SpineWaits down;
+    for (int j = 0; j < kMaxParts; ++j) down.e[j] = j + 1 < kMaxParts ? waits.e[j + 1] : nullptr;
+    solve_rec(R, K0, mid, d + 1, 2 * p, down);
+    if (waits.e[0] && hipStreamWaitEvent(R.s, waits.e[0], 0) != hipSuccess) R.failed = true;
+    SpineWaits done;
+    enqueue_prop(R, K0, mid, K1, d, p, done);
+    solve_rec(R, mid, K1, d + 1, 2 * p + 1, done);
 }
 
 }  // namespace
@@ -1149,7 +1167,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.sched = sched;
     if (p.sg.levels > 0)
         launch(prof, KK_SCHED, 0.0, 4.0 * (double)p.sched_entries, k_sched,
-               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u, 3u), dim3(256), s, p.sg, sched);
+               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u, (unsigned)kMaxParts), dim3(256), s, p.sg, sched);
     if (p.sg.split_depth > 0) {
         static std::once_flag attrs;
         std::call_once(attrs, [] {
@@ -1165,7 +1183,9 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
             }
         });
     }
-    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, nullptr, nullptr);
+    SpineWaits none;
+    for (hipEvent_t& e : none.e) e = nullptr;
+    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, none);
     // every far part is waited for by the right child of its node, so all
     // of them are ordered before the rest of the work on s
     for (hipEvent_t e : R.events) (void)hipEventDestroy(e);
