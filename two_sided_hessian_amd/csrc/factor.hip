@@ -49,22 +49,33 @@ __global__ __launch_bounds__(256) void k_diag_mean(const float* __restrict__ A, 
 
 // dst (Np x Np, pitch ld) = lower triangle of A + frac * mean * I; identity on
 // the padding diagonal, zeros elsewhere (the upper triangle is not read).
+// Each thread writes four adjacent columns with one 16-byte store; rows of A
+// are read with 16-byte loads where a group lies below the diagonal and A's
+// rows are 16-byte aligned (vec), element by element elsewhere.
 __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A, int64_t n,
                                                      float* __restrict__ dst, int64_t Np, int64_t ld,
-                                                     const float* __restrict__ mean, float frac)
+                                                     const float* __restrict__ mean, float frac, int vec)
 {
     // frac == 0 adds nothing (not 0 * mean, which is NaN for a non-finite diagonal)
     const float add = frac != 0.f ? frac * mean[0] : 0.f;
     for (int64_t i = blockIdx.y; i < Np; i += gridDim.y)
-        for (int64_t j = blockIdx.x * 256 + threadIdx.x; j < Np; j += (int64_t)gridDim.x * 256) {
-            float v = 0.f;
-            if (i < n && j < n) {
-                if (j < i) v = A[i * n + j];
-                else if (j == i) v = A[i * n + j] + add;
-            } else if (i == j) {
-                v = 1.f;
+        for (int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); j < Np; j += (int64_t)gridDim.x * 1024) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (vec && i < n && j + 3 < i && j + 3 < n) {
+                v = *reinterpret_cast<const f32x4*>(A + i * n + j);
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t c = j + q;
+                    if (i < n && c < n) {
+                        if (c < i) v[q] = A[i * n + c];
+                        else if (c == i) v[q] = A[i * n + c] + add;
+                    } else if (i == c) {
+                        v[q] = 1.f;
+                    }
+                }
             }
-            dst[i * ld + j] = v;
+            *reinterpret_cast<f32x4*>(dst + i * ld + j) = v;
         }
 }
 
@@ -743,9 +754,10 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     launch(prof, KK_F_CLEAR, 0.0, 4.0, k_clear_info, dim3(1), dim3(64), s, info);
     launch(prof, KK_F_MEAN, 0.0, 4.0 * dn, k_diag_mean, dim3(1), dim3(256), s, A, n, mean);
     {
-        dim3 g((unsigned)ceil_div(p.Np, 256), (unsigned)std::min<int64_t>(p.Np, 32768));
+        dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 32768));
+        const int vec = (n % 4 == 0 && aligned16(A)) ? 1 : 0;
         launch(prof, KK_F_LOAD, dn, 4.0 * (tri(dn) + dN * dN), k_load_damped, g, dim3(256), s, A, n, R.Pbuf,
-               p.Np, p.Np, (const float*)mean, damp_frac);
+               p.Np, p.Np, (const float*)mean, damp_frac, vec);
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, 0, p.Np)) return -1;

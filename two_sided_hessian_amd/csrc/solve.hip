@@ -46,13 +46,27 @@
 namespace bk {
 
 // dst (R x C, pitch ldd) = src (rows x cols, pitch lds) with zeros outside.
+// C and ldd are multiples of 4: each thread writes four adjacent columns
+// with one 16-byte store, reading them with one 16-byte load where they lie
+// inside src and src's rows are 16-byte aligned (vec).
 __global__ __launch_bounds__(256) void k_copy_pad(const float* __restrict__ src, int64_t rows, int64_t cols,
                                                   int64_t lds, float* __restrict__ dst, int64_t R, int64_t C,
-                                                  int64_t ldd)
+                                                  int64_t ldd, int vec)
 {
     for (int64_t i = blockIdx.y; i < R; i += gridDim.y)
-        for (int64_t j = blockIdx.x * 256 + threadIdx.x; j < C; j += (int64_t)gridDim.x * 256)
-            dst[i * ldd + j] = (i < rows && j < cols) ? src[i * lds + j] : 0.f;
+        for (int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x); j < C; j += (int64_t)gridDim.x * 1024) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (i < rows) {
+                if (vec && j + 3 < cols) {
+                    v = *reinterpret_cast<const f32x4*>(src + i * lds + j);
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        if (j + q < cols) v[q] = src[i * lds + j + q];
+                }
+            }
+            *reinterpret_cast<f32x4*>(dst + i * ldd + j) = v;
+        }
 }
 
 struct LeafArgs {
@@ -844,8 +858,10 @@ SolvePlan plan_solve(int64_t m, int64_t n, bool split)
 
 dim3 copy_grid(int64_t R, int64_t C)
 {
-    return dim3((unsigned)ceil_div(C, 256), (unsigned)std::min<int64_t>(R, 32768));
+    return dim3((unsigned)ceil_div(C, 1024), (unsigned)std::min<int64_t>(R, 32768));
 }
+
+int copy_vec(const float* src, int64_t lds) { return (lds % 4 == 0 && aligned16(src)) ? 1 : 0; }
 
 struct SolveRun {
     LeafArgs leaf;
@@ -1124,7 +1140,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     if (p.pad_a) {
         float* pa = reinterpret_cast<float*>(w + p.off_pa);
         launch(prof, KK_COPY_PAD, 0.0, 4.0 * (dn * dn + (double)(p.Np * p.Np)), k_copy_pad, copy_grid(p.Np, p.Np),
-               dim3(256), s, PA, n, n, n, pa, p.Np, p.Np, p.Np);
+               dim3(256), s, PA, n, n, n, pa, p.Np, p.Np, p.Np, copy_vec(PA, n));
         g.PA = pa;
         g.lda = p.Np;
     } else {
@@ -1134,7 +1150,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     if (p.pad_b) {
         float* pb = reinterpret_cast<float*>(w + p.off_pb);
         launch(prof, KK_COPY_PAD, 0.0, 4.0 * (dm * dm + (double)(p.Mp * p.Mp)), k_copy_pad, copy_grid(p.Mp, p.Mp),
-               dim3(256), s, PB, m, m, m, pb, p.Mp, p.Mp, p.Mp);
+               dim3(256), s, PB, m, m, m, pb, p.Mp, p.Mp, p.Mp, copy_vec(PB, m));
         g.PB = pb;
         g.ldb = p.Mp;
     } else {
@@ -1142,7 +1158,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
         g.ldb = m;
     }
     launch(prof, KK_COPY_PAD, 0.0, 4.0 * (dm * dn + (double)(p.Mp * p.Np)), k_copy_pad, copy_grid(p.Mp, p.Np),
-           dim3(256), s, W, m, n, n, g.Wt, p.Mp, p.Np, p.Np);
+           dim3(256), s, W, m, n, n, g.Wt, p.Mp, p.Np, p.Np, copy_vec(W, n));
     if (launch_ok()) return -1;
     g.scale = scale;
     g.zero = zero;
