@@ -17,19 +17,24 @@
 //    steps quantize up to 64 entries each.  The value of entry (a, b) is
 //        W~in[a,b] - sum_{a'<=a} P_B[a,a'] U[a',b],
 //        U[a',b] = sum_{b'<=b, done} e[a',b'] P_A[b,b'],
-//    two length-64 dot products per entry, split over 4 lanes and reduced
-//    with lane shuffles.
+//    two length-64 dot products per entry, split over 8 lanes and reduced
+//    with lane shuffles (see k_leaf).
 //  * Internal node (K0, mid, K1): stage 1 forms, per tile row I, the partial
 //    products Y[I, J'] = sum_J E[I, J] P_A[J', J]^T over the source tiles
 //    (K0 <= I + J < mid, J <= J'); stage 2 subtracts
 //    sum_I P_B[I', I] Y[I, J'] from every target tile (mid <= I' + J' < K1).
 //    Both are fp32 MFMA GEMMs whose K range follows the staircase of the
 //    tile band.
+//  * On the upper levels a node's propagation is cut by target
+//    anti-diagonal into parts with different due times; only the first is
+//    on the caller's stream, the others run on library-owned streams beside
+//    the latency-bound leaves (see the block schedule and enqueue_prop).
 //
 // Workspace (pitch Np = 64 * ceil(n / 64), Mp = 64 * ceil(m / 64)):
 //   Wt  Mp x Np  working weights (W copied in, zero padded)
 //   E   Mp x Np  raw errors of solved tiles
-//   Y   Mp x Np  stage-1 partial products
+//   Y   Mp x Np  stage-1 partial products of unsplit nodes
+//   Yd  Mp x Np  the same for the split nodes of depth d, one per depth
 //   obj Mt x Nt  per-tile objective partials (double)
 //   PAp Np x Np, PBp Mp x Mp  padded copies, only when n (m) is not a
 //        multiple of 64.
