@@ -389,16 +389,22 @@ def kernel_bound(name):
 
 
 def sources_digest():
-    """sha256 over the library's device and host sources (csrc/): the HBM
-    counters in profiles/ are valid only for the code they were taken on."""
+    """sha256 over the library's device and host code (csrc/, comments and
+    blank space left out): the HBM counters in profiles/ are valid only for
+    the code they were taken on."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "two_sided_hessian_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         path = os.path.join(csrc, f)
         if path.endswith((".hip", ".hpp")):
-            with open(path, "rb") as fh:
-                h.update(f.encode() + b"\0" + fh.read())
+            with open(path, encoding="utf-8") as fh:
+                code = fh.read()
+            code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+            code = re.sub(r"//[^\n]*", " ", code)
+            code = " ".join(code.split())
+            h.update(f.encode() + b"\0" + code.encode())
     return h.hexdigest()
 
 
