@@ -4,6 +4,9 @@
 #include <math.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
 
 #include "../../include/bakron.h"
 #include "internal.hpp"
@@ -285,6 +288,18 @@ const char* kernel_name(int kind)
         "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj", "k_row_sqnorms", "k_moment<false>",
         "k_moment<true>", "k_prop_rows_far", "k_prop_rows_t_far", "k_prop_cols_far", "k_prop_cols_t_far"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
+}
+
+hipStream_t side_stream(hipStream_t caller, int slot)
+{
+    static std::mutex mu;
+    static std::map<std::tuple<int, hipStream_t, int>, hipStream_t> table;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    hipStream_t& st = table[std::make_tuple(dev, caller, slot)];
+    if (!st && hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) st = nullptr;
+    return st;
 }
 
 int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)

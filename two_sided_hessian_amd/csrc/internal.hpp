@@ -81,6 +81,13 @@ inline void launch_shm(Prof* p, int kind, double flops, double bytes, void (*ker
     p->recs.push_back(r);
 }
 
+// A library-owned stream (default priority, non-blocking) for work that a
+// call forks off the caller's stream `caller` and joins back with events.
+// One per (device, caller stream, slot), created on first use and kept for
+// the life of the process, so that calls on different caller streams never
+// queue behind each other.  nullptr when it cannot be created.
+hipStream_t side_stream(hipStream_t caller, int slot);
+
 // Drain the stream, sum the per-launch event times per kernel kind into
 // stats (at most max_stats entries, in KernelKind order), release events.
 int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);

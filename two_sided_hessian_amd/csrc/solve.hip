@@ -41,7 +41,6 @@
 //   sched  block lists of the propagation launches (k_sched)
 // Padding entries are forced to zero error, so they never touch real ones.
 #include <algorithm>
-#include <map>
 #include <mutex>
 #include <vector>
 
@@ -882,24 +881,6 @@ struct SolveRun {
     Prof* prof;
 };
 
-// Library-owned streams for far parts (default priority, non-blocking),
-// created on first use per device and kept for the life of the process.
-hipStream_t far_stream(int d)
-{
-    static std::mutex mu;
-    static std::map<int, std::vector<hipStream_t>> table;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    std::vector<hipStream_t>& v = table[dev];
-    while ((int)v.size() <= d) {
-        hipStream_t st = nullptr;
-        if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) return nullptr;
-        v.push_back(st);
-    }
-    return v[d];
-}
-
 hipEvent_t new_event(SolveRun& R)
 {
     hipEvent_t e = nullptr;
@@ -1133,7 +1114,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.failed = false;
     for (int d = 0; d < kSplitDepth; ++d) {
         R.Ysplit[d] = d < p.sg.split_depth ? reinterpret_cast<float*>(w + p.off_ysplit[d]) : nullptr;
-        R.far[d] = d < p.sg.split_depth ? far_stream(d) : nullptr;
+        R.far[d] = d < p.sg.split_depth ? side_stream(s, d) : nullptr;
         if (d < p.sg.split_depth && !R.far[d]) p.sg.split_depth = p.sg.split3_depth = 0;   // no stream: nothing is split
     }
     LeafArgs& g = R.leaf;
