@@ -55,3 +55,28 @@ def test_batch_equals_single_solves(n_streams):
         v = R.validate(d["W"], outs[k]["codes"].cpu().numpy(), d["scale"], d["zero"], d["maxq"], tau=1e-4,
                        PA=PA.astype(np.float64), PB=PB.astype(np.float64))
         assert v["bad"] == 0 and v["max_step"] <= 1, (SHAPES[k], v)
+
+
+@pytest.mark.parametrize("name", ["sq4096_t5", "sq8192_mixed"])
+def test_split_schedule_equals_unsplit_at_full_size(name):
+    # bakron_solve cuts the upper nodes' propagation into parts run on
+    # library-owned streams; a batch layer runs the same kernels unsplit on
+    # its stream.  At the full workload sizes every output must agree bit for
+    # bit (the parts sum the same products in the same order).
+    import workloads as WL
+    spec = WL.by_name(name)
+    d = WL.generate(spec)
+    print(f"split vs unsplit: {name} {spec.m}x{spec.n}", flush=True)
+    A, Bm = to_dev(d["A"]), to_dev(d["B"])
+    LA, PA, ia = B.factor(A, 0.01)
+    LB, PB, ib = B.factor(Bm, 0.01)
+    torch.cuda.synchronize()
+    assert int(ia.item()) == 0 and int(ib.item()) == 0
+    prob = {"W": to_dev(d["W"]), "LA": LA, "PA": PA, "LB": LB, "PB": PB, "scale": to_dev(d["scale"]),
+            "zero": to_dev(d["zero"]), "maxq": to_dev(d["maxq"])}
+    ref = B.solve(prob["W"], LA, PA, LB, PB, prob["scale"], prob["zero"], prob["maxq"], want_err=True)
+    torch.cuda.synchronize()
+    (out,) = B.solve_batch([prob], [torch.cuda.current_stream()], want_err=True)
+    torch.cuda.synchronize()
+    for key in ("codes", "V", "err", "objective"):
+        assert torch.equal(out[key], ref[key]), key
