@@ -216,18 +216,25 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[8
     t1 = fmaf(pbz[7], u1.w, t1);
     const float psn = sum8(need_ps ? t0 + t1 : 0.f);
     // move the window one column on: logical 0 (column b, done) becomes
-    // logical 7 and takes the next lane's logical 0 (column b + 8 (sg + 1);
-    // nothing past the tile for the last lane of the row)
+    // logical 7 and takes the next lane's logical 0 (column b + 8 (sg + 1)).
+    // For the row's last lane (sg = 7) that is column b + 64: lane 7 of an
+    // even row takes the next row's lane 0 and the last lane of a DPP row
+    // keeps its own value.  Either way the value is past the tile for a row
+    // that has started, and zero for one that has not (so is the next row's
+    // whole window then), so no lane needs masking.
     constexpr int P0 = U & 7;
-    const int nb = __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, R[P0]), 0x101, 0xF, 0xF, false);   // row_shl:1
-    R[P0] = L.sg == 7 ? 0.f : __builtin_bit_cast(float, nb);
+    R[P0] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, R[P0]),
+                                                                  __builtin_bit_cast(int, R[P0]), 0x101, 0xF, 0xF,
+                                                                  false));   // row_shl:1
     // pu of the next step: logical 0 of lane 0 of the row's group
     const float pun = bcast8_lane0(R[(U + 1) & 7]);
-    if (actn) {
-        pu = pun;
-        psp = psn;
-        wcur = wnext;
-    }
+    // unconditional: a row that has not started reads clamped (real)
+    // operands and gets pu = 0 (no errors yet), psp = 0 (no U reads) and some
+    // W~ value, all set again at the step before its first column; a finished
+    // row's values are not used
+    pu = pun;
+    psp = psn;
+    wcur = wnext;
     __syncthreads();
 }
 
