@@ -214,7 +214,7 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[8
     t1 = fmaf(pbz[5], u1.y, t1);
     t0 = fmaf(pbz[6], u1.z, t0);
     t1 = fmaf(pbz[7], u1.w, t1);
-    const float psn = sum8(need_ps ? t0 + t1 : 0.f);
+    const float psn = sum8(t0 + t1);   // lanes without rows r < a - 1 read the zero block
     // move the window one column on: logical 0 (column b, done) becomes
     // logical 7 and takes the next lane's logical 0 (column b + 8 (sg + 1)).
     // For the row's last lane (sg = 7) that is column b + 64: lane 7 of an
