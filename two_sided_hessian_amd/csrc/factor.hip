@@ -85,12 +85,14 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
 // with the block and its inverse resident in LDS (2 x 128 x 132 floats).
 //
 // Factor: right-looking over 16 x 16 diagonal blocks, last first.  For
-// block b: one wave factors and inverts it (base16: L_bb, X_bb = L_bb^-1);
-// then all four waves form the panel L[b][0:16b] = X_bb^T A[b][0:16b] and
-// update the leading part, A[0:16b][0:16b] -= L[b]^T L[b] (lower triangle).
-// This is A = L^T L eliminated from the last row up, 16 rows at a time.
+// block b: one wave factors it (chol16: L_bb); then the panel
+// L[b][0:16b] = L_bb^-T A[b][0:16b] is solved column by column (one thread
+// per column, last row first), and the leading part is updated,
+// A[0:16b][0:16b] -= L[b]^T L[b] (lower triangle).  This is A = L^T L
+// eliminated from the last row up, 16 rows at a time.  The inverses of the
+// 16-blocks are left out of this chain and formed afterwards.
 //
-// Inverse: the diagonal 16-blocks come from base16; the off-diagonal part
+// Inverse: the diagonal 16-blocks come from inv16; the off-diagonal part
 // by the block rule L^-1 = [[X11, 0], [-X22 L21 X11, X22]] applied to 2 x 16,
 // then 2 x 32, then 2 x 64 blocks (the last two on the MFMA units).  Each
 // level parks T = L21 X11 in the upper block of its pair and clears it
@@ -110,22 +112,21 @@ __device__ __forceinline__ float wave_get(float v, int lane)
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// base16: reverse Cholesky S = L^T L of the 16 x 16 block at S (pitch kDP,
-// lower part read) and X = L^-1, by one wave with no LDS traffic between
-// steps.  Lane 4i + q holds row i, columns 4q .. 4q + 3, of the symmetric
+// chol16: reverse Cholesky S - U^T U = L^T L of the 16 x 16 block at S
+// (pitch kDP, lower part read), by one wave with no LDS traffic between
+// steps.  U (16 x 16, pitch kDP, may be null) is the block of the panel rows
+// above S, whose update of S is applied here rather than by the leading-part
+// update.  Lane 4i + q holds row i, columns 4q .. 4q + 3, of the symmetric
 // working matrix (both triangles, so S[i][k] is in the lane's own quad).
 // Step k (15 .. 0) takes row k from lanes 4k + q (ds_bpermute) and
-// S[i][k] from the quad (DPP), and eliminates: S[i][j] -= S[i][k] S[k][j] /
+// S[i][k] from the quad, and eliminates: S[i][j] -= S[i][k] S[k][j] /
 // S[k][k] for i < k; rows stay unscaled and are scaled once at the end,
 // L[i][j] = S[i][j] / sqrt(S[i][i]) (S[i][i] taken when row i was the pivot).
-// The inverse solves L X = I by rows, forward: with R[i] = L[i][i] X[i],
-// R[i] = e_i - sum_{k<i} (L[i][k] / L[k][k]) R[k], one row broadcast a step.
 // Reciprocals and square roots use the hardware approximations (about one
 // ulp): the factor is judged by its backward error, not by correct
-// rounding.  L overwrites S, X is written to X (zeros above both
-// diagonals).  Returns the block row of the first non-positive (or NaN)
-// pivot met, or -1.
-__device__ __forceinline__ int base16(float* __restrict__ S, float* __restrict__ X)
+// rounding.  L overwrites S (zeros above the diagonal).  Returns the block
+// row of the first non-positive (or NaN) pivot met, or -1.
+__device__ __forceinline__ int chol16(float* __restrict__ S, const float* __restrict__ U)
 {
     const int lane = threadIdx.x & 63;
     const int i = lane >> 2, q = lane & 3, c0 = 4 * q;
@@ -134,6 +135,19 @@ __device__ __forceinline__ int base16(float* __restrict__ S, float* __restrict__
     for (int u = 0; u < 4; ++u) {
         const int j = c0 + u;
         s[u] = (j <= i) ? S[i * kDP + j] : S[j * kDP + i];
+    }
+    if (U) {
+        float ui[16];
+        f32x4 uj[16];
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt) {
+            ui[tt] = U[tt * kDP + i];
+            uj[tt] = *reinterpret_cast<const f32x4*>(U + tt * kDP + c0);
+        }
+#pragma unroll
+        for (int tt = 0; tt < 16; ++tt)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) s[u] = fmaf(-ui[tt], uj[tt][u], s[u]);
     }
     int fail = -1;
     float mypiv = 1.f;
@@ -174,9 +188,23 @@ __device__ __forceinline__ int base16(float* __restrict__ S, float* __restrict__
         chol2(4 * g + 1, 1, 0);
     }
     const float rs = __builtin_amdgcn_rsqf(mypiv);   // 1 / L[i][i]
+#pragma unroll
+    for (int u = 0; u < 4; ++u) S[i * kDP + c0 + u] = (c0 + u <= i) ? s[u] * rs : 0.f;
+    return fail;
+}
+
+// inv16: X = L^-1 for the 16 x 16 lower-triangular L at S (pitch kDP), by one
+// wave, in chol16's lane layout.  It solves L X = I by rows, forward: with
+// R[i] = L[i][i] X[i], R[i] = e_i - sum_{k<i} (L[i][k] / L[k][k]) R[k], one
+// row broadcast a step.  X gets zeros above its diagonal.
+__device__ __forceinline__ void inv16(const float* __restrict__ S, float* __restrict__ X)
+{
+    const int lane = threadIdx.x & 63;
+    const int i = lane >> 2, q = lane & 3, c0 = 4 * q;
     float l[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) l[u] = (c0 + u <= i) ? s[u] * rs : 0.f;
+    for (int u = 0; u < 4; ++u) l[u] = S[i * kDP + c0 + u];
+    const float rs = __builtin_amdgcn_rcpf(S[i * kDP + i]);   // 1 / L[i][i]
     float r[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) r[u] = (c0 + u == i) ? 1.f : 0.f;
@@ -210,11 +238,7 @@ __device__ __forceinline__ int base16(float* __restrict__ S, float* __restrict__
         inv2(4 * g + 2, 2, 3);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        S[i * kDP + c0 + u] = l[u];
-        X[i * kDP + c0 + u] = (c0 + u <= i) ? r[u] * rs : 0.f;
-    }
-    return fail;
+    for (int u = 0; u < 4; ++u) X[i * kDP + c0 + u] = (c0 + u <= i) ? r[u] * rs : 0.f;
 }
 
 // MFMA fragment of LDS operand element (r, k .. k + 3) (pitch kDP):
@@ -372,55 +396,44 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
     __syncthreads();
 
     // factor, 16 rows at a time from the bottom, with a one-block lookahead:
-    // once the panel of block b is formed, wave 0 updates only the diagonal
-    // block b - 1 and factors it (base16) while waves 1 - 3 apply the rest of
-    // block b's update to the remaining upper-left part.
+    // once the panel of block b is formed, wave 0 factors diagonal block
+    // b - 1 (chol16, which applies that block's share of the update itself)
+    // while waves 1 - 3 apply the rest of block b's update to the remaining
+    // upper-left part.
     if (wave == 0) {
         const int b = nb / 16 - 1;
-        const int f = base16(sA + 16 * b * (kDP + 1), sX + 16 * b * (kDP + 1));
+        const int f = chol16(sA + 16 * b * (kDP + 1), nullptr);
         if (t == 0 && f >= 0) sfail = 16 * b + f;
     }
     __syncthreads();
     for (int b = nb / 16 - 1; b >= 1; --b) {
         const int W = 16 * b;
         float* Pr = sA + W * kDP;                    // rows of block b
-        {   // panel: Pr[r][c] = sum_t Xbb[t][r] Pr[t][c], c < W; thread (r, cg)
-            // takes columns cg, cg + 16, ... (one 16-deep dot each)
-            const float* Xbb = sX + W * (kDP + 1);
-            const int r = t & 15, cg = t >> 4;
-            float xr[16];
+        if (t < W) {   // panel: solve L_bb^T Z = Pr for column t, from the last row up
+            const float* Lbb = sA + W * (kDP + 1);
+            float p[16];
 #pragma unroll
-            for (int tt = 0; tt < 16; ++tt) xr[tt] = Xbb[tt * kDP + r];
-            float acc[7];
-#pragma unroll 1
-            for (int j = 0; j < b; ++j) {
-                float a = 0.f;
+            for (int r = 0; r < 16; ++r) p[r] = Pr[r * kDP + t];
 #pragma unroll
-                for (int tt = 0; tt < 16; ++tt) a = fmaf(xr[tt], Pr[tt * kDP + cg + 16 * j], a);
-                acc[j] = a;
+            for (int tt = 15; tt >= 0; --tt) {
+                f32x4 lr[4];   // row tt of L_bb, the same for every lane
+#pragma unroll
+                for (int v = 0; v <= tt / 4; ++v) lr[v] = *reinterpret_cast<const f32x4*>(Lbb + tt * kDP + 4 * v);
+                p[tt] *= __builtin_amdgcn_rcpf(lr[tt / 4][tt % 4]);
+#pragma unroll
+                for (int r = 0; r < tt; ++r) p[r] = fmaf(-lr[r / 4][r % 4], p[tt], p[r]);
             }
-            __syncthreads();
-#pragma unroll 1
-            for (int j = 0; j < b; ++j) Pr[r * kDP + cg + 16 * j] = acc[j];
-            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) Pr[r * kDP + t] = p[r];
         }
+        __syncthreads();
         // A[0:W][0:W] -= Pr^T Pr on the 4 x 4 tiles of the lower triangle;
         // the tiles of diagonal block b - 1 (rows and columns W - 16 .. W - 1)
-        // go to wave 0, which then factors that block
+        // are left to wave 0's chol16
         const int n4 = W / 4, ntile = n4 * (n4 + 1) / 2;
         const int d4 = n4 - 4;                       // first 4-row of block b - 1
         if (wave == 0) {
-            const int l = t;                         // 10 tiles of the diagonal block's lower triangle
-            if (l < 10) {
-                int br = 0;
-                while ((br + 1) * (br + 2) / 2 <= l) ++br;
-                const int r0 = 4 * (d4 + br), cc = 4 * (d4 + l - br * (br + 1) / 2);
-                syrk_tile4(sA, Pr, r0, cc);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int f = base16(sA + 16 * (b - 1) * (kDP + 1), sX + 16 * (b - 1) * (kDP + 1));
+            const int f = chol16(sA + 16 * (b - 1) * (kDP + 1), Pr + W - 16);
             if (t == 0 && f >= 0 && sfail < 0) sfail = 16 * (b - 1) + f;
         } else {
             for (int idx = t - 64; idx < ntile; idx += 192) {
@@ -435,8 +448,11 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
         __syncthreads();
     }
 
-    // inverse: 2 x 16 blocks (one wave each), 2 x 32 (MFMA, one wave each),
-    // 2 x 64 (MFMA, four waves); T goes to the upper block of each pair
+    // inverse: the 16-blocks (inv16, one wave each), then merged pairs of
+    // 2 x 16 blocks (one wave each), 2 x 32 (MFMA, one wave each), 2 x 64
+    // (MFMA, four waves); T goes to the upper block of each pair
+    for (int k = wave; k < nb / 16; k += 4) inv16(sA + 16 * k * (kDP + 1), sX + 16 * k * (kDP + 1));
+    __syncthreads();
     if (wave < nb / 32) inv_merge16(sA, sX, 32 * wave);
     __syncthreads();
     if (wave < nb / 64) {
