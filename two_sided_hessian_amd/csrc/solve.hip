@@ -629,14 +629,14 @@ __device__ __forceinline__ void prop_rows_body(const float* __restrict__ E, cons
         block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
     }
 }
-__global__ __launch_bounds__(256) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
+__global__ __launch_bounds__(256, 2) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
                                                    float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                    int K0, int mid, int y0, int y1, int Mt, int Nt,
                                                    const uint32_t* __restrict__ list, unsigned count)
 {
     prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count);
 }
-__global__ __launch_bounds__(256) void k_prop_rows_far(const float* __restrict__ E, const float* __restrict__ PA,
+__global__ __launch_bounds__(256, 2) void k_prop_rows_far(const float* __restrict__ E, const float* __restrict__ PA,
                                                        float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                        int K0, int mid, int y0, int y1, int Mt, int Nt,
                                                        const uint32_t* __restrict__ list, unsigned count)
