@@ -2,9 +2,13 @@
 """Benchmark of the BaKron hot path on one MI355X.
 
 One step = the whole hot path on one synthetic layer, inputs already in HBM:
-bakron_factor(A) and bakron_factor(B) (damping, reverse Cholesky, normalised
-inverse; independent, so they run on two streams at once), then
-bakron_solve (leaf sweeps, error propagation, objective).
+one bakron_quantize call, i.e. the factorisations of A and B (damping,
+reverse Cholesky, normalised inverse; independent, so they run on two
+library streams at once) and the solve (leaf sweeps, error propagation,
+objective), which starts on the factors' leading blocks while their last
+products run.  The same work as three calls (bakron_factor twice, then
+bakron_solve) is timed too, for the factor / solve split, and must give the
+same results.
 Default workload: the 8192 x 8192 layer (mixed 2/3-bit grids, 2.80 bits per
 weight, log-normal channel scales, 8192 samples per factor).
 
@@ -84,12 +88,23 @@ def main():
     out = {"V": torch.empty((m, n), device=dev), "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
            "objective": torch.empty(1, dtype=torch.float64, device=dev)}
     stream = torch.cuda.current_stream()
-    # the two factors are independent: each runs on its own stream (default
-    # priority) and the solve waits for both
-    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    # The step: bakron_quantize, both factorisations and the solve in one
+    # call (the library overlaps the solve's start with the factors' last
+    # products).  `separate` below runs the same work as three calls (the two
+    # factors on two streams of their own, default priority, then the solve)
+    # to report the factor / solve split and the per-kernel profile.
+    ws_q = B._binding.workspace(B.quantize_workspace_bytes(m, n), dev)
+    qout = {"V": out["V"], "codes": out["codes"], "objective": out["objective"], "L_A": fa[0], "P_A": fa[1],
+            "info_A": fa[2], "L_B": fb[0], "P_B": fb[1], "info_B": fb[2]}
+
+    def fused():
+        B.quantize(T["W"], T["A"], T["B"], T["scale"], T["zero"], T["maxq"], 0.01, out=qout, ws=ws_q,
+                   stream=stream)
+
+    sA = sB = None
     fork, joinA, joinB = (torch.cuda.Event() for _ in range(3))
 
-    def step(ev=None, profile=None):
+    def separate(ev=None, profile=None):
         fork.record(stream)
         sA.wait_event(fork)
         sB.wait_event(fork)
@@ -120,30 +135,49 @@ def main():
                 stream=stream, profile=profile)
 
     for _ in range(args.warmup):
-        step()
+        fused()
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup} done")
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     starts[0].record(stream)
     for k in range(args.steps):
-        step(mids[k])
+        fused()
         starts[k + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     step_ms = [starts[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
-    factor_ms = [starts[k].elapsed_time(mids[k]) for k in range(args.steps)]
-    solve_ms = [mids[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
     ms_per_step = float(np.mean(step_ms))
     info = (int(fa[2].item()), int(fb[2].item()))
     obj = float(out["objective"].item())
-    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (factor {np.mean(factor_ms):.3f} ms, "
-        f"solve {np.mean(solve_ms):.3f} ms), wall {wall:.3f}s, info {info}, objective {obj:.6e}")
+    codes_fused = out["codes"].clone()
+
+    # the same work as three calls, timed apart (after the fused timing, so
+    # that its streams do not change how the fused call's streams map to
+    # hardware queues)
+    sA, sB = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(args.warmup):
+        separate()
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    starts[0].record(stream)
+    for k in range(args.steps):
+        separate(mids[k])
+        starts[k + 1].record(stream)
+    torch.cuda.synchronize()
+    sep_ms = [starts[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
+    factor_ms = [starts[k].elapsed_time(mids[k]) for k in range(args.steps)]
+    solve_ms = [mids[k].elapsed_time(starts[k + 1]) for k in range(args.steps)]
+    same = bool(torch.equal(codes_fused, out["codes"])) and float(out["objective"].item()) == obj
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step fused; as three calls {np.mean(sep_ms):.3f} ms "
+        f"(factor {np.mean(factor_ms):.3f} ms, solve {np.mean(solve_ms):.3f} ms), wall {wall:.3f}s, info {info}, "
+        f"objective {obj:.6e}, same results {same}")
     if info != (0, 0):
         raise SystemExit(f"factor reported a non-positive pivot: {info}")
+    if not same:
+        raise SystemExit("the fused call and the three calls disagree")
 
     alg_solve = float(m) * n * (m + n)
     alg_factor = 2.0 * (float(m) ** 3 + float(n) ** 3) / 3.0
@@ -153,7 +187,7 @@ def main():
     kernels = None
     if not args.no_profile:
         prof = []
-        step(profile=prof)
+        separate(profile=prof)
         torch.cuda.synchronize()
         agg = {}
         for r in prof:
@@ -205,7 +239,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": spec.name, "m": m, "n": n, "samples": spec.samples,
                    "bits": "mixed 2/3 (2.80 bpw)" if spec.mixed_low_rows else spec.bits,
-                   "damping": 0.01, "step": "factor(A) || factor(B) on two streams, then solve"},
+                   "damping": 0.01,
+                   "step": "bakron_quantize: factor(A) || factor(B) on library streams, solve overlapping their end"},
+        "separate_s": round(float(np.mean(sep_ms)) / 1e3, 6),
         "solve_s": round(solve_s, 6),
         "factor_s": round(float(np.median(factor_ms)) / 1e3, 6),
         "solve_alg_tflops": round(alg_solve / solve_s / 1e12, 3),

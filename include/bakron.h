@@ -157,6 +157,42 @@ int bakron_solve(const float* W, int64_t m, int64_t n,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Workspace bytes that bakron_quantize needs for an m x n weight (0 when
+ * m or n is not positive or above BAKRON_MAX_DIM).  Host only.
+ */
+size_t bakron_quantize_workspace_bytes(int64_t m, int64_t n);
+
+/*
+ * bakron_quantize -- the whole BaKron rounding of one layer: bakron_factor(A),
+ * bakron_factor(B) and bakron_solve in one call ([S] derivation, Theorem 3.2,
+ * Corollary 3.4: the method takes W, the Kronecker factors A and B of the
+ * Hessian and a grid, and returns the rounded weights).  The results equal
+ * those of the three calls made one after the other.
+ *
+ * The two factorisations run on library-owned streams forked from `stream`
+ * (as in bakron_solve); the solve starts on `stream` as soon as the leading
+ * block of each factor is final (rows and columns below the top split of
+ * the factorisation, when the dimension is a multiple of 64 and above 128)
+ * and waits for the rest before its first tile outside those blocks.  All
+ * outputs are complete for later work on `stream`.
+ *
+ * W, m, n, scale, zero, maxq, V, codes, err, objective: as in bakron_solve.
+ * A, B       [in]  n x n and m x m, as in bakron_factor.  Not modified.
+ * damp_frac  [in]  as in bakron_factor, for both factors.
+ * L_A, P_A, info_A [out] bakron_factor(A)'s outputs (n x n, 16-byte aligned).
+ * L_B, P_B, info_B [out] bakron_factor(B)'s outputs (m x m, 16-byte aligned).
+ * workspace, workspace_bytes [in] scratch, >= bakron_quantize_workspace_bytes.
+ * stream     [in]  HIP stream of the current device.
+ * Returns BAKRON_SUCCESS, or an error code for invalid arguments (nothing is
+ * enqueued then) or a failed launch.
+ */
+int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const float* B,
+                    float damp_frac, const float* scale, const float* zero, const int32_t* maxq,
+                    float* L_A, float* P_A, int32_t* info_A, float* L_B, float* P_B, int32_t* info_B,
+                    float* V, uint8_t* codes, float* err, double* objective,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Batched solves of independent layers ([S]: every linear layer has its own
  * W, A and B, so layers share nothing).  One descriptor per layer; the
  * fields mean what the arguments of bakron_solve mean.

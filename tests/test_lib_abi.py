@@ -33,7 +33,8 @@ def test_header_declares_the_api():
                             "bakron_factor_profiled", "bakron_solve_profiled",
                             "bakron_gptq_workspace_bytes", "bakron_gptq", "bakron_gptq_profiled",
                             "bakron_row_sqnorms", "bakron_moment", "bakron_moment_profiled",
-                            "bakron_solve_batch_workspace_bytes", "bakron_solve_batch"])
+                            "bakron_solve_batch_workspace_bytes", "bakron_solve_batch",
+                            "bakron_quantize_workspace_bytes", "bakron_quantize"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -58,6 +59,11 @@ def test_host_only_calls(B):
     assert "workspace" in B.strerror(-3)
     assert "unknown" in B.strerror(12345)
     assert B.factor_workspace_bytes(0) == 0
+    # the fused call's workspace holds both factor workspaces and the solve's
+    m, n = 256, 320
+    assert B.quantize_workspace_bytes(m, n) >= (B.factor_workspace_bytes(n) + B.factor_workspace_bytes(m)
+                                                + B.solve_workspace_bytes(m, n))
+    assert B.quantize_workspace_bytes(0, n) == 0
     assert B.solve_workspace_bytes(0, 5) == 0
     assert B.solve_workspace_bytes(-1, 5) == 0
     # three m x n float32 matrices at least, plus padded copies when ragged
@@ -112,6 +118,22 @@ def test_host_side_argument_errors(B):
     assert L.bakron_gptq(*a) == 0
     a = list(g); a[11] = fake; a[3] = None          # objective requested without L_A
     assert L.bakron_gptq(*a) == -1
+    # bakron_quantize(W, m, n, A, B, damp, scale, zero, maxq, L_A, P_A, info_A, L_B, P_B, info_B,
+    #                 V, codes, err, objective, ws, bytes, stream)
+    q = [fake, 64, 64, fake, fake, ctypes.c_float(0.01), fake, fake, fake, fake, fake, fake, fake, fake, fake,
+         fake, fake, None, None, fake, 1 << 30, None]
+    a = list(q); a[4] = None
+    assert L.bakron_quantize(*a) == -1
+    a = list(q); a[1] = -1
+    assert L.bakron_quantize(*a) == -2
+    a = list(q); a[5] = ctypes.c_float(-0.5)
+    assert L.bakron_quantize(*a) == -4
+    a = list(q); a[2] = 0
+    assert L.bakron_quantize(*a) == 0
+    a = list(q); a[20] = 1000
+    assert L.bakron_quantize(*a) == -3
+    a = list(q); a[13] = ctypes.c_void_p(4104)      # misaligned P_B
+    assert L.bakron_quantize(*a) == -4
     a = list(g); a[13] = 100
     assert L.bakron_gptq(*a) == -3
     a = list(g); a[4] = ctypes.c_void_p(4104)

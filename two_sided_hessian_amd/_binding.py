@@ -38,6 +38,9 @@ SIGNATURES = {
     "bakron_gptq": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "bakron_row_sqnorms": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP]),
     "bakron_moment": (ctypes.c_int, [_VP, _I64, _I64, _VP, ctypes.c_float, _VP, _VP]),
+    "bakron_quantize_workspace_bytes": (_SZ, [_I64, _I64]),
+    "bakron_quantize": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, ctypes.c_float, _VP, _VP, _VP,
+                                       _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
 }
 
 
@@ -217,6 +220,51 @@ def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objectiv
         profile.extend(_stats_list(arr, cnt))
     if rc != BAKRON_SUCCESS:
         raise BakronError(rc, "bakron_solve")
+    return out
+
+
+def quantize_workspace_bytes(m: int, n: int) -> int:
+    return int(lib().bakron_quantize_workspace_bytes(m, n))
+
+
+def quantize(W, A, B, scale, zero, maxq, damp_frac: float = 0.01, *, want_err=False, want_objective=True,
+             out=None, ws=None, stream=None):
+    """bakron_quantize (both factors and the solve in one call): returns
+    dict(V, codes, err?, objective?, L_A, P_A, info_A, L_B, P_B, info_B) of
+    device tensors."""
+    m, n = W.shape
+    _check_dev("W", W, torch.float32, (m, n))
+    _check_dev("A", A, torch.float32, (n, n))
+    _check_dev("B", B, torch.float32, (m, m))
+    _check_dev("scale", scale, torch.float32, (m,))
+    _check_dev("zero", zero, torch.float32, (m,))
+    _check_dev("maxq", maxq, torch.int32, (m,))
+    dev = W.device
+    if out is None:
+        out = {
+            "V": torch.empty((m, n), dtype=torch.float32, device=dev),
+            "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
+            "L_A": torch.empty((n, n), dtype=torch.float32, device=dev),
+            "P_A": torch.empty((n, n), dtype=torch.float32, device=dev),
+            "info_A": torch.zeros((1,), dtype=torch.int32, device=dev),
+            "L_B": torch.empty((m, m), dtype=torch.float32, device=dev),
+            "P_B": torch.empty((m, m), dtype=torch.float32, device=dev),
+            "info_B": torch.zeros((1,), dtype=torch.int32, device=dev),
+        }
+        if want_err:
+            out["err"] = torch.empty((m, n), dtype=torch.float32, device=dev)
+        if want_objective:
+            out["objective"] = torch.empty((1,), dtype=torch.float64, device=dev)
+    need = quantize_workspace_bytes(m, n)
+    if ws is None:
+        ws = workspace(need, dev)
+    rc = lib().bakron_quantize(_ptr(W), m, n, _ptr(A), _ptr(B), float(damp_frac), _ptr(scale), _ptr(zero),
+                               _ptr(maxq), _ptr(out["L_A"]), _ptr(out["P_A"]), _ptr(out["info_A"]),
+                               _ptr(out["L_B"]), _ptr(out["P_B"]), _ptr(out["info_B"]), _ptr(out["V"]),
+                               _ptr(out["codes"]), _ptr(out.get("err")), _ptr(out.get("objective")), _ptr(ws),
+                               ws.numel(), _stream(stream))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_quantize")
     return out
 
 

@@ -120,6 +120,67 @@ int bakron_solve_profiled(const float* W, int64_t m, int64_t n, const float* L_A
     return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
 }
 
+size_t bakron_quantize_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return 0;
+    return bk::align_up(bk::factor_workspace_bytes(n)) + bk::align_up(bk::factor_workspace_bytes(m)) +
+           bk::solve_workspace_bytes(m, n);
+}
+
+int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const float* B, float damp_frac,
+                    const float* scale, const float* zero, const int32_t* maxq, float* L_A, float* P_A,
+                    int32_t* info_A, float* L_B, float* P_B, int32_t* info_B, float* V, uint8_t* codes,
+                    float* err, double* objective, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (!(damp_frac >= 0.f) || !isfinite(damp_frac)) return BAKRON_ERR_BAD_ARG;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !A || !B || !scale || !zero || !maxq || !L_A || !P_A || !info_A || !L_B || !P_B || !info_B || !V ||
+        !codes)
+        return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(L_A) || !bk::aligned16(P_A) || !bk::aligned16(L_B) || !bk::aligned16(P_B))
+        return BAKRON_ERR_BAD_ARG;
+    const int w = check_ws(workspace, workspace_bytes, bakron_quantize_workspace_bytes(m, n));
+    if (w) return w;
+    char* ws = static_cast<char*>(workspace);
+    void* ws_a = ws;
+    void* ws_b = ws + bk::align_up(bk::factor_workspace_bytes(n));
+    void* ws_s = ws + bk::align_up(bk::factor_workspace_bytes(n)) + bk::align_up(bk::factor_workspace_bytes(m));
+    // The factors run on two library-owned streams forked from `stream`;
+    // the solve starts on `stream` once the leading blocks of both are final
+    // and waits for the rest just before its first tile outside them.
+    // (the streams of the solve's depth-0 and depth-1 far parts, which only
+    // start once both factors are complete)
+    hipStream_t sa = bk::side_stream(stream, 0), sb = bk::side_stream(stream, 1);
+    hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // fork, lead A, lead B, full A, full B
+    int rc = BAKRON_SUCCESS;
+    for (hipEvent_t& e : ev)
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) rc = BAKRON_ERR_HIP;
+    if (!sa || !sb) rc = BAKRON_ERR_HIP;
+    if (rc == BAKRON_SUCCESS) {
+        const bool lead_a = bk::factor_lead(n) > 0, lead_b = bk::factor_lead(m) > 0;
+        bk::SolveWait wait;
+        wait.full[0] = ev[3];
+        wait.full[1] = ev[4];
+        wait.lead_n = bk::factor_lead(n);
+        wait.lead_m = bk::factor_lead(m);
+        if (hipEventRecord(ev[0], stream) != hipSuccess || hipStreamWaitEvent(sa, ev[0], 0) != hipSuccess ||
+            hipStreamWaitEvent(sb, ev[0], 0) != hipSuccess ||
+            bk::factor_enqueue(A, n, damp_frac, L_A, P_A, info_A, ws_a, sa, nullptr, ev[1]) ||
+            hipEventRecord(ev[3], sa) != hipSuccess ||
+            bk::factor_enqueue(B, m, damp_frac, L_B, P_B, info_B, ws_b, sb, nullptr, ev[2]) ||
+            hipEventRecord(ev[4], sb) != hipSuccess ||
+            hipStreamWaitEvent(stream, lead_a ? ev[1] : ev[3], 0) != hipSuccess ||
+            hipStreamWaitEvent(stream, lead_b ? ev[2] : ev[4], 0) != hipSuccess ||
+            bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective, ws_s,
+                              stream, nullptr, true, &wait))
+            rc = BAKRON_ERR_HIP;
+    }
+    for (hipEvent_t e : ev)
+        if (e) (void)hipEventDestroy(e);
+    return rc;
+}
+
 static int check_solve_args(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
                             const float* L_B, const float* P_B, const float* scale, const float* zero,
                             const int32_t* maxq, float* V, uint8_t* codes, double* objective)

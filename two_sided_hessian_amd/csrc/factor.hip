@@ -20,8 +20,12 @@
 // Buffers: Pbuf starts as A_d (lower part used) and ends as Li; Lbuf
 // receives L.  Both are n x n with pitch ld.  The temporary T (n2 x n1) lives
 // in the workspace.  A final pass scales Li's columns by diag(L) (giving P)
-// and writes zeros above both diagonals.
+// and writes zeros above both diagonals.  When n is a multiple of 64 (and
+// above 128), the top level runs that pass on its leading block as soon as
+// the block is final, and forms P21 from it directly (see factor_rec), so a
+// solve can start on the leading block while the last two GEMMs run.
 #include <algorithm>
+#include <mutex>
 
 #include "gemm.hpp"
 #include "internal.hpp"
@@ -551,6 +555,53 @@ __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, flo
     block_store<2, 2>(Pbuf + (o2 + r0) * ld + o1 + c0, ld, n2 - r0, n1 - c0, -1.f, 0.f, acc);
 }
 
+// The top level's T and Li21 products while a solve runs beside them on the
+// factor's leading block (factor_enqueue with `lead`): at most kLeadGrid
+// workgroups, each looping over blocks q = blockIdx.x, + gridDim.x, ... in
+// the order of the plain launch (q = x + nx y), and each reserving enough LDS
+// (dynamic, kLeadPad bytes) that no leaf of the solve fits beside it.  Two
+// factors at once then leave 256 - 2 kLeadGrid CUs to the solve's leaves.
+#ifndef BAKRON_LEAD_GRID
+#define BAKRON_LEAD_GRID 96
+#endif
+constexpr unsigned kLeadGrid = BAKRON_LEAD_GRID;
+constexpr size_t kLeadPad = 160 * 1024 - kLeafLdsBytes - sizeof(float) * Gemm<2, 2, RowK, KRow>::LDS_FLOATS + 1024;
+
+__global__ __launch_bounds__(256) void k_f_right_lead(const float* __restrict__ Lbuf, const float* __restrict__ Pbuf,
+                                                      float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
+                                                      int n1, int n2, unsigned nx, unsigned count)
+{
+    __shared__ __align__(16) float lds[Gemm<2, 2, RowK, KRow>::LDS_FLOATS];
+    extern __shared__ float reserve[];
+    (void)reserve;
+    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+        const int r0 = (int)(q % nx) * FBM, c0 = (int)(q / nx) * FBN;
+        Acc acc;
+        acc_zero(acc);
+        block_gemm<2, 2, RowK, KRow>(Lbuf + (o2 + r0) * ld + o1, ld, n2 - r0,
+                                     Pbuf + o1 * ld + o1 + c0, ld, n1 - c0, c0, n1, lds, acc);
+        block_store<2, 2>(T + (int64_t)r0 * n1 + c0, n1, n2 - r0, n1 - c0, 1.f, 0.f, acc);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_f_left_lead(const float* __restrict__ T, float* __restrict__ Pbuf,
+                                                     int64_t ld, int64_t o1, int64_t o2, int n1, int n2,
+                                                     unsigned nx, unsigned ny, unsigned count)
+{
+    __shared__ __align__(16) float lds[Gemm<2, 2, RowK, KRow>::LDS_FLOATS];
+    extern __shared__ float reserve[];
+    (void)reserve;
+    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+        const int r0 = (int)(ny - 1 - q / nx) * FBM, c0 = (int)(q % nx) * FBN;
+        const int kend = min(r0 + FBM, n2);
+        Acc acc;
+        acc_zero(acc);
+        block_gemm<2, 2, RowK, KRow>(Pbuf + (o2 + r0) * ld + o2, ld, n2 - r0,
+                                     T + c0, n1, n1 - c0, 0, kend, lds, acc);
+        block_store<2, 2>(Pbuf + (o2 + r0) * ld + o1 + c0, ld, n2 - r0, n1 - c0, -1.f, 0.f, acc);
+    }
+}
+
 // The same four products with one 64 x 64 output tile per workgroup (one
 // 32 x 32 quadrant per wave) for the levels whose 128 x 128 grids are too
 // small to fill the GPU.  MODE: 0 panel, 1 syrk, 2 right, 3 left.
@@ -603,15 +654,15 @@ __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float*
 // Each thread owns four adjacent columns for a stripe of rows, so the
 // diagonal entries it scales by are read once.
 __global__ __launch_bounds__(256) void k_f_finish(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
-                                                  int64_t Np, int64_t n, float* __restrict__ Lout,
-                                                  float* __restrict__ Pout)
+                                                  int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t n,
+                                                  float* __restrict__ Lout, float* __restrict__ Pout)
 {
-    const int64_t j = 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
-    if (j >= Np) return;
+    const int64_t j = j0 + 4 * ((int64_t)blockIdx.x * 256 + threadIdx.x);
+    if (j >= j1) return;
     float dg[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) dg[q] = Lbuf[(j + q) * ld + j + q];
-    for (int64_t i = blockIdx.y; i < Np; i += gridDim.y) {
+    for (int64_t i = i0 + blockIdx.y; i < i1; i += gridDim.y) {
         f32x4 l = {0.f, 0.f, 0.f, 0.f}, p = {0.f, 0.f, 0.f, 0.f};
         if (j <= i) {
             l = *reinterpret_cast<const f32x4*>(Lbuf + i * ld + j);
@@ -680,7 +731,20 @@ struct FactorRun {
     int32_t* info;
     hipStream_t s;
     Prof* prof;
+    bool early;        // the top level finishes its leading block before the last two GEMMs
+    hipEvent_t lead;   // nullable: recorded once that leading block is final
+    int64_t n;
 };
+
+// The finish pass over rows [i0, i1) and columns [j0, j1) (multiples of 4):
+// P = Li diag(L) below the diagonal, zeros above both diagonals.
+void enqueue_finish(const FactorRun& R, int64_t i0, int64_t i1, int64_t j0, int64_t j1)
+{
+    const double rows = (double)(i1 - i0), cols = (double)(j1 - j0);
+    dim3 g((unsigned)ceil_div(j1 - j0, 1024), (unsigned)std::min<int64_t>(i1 - i0, 256));
+    launch(R.prof, KK_F_FINISH, rows * cols / 2.0, 4.0 * 4.0 * rows * cols, k_f_finish, g, dim3(256), R.s,
+           R.Lbuf, R.Pbuf, R.ld, i0, i1, j0, j1, R.n, (float*)nullptr, (float*)nullptr);
+}
 
 // Algorithmic work (fp32 flops = 2 x multiply-adds on the nonzero triangle /
 // block support) and bytes (each operand read once, each output written once).
@@ -725,6 +789,14 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, o1, n1)) return -1;
+    if (R.early && o == 0 && nsz == R.ld) {
+        // The leading block is final: finish it now (P11 = Li11 diag(L11)),
+        // so that a solve waiting on `lead` can start on it.  The two GEMMs
+        // below then give P21 directly: with T' = L21 P11,
+        // P21 = Li21 diag(L11) = -Li22 L21 Li11 diag(L11) = -Li22 T'.
+        enqueue_finish(R, 0, n1, 0, n1);
+        if (launch_ok() || (R.lead && hipEventRecord(R.lead, R.s) != hipSuccess)) return -1;
+    }
     {
         const double fr = 2.0 * d2 * tri(d1), br = 4.0 * (2.0 * d2 * d1 + tri(d1));
         const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
@@ -733,6 +805,19 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
                    R.ld, o1, o2, n1, n2);
             launch(R.prof, KK_F_LEFT_T, fl, bl, k_f_tile<3>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
                    R.ld, o1, o2, n1, n2);
+        } else if (R.lead && o == 0 && nsz == R.ld) {
+            static std::once_flag attrs;
+            std::call_once(attrs, [] {
+                (void)hipFuncSetAttribute((const void*)k_f_right_lead, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)kLeadPad);
+                (void)hipFuncSetAttribute((const void*)k_f_left_lead, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          (int)kLeadPad);
+            });
+            const unsigned cnt = g.x * g.y, grid = std::min(cnt, kLeadGrid);
+            launch_shm(R.prof, KK_F_RIGHT, fr, br, k_f_right_lead, dim3(grid), dim3(256), kLeadPad, R.s,
+                       (const float*)R.Lbuf, (const float*)R.Pbuf, R.T, R.ld, o1, o2, n1, n2, g.y, cnt);
+            launch_shm(R.prof, KK_F_LEFT, fl, bl, k_f_left_lead, dim3(grid), dim3(256), kLeadPad, R.s,
+                       (const float*)R.T, R.Pbuf, R.ld, o1, o2, n1, n2, g.x, g.y, cnt);
         } else {
             launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, dim3(g.y, g.x), dim3(256), R.s, (const float*)R.Lbuf,
                    (const float*)R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
@@ -751,8 +836,14 @@ size_t factor_workspace_bytes(int64_t n)
     return plan_factor(n).total;
 }
 
+int64_t factor_lead(int64_t n)
+{
+    if (n <= 2 * kTile || n % kTile != 0) return 0;
+    return kTile * (n / kTile / 2);
+}
+
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
-                   void* ws, hipStream_t s, Prof* prof)
+                   void* ws, hipStream_t s, Prof* prof, hipEvent_t lead)
 {
     const FactorPlan p = plan_factor(n);
     char* w = static_cast<char*>(ws);
@@ -763,6 +854,9 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     R.info = info;
     R.s = s;
     R.prof = prof;
+    R.early = factor_lead(n) > 0;
+    R.lead = R.early ? lead : nullptr;
+    R.n = n;
     R.Lbuf = p.padded ? reinterpret_cast<float*>(w + p.off_L) : L;
     R.Pbuf = p.padded ? reinterpret_cast<float*>(w + p.off_P) : P;
     const double dn = (double)n, dN = (double)p.Np;
@@ -777,10 +871,15 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, 0, p.Np)) return -1;
-    {
+    if (R.early) {   // the trailing block, and the zeros right of the leading block (P21 is done)
+        const int64_t n1 = factor_lead(n);
+        enqueue_finish(R, n1, p.Np, n1, p.Np);
+        enqueue_finish(R, 0, n1, n1, p.Np);
+    } else {
         dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 256));
         launch(prof, KK_F_FINISH, dn * dn / 2.0, 4.0 * (2.0 * tri(dN) + 2.0 * dn * dn), k_f_finish, g, dim3(256),
-               s, R.Lbuf, R.Pbuf, p.Np, p.Np, n, p.padded ? L : (float*)nullptr, p.padded ? P : (float*)nullptr);
+               s, R.Lbuf, R.Pbuf, p.Np, (int64_t)0, p.Np, (int64_t)0, p.Np, n, p.padded ? L : (float*)nullptr,
+               p.padded ? P : (float*)nullptr);
     }
     return launch_ok();
 }

@@ -95,6 +95,7 @@ int prof_collect(Prof& p, hipStream_t s, bakron_kernel_stat* stats, int32_t max_
 constexpr int kTile = 64;            // tile edge of the solve and of the factor's base blocks
 constexpr int kMaxDim = BAKRON_MAX_DIM;
 constexpr size_t kAlign = 256;       // workspace sub-buffer alignment
+constexpr size_t kLeafLdsBytes = 72800;   // LDS of one solve leaf workgroup (k_leaf)
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -102,16 +103,27 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // Factor (factor.hip)
 size_t factor_workspace_bytes(int64_t n);
+// With `lead`, the event is recorded on `stream` as soon as rows and columns
+// [0, factor_lead(n)) of L and P are final (when factor_lead(n) > 0).
+int64_t factor_lead(int64_t n);
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
-                   void* ws, hipStream_t stream, Prof* prof);
+                   void* ws, hipStream_t stream, Prof* prof, hipEvent_t lead = nullptr);
 
 // Solve (solve.hip).  With `split`, the far parts of the upper nodes run on
 // library-owned streams, ordered against `stream` by events.
 size_t solve_workspace_bytes(int64_t m, int64_t n, bool split = true);
+// A solve that starts while its factors are still being finished: rows and
+// columns [0, lead_n) of L_A, P_A and [0, lead_m) of L_B, P_B are final when
+// the solve's work reaches `stream`; the rest when the events `full` (either
+// may be null) complete.
+struct SolveWait {
+    hipEvent_t full[2];
+    int64_t lead_m, lead_n;
+};
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,
                   const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                  void* ws, hipStream_t stream, Prof* prof, bool split = true);
+                  void* ws, hipStream_t stream, Prof* prof, bool split = true, const SolveWait* wait = nullptr);
 
 // One-sided case B = I (gptq.hip)
 size_t gptq_workspace_bytes(int64_t m, int64_t n);

@@ -886,7 +886,21 @@ struct SolveRun {
     std::vector<hipEvent_t> events;
     bool failed;
     Prof* prof;
+    // Factors still being finished (SolveWait): `full` is waited for on s
+    // before the first work on a tile anti-diagonal >= Kq.
+    hipEvent_t full[2];
+    int Kq;
+    bool full_pending;
 };
+
+// Before work that touches tile anti-diagonals up to khi.
+void ensure_full(SolveRun& R, int khi)
+{
+    if (!R.full_pending || khi < R.Kq) return;
+    R.full_pending = false;
+    for (hipEvent_t e : R.full)
+        if (e && hipStreamWaitEvent(R.s, e, 0) != hipSuccess) R.failed = true;
+}
 
 hipEvent_t new_event(SolveRun& R)
 {
@@ -941,6 +955,7 @@ constexpr unsigned kFarGrid = BAKRON_FAR_GRID;
 constexpr int64_t kFarBlockMin = BAKRON_FAR_BLOCK_MIN;   // the block kernel from this many blocks
 constexpr size_t kLdsPerCU = 160 * 1024;
 constexpr size_t kLeafLds = sizeof(float) * (64 * 64 + 3 * 64 * kLP + 8) + 64 * 64 + 8 * sizeof(double);   // k_leaf's arrays
+static_assert(kLeafLds == kLeafLdsBytes, "k_leaf's LDS as the factor's lead launches assume it");
 constexpr size_t pad_to_exclude(size_t static_lds)
 {
     return static_lds + kLeafLds > kLdsPerCU ? 0 : kLdsPerCU - kLeafLds - static_lds + 1024;
@@ -1087,6 +1102,7 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits
 void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits)
 {
     if (K1 - K0 == 1) {   // (the nodes that carry waits are never leaves)
+        ensure_full(R, K0);
         enqueue_leaf(R, K0);
         return;
     }
@@ -1096,6 +1112,7 @@ void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& wait
     solve_rec(R, K0, mid, d + 1, 2 * p, down);
     if (waits.e[0] && hipStreamWaitEvent(R.s, waits.e[0], 0) != hipSuccess) R.failed = true;
     SpineWaits done;
+    ensure_full(R, K1 - 1);
     enqueue_prop(R, K0, mid, K1, d, p, done);
     solve_rec(R, mid, K1, d + 1, 2 * p + 1, done);
 }
@@ -1111,7 +1128,7 @@ size_t solve_workspace_bytes(int64_t m, int64_t n, bool split)
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,
                   const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                  void* ws, hipStream_t s, Prof* prof, bool split)
+                  void* ws, hipStream_t s, Prof* prof, bool split, const SolveWait* wait)
 {
     SolvePlan p = plan_solve(m, n, split);
     char* w = static_cast<char*>(ws);
@@ -1119,6 +1136,13 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.prof = prof;
     R.s = s;
     R.failed = false;
+    R.full[0] = wait ? wait->full[0] : nullptr;
+    R.full[1] = wait ? wait->full[1] : nullptr;
+    R.full_pending = wait != nullptr;
+    // Tiles on anti-diagonals K < Kq have rows below lead_m and columns below
+    // lead_n; the padded copies of P_A and P_B need the whole factors.
+    R.Kq = (!wait || p.pad_a || p.pad_b) ? 0 : (int)(std::min(wait->lead_m, wait->lead_n) / kTile);
+    if (R.Kq == 0) ensure_full(R, 0);
     for (int d = 0; d < kSplitDepth; ++d) {
         R.Ysplit[d] = d < p.sg.split_depth ? reinterpret_cast<float*>(w + p.off_ysplit[d]) : nullptr;
         R.far[d] = d < p.sg.split_depth ? side_stream(s, d) : nullptr;
@@ -1195,6 +1219,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     SpineWaits none;
     for (hipEvent_t& e : none.e) e = nullptr;
     solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, none);
+    ensure_full(R, R.Mt + R.Nt);   // s is ordered after the factors in any case
     // every far part is waited for by the right child of its node, so all
     // of them are ordered before the rest of the work on s
     for (hipEvent_t e : R.events) (void)hipEventDestroy(e);
