@@ -949,8 +949,12 @@ constexpr int64_t kBlockLaunchMin = BAKRON_BLOCK_LAUNCH_MIN;
 #define BAKRON_FAR_GRID 192
 #endif
 constexpr unsigned kFarGrid = BAKRON_FAR_GRID;
+// Far parts switch to the block kernels much earlier than near ones: on the
+// capped grid each workgroup has a CU to itself (the LDS reserve), where a
+// 64 x 64 tile keeps one MFMA accumulator chain per SIMD busy and a 64 x 256
+// block four.
 #ifndef BAKRON_FAR_BLOCK_MIN
-#define BAKRON_FAR_BLOCK_MIN BAKRON_BLOCK_LAUNCH_MIN
+#define BAKRON_FAR_BLOCK_MIN 128
 #endif
 constexpr int64_t kFarBlockMin = BAKRON_FAR_BLOCK_MIN;   // the block kernel from this many blocks
 constexpr size_t kLdsPerCU = 160 * 1024;
