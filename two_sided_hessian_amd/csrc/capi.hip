@@ -147,8 +147,9 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
     void* ws_b = ws + bk::align_up(bk::factor_workspace_bytes(n));
     void* ws_s = ws + bk::align_up(bk::factor_workspace_bytes(n)) + bk::align_up(bk::factor_workspace_bytes(m));
     // The factors run on two library-owned streams forked from `stream`;
-    // the solve starts on `stream` once the leading blocks of both are final
-    // and waits for the rest just before its first tile outside them.
+    // the solve's first work (copies, block lists) starts at once, its first
+    // leaf waits for the leading blocks of both factors, and its first tile
+    // outside them for the whole factors.
     // (the streams of the solve's depth-0 and depth-1 far parts, which only
     // start once both factors are complete)
     hipStream_t sa = bk::side_stream(stream, 0), sb = bk::side_stream(stream, 1);
@@ -160,6 +161,8 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
     if (rc == BAKRON_SUCCESS) {
         const bool lead_a = bk::factor_lead(n) > 0, lead_b = bk::factor_lead(m) > 0;
         bk::SolveWait wait;
+        wait.lead[0] = lead_a ? ev[1] : ev[3];
+        wait.lead[1] = lead_b ? ev[2] : ev[4];
         wait.full[0] = ev[3];
         wait.full[1] = ev[4];
         wait.lead_n = bk::factor_lead(n);
@@ -170,8 +173,6 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
             hipEventRecord(ev[3], sa) != hipSuccess ||
             bk::factor_enqueue(B, m, damp_frac, L_B, P_B, info_B, ws_b, sb, nullptr, ev[2]) ||
             hipEventRecord(ev[4], sb) != hipSuccess ||
-            hipStreamWaitEvent(stream, lead_a ? ev[1] : ev[3], 0) != hipSuccess ||
-            hipStreamWaitEvent(stream, lead_b ? ev[2] : ev[4], 0) != hipSuccess ||
             bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective, ws_s,
                               stream, nullptr, true, &wait))
             rc = BAKRON_ERR_HIP;

@@ -112,12 +112,13 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
 // Solve (solve.hip).  With `split`, the far parts of the upper nodes run on
 // library-owned streams, ordered against `stream` by events.
 size_t solve_workspace_bytes(int64_t m, int64_t n, bool split = true);
-// A solve that starts while its factors are still being finished: rows and
-// columns [0, lead_n) of L_A, P_A and [0, lead_m) of L_B, P_B are final when
-// the solve's work reaches `stream`; the rest when the events `full` (either
-// may be null) complete.
+// A solve enqueued while its factors are still being computed: rows and
+// columns [0, lead_n) of L_A, P_A and [0, lead_m) of L_B, P_B are final once
+// the events `lead` complete, everything once the events `full` complete
+// (any of them may be null: nothing to wait for).  The solve waits for each
+// just before its first work that needs it.
 struct SolveWait {
-    hipEvent_t full[2];
+    hipEvent_t lead[2], full[2];
     int64_t lead_m, lead_n;
 };
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,

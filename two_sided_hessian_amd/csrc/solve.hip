@@ -886,19 +886,22 @@ struct SolveRun {
     std::vector<hipEvent_t> events;
     bool failed;
     Prof* prof;
-    // Factors still being finished (SolveWait): `full` is waited for on s
-    // before the first work on a tile anti-diagonal >= Kq.
-    hipEvent_t full[2];
+    // Factors still being finished (SolveWait): `lead` is waited for on s
+    // before the first work that reads them, `full` before the first work on
+    // a tile anti-diagonal >= Kq.
+    hipEvent_t lead[2], full[2];
     int Kq;
-    bool full_pending;
+    bool lead_pending, full_pending;
 };
 
-// Before work that touches tile anti-diagonals up to khi.
+// Before work that reads the factors on tile anti-diagonals up to khi.
 void ensure_full(SolveRun& R, int khi)
 {
-    if (!R.full_pending || khi < R.Kq) return;
-    R.full_pending = false;
-    for (hipEvent_t e : R.full)
+    const bool full = R.full_pending && khi >= R.Kq;
+    if (!full && !R.lead_pending) return;
+    R.lead_pending = false;   // (each full event follows its lead event on the factor's stream)
+    if (full) R.full_pending = false;
+    for (hipEvent_t e : full ? R.full : R.lead)
         if (e && hipStreamWaitEvent(R.s, e, 0) != hipSuccess) R.failed = true;
 }
 
@@ -1140,9 +1143,11 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.prof = prof;
     R.s = s;
     R.failed = false;
-    R.full[0] = wait ? wait->full[0] : nullptr;
-    R.full[1] = wait ? wait->full[1] : nullptr;
-    R.full_pending = wait != nullptr;
+    for (int k = 0; k < 2; ++k) {
+        R.lead[k] = wait ? wait->lead[k] : nullptr;
+        R.full[k] = wait ? wait->full[k] : nullptr;
+    }
+    R.lead_pending = R.full_pending = wait != nullptr;
     // Tiles on anti-diagonals K < Kq have rows below lead_m and columns below
     // lead_n; the padded copies of P_A and P_B need the whole factors.
     R.Kq = (!wait || p.pad_a || p.pad_b) ? 0 : (int)(std::min(wait->lead_m, wait->lead_n) / kTile);
