@@ -411,7 +411,8 @@ def bench_batch(B, WL, dev, args, layers=16, name="sq1024"):
 # (the leaf sweep, the diagonal-block factor, the schedule and the objective
 # reduction) are chains of dependent vector arithmetic and LDS traffic,
 # priced against the fp32 vector peak.
-MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_prop_rows_far", "k_prop_rows_t_far",
+MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_prop_pair", "k_prop_rows_far",
+                "k_prop_rows_t_far",
                 "k_prop_cols_far", "k_prop_cols_t_far", "k_f_panel", "k_f_right",
                 "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_gptq_update",
                 "k_gptq_update_t", "k_moment<false>", "k_moment<true>"}

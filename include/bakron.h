@@ -334,7 +334,7 @@ int bakron_moment(const float* X, int64_t N, int64_t n, const float* w, float sc
  * max_stats [in]  capacity (BAKRON_MAX_KERNEL_KINDS is always enough).
  * n_stats   [out] host int32: number of entries written (kernels launched).
  */
-#define BAKRON_MAX_KERNEL_KINDS 32
+#define BAKRON_MAX_KERNEL_KINDS 48
 
 typedef struct bakron_kernel_stat {
     const char* name;     /* kernel name (static storage) */

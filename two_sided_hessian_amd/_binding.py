@@ -63,7 +63,7 @@ class KernelStat(ctypes.Structure):
                 ("alg_flops", ctypes.c_double), ("alg_bytes", ctypes.c_double)]
 
 
-BAKRON_MAX_KERNEL_KINDS = 32
+BAKRON_MAX_KERNEL_KINDS = 48
 _PSTAT = ctypes.POINTER(KernelStat)
 SIGNATURES["bakron_factor_profiled"] = (ctypes.c_int, SIGNATURES["bakron_factor"][1] + [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_solve_profiled"] = (ctypes.c_int, SIGNATURES["bakron_solve"][1] + [_PSTAT, ctypes.c_int32, _VP])

@@ -769,6 +769,73 @@ __global__ __launch_bounds__(256) void k_prop_cols_t_far(const float* __restrict
     prop_cols_t_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, span, count);
 }
 
+// Nodes of two leaves, (K0, K0 + 1, K0 + 2): both stages in one launch, one
+// workgroup per target tile (I', J') on anti-diagonal K0 + 1.  Its sources
+// are the rows I in [max(0, I' - 1), min(K0, I')], each with the one source
+// tile (I, K0 - I), and every Y tile it needs is needed by no other target:
+//   Y_I = E[I, K0 - I] P_A[J', K0 - I]^T            (stage 1, K = 64)
+//   W~[I', J'] -= sum_I P_B[I', I] Y_I              (stage 2, I ascending)
+// The Y tiles stay in LDS.  Fragments come straight from global memory into
+// registers (the K extents are 64 and 128), with the MFMAs of the tile
+// kernels in their order, and Y rounded as those kernels store it, so the
+// results are theirs bit for bit.
+constexpr int kYP = 68;   // LDS pitch of a Y tile
+__global__ __launch_bounds__(256) void k_prop_pair(const float* __restrict__ E, const float* __restrict__ PA,
+                                                   const float* __restrict__ PB, float* __restrict__ Wt,
+                                                   int64_t ldw, int64_t lda, int64_t ldb, int K0, int I_lo)
+{
+    __shared__ __align__(16) float sY[2 * 64 * kYP];
+    const int Ip = I_lo + (int)blockIdx.x, Jp = K0 + 1 - Ip;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ml = lane & 31, kl = 4 * (lane >> 5);
+    const int ra = 32 * (wave >> 1) + ml, rb = 32 * (wave & 1) + ml;
+    const int Ilo = max(0, Ip - 1), Ihi = min(K0, Ip);
+    for (int I = Ilo; I <= Ihi; ++I) {
+        const int J = K0 - I;
+        const float* a0 = E + (int64_t)I * 64 * ldw + (int64_t)J * 64;
+        const float* b0 = PA + (int64_t)Jp * 64 * lda + (int64_t)J * 64;
+        f32x4 a[8], b[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * ldw + 8 * st + kl);
+            b[st] = *reinterpret_cast<const f32x4*>(b0 + (int64_t)rb * lda + 8 * st + kl);
+        }
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], b[st][q], acc, 0, 0, 0);
+        float* y = sY + (I - Ilo) * 64 * kYP + 32 * (wave >> 1) * kYP + 32 * (wave & 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float one = 1.f, none = 0.f;   // as stage 1 stores Y: 1 acc + 0 0
+            y[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kYP + ml] = one * acc[r] + none * none;
+        }
+    }
+    __syncthreads();
+    f32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int I = Ilo; I <= Ihi; ++I) {
+        const float* a0 = PB + (int64_t)Ip * 64 * ldb + (int64_t)I * 64;
+        const float* y = sY + (I - Ilo) * 64 * kYP + rb;
+        f32x4 a[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * ldb + 8 * st + kl);
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const float* c = y + (8 * st + kl) * kYP;
+            const f32x4 bv = {c[0], c[kYP], c[2 * kYP], c[3 * kYP]};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], bv[q], acc, 0, 0, 0);
+        }
+    }
+    const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1), c = (int64_t)Jp * 64 + 32 * (wave & 1);
+    wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
+}
+
 __global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t count,
                                                     double* __restrict__ out)
 {
@@ -1106,6 +1173,26 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits
 
 // `waits`: far parts of ancestors due before the propagation of this node
 // and of the nodes down its left spine.
+#ifndef BAKRON_PAIR_FUSE
+#define BAKRON_PAIR_FUSE 1
+#endif
+// The propagation of a node of two leaves (K0, K0 + 1, K0 + 2) (k_prop_pair).
+void enqueue_pair(SolveRun& R, int K0)
+{
+    const int I_lo = std::max(0, K0 + 1 - (R.Nt - 1)), I_hi = std::min(R.Mt - 1, K0 + 1);
+    if (I_hi < I_lo) return;
+    double fl = 0.0, by = 0.0;
+    for (int Ip = I_lo; Ip <= I_hi; ++Ip) {
+        const int srcs = std::min(K0, Ip) - std::max(0, Ip - 1) + 1;
+        // per source: a diagonal and a full block product in each stage;
+        // E, P_A and P_B tiles in, W~ read and written
+        fl += srcs * 2.0 * 2.0 * (kTriB + kFull) / 2.0;
+        by += srcs * 3.0 * kTileB + 2.0 * kTileB;
+    }
+    launch(R.prof, KK_PROP_PAIR, fl, by, k_prop_pair, dim3((unsigned)(I_hi - I_lo + 1)), dim3(256), R.s,
+           (const float*)R.leaf.E, R.leaf.PA, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.lda, R.leaf.ldb, K0, I_lo);
+}
+
 void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits)
 {
     if (K1 - K0 == 1) {   // (the nodes that carry waits are never leaves)
@@ -1120,7 +1207,12 @@ void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& wait
     if (waits.e[0] && hipStreamWaitEvent(R.s, waits.e[0], 0) != hipSuccess) R.failed = true;
     SpineWaits done;
     ensure_full(R, K1 - 1);
-    enqueue_prop(R, K0, mid, K1, d, p, done);
+    if (BAKRON_PAIR_FUSE && K1 - K0 == 2) {   // (never cut in parts)
+        for (hipEvent_t& e : done.e) e = nullptr;
+        enqueue_pair(R, K0);
+    } else {
+        enqueue_prop(R, K0, mid, K1, d, p, done);
+    }
     solve_rec(R, mid, K1, d + 1, 2 * p + 1, done);
 }
 
