@@ -6,7 +6,8 @@ while the factorisations finish on library-owned streams, so the comparison
 pins that overlap (and the point where the solve waits for the whole factors)
 to the plain order.  Shapes cover dimensions with and without the early
 leading block (multiples of 64 above 128, and ragged or small ones), m != n,
-two calls in a row on one workspace, and the full 8192^2 workload.
+degenerate single-row and two-column layers, two calls in a row on one
+workspace, and the full 8192^2 workload.
 
 Pages: [S] paper summary "FastKron: Efficient Quantization with
 Kronecker-Factored Hessians" (derivation, Theorem 3.2, Corollary 3.4).
@@ -21,7 +22,8 @@ from workloads import make_problem
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
-SHAPES = [(64, 64), (130, 70), (256, 192), (192, 1024), (1024, 1024), (2048, 640), (1000, 1500)]
+SHAPES = [(64, 64), (130, 70), (256, 192), (192, 1024), (1024, 1024), (2048, 640), (1000, 1500), (1, 256),
+          (320, 2)]
 
 
 def to_dev(a):
@@ -42,7 +44,7 @@ KEYS = ("codes", "V", "err", "objective", "L_A", "P_A", "info_A", "L_B", "P_B", 
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}" for m, n in SHAPES])
 def test_quantize_equals_separate_calls(shape):
     m, n = shape
-    d = make_problem(m, n, 70 + m % 97)
+    d = make_problem(m, n, 70 + m % 97, global_grid=(n < 4))
     print(f"quantize vs separate: {m}x{n}", flush=True)
     T = {k: to_dev(d[k]) for k in ("W", "A", "B", "scale", "zero", "maxq")}
     ref = separate(T)
