@@ -146,12 +146,11 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
     void* ws_a = ws;
     void* ws_b = ws + bk::align_up(bk::factor_workspace_bytes(n));
     void* ws_s = ws + bk::align_up(bk::factor_workspace_bytes(n)) + bk::align_up(bk::factor_workspace_bytes(m));
-    // The factors run on two library-owned streams forked from `stream`;
-    // the solve's first work (copies, block lists) starts at once, its first
-    // leaf waits for the leading blocks of both factors, and its first tile
-    // outside them for the whole factors.
-    // (the streams of the solve's depth-0 and depth-1 far parts, which only
-    // start once both factors are complete)
+    // The factors run on two library-owned streams forked from `stream` (the
+    // streams of the solve's depth-0 and depth-1 far parts, which only start
+    // once both factors are complete); the solve's first work (copies, block
+    // lists) starts at once, its first leaf waits for the leading blocks of
+    // both factors, and its first tile outside them for the whole factors.
     hipStream_t sa = bk::side_stream(stream, 0), sb = bk::side_stream(stream, 1);
     hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // fork, lead A, lead B, full A, full B
     int rc = BAKRON_SUCCESS;
