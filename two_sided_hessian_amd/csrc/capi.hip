@@ -7,6 +7,7 @@
 #include <map>
 #include <mutex>
 #include <tuple>
+#include <vector>
 
 #include "../../include/bakron.h"
 #include "internal.hpp"
@@ -148,30 +149,34 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
     void* ws_s = ws + bk::align_up(bk::factor_workspace_bytes(n)) + bk::align_up(bk::factor_workspace_bytes(m));
     // The factors run on two library-owned streams forked from `stream` (the
     // streams of the solve's depth-0 and depth-1 far parts, which only start
-    // once both factors are complete); the solve's first work (copies, block
-    // lists) starts at once, its first leaf waits for the leading blocks of
-    // both factors, and its first tile outside them for the whole factors.
+    // once both factors are complete).  Each records an event as each of its
+    // leading blocks becomes final; the solve's first work (copies, block
+    // lists) starts at once, and each later kernel of it waits for the
+    // smallest leading blocks that hold its tiles.
     hipStream_t sa = bk::side_stream(stream, 0), sb = bk::side_stream(stream, 1);
-    hipEvent_t ev[5] = {nullptr, nullptr, nullptr, nullptr, nullptr};   // fork, lead A, lead B, full A, full B
-    int rc = BAKRON_SUCCESS;
-    for (hipEvent_t& e : ev)
+    bk::SolveWait wait;
+    wait.lead[0].count = bk::factor_leads(n, wait.lead[0].size);
+    wait.lead[1].count = bk::factor_leads(m, wait.lead[1].size);
+    std::vector<hipEvent_t> ev;   // fork, full A, full B, then the lead events
+    int rc = (sa && sb) ? BAKRON_SUCCESS : BAKRON_ERR_HIP;
+    const int nev = 3 + wait.lead[0].count + wait.lead[1].count;
+    for (int k = 0; k < nev && rc == BAKRON_SUCCESS; ++k) {
+        hipEvent_t e = nullptr;
         if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) rc = BAKRON_ERR_HIP;
-    if (!sa || !sb) rc = BAKRON_ERR_HIP;
+        else ev.push_back(e);
+    }
     if (rc == BAKRON_SUCCESS) {
-        const bool lead_a = bk::factor_lead(n) > 0, lead_b = bk::factor_lead(m) > 0;
-        bk::SolveWait wait;
-        wait.lead[0] = lead_a ? ev[1] : ev[3];
-        wait.lead[1] = lead_b ? ev[2] : ev[4];
-        wait.full[0] = ev[3];
-        wait.full[1] = ev[4];
-        wait.lead_n = bk::factor_lead(n);
-        wait.lead_m = bk::factor_lead(m);
+        wait.full[0] = ev[1];
+        wait.full[1] = ev[2];
+        int next = 3;
+        for (int f = 0; f < 2; ++f)
+            for (int k = 0; k < wait.lead[f].count; ++k) wait.lead[f].ev[k] = ev[next++];
         if (hipEventRecord(ev[0], stream) != hipSuccess || hipStreamWaitEvent(sa, ev[0], 0) != hipSuccess ||
             hipStreamWaitEvent(sb, ev[0], 0) != hipSuccess ||
-            bk::factor_enqueue(A, n, damp_frac, L_A, P_A, info_A, ws_a, sa, nullptr, ev[1]) ||
-            hipEventRecord(ev[3], sa) != hipSuccess ||
-            bk::factor_enqueue(B, m, damp_frac, L_B, P_B, info_B, ws_b, sb, nullptr, ev[2]) ||
-            hipEventRecord(ev[4], sb) != hipSuccess ||
+            bk::factor_enqueue(A, n, damp_frac, L_A, P_A, info_A, ws_a, sa, nullptr, &wait.lead[0]) ||
+            hipEventRecord(ev[1], sa) != hipSuccess ||
+            bk::factor_enqueue(B, m, damp_frac, L_B, P_B, info_B, ws_b, sb, nullptr, &wait.lead[1]) ||
+            hipEventRecord(ev[2], sb) != hipSuccess ||
             bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective, ws_s,
                               stream, nullptr, true, &wait))
             rc = BAKRON_ERR_HIP;

@@ -21,9 +21,10 @@
 // receives L.  Both are n x n with pitch ld.  The temporary T (n2 x n1) lives
 // in the workspace.  A final pass scales Li's columns by diag(L) (giving P)
 // and writes zeros above both diagonals.  When n is a multiple of 64 (and
-// above 128), the top level runs that pass on its leading block as soon as
-// the block is final, and forms P21 from it directly (see factor_rec), so a
-// solve can start on the leading block while the last two GEMMs run.
+// above 128), the nodes of the leading spine (the blocks [0, nsz)^2) run that
+// pass on their blocks as soon as these are final, and form their P21 from
+// the finished P11 directly (see factor_rec), so a solve can start on the
+// leading blocks while the rest of the factorisation runs.
 #include <algorithm>
 #include <mutex>
 
@@ -731,10 +732,19 @@ struct FactorRun {
     int32_t* info;
     hipStream_t s;
     Prof* prof;
-    bool early;        // the top level finishes its leading block before the last two GEMMs
-    hipEvent_t lead;   // nullable: recorded once that leading block is final
+    bool early;                // the leading spine finishes its blocks early (see factor_rec)
+    const FactorLeads* leads;  // nullable: events of the leading blocks, recorded as they become final
     int64_t n;
 };
+
+// Records the event of the leading block [0, size)^2 (size below n).
+int record_lead(const FactorRun& R, int64_t size)
+{
+    if (!R.leads) return 0;
+    for (int k = 0; k < R.leads->count; ++k)
+        if (R.leads->size[k] == size) return hipEventRecord(R.leads->ev[k], R.s) == hipSuccess ? 0 : -1;
+    return 0;
+}
 
 // The finish pass over rows [i0, i1) and columns [j0, j1) (multiples of 4):
 // P = Li diag(L) below the diagonal, zeros above both diagonals.
@@ -752,13 +762,26 @@ inline double tri(double k) { return k * (k + 1.0) / 2.0; }
 
 int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
 
+// On the leading spine (o == 0, with `early`) every node ends with its
+// whole block [0, nsz)^2 finished (P = Li diag(L), zeros above both
+// diagonals) and records that block's event: the base block is finished
+// after its factorisation; an inner node's two last products use the
+// finished P11 and give P21 directly, T' = L21 P11 and
+// P21 = Li21 diag(L11) = -Li22 L21 Li11 diag(L11) = -Li22 T', and it then
+// finishes its trailing block.  Off the spine the blocks stay unscaled (the
+// products of the levels above read Li).
 int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
 {
+    const bool spine = R.early && o == 0;
     if (nsz <= 2 * kTile) {
         // factor (b^3 / 3 multiply-adds) and inverse (b^3 / 6) of the block
         const double b = (double)nsz;
         launch(R.prof, KK_F_DIAG, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
                R.Lbuf, R.Pbuf, R.ld, o, (int)nsz, R.info);
+        if (spine) {
+            enqueue_finish(R, 0, nsz, 0, nsz);
+            if (launch_ok() || record_lead(R, nsz)) return -1;
+        }
         return launch_ok();
     }
     const int64_t nt = nsz / kTile;
@@ -789,14 +812,6 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, o1, n1)) return -1;
-    if (R.early && o == 0 && nsz == R.ld) {
-        // The leading block is final: finish it now (P11 = Li11 diag(L11)),
-        // so that a solve waiting on `lead` can start on it.  The two GEMMs
-        // below then give P21 directly: with T' = L21 P11,
-        // P21 = Li21 diag(L11) = -Li22 L21 Li11 diag(L11) = -Li22 T'.
-        enqueue_finish(R, 0, n1, 0, n1);
-        if (launch_ok() || (R.lead && hipEventRecord(R.lead, R.s) != hipSuccess)) return -1;
-    }
     {
         const double fr = 2.0 * d2 * tri(d1), br = 4.0 * (2.0 * d2 * d1 + tri(d1));
         const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
@@ -805,7 +820,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
                    R.ld, o1, o2, n1, n2);
             launch(R.prof, KK_F_LEFT_T, fl, bl, k_f_tile<3>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
                    R.ld, o1, o2, n1, n2);
-        } else if (R.lead && o == 0 && nsz == R.ld) {
+        } else if (R.leads && o == 0 && nsz == R.ld) {
             static std::once_flag attrs;
             std::call_once(attrs, [] {
                 (void)hipFuncSetAttribute((const void*)k_f_right_lead, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -825,6 +840,11 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
                    n1, n2);
         }
     }
+    if (spine) {   // the trailing block, and the zeros right of the leading block (P21 is done)
+        enqueue_finish(R, n1, nsz, n1, nsz);
+        enqueue_finish(R, 0, n1, n1, nsz);
+        if (launch_ok() || (nsz < R.ld && record_lead(R, nsz))) return -1;
+    }
     return launch_ok();
 }
 
@@ -836,14 +856,21 @@ size_t factor_workspace_bytes(int64_t n)
     return plan_factor(n).total;
 }
 
-int64_t factor_lead(int64_t n)
+int factor_leads(int64_t n, int64_t* sizes)
 {
     if (n <= 2 * kTile || n % kTile != 0) return 0;
-    return kTile * (n / kTile / 2);
+    int count = 0;
+    int64_t spine[kMaxLeads];
+    for (int64_t sz = n; sz > 2 * kTile && count < kMaxLeads;) {
+        sz = kTile * (sz / kTile / 2);
+        spine[count++] = sz;
+    }
+    for (int k = 0; k < count; ++k) sizes[k] = spine[count - 1 - k];   // smallest first
+    return count;
 }
 
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
-                   void* ws, hipStream_t s, Prof* prof, hipEvent_t lead)
+                   void* ws, hipStream_t s, Prof* prof, const FactorLeads* leads)
 {
     const FactorPlan p = plan_factor(n);
     char* w = static_cast<char*>(ws);
@@ -854,8 +881,9 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     R.info = info;
     R.s = s;
     R.prof = prof;
-    R.early = factor_lead(n) > 0;
-    R.lead = R.early ? lead : nullptr;
+    int64_t sizes[kMaxLeads];
+    R.early = factor_leads(n, sizes) > 0;
+    R.leads = R.early ? leads : nullptr;
     R.n = n;
     R.Lbuf = p.padded ? reinterpret_cast<float*>(w + p.off_L) : L;
     R.Pbuf = p.padded ? reinterpret_cast<float*>(w + p.off_P) : P;
@@ -871,11 +899,7 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     }
     if (launch_ok()) return -1;
     if (factor_rec(R, 0, p.Np)) return -1;
-    if (R.early) {   // the trailing block, and the zeros right of the leading block (P21 is done)
-        const int64_t n1 = factor_lead(n);
-        enqueue_finish(R, n1, p.Np, n1, p.Np);
-        enqueue_finish(R, 0, n1, n1, p.Np);
-    } else {
+    if (!R.early) {   // (on the early path every block of the spine has been finished)
         dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 256));
         launch(prof, KK_F_FINISH, dn * dn / 2.0, 4.0 * (2.0 * tri(dN) + 2.0 * dn * dn), k_f_finish, g, dim3(256),
                s, R.Lbuf, R.Pbuf, p.Np, (int64_t)0, p.Np, (int64_t)0, p.Np, n, p.padded ? L : (float*)nullptr,

@@ -103,23 +103,32 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 // Factor (factor.hip)
 size_t factor_workspace_bytes(int64_t n);
-// With `lead`, the event is recorded on `stream` as soon as rows and columns
-// [0, factor_lead(n)) of L and P are final (when factor_lead(n) > 0).
-int64_t factor_lead(int64_t n);
+// Leading blocks: when n is a multiple of 64 above 128, the factorisation
+// finishes the blocks [0, size)^2 of L and P one after the other, for the
+// sizes that factor_leads(n, sizes) lists (smallest first; none otherwise).
+// With `leads`, event ev[k] is recorded on `stream` once block size[k] is
+// final (events the caller created; sizes not listed are not recorded).
+constexpr int kMaxLeads = 16;
+struct FactorLeads {
+    int count;
+    int64_t size[kMaxLeads];
+    hipEvent_t ev[kMaxLeads];
+};
+int factor_leads(int64_t n, int64_t* sizes);
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
-                   void* ws, hipStream_t stream, Prof* prof, hipEvent_t lead = nullptr);
+                   void* ws, hipStream_t stream, Prof* prof, const FactorLeads* leads = nullptr);
 
 // Solve (solve.hip).  With `split`, the far parts of the upper nodes run on
 // library-owned streams, ordered against `stream` by events.
 size_t solve_workspace_bytes(int64_t m, int64_t n, bool split = true);
-// A solve enqueued while its factors are still being computed: rows and
-// columns [0, lead_n) of L_A, P_A and [0, lead_m) of L_B, P_B are final once
-// the events `lead` complete, everything once the events `full` complete
-// (any of them may be null: nothing to wait for).  The solve waits for each
-// just before its first work that needs it.
+// A solve enqueued while its factors are still being computed: for factor
+// f (0: A, whose rows and columns are W's columns; 1: B, W's rows), the
+// leading block [0, lead[f].size[k])^2 of L and P is final once
+// lead[f].ev[k] completes, and everything once full[f] completes.  The solve
+// waits for each event just before its first work that needs that block.
 struct SolveWait {
-    hipEvent_t lead[2], full[2];
-    int64_t lead_m, lead_n;
+    FactorLeads lead[2];
+    hipEvent_t full[2];
 };
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,

@@ -40,6 +40,8 @@
 //        multiple of 64.
 //   sched  block lists of the propagation launches (k_sched)
 // Padding entries are forced to zero error, so they never touch real ones.
+#include <limits.h>
+
 #include <algorithm>
 #include <mutex>
 #include <vector>
@@ -953,23 +955,29 @@ struct SolveRun {
     std::vector<hipEvent_t> events;
     bool failed;
     Prof* prof;
-    // Factors still being finished (SolveWait): `lead` is waited for on s
-    // before the first work that reads them, `full` before the first work on
-    // a tile anti-diagonal >= Kq.
-    hipEvent_t lead[2], full[2];
-    int Kq;
-    bool lead_pending, full_pending;
+    // Factors still being computed (SolveWait), per factor f: event k of
+    // ev[f] makes tile rows / columns below Kq[f][k] final (the last one,
+    // the whole factor, has Kq = INT_MAX); waited[f] is the last one waited for.
+    int nwait[2] = {0, 0};
+    int Kq[2][kMaxLeads + 1];
+    hipEvent_t ev[2][kMaxLeads + 1];
+    int waited[2] = {-1, -1};
 };
 
-// Before work that reads the factors on tile anti-diagonals up to khi.
+// Before work that reads the factors on tile anti-diagonals up to khi (so
+// on tile rows and columns up to khi): wait for the first event of each
+// factor whose block reaches beyond khi, unless a later one was waited for.
+// Each factor's events complete in order (one stream), so one wait covers
+// the earlier ones.
 void ensure_full(SolveRun& R, int khi)
 {
-    const bool full = R.full_pending && khi >= R.Kq;
-    if (!full && !R.lead_pending) return;
-    R.lead_pending = false;   // (each full event follows its lead event on the factor's stream)
-    if (full) R.full_pending = false;
-    for (hipEvent_t e : full ? R.full : R.lead)
-        if (e && hipStreamWaitEvent(R.s, e, 0) != hipSuccess) R.failed = true;
+    for (int f = 0; f < 2; ++f) {
+        int k = 0;
+        while (k < R.nwait[f] && R.Kq[f][k] <= khi) ++k;
+        if (k >= R.nwait[f] || k <= R.waited[f]) continue;
+        R.waited[f] = k;
+        if (hipStreamWaitEvent(R.s, R.ev[f][k], 0) != hipSuccess) R.failed = true;
+    }
 }
 
 hipEvent_t new_event(SolveRun& R)
@@ -1235,15 +1243,21 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.prof = prof;
     R.s = s;
     R.failed = false;
-    for (int k = 0; k < 2; ++k) {
-        R.lead[k] = wait ? wait->lead[k] : nullptr;
-        R.full[k] = wait ? wait->full[k] : nullptr;
+    if (wait) {
+        // The padded copies of P_A and P_B need the whole factors.
+        const bool whole = p.pad_a || p.pad_b;
+        for (int f = 0; f < 2; ++f) {
+            int k = 0;
+            for (int j = 0; !whole && j < wait->lead[f].count; ++j) {
+                R.Kq[f][k] = (int)(wait->lead[f].size[j] / kTile);
+                R.ev[f][k++] = wait->lead[f].ev[j];
+            }
+            R.Kq[f][k] = INT_MAX;
+            R.ev[f][k++] = wait->full[f];
+            R.nwait[f] = k;
+        }
+        if (whole) ensure_full(R, 0);
     }
-    R.lead_pending = R.full_pending = wait != nullptr;
-    // Tiles on anti-diagonals K < Kq have rows below lead_m and columns below
-    // lead_n; the padded copies of P_A and P_B need the whole factors.
-    R.Kq = (!wait || p.pad_a || p.pad_b) ? 0 : (int)(std::min(wait->lead_m, wait->lead_n) / kTile);
-    if (R.Kq == 0) ensure_full(R, 0);
     for (int d = 0; d < kSplitDepth; ++d) {
         R.Ysplit[d] = d < p.sg.split_depth ? reinterpret_cast<float*>(w + p.off_ysplit[d]) : nullptr;
         R.far[d] = d < p.sg.split_depth ? side_stream(s, d) : nullptr;
@@ -1320,7 +1334,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     SpineWaits none;
     for (hipEvent_t& e : none.e) e = nullptr;
     solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, none);
-    ensure_full(R, R.Mt + R.Nt);   // s is ordered after the factors in any case
+    ensure_full(R, INT_MAX - 1);   // s is ordered after the factors in any case
     // every far part is waited for by the right child of its node, so all
     // of them are ordered before the rest of the work on s
     for (hipEvent_t e : R.events) (void)hipEventDestroy(e);
