@@ -170,11 +170,12 @@ size_t bakron_quantize_workspace_bytes(int64_t m, int64_t n);
  * those of the three calls made one after the other.
  *
  * The two factorisations run on library-owned streams forked from `stream`
- * (as in bakron_solve); the solve starts on `stream` as soon as the leading
- * block of each factor is final (rows and columns below the top split of
- * the factorisation, when the dimension is a multiple of 64 and above 128)
- * and waits for the rest before its first tile outside those blocks.  All
- * outputs are complete for later work on `stream`.
+ * (as in bakron_solve).  When a dimension is a multiple of 64 and above 128,
+ * its factorisation completes leading blocks [0, s)^2 of L and P one after
+ * the other (s = the splits of its recursion on the leading half), and the
+ * solve, on `stream`, runs each of its kernels as soon as the blocks that
+ * hold its tiles are complete.  All outputs are complete for later work on
+ * `stream`.
  *
  * W, m, n, scale, zero, maxq, V, codes, err, objective: as in bakron_solve.
  * A, B       [in]  n x n and m x m, as in bakron_factor.  Not modified.
