@@ -134,7 +134,7 @@ struct Direct {
     static __device__ __forceinline__ void issue(const float* __restrict__ p, int64_t ld, int rlim, int k0, float* s)
     {
         const int lane = threadIdx.x & 63;
-        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);   // (within a 4-wave group)
 #pragma unroll
         for (int i = 0; i < PER_WAVE; ++i) {
             const int q = wave + 4 * i;
@@ -252,6 +252,59 @@ __device__ __forceinline__ void block_gemm(const float* __restrict__ A, int64_t 
     __syncthreads();
 }
 
+// block_gemm for one half of a 512-thread workgroup whose two 4-wave halves
+// work on two blocks at once (threads 0 - 255 and 256 - 511, each with its
+// own `lds`).  Every barrier is shared: both halves run nmax chunk steps,
+// nmax the larger of their chunk counts, and a half with fewer chunks waits
+// out the rest.  The MFMAs of a block are those of block_gemm, in the same
+// order.
+template <int WM, int WN, int ALAY, int BLAY>
+__device__ __forceinline__ void dual_block_gemm(const float* __restrict__ A, int64_t lda, int alim,
+                                                const float* __restrict__ B, int64_t ldb, int blim,
+                                                int k0, int k1, int nmax, float* lds, Acc& acc)
+{
+    typedef Gemm<WM, WN, ALAY, BLAY> G;
+    typedef typename G::OA OA;
+    typedef typename G::OB OB;
+    const int lane = threadIdx.x & 63;
+    const int wave = (threadIdx.x >> 6) & 3;
+    const int wy = wave / WN, wx = wave % WN;
+    const int ml = lane & 31;
+    const int nchunk = k1 > k0 ? (k1 - k0) / kBK : 0;
+    if (nchunk > 0) {
+        OA::issue(A, lda, alim, k0, lds);
+        OB::issue(B, ldb, blim, k0, lds + OA::FLOATS);
+    }
+    for (int c = 0; c < nmax; ++c) {
+        wait_direct_loads();
+        __syncthreads();
+        if (c + 1 < nchunk) {
+            float* nb = lds + ((c + 1) & 1) * G::BUF;
+            OA::issue(A, lda, alim, k0 + (c + 1) * kBK, nb);
+            OB::issue(B, ldb, blim, k0 + (c + 1) * kBK, nb + OA::FLOATS);
+        }
+        if (c < nchunk) {
+            const float* sa = lds + (c & 1) * G::BUF;
+            const float* sb = sa + OA::FLOATS;
+#pragma unroll
+            for (int kc = 0; kc < kBK; kc += 8) {
+                const f32x4 a0 = OA::frag(sa, wy * 64 + ml, kc);
+                const f32x4 a1 = OA::frag(sa, wy * 64 + 32 + ml, kc);
+                const f32x4 b0 = OB::frag(sb, wx * 64 + ml, kc);
+                const f32x4 b1 = OB::frag(sb, wx * 64 + 32 + ml, kc);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc.c[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[q], b0[q], acc.c[0][0], 0, 0, 0);
+                    acc.c[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0[q], b1[q], acc.c[0][1], 0, 0, 0);
+                    acc.c[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], b0[q], acc.c[1][0], 0, 0, 0);
+                    acc.c[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1[q], b1[q], acc.c[1][1], 0, 0, 0);
+                }
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // Row / column (within the block) of accumulator element r of tile (mi, ni)
 // for this lane: the v_mfma_f32_32x32x2f32 output layout.
 __device__ __forceinline__ int acc_row(int mi, int r)
@@ -273,7 +326,7 @@ template <int WM, int WN>
 __device__ __forceinline__ void block_store(float* __restrict__ C, int64_t ldc, int rlim, int clim,
                                             float alpha, float beta, const Acc& acc, int diag = kNoDiag)
 {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane((threadIdx.x >> 6) & 3);   // (within a 4-wave group)
     const int wy = wave / WN, wx = wave % WN;
     // rlim and clim are multiples of 64, so a wave's 64 x 64 sub-block is
     // either inside or outside: one wave-uniform test.

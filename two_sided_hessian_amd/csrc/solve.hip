@@ -606,8 +606,10 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
 // A launch covers `count` list entries with gridDim.x <= count workgroups,
 // each taking entries blockIdx.x, blockIdx.x + gridDim.x, ... (a far part
 // runs on a capped grid, next to the leaves; see enqueue_prop).  Every
-// kernel has a `_far` twin with the same body, used for the far parts, so
-// that timings of the two kinds of launch are told apart.
+// kernel has a `_far` twin, used for the far parts, so that timings of the
+// two kinds of launch are told apart: the same body, except for this stage's
+// block kernel, whose far twin takes two blocks per workgroup (same blocks,
+// same results).
 __device__ __forceinline__ void prop_rows_body(const float* __restrict__ E, const float* __restrict__ PA,
                                                float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                int K0, int mid, int y0, int y1, int Mt, int Nt,
@@ -631,17 +633,64 @@ __device__ __forceinline__ void prop_rows_body(const float* __restrict__ E, cons
         block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
     }
 }
+// One stage-1 list entry's geometry: tile row I, target columns j0 .. jh,
+// K range [kb, ke); false when the entry has no work.
+struct RowEntry {
+    int I, j0, jh, kb, ke;
+    __device__ __forceinline__ bool load(const uint32_t* __restrict__ list, unsigned q, unsigned count, int K0,
+                                         int mid, int y0, int y1, int Mt, int Nt)
+    {
+        if (q >= count) return false;
+        const uint32_t e = list[xcd_entry(q, count)];
+        I = (int)(e >> 16);
+        const int b = (int)(e & 0xffffu);
+        if (I < rows_lo(K0, Nt) || I > rows_hi(mid, Mt)) return false;
+        const RowSpan s(I, K0, mid, y0, y1, Nt);
+        j0 = s.tl + 4 * b;
+        if (j0 > s.th) return false;
+        jh = min(s.th, j0 + 3);
+        kb = 64 * s.sl;
+        ke = 64 * (min(s.sh, jh) + 1);
+        return true;
+    }
+};
+
+// A far part's stage 1 (the far twin of k_prop_rows, same blocks and
+// results) on workgroups of 512 threads: the two 4-wave halves
+// take list entries 2 p and 2 p + 1 of pair p = blockIdx.x, + gridDim.x, ...
+// (neighbours in the longest-first list, so their K extents are close) and
+// share each chunk barrier (dual_block_gemm).  Two 80 KB halves fill a CU's
+// LDS, so no leaf runs beside one, and a CU keeps two blocks in flight.
+__global__ __launch_bounds__(512) void k_prop_rows_far(const float* __restrict__ E, const float* __restrict__ PA,
+                                                        float* __restrict__ Y, int64_t ldw, int64_t lda,
+                                                        int K0, int mid, int y0, int y1, int Mt, int Nt,
+                                                        const uint32_t* __restrict__ list, unsigned count)
+{
+    __shared__ __align__(16) float lds[2 * RowBlk::LDS_FLOATS];
+    const int h = threadIdx.x >> 8;
+    for (unsigned pr = blockIdx.x; 2 * pr < count; pr += gridDim.x) {
+        int nother;
+        {
+            RowEntry o;
+            nother = o.load(list, 2 * pr + (1 - h), count, K0, mid, y0, y1, Mt, Nt) ? (o.ke - o.kb) / kBK : 0;
+        }
+        RowEntry c;
+        const bool ok = c.load(list, 2 * pr + h, count, K0, mid, y0, y1, Mt, Nt);
+        const int nmax = max(ok ? (c.ke - c.kb) / kBK : 0, nother);
+        const int64_t r0 = (int64_t)(ok ? c.I : 0) * 64, cc = (int64_t)(ok ? c.j0 : 0) * 64;
+        const int cols = ok ? 64 * (c.jh - c.j0 + 1) : 64;
+        Acc acc;
+        acc_zero(acc);
+        dual_block_gemm<1, 4, RowK, RowK>(E + r0 * ldw, ldw, 64, PA + cc * lda, lda, cols, ok ? c.kb : 0,
+                                          ok ? c.ke : 0, nmax, lds + h * RowBlk::LDS_FLOATS, acc);
+        if (ok) block_store<1, 4>(Y + r0 * ldw + cc, ldw, 64, cols, 1.f, 0.f, acc);
+    }
+}
+
 __global__ __launch_bounds__(256, 2) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
                                                    float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                    int K0, int mid, int y0, int y1, int Mt, int Nt,
                                                    const uint32_t* __restrict__ list, unsigned count)
-{
-    prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count);
-}
-__global__ __launch_bounds__(256, 2) void k_prop_rows_far(const float* __restrict__ E, const float* __restrict__ PA,
-                                                       float* __restrict__ Y, int64_t ldw, int64_t lda,
-                                                       int K0, int mid, int y0, int y1, int Mt, int Nt,
-                                                       const uint32_t* __restrict__ list, unsigned count)
 {
     prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count);
 }
@@ -1022,7 +1071,9 @@ constexpr int64_t kBlockLaunchMin = BAKRON_BLOCK_LAUNCH_MIN;
 // which are latency-bound: a leaf sharing a CU with a propagation workgroup
 // runs about three times slower.  So a far launch takes at most kFarGrid
 // workgroups (looping over its blocks) and reserves enough extra LDS that no
-// leaf fits next to one of them: leaves then run on CUs of their own.
+// leaf fits next to one of them: leaves then run on CUs of their own.  (The
+// far stage-1 block kernel needs no reserve: its 512-thread workgroups work
+// on two blocks at once and fill a CU's LDS by themselves.)
 #ifndef BAKRON_FAR_GRID
 #define BAKRON_FAR_GRID 192
 #endif
@@ -1078,11 +1129,14 @@ void enqueue_stage1(SolveRun& R, int K0, int mid, int y0, int y1, const uint32_t
     }
     if (R.prof)   // distinct P_A blocks
         for (uint8_t u : pa_used) by += u ? kTileB : 0.0;
-    if (blocks >= (far ? kFarBlockMin : kBlockLaunchMin)) {
+    if (far && blocks >= kFarBlockMin) {
         const unsigned n = (unsigned)blocks;
-        launch_shm(R.prof, far ? KK_PROP_ROWS_FAR : KK_PROP_ROWS, fl, by, far ? k_prop_rows_far : k_prop_rows, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
-                   far ? kFarPadBlock : 0, st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid,
-                   y0, y1, Mt, Nt, list, n);
+        launch(R.prof, KK_PROP_ROWS_FAR, fl, by, k_prop_rows_far, dim3(std::min((n + 1) / 2, kFarGrid)), dim3(512),
+               st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid, y0, y1, Mt, Nt, list, n);
+    } else if (blocks >= kBlockLaunchMin) {
+        const unsigned n = (unsigned)blocks;
+        launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3(n), dim3(256), st, (const float*)R.leaf.E, R.leaf.PA,
+               Y, R.leaf.ldw, R.leaf.lda, K0, mid, y0, y1, Mt, Nt, list, n);
     } else if (blocks > 0) {
         const unsigned n = (unsigned)span * (unsigned)(I_hi - I_lo + 1);
         launch_shm(R.prof, far ? KK_PROP_ROWS_T_FAR : KK_PROP_ROWS_T, fl, by, far ? k_prop_rows_t_far : k_prop_rows_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
@@ -1319,8 +1373,6 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     if (p.sg.split_depth > 0) {
         static std::once_flag attrs;
         std::call_once(attrs, [] {
-            (void)hipFuncSetAttribute((const void*)k_prop_rows_far, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)kFarPadBlock);
             (void)hipFuncSetAttribute((const void*)k_prop_cols_far, hipFuncAttributeMaxDynamicSharedMemorySize,
                                       (int)kFarPadBlock);
             if (kFarPadTile) {
