@@ -603,9 +603,14 @@ __global__ __launch_bounds__(256) void k_f_left_lead(const float* __restrict__ T
     }
 }
 
-// The same four products with one 64 x 64 output tile per workgroup (one
-// 32 x 32 quadrant per wave) for the levels whose 128 x 128 grids are too
-// small to fill the GPU.  MODE: 0 panel, 1 syrk, 2 right, 3 left.
+// The products with one 64 x 64 output tile per workgroup (one 32 x 32
+// quadrant per wave) for the levels whose 128 x 128 grids are too small to
+// fill the GPU.  There the inverse block is grouped as
+// Li21 = (-Li22 L21) Li11: U = -Li22 L21 needs only the panel, so it shares
+// one launch with the SYRK, and one product U Li11 is left for after the
+// leading block's factorisation.  MODE: 0 panel; 1 syrk; 2 Li21 = U Li11;
+// 3 syrk (first tb (tb + 1) / 2 workgroups) and U = -Li22 L21.  T is U
+// (n2 x n1, leading dimension n1).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
                                                 float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
@@ -613,20 +618,27 @@ __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float*
 {
     __shared__ __align__(16) float lds[kLds64];
     int r0, c0;
-    if (MODE == 1) {   // linear index -> lower-triangular tile (br >= bc)
+    bool syrk = (MODE == 1);
+    if (MODE == 3) {
+        const int tb = n1 / 64;
+        const int q = (int)blockIdx.x - tb * (tb + 1) / 2;
+        syrk = q < 0;
+        if (!syrk) {   // U tiles, heaviest (largest K, last row tiles) first
+            r0 = 64 * (n2 / 64 - 1 - q / tb);
+            c0 = 64 * (q % tb);
+        }
+    }
+    if (syrk) {   // linear index -> lower-triangular tile (br >= bc)
         const int q = blockIdx.x;
         int br = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
         while ((br + 1) * (br + 2) / 2 <= q) ++br;
         while (br * (br + 1) / 2 > q) --br;
         r0 = 64 * br;
         c0 = 64 * (q - br * (br + 1) / 2);
-    } else if (MODE == 3) {   // heaviest (largest K) first
-        r0 = 64 * (int)(gridDim.y - 1 - blockIdx.y);
-        c0 = 64 * (int)blockIdx.x;
     } else if (MODE == 2) {   // rows along x: the longest column tiles first
         r0 = 64 * (int)blockIdx.x;
         c0 = 64 * (int)blockIdx.y;
-    } else {
+    } else if (MODE == 0) {
         r0 = 64 * (int)blockIdx.y;
         c0 = 64 * (int)blockIdx.x;
     }
@@ -638,15 +650,15 @@ __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float*
     if (MODE == 0) {          // L21 = Li22^T A21, K in [r0, n2)
         block_gemm64<KRow, KRow>(Pbuf + o2 * ld + o2 + r0, ld, Pbuf + o2 * ld + o1 + c0, ld, r0, n2, lds, acc);
         wave_store32(Lbuf + (o2 + r0 + qr) * ld + o1 + c0 + qc, ld, 1.f, 0.f, acc);
-    } else if (MODE == 1) {   // A11 -= L21^T L21, lower part
+    } else if (MODE == 2) {   // Li21 = U Li11, K in [c0, n1)
+        block_gemm64<RowK, KRow>(T + (int64_t)r0 * n1, n1, Pbuf + o1 * ld + o1 + c0, ld, c0, n1, lds, acc);
+        wave_store32(Pbuf + (o2 + r0 + qr) * ld + o1 + c0 + qc, ld, 1.f, 0.f, acc);
+    } else if (syrk) {        // A11 -= L21^T L21, lower part
         block_gemm64<KRow, KRow>(Lbuf + o2 * ld + o1 + r0, ld, Lbuf + o2 * ld + o1 + c0, ld, 0, n2, lds, acc);
         wave_store32(Pbuf + (o1 + r0 + qr) * ld + o1 + c0 + qc, ld, -1.f, 1.f, acc, (c0 + qc) - (r0 + qr));
-    } else if (MODE == 2) {   // T = L21 Li11, K in [c0, n1)
-        block_gemm64<RowK, KRow>(Lbuf + (o2 + r0) * ld + o1, ld, Pbuf + o1 * ld + o1 + c0, ld, c0, n1, lds, acc);
-        wave_store32(T + (int64_t)(r0 + qr) * n1 + c0 + qc, n1, 1.f, 0.f, acc);
-    } else {                  // Li21 = -Li22 T, K in [0, r0 + 64)
-        block_gemm64<RowK, KRow>(Pbuf + (o2 + r0) * ld + o2, ld, T + c0, n1, 0, r0 + 64, lds, acc);
-        wave_store32(Pbuf + (o2 + r0 + qr) * ld + o1 + c0 + qc, ld, -1.f, 0.f, acc);
+    } else {                  // U = -Li22 L21, K in [0, r0 + 64)
+        block_gemm64<RowK, KRow>(Pbuf + (o2 + r0) * ld + o2, ld, Lbuf + o2 * ld + o1 + c0, ld, 0, r0 + 64, lds, acc);
+        wave_store32(T + (int64_t)(r0 + qr) * n1 + c0 + qc, n1, -1.f, 0.f, acc);
     }
 }
 
@@ -694,11 +706,25 @@ __global__ __launch_bounds__(256) void k_f_finish(float* __restrict__ Lbuf, floa
 
 namespace {
 
+// Depths of the recursion: sizes halve from at most kMaxDim down to 2 kTile.
+constexpr int kFactorDepths = 16;
+
 struct FactorPlan {
     int64_t n, Np;
     bool padded;
     size_t off_mean, off_T, off_L, off_P, total;
+    int64_t tbase[kFactorDepths];   // offset (floats) of each depth's n2 x n1 product buffer within T
 };
+
+// Largest n1 n2 of the nodes at each depth (the split of factor_rec).
+void depth_products(int64_t nsz, int d, int64_t* most)
+{
+    if (nsz <= 2 * kTile) return;
+    const int64_t nt = nsz / kTile, n1 = kTile * (nt / 2), n2 = nsz - n1;
+    most[d] = std::max(most[d], n1 * n2);
+    depth_products(n2, d + 1, most);
+    if (n1 != n2) depth_products(n1, d + 1, most);
+}
 
 FactorPlan plan_factor(int64_t n)
 {
@@ -706,13 +732,21 @@ FactorPlan plan_factor(int64_t n)
     p.n = n;
     p.Np = ceil_div(n, kTile) * kTile;
     p.padded = (n % kTile) != 0;
-    const int64_t nt = p.Np / kTile;
-    const int64_t n1 = kTile * (nt / 2), n2 = p.Np - n1;
+    // a node's n2 x n1 product (T, or U = -Li22 L21) lives from before its
+    // leading block's factorisation to its last product, so every depth has
+    // its own buffer: an ancestor's stays intact under its descendants
+    int64_t most[kFactorDepths] = {0};
+    depth_products(p.Np, 0, most);
+    int64_t tfloats = 0;
+    for (int d = 0; d < kFactorDepths; ++d) {
+        p.tbase[d] = tfloats;
+        tfloats += most[d];
+    }
     size_t off = 0;
     p.off_mean = off;
     off += kAlign;
     p.off_T = off;
-    off = align_up(off + sizeof(float) * (size_t)(n1 * n2));
+    off = align_up(off + sizeof(float) * (size_t)tfloats);
     p.off_L = p.off_P = 0;
     if (p.padded) {
         p.off_L = off;
@@ -727,7 +761,8 @@ FactorPlan plan_factor(int64_t n)
 struct FactorRun {
     float* Lbuf;
     float* Pbuf;
-    float* T;
+    float* T;                  // the depths' product buffers (tbase)
+    const int64_t* tbase;
     int64_t ld;
     int32_t* info;
     hipStream_t s;
@@ -770,7 +805,7 @@ int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
 // P21 = Li21 diag(L11) = -Li22 L21 Li11 diag(L11) = -Li22 T', and it then
 // finishes its trailing block.  Off the spine the blocks stay unscaled (the
 // products of the levels above read Li).
-int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
+int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
 {
     const bool spine = R.early && o == 0;
     if (nsz <= 2 * kTile) {
@@ -789,7 +824,9 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     const int n2 = (int)(nsz - n1);
     const int64_t o1 = o, o2 = o + n1;
     const double d1 = n1, d2 = n2;
-    if (factor_rec(R, o2, n2)) return -1;
+    if (depth >= kFactorDepths) return -1;
+    float* const T = R.T + R.tbase[depth];
+    if (factor_rec(R, o2, n2, depth + 1)) return -1;
     // 128 x 128 blocks while they fill the GPU, else 64 x 64 tiles
     const bool tiles = ceil_div(n1, FBN) * ceil_div(n2, FBM) < kFactorBlockMin;
     const dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
@@ -797,28 +834,34 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
     const double fl_panel = 2.0 * d1 * tri(d2), by_panel = 4.0 * (tri(d2) + 2.0 * d2 * d1);
     if (tiles)
         launch(R.prof, KK_F_PANEL_T, fl_panel, by_panel, k_f_tile<0>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf,
-               R.T, R.ld, o1, o2, n1, n2);
+               T, R.ld, o1, o2, n1, n2);
     else
         launch(R.prof, KK_F_PANEL, fl_panel, by_panel, k_f_panel, g, dim3(256), R.s, R.Pbuf, R.Lbuf, R.ld, o1, o2,
                n1, n2);
     {
         // SYRK on 64 x 64 tiles at every level: its K extent is uniform, so
         // the finer grid only helps (a triangle of 128-blocks quantizes badly
-        // over the CUs, e.g. 528 blocks at n1 = 4096).
+        // over the CUs, e.g. 528 blocks at n1 = 4096).  On the tile levels
+        // the same launch forms U = -Li22 L21.
         const double fl = 2.0 * d2 * tri(d1), by = 4.0 * (d2 * d1 + 2.0 * tri(d1));
-        const int64_t tb = n1 / kTile;
-        launch(R.prof, KK_F_SYRK_T, fl, by, k_f_tile<1>, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), R.s, R.Lbuf,
-               R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
+        const int64_t tb = n1 / kTile, nsyrk = tb * (tb + 1) / 2;
+        if (tiles) {
+            const double fu = 2.0 * d1 * tri(d2), bu = 4.0 * (2.0 * d2 * d1 + tri(d2));
+            launch(R.prof, KK_F_LEFT_T, fl + fu, by + bu, k_f_tile<3>, dim3((unsigned)(nsyrk + gt.x * gt.y)),
+                   dim3(256), R.s, R.Lbuf, R.Pbuf, T, R.ld, o1, o2, n1, n2);
+        } else {
+            launch(R.prof, KK_F_SYRK_T, fl, by, k_f_tile<1>, dim3((unsigned)nsyrk), dim3(256), R.s, R.Lbuf, R.Pbuf,
+                   T, R.ld, o1, o2, n1, n2);
+        }
     }
     if (launch_ok()) return -1;
-    if (factor_rec(R, o1, n1)) return -1;
+    if (factor_rec(R, o1, n1, depth + 1)) return -1;
     {
         const double fr = 2.0 * d2 * tri(d1), br = 4.0 * (2.0 * d2 * d1 + tri(d1));
         const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
         if (tiles) {
-            launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
-                   R.ld, o1, o2, n1, n2);
-            launch(R.prof, KK_F_LEFT_T, fl, bl, k_f_tile<3>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf, R.T,
+            // Li21 = U Li11 (on the spine U P11 = P21, P11 being finished)
+            launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf, R.Pbuf, T,
                    R.ld, o1, o2, n1, n2);
         } else if (R.leads && o == 0 && nsz == R.ld) {
             static std::once_flag attrs;
@@ -830,13 +873,13 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz)
             });
             const unsigned cnt = g.x * g.y, grid = std::min(cnt, kLeadGrid);
             launch_shm(R.prof, KK_F_RIGHT, fr, br, k_f_right_lead, dim3(grid), dim3(256), kLeadPad, R.s,
-                       (const float*)R.Lbuf, (const float*)R.Pbuf, R.T, R.ld, o1, o2, n1, n2, g.y, cnt);
+                       (const float*)R.Lbuf, (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2, g.y, cnt);
             launch_shm(R.prof, KK_F_LEFT, fl, bl, k_f_left_lead, dim3(grid), dim3(256), kLeadPad, R.s,
-                       (const float*)R.T, R.Pbuf, R.ld, o1, o2, n1, n2, g.x, g.y, cnt);
+                       (const float*)T, R.Pbuf, R.ld, o1, o2, n1, n2, g.x, g.y, cnt);
         } else {
             launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, dim3(g.y, g.x), dim3(256), R.s, (const float*)R.Lbuf,
-                   (const float*)R.Pbuf, R.T, R.ld, o1, o2, n1, n2);
-            launch(R.prof, KK_F_LEFT, fl, bl, k_f_left, g, dim3(256), R.s, (const float*)R.T, R.Pbuf, R.ld, o1, o2,
+                   (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2);
+            launch(R.prof, KK_F_LEFT, fl, bl, k_f_left, g, dim3(256), R.s, (const float*)T, R.Pbuf, R.ld, o1, o2,
                    n1, n2);
         }
     }
@@ -877,6 +920,7 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     float* mean = reinterpret_cast<float*>(w + p.off_mean);
     FactorRun R;
     R.T = reinterpret_cast<float*>(w + p.off_T);
+    R.tbase = p.tbase;
     R.ld = p.Np;
     R.info = info;
     R.s = s;
@@ -898,7 +942,7 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
                p.Np, p.Np, (const float*)mean, damp_frac, vec);
     }
     if (launch_ok()) return -1;
-    if (factor_rec(R, 0, p.Np)) return -1;
+    if (factor_rec(R, 0, p.Np, 0)) return -1;
     if (!R.early) {   // (on the early path every block of the spine has been finished)
         dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 256));
         launch(prof, KK_F_FINISH, dn * dn / 2.0, 4.0 * (2.0 * tri(dN) + 2.0 * dn * dn), k_f_finish, g, dim3(256),
