@@ -70,6 +70,9 @@ def test_host_only_calls(B):
     assert B.solve_workspace_bytes(128, 128) >= 3 * 128 * 128 * 4
     assert B.solve_workspace_bytes(100, 70) >= 3 * 128 * 128 * 4 + 128 * 128 * 4 + 128 * 128 * 4
     assert B.factor_workspace_bytes(8192) >= 4096 * 4096 * 4
+    # one n2 x n1 product buffer per depth of the recursion (8192: 4096^2 + 2048^2 + ... + 128^2 floats)
+    assert B.factor_workspace_bytes(8192) >= 4 * sum((4096 >> d) ** 2 for d in range(6))
+    assert B.factor_workspace_bytes(8192 + 64) > B.factor_workspace_bytes(8192)
     assert B.factor_workspace_bytes(100) >= 2 * 128 * 128 * 4
     # the one-sided path: working weights and errors, padded copy of P_A when ragged
     assert B.gptq_workspace_bytes(0, 64) == 0
