@@ -14,12 +14,15 @@
 //   L^-1 = [[L11^-1, 0], [-L22^-1 L21 L11^-1, L22^-1]].
 // So: recurse on 2 (gives L22 and Li22 = L22^-1); L21 = Li22^T A21 (GEMM,
 // triangular left operand); A11 -= L21^T L21 (SYRK, lower blocks only);
-// recurse on 1; Li21 = -Li22 (L21 Li11) (two GEMMs).  Diagonal blocks of 128
+// recurse on 1; Li21 = -Li22 (L21 Li11) (two GEMMs).  On the levels that use
+// 64 x 64 tiles the last two products are grouped the other way,
+// U = -Li22 L21 in the SYRK's launch and Li21 = U Li11 after the recursion
+// on 1, so each node has one dependent launch fewer.  Diagonal blocks of 128
 // (or 64) are factored and inverted in LDS by one workgroup.
 //
 // Buffers: Pbuf starts as A_d (lower part used) and ends as Li; Lbuf
-// receives L.  Both are n x n with pitch ld.  The temporary T (n2 x n1) lives
-// in the workspace.  A final pass scales Li's columns by diag(L) (giving P)
+// receives L.  Both are n x n with pitch ld.  The n2 x n1 temporary (T or U)
+// lives in the workspace, one per depth of the recursion.  A final pass scales Li's columns by diag(L) (giving P)
 // and writes zeros above both diagonals.  When n is a multiple of 64 (and
 // above 128), the nodes of the leading spine (the blocks [0, nsz)^2) run that
 // pass on their blocks as soon as these are final, and form their P21 from
