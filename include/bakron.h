@@ -131,8 +131,11 @@ size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);
  * scale    [in]  m floats, finite and > 0 (grid step of each output row).
  * zero     [in]  m floats, finite (zero point, fractional allowed).
  * maxq     [in]  m int32 in [1, 255] (largest code of each row).
- *                The grid contract is the caller's to keep; the device does
- *                not check it.
+ *                The grid contract is the caller's to keep: the grid is
+ *                device memory and the library does not read it on the host
+ *                (the Python binding's check_grid checks it before it
+ *                enqueues anything).  Outside the contract the outputs are
+ *                undefined (a maxq above 255 does not fit the uint8 codes).
  * V        [out] m x n float32, V_ij = scale_i (c_ij - zero_i).
  * codes    [out] m x n uint8 codes c_ij.
  * err      [out, nullable] m x n float32 raw errors e_ij = w~_ij - V_ij.
@@ -142,12 +145,15 @@ size_t bakron_solve_workspace_bytes(int64_t m, int64_t n);
  * workspace, workspace_bytes [in] scratch, >= bakron_solve_workspace_bytes(m, n).
  * stream   [in]  HIP stream of the current device.  All work is ordered on
  *                it: part of the propagation of the upper recursion levels
- *                runs on library-owned streams of the same device (created
- *                on first use, default priority, kept until the process
- *                ends), forked from and joined back into `stream` with
- *                events before the call's last kernel, so later work on
- *                `stream` sees every result.  Two calls that share one
- *                workspace must be ordered on one stream.
+ *                runs on library-owned streams of the same device, forked
+ *                from and joined back into `stream` with events before the
+ *                call's last kernel, so later work on `stream` sees every
+ *                result.  The library-owned streams are a fixed pool of four
+ *                per device (created on first use, default priority, kept
+ *                until the process ends); calls from different caller
+ *                streams share them, so their side work runs in the order it
+ *                was enqueued.  Two calls that share one workspace must be
+ *                ordered on one stream.
  */
 int bakron_solve(const float* W, int64_t m, int64_t n,
                  const float* L_A, const float* P_A,
@@ -169,8 +175,8 @@ size_t bakron_quantize_workspace_bytes(int64_t m, int64_t n);
  * Hessian and a grid, and returns the rounded weights).  The results equal
  * those of the three calls made one after the other.
  *
- * The two factorisations run on library-owned streams forked from `stream`
- * (as in bakron_solve).  When a dimension is a multiple of 64 and above 128,
+ * The two factorisations run on two of the library-owned streams of
+ * bakron_solve (the fixed per-device pool), forked from `stream`.  When a dimension is a multiple of 64 and above 128,
  * its factorisation completes leading blocks [0, s)^2 of L and P one after
  * the other (s = the splits of its recursion on the leading half), and the
  * solve, on `stream`, runs each of its kernels as soon as the blocks that

@@ -352,10 +352,14 @@ def implied_errors(W, V, LA, LB) -> np.ndarray:
 
 def implied_errors_p(W, V, PA, PB) -> np.ndarray:
     """Same as ``implied_errors`` but from P_A, P_B directly:
-    E = PB^-1 (W - V) PA^-T by two unit-lower triangular solves."""
+    E = PB^-1 (W - V) PA^-T by two unit-lower triangular solves.
+    PB None stands for the identity (the one-sided case B = I)."""
     from scipy.linalg import solve_triangular
     D = np.asarray(W, np.float64) - np.asarray(V, np.float64)
-    X = solve_triangular(np.asarray(PB, np.float64), D, lower=True, unit_diagonal=True)
+    if PB is None:
+        X = D
+    else:
+        X = solve_triangular(np.asarray(PB, np.float64), D, lower=True, unit_diagonal=True)
     Et = solve_triangular(np.asarray(PA, np.float64), X.T, lower=True, unit_diagonal=True)
     return np.ascontiguousarray(Et.T)
 
@@ -374,7 +378,8 @@ def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None,
     in exact arithmetic), so a mismatch is a "tie" when x lies within
     ``tau`` grid steps of the boundary and the codes are adjacent.
 
-    The factors are given either as L_A, L_B or as P_A, P_B.
+    The factors are given either as L_A, L_B or as P_A, P_B (P_B None: the
+    identity, i.e. the one-sided case B = I).
     Returns counts: entries, mismatches, ties (allowed), bad (outside the
     tie band or more than one step apart), max_step, min_margin; with
     ``return_errors`` also the implied errors as "E" and the boolean masks

@@ -28,7 +28,7 @@ import workloads as WL  # noqa: E402
 from oracle import recursive as O2  # noqa: E402
 from oracle import reference as R  # noqa: E402
 
-NAMES = ("tiny64", "sq1024", "sq4096_t5")
+NAMES = ("tiny64", "sq1024", "sq4096_t5", "glu_up_4096x14336", "glu_down_14336x4096", "sq8192_mixed")
 
 
 def spread(name):

@@ -18,7 +18,8 @@ streams, then the solve.  The checks:
   for bit; the raw errors match the implied ones within 1e-3 grid steps; the
   objective equals sum (L_B,ii e_ij L_A,jj)^2 of the returned errors (1e-6)
   and of the implied errors (1e-3, the objective bar);
-* where the float64 oracle finishes in seconds (up to 4096 x 4096):
+* on every configuration, the float64 oracle (the C quadtree recursion) on
+  the whole layer:
   - same factors: the oracle's solve with the GPU factors (float64), following
     the GPU's code wherever its own decision lies within TAU grid steps of a
     rounding boundary (both roundings are valid there, and the trajectories
@@ -31,6 +32,9 @@ streams, then the solve.  The checks:
     codes within 1e-4 of the entries where that spread shows no differing
     code (elsewhere the count is printed: a trajectory that parts at one
     entry legitimately differs at many).
+The checks of one configuration are separate tests sharing one GPU run
+(a module fixture, one configuration held at a time), so that none of them
+runs for long without reporting.
 """
 import json
 import os
@@ -48,7 +52,6 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 TAU = 1e-4
 U32 = 2.0 ** -24
-FULL_ORACLE = ("tiny64", "sq1024", "sq4096_t5")
 with open(os.path.join(os.path.dirname(__file__), "golden", "trajectory_spread.json")) as _f:
     SPREAD = json.load(_f)
 
@@ -98,55 +101,85 @@ def check_factor_sampled(A32, L, P, rng, label):
     assert worst_b <= 1.0 and worst_i <= 1.0
 
 
-@pytest.mark.parametrize("name", [s.name for s in WL.CONFIGS])
-def test_config_end_to_end(name):
+@pytest.fixture(scope="module", params=[s.name for s in WL.CONFIGS])
+def run(request):
+    """One configuration: its inputs and the GPU run, launched as the bench
+    launches it (held while this configuration's tests run)."""
+    name = request.param
     spec = WL.by_name(name)
     d = WL.generate(spec)
-    m, n = spec.m, spec.n
-    print(f"config {name}: {m}x{n}", flush=True)
+    print(f"config {name}: {spec.m}x{spec.n}", flush=True)
     LA, PA, ia, LB, PB, ib, out = run_like_bench(d)
-    assert ia == 0 and ib == 0
-    rng = np.random.default_rng(5)
-    check_factor_sampled(d["A"], LA, PA, rng, f"{name} factor A")
-    check_factor_sampled(d["B"], LB, PB, rng, f"{name} factor B")
+    return {"name": name, "d": d, "LA": LA, "PA": PA, "ia": ia, "LB": LB, "PB": PB, "ib": ib, "out": out}
 
+
+def test_config_factors(run):
+    assert run["ia"] == 0 and run["ib"] == 0
+    rng = np.random.default_rng(5)
+    check_factor_sampled(run["d"]["A"], run["LA"], run["PA"], rng, f"{run['name']} factor A")
+    check_factor_sampled(run["d"]["B"], run["LB"], run["PB"], rng, f"{run['name']} factor B")
+
+
+def test_config_solve_valid(run):
+    name, d, out = run["name"], run["d"], run["out"]
+    m, n = d["W"].shape
     s, z, mq = d["scale"], d["zero"], d["maxq"]
     codes = out["codes"].astype(np.int64)
     assert np.all(codes <= mq[:, None])
     Vexp = (s[:, None] * (codes.astype(np.float32) - z[:, None])).astype(np.float32)
     assert np.array_equal(out["V"], Vexp)
-    v = R.validate(d["W"], codes, s, z, mq, tau=TAU, PA=PA.astype(np.float64), PB=PB.astype(np.float64),
-                   return_errors=True)
-    E, ties = v.pop("E"), v.pop("tie_mask")
-    v.pop("bad_mask")
+    v = R.validate(d["W"], codes, s, z, mq, tau=TAU, PA=run["PA"].astype(np.float64),
+                   PB=run["PB"].astype(np.float64), return_errors=True)
+    E = v.pop("E")
+    v.pop("tie_mask"), v.pop("bad_mask")
     print(f"{name}: validator {v}", flush=True)
     assert v["bad"] == 0 and v["max_step"] <= 1
     assert v["mismatches"] <= max(1, 1e-4 * m * n)
     steps = np.abs(out["err"] - E) / s[:, None]
     assert steps.max() < 1e-3, steps.max()
     obj = float(out["objective"][0])
-    assert obj == pytest.approx(R.objective_from_errors(out["err"], LA, LB), rel=1e-6)
-    assert obj == pytest.approx(R.objective_from_errors(E, LA, LB), rel=1e-3)
+    assert obj == pytest.approx(R.objective_from_errors(out["err"], run["LA"], run["LB"]), rel=1e-6)
+    assert obj == pytest.approx(R.objective_from_errors(E, run["LA"], run["LB"]), rel=1e-3)
 
-    if name in FULL_ORACLE:
-        # same factors, following the GPU at near-ties: identical codes
-        c_same, _, _, adopted = O2.bakron_recursive(d["W"], PA.astype(np.float64), PB.astype(np.float64), s, z, mq,
-                                                    follow=codes, tau=TAU)
-        same_diff = int((codes != c_same).sum())
-        print(f"{name}: oracle on the same factors adopted {adopted} near-tie codes; {same_diff} codes differ",
-              flush=True)
-        assert adopted <= max(1, 1e-4 * m * n)
-        assert same_diff == 0
-        # end to end against the float64 factors
-        fa, fb = R.factor(d["A"]), R.factor(d["B"])
-        c_or, V_or, _ = O2.bakron_recursive(d["W"], fa["P"], fb["P"], s, z, mq)
-        diff = int((codes != c_or).sum())
-        o_gpu = R.objective(d["W"], out["V"], fa["L"], fb["L"])
-        o_or = R.objective(d["W"], V_or, fa["L"], fb["L"])
-        sp = SPREAD[name]
-        print(f"{name}: end to end, {diff} codes differ from the float64 oracle (recorded spread "
-              f"{sp['differ_frac']:.4f}), objective rel {abs(o_gpu - o_or) / o_or:.3e}", flush=True)
-        assert o_gpu == pytest.approx(o_or, rel=max(1e-3, 5 * sp["objective_rel"]))
-        if sp["differ_frac"] == 0.0:
-            assert diff <= max(1, 1e-4 * m * n)
-            assert np.abs(codes - c_or).max() <= 1
+
+def test_config_oracle_same_factors(run):
+    """The oracle on the GPU's factors, following the GPU's code at near-ties
+    only: identical codes everywhere, at most 1e-4 of them followed."""
+    name, d, out = run["name"], run["d"], run["out"]
+    m, n = d["W"].shape
+    codes = out["codes"].astype(np.int64)
+    c_same, _, E_same, adopted = O2.bakron_recursive(d["W"], run["PA"].astype(np.float64),
+                                                     run["PB"].astype(np.float64), d["scale"], d["zero"],
+                                                     d["maxq"], follow=codes, tau=TAU)
+    same_diff = int((codes != c_same).sum())
+    dA, dB = np.diag(run["LA"]).astype(np.float64), np.diag(run["LB"]).astype(np.float64)
+    o_or = float(np.sum((dB[:, None] * E_same * dA[None, :]) ** 2))
+    o_gpu = float(out["objective"][0])
+    print(f"{name}: oracle on the same factors adopted {adopted} near-tie codes of {m * n}; {same_diff} codes "
+          f"differ; objective rel {abs(o_gpu - o_or) / o_or:.3e}", flush=True)
+    assert adopted <= max(1, 1e-4 * m * n)
+    assert same_diff == 0
+    assert o_gpu == pytest.approx(o_or, rel=1e-3)
+
+
+def test_config_oracle_end_to_end(run):
+    """GPU factors and solve against the float64 oracle's own factors and
+    solve (free running)."""
+    name, d, out = run["name"], run["d"], run["out"]
+    m, n = d["W"].shape
+    s, z, mq = d["scale"], d["zero"], d["maxq"]
+    codes = out["codes"].astype(np.int64)
+    fa = R.factor(d["A"])
+    fb = R.factor(d["B"])
+    c_or, V_or, _ = O2.bakron_recursive(d["W"], fa["P"], fb["P"], s, z, mq)
+    diff = int((codes != c_or).sum())
+    o_gpu = R.objective(d["W"], out["V"], fa["L"], fb["L"])
+    o_or = R.objective(d["W"], V_or, fa["L"], fb["L"])
+    sp = SPREAD[name]
+    print(f"{name}: end to end, {diff} codes of {m * n} differ from the float64 oracle (recorded spread "
+          f"{sp['differ_frac']:.4f}), objective rel {abs(o_gpu - o_or) / o_or:.3e} (bar "
+          f"{max(1e-3, 5 * sp['objective_rel']):.3e})", flush=True)
+    assert o_gpu == pytest.approx(o_or, rel=max(1e-3, 5 * sp["objective_rel"]))
+    if sp["differ_frac"] == 0.0:
+        assert diff <= max(1, 1e-4 * m * n)
+        assert np.abs(codes - c_or).max() <= 1

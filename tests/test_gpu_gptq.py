@@ -112,7 +112,9 @@ def test_gptq_equals_two_sided_solve_with_identity_b():
 
 
 @pytest.mark.parametrize("name", ["sq4096_t5", "sq8192_mixed"])
-def test_gptq_full_size_sampled_rows(name):
+def test_gptq_full_size(name):
+    """Every row through the validator (rows are independent, P_B = I), and
+    sampled rows through the oracle in tie-following mode."""
     spec = WL.by_name(name)
     d = WL.generate(spec)
     m, n = spec.m, spec.n
@@ -122,6 +124,18 @@ def test_gptq_full_size_sampled_rows(name):
     assert int(info.item()) == 0
     LA, PA = LA.cpu().numpy(), PA.cpu().numpy()
     out = gpu_gptq(d, LA, PA)
+    s, z, mq = d["scale"], d["zero"], d["maxq"]
+    codes = out["codes"].astype(np.int64)
+    assert np.all(codes <= mq[:, None])
+    assert np.array_equal(out["V"], (s[:, None] * (codes.astype(np.float32) - z[:, None])).astype(np.float32))
+    v = R.validate(d["W"], codes, s, z, mq, tau=TAU, PA=PA.astype(np.float64), PB=None, return_errors=True)
+    E = v.pop("E")
+    v.pop("tie_mask"), v.pop("bad_mask")
+    print(f"gptq {name}: validator over all {m} rows {v}", flush=True)
+    assert v["bad"] == 0 and v["max_step"] <= 1
+    assert v["mismatches"] <= max(1, 1e-4 * m * n)
+    assert (np.abs(out["err"] - E) / s[:, None]).max() < 1e-3
+    del E
     rng = np.random.default_rng(3)
     rows = np.unique(np.concatenate([[0, m - 1], rng.choice(m, size=30, replace=False)]))
     check_rows(d, PA, out, rows, f"gptq {name} rows {len(rows)}")

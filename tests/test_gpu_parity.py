@@ -177,6 +177,42 @@ def test_solve_repeatable_and_stream_ordered():
         assert np.array_equal(a[k], b[k]), k
 
 
+def test_golden_grid_fixture_on_the_gpu():
+    """The hand-worked fixture tests/golden/hand_grid_2x2.json (non-unit
+    steps, fractional zero points, a clip at maxq, a clip at 0 and an exact
+    half-way tie resolved to even; every value dyadic, so the float32 path is
+    exact): the GPU's solve on the fixture's factors, its own factors and
+    solve (no damping), and its one-sided path reproduce the hand-derived
+    codes, values, errors and objectives exactly."""
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_grid_2x2.json")))
+    f32 = lambda k: np.array(g[k], np.float32)   # noqa: E731
+    d = {"W": f32("W"), "scale": f32("scale"), "zero": f32("zero"), "maxq": np.array(g["maxq"], np.int32)}
+    out = gpu_solve(d, f32("L_A"), f32("P_A"), f32("L_B"), f32("P_B"))
+    assert np.array_equal(out["codes"], np.array(g["codes"]))
+    assert np.array_equal(out["V"], f32("V")) and np.array_equal(out["err"], f32("E"))
+    assert out["objective"][0] == g["objective"]
+    LA, PA, ia = gpu_factor(f32("A"), 0.0)
+    LB, PB, ib = gpu_factor(f32("B"), 0.0)
+    assert ia == 0 and ib == 0
+    assert np.array_equal(LA, f32("L_A")) and np.array_equal(PA, f32("P_A"))
+    assert np.array_equal(LB, f32("L_B")) and np.array_equal(PB, f32("P_B"))
+    q = B.quantize(to_dev(d["W"]), to_dev(f32("A")), to_dev(f32("B")), to_dev(d["scale"]), to_dev(d["zero"]),
+                   to_dev(d["maxq"]), 0.0, want_err=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(q["codes"].cpu().numpy(), np.array(g["codes"]))
+    assert np.array_equal(q["err"].cpu().numpy(), f32("E"))
+    o = g["one_sided"]
+    r = B.gptq(to_dev(d["W"]), to_dev(f32("L_A")), to_dev(f32("P_A")), to_dev(d["scale"]), to_dev(d["zero"]),
+               to_dev(d["maxq"]), want_err=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(r["codes"].cpu().numpy(), np.array(o["codes"]))
+    assert np.array_equal(r["V"].cpu().numpy(), np.array(o["V"], np.float32))
+    assert np.array_equal(r["err"].cpu().numpy(), np.array(o["E"], np.float32))
+    assert r["objective"].item() == o["objective"]
+
+
 # ---------------------------------------------------------- end to end
 
 @pytest.mark.parametrize("m,n,seed", [(64, 64, 0), (256, 192, 1), (200, 330, 2)])

@@ -76,7 +76,7 @@ def test_recursive_matches_naive_1024():
 
 
 # Hand-worked fixtures (tests/golden/*.json, derivations inside).
-@pytest.mark.parametrize("name", ["hand_1x2.json", "hand_2x2.json"])
+@pytest.mark.parametrize("name", ["hand_1x2.json", "hand_2x2.json", "hand_grid_2x2.json"])
 def test_golden_hand_examples(name):
     g = json.load(open(os.path.join(GOLD, name)))
     W = np.array(g["W"], dtype=np.float64)
@@ -104,6 +104,77 @@ def test_golden_hand_examples(name):
         assert R.objective_from_errors(E, fa["L"], fb["L"]) == pytest.approx(g["objective"], rel=1e-12)
     c, V = R.gptq_vectorized(W, fa["Ad"], fb["Ad"], s, z, mq)
     assert np.array_equal(c, g["codes"])
+    np.testing.assert_allclose(V, g["V"], atol=1e-12)
+    # tie following on its own codes adopts nothing, even at the exact tie
+    c2, _, _, k = O2.bakron_recursive(W, fa["P"], fb["P"], s, z, mq, leaf=1, follow=np.array(g["codes"]))
+    assert k == 0 and np.array_equal(c2, g["codes"])
+    v = R.validate(W, np.array(g["codes"]), s, z, mq, fa["L"], fb["L"])
+    assert v["mismatches"] == 0
+
+
+def _grid_fixture():
+    g = json.load(open(os.path.join(GOLD, "hand_grid_2x2.json")))
+    W = np.array(g["W"], dtype=np.float64)
+    fa, fb = R.factor(np.array(g["A"]), g["damping"]), R.factor(np.array(g["B"]), g["damping"])
+    return g, W, fa, fb, np.array(g["scale"], np.float32), np.array(g["zero"], np.float32), \
+        np.array(g["maxq"], np.int32)
+
+
+def test_golden_grid_example_one_sided():
+    """The fixture's B = I case (hand-worked in the fixture): the one-sided
+    form, BaKron-naive with P_B = I and textbook GPTQ all reproduce it."""
+    g, W, fa, _, s, z, mq = _grid_fixture()
+    o = g["one_sided"]
+    c, V, E = R.gptq_columns(W, fa["P"], s, z, mq)
+    assert np.array_equal(c, o["codes"])
+    np.testing.assert_allclose(V, o["V"], atol=1e-12)
+    np.testing.assert_allclose(E, o["E"], atol=1e-12)
+    assert R.objective_from_errors(E, fa["L"], np.eye(2)) == pytest.approx(o["objective"], rel=1e-12)
+    c2, _, E2 = R.bakron_naive(W, fa["P"], np.eye(2), s, z, mq)
+    assert np.array_equal(c2, o["codes"]) and np.allclose(E2, o["E"], atol=1e-12)
+    assert np.array_equal(_textbook_gptq_rows(W, fa["Ad"], s, z, mq), o["codes"])
+
+
+def _quant_half_up(w, s, z, maxq):
+    x = (np.asarray(w, np.float64).astype(np.float32) / np.asarray(s, np.float32)).astype(np.float32) \
+        + np.asarray(z, np.float32)
+    c = np.clip(np.floor(x.astype(np.float64) + 0.5), 0, np.asarray(maxq, np.float64))
+    return c, np.asarray(s, np.float64) * (c - np.asarray(z, np.float64))
+
+
+def _quant_no_upper_clip(w, s, z, maxq):
+    return _ORIG_QUANT(w, s, z, np.full(np.shape(maxq), 10 ** 6))
+
+
+def _quant_no_lower_clip(w, s, z, maxq):
+    x = (np.asarray(w, np.float64).astype(np.float32) / np.asarray(s, np.float32)).astype(np.float32) \
+        + np.asarray(z, np.float32)
+    c = np.minimum(np.rint(x), np.asarray(maxq)).astype(np.float64)
+    return c, np.asarray(s, np.float64) * (c - np.asarray(z, np.float64))
+
+
+def _quant_integer_zero(w, s, z, maxq):
+    return _ORIG_QUANT(w, s, np.rint(np.asarray(z, np.float32)), maxq)
+
+
+def _quant_unit_step(w, s, z, maxq):
+    return _ORIG_QUANT(w, np.ones_like(np.asarray(s, np.float32)), z, maxq)
+
+
+_ORIG_QUANT = R.quantize
+
+
+# Mistakes planted in the oracle's base quantizer (on the CPU): each one of
+# them changes the hand-worked fixture's codes, so the fixture pins every
+# branch of the rounding rule.
+@pytest.mark.parametrize("plant", [_quant_half_up, _quant_no_upper_clip, _quant_no_lower_clip,
+                                   _quant_integer_zero, _quant_unit_step])
+def test_golden_grid_example_catches_planted_quantizer_mistakes(plant, monkeypatch):
+    g, W, fa, fb, s, z, mq = _grid_fixture()
+    monkeypatch.setattr(R, "quantize", plant)
+    c, V, _ = R.bakron_naive(W, fa["P"], fb["P"], s, z, mq)
+    same = np.array_equal(c, g["codes"]) and np.allclose(V, g["V"], rtol=0, atol=1e-12)
+    assert not same, plant.__name__
 
 
 # RevCholesky ([S] Corollary 3.4): A_d = L^T L, L lower with positive diagonal.
@@ -319,6 +390,21 @@ def test_validator_from_p_matches_from_l():
     np.testing.assert_allclose(R.implied_errors_p(d["W"], V, fa["P"], fb["P"]), E, atol=1e-12)
     r = R.validate(d["W"], c, d["scale"], d["zero"], d["maxq"], PA=fa["P"], PB=fb["P"])
     assert r["mismatches"] == 0
+
+
+def test_validator_one_sided_identity_shortcut():
+    # P_B omitted means B = I: the same implied errors and verdict as the
+    # explicit identity
+    d = make_problem(20, 36, 17)
+    fa = R.factor(d["A"])
+    c, V, E = R.gptq_columns(d["W"], fa["P"], d["scale"], d["zero"], d["maxq"])
+    np.testing.assert_allclose(R.implied_errors_p(d["W"], V, fa["P"], None), E, atol=1e-12)
+    a = R.validate(d["W"], c, d["scale"], d["zero"], d["maxq"], PA=fa["P"], PB=None)
+    b = R.validate(d["W"], c, d["scale"], d["zero"], d["maxq"], PA=fa["P"], PB=np.eye(20))
+    assert a == b and a["mismatches"] == 0
+    flip = c.copy()
+    flip[7, 20] = flip[7, 20] + 1 if flip[7, 20] < d["maxq"][7] else flip[7, 20] - 1
+    assert R.validate(d["W"], flip, d["scale"], d["zero"], d["maxq"], PA=fa["P"], PB=None)["bad"] >= 1
 
 
 def test_dependency_cone_brute_force():

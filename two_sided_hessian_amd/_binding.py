@@ -123,6 +123,34 @@ def _check_dev(name, t, dtype, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
+class GridError(ValueError):
+    """A per-row grid that breaks the contract of include/bakron.h."""
+
+
+MAXQ_LIMIT = 255   # codes are stored as uint8
+
+
+def check_grid(scale, zero, maxq) -> None:
+    """Raise GridError unless every scale is finite and > 0, every zero point
+    finite and every maxq in [1, 255] (the grid contract of bakron_solve,
+    bakron_quantize and bakron_gptq; the device does not check it).  Takes
+    torch tensors on any device (a device tensor is copied to the host, which
+    waits for the work that produces it) or numpy arrays."""
+    def host(x):
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu")
+        return torch.as_tensor(x)
+    s, z, q = host(scale), host(zero), host(maxq)
+    if s.numel() and not bool(torch.isfinite(s).all()):
+        raise GridError("scale must be finite")
+    if s.numel() and not bool((s > 0).all()):
+        raise GridError("scale must be > 0")
+    if z.numel() and not bool(torch.isfinite(z).all()):
+        raise GridError("zero must be finite")
+    if q.numel() and not bool(((q >= 1) & (q <= MAXQ_LIMIT)).all()):
+        raise GridError(f"maxq must lie in [1, {MAXQ_LIMIT}]")
+
+
 def workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator returns >= 512-byte aligned blocks
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -182,9 +210,11 @@ def factor(A: torch.Tensor, damp_frac: float = 0.01, *, out=None, ws=None, strea
 
 
 def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objective=True,
-          out=None, ws=None, stream=None, profile=None):
+          out=None, ws=None, stream=None, profile=None, check=True):
     """bakron_solve: returns dict(V, codes, err?, objective?) of device tensors.
-    ``profile``: as in factor()."""
+    ``profile``: as in factor().  ``check``: check the grid contract first
+    (check_grid; it reads the grid back to the host, so a caller that runs
+    the same grid many times may check it once and pass check=False)."""
     m, n = W.shape
     _check_dev("W", W, torch.float32, (m, n))
     _check_dev("P_A", PA, torch.float32, (n, n))
@@ -195,6 +225,8 @@ def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objectiv
     if want_objective:
         _check_dev("L_A", LA, torch.float32, (n, n))
         _check_dev("L_B", LB, torch.float32, (m, m))
+    if check:
+        check_grid(scale, zero, maxq)
     dev = W.device
     if out is None:
         out = {
@@ -228,10 +260,10 @@ def quantize_workspace_bytes(m: int, n: int) -> int:
 
 
 def quantize(W, A, B, scale, zero, maxq, damp_frac: float = 0.01, *, want_err=False, want_objective=True,
-             out=None, ws=None, stream=None):
+             out=None, ws=None, stream=None, check=True):
     """bakron_quantize (both factors and the solve in one call): returns
     dict(V, codes, err?, objective?, L_A, P_A, info_A, L_B, P_B, info_B) of
-    device tensors."""
+    device tensors.  ``check``: as in solve()."""
     m, n = W.shape
     _check_dev("W", W, torch.float32, (m, n))
     _check_dev("A", A, torch.float32, (n, n))
@@ -239,6 +271,8 @@ def quantize(W, A, B, scale, zero, maxq, damp_frac: float = 0.01, *, want_err=Fa
     _check_dev("scale", scale, torch.float32, (m,))
     _check_dev("zero", zero, torch.float32, (m,))
     _check_dev("maxq", maxq, torch.int32, (m,))
+    if check:
+        check_grid(scale, zero, maxq)
     dev = W.device
     if out is None:
         out = {
@@ -269,9 +303,10 @@ def quantize(W, A, B, scale, zero, maxq, damp_frac: float = 0.01, *, want_err=Fa
 
 
 def gptq(W, LA, PA, scale, zero, maxq, *, want_err=False, want_objective=True, out=None, ws=None, stream=None,
-         profile=None):
+         profile=None, check=True):
     """bakron_gptq (the one-sided case B = I): returns dict(V, codes, err?,
-    objective?) of device tensors.  ``profile``: as in factor()."""
+    objective?) of device tensors.  ``profile``: as in factor(); ``check``:
+    as in solve()."""
     m, n = W.shape
     _check_dev("W", W, torch.float32, (m, n))
     _check_dev("P_A", PA, torch.float32, (n, n))
@@ -280,6 +315,8 @@ def gptq(W, LA, PA, scale, zero, maxq, *, want_err=False, want_objective=True, o
     _check_dev("maxq", maxq, torch.int32, (m,))
     if want_objective:
         _check_dev("L_A", LA, torch.float32, (n, n))
+    if check:
+        check_grid(scale, zero, maxq)
     dev = W.device
     if out is None:
         out = {
@@ -356,13 +393,22 @@ def shampoo_factors(Xa, Xb, *, stream=None):
     return moment(Xa, wb, stream=stream), moment(Xb, wa, stream=stream)
 
 
-def solve_batch(problems, streams=None, *, want_err=False, want_objective=True, ws=None):
+def solve_batch(problems, streams=None, *, want_err=False, want_objective=True, ws=None, check=True):
     """bakron_solve_batch: ``problems`` is a list of dicts with device
     tensors W, LA, PA, LB, PB, scale, zero, maxq (one per layer); layer k runs
     on streams[k % len(streams)] (default: the current stream only).
-    Returns one output dict per layer, as solve() does."""
+    Returns one output dict per layer, as solve() does.
+
+    Stream order: the outputs and the workspace are allocated on the current
+    stream, so every batch stream first waits for the current stream (the
+    inputs may still be in production there), and the current stream waits
+    for every batch stream after the call: the outputs are complete for
+    later work on the current stream, and the workspace is not handed out
+    again by torch's allocator while a batch kernel may still use it.
+    ``check``: as in solve(), for every layer."""
+    cur = torch.cuda.current_stream()
     if streams is None:
-        streams = [torch.cuda.current_stream()]
+        streams = [cur]
     outs, descs = [], []
     for p in problems:
         W = p["W"]
@@ -376,6 +422,8 @@ def solve_batch(problems, streams=None, *, want_err=False, want_objective=True, 
         if want_objective:
             _check_dev("L_A", p["LA"], torch.float32, (n, n))
             _check_dev("L_B", p["LB"], torch.float32, (m, m))
+        if check:
+            check_grid(p["scale"], p["zero"], p["maxq"])
         dev = W.device
         o = {"V": torch.empty((m, n), dtype=torch.float32, device=dev),
              "codes": torch.empty((m, n), dtype=torch.uint8, device=dev)}
@@ -394,7 +442,13 @@ def solve_batch(problems, streams=None, *, want_err=False, want_objective=True, 
     need = lib().bakron_solve_batch_workspace_bytes(arr, len(descs), len(streams))
     if ws is None:
         ws = workspace(need, problems[0]["W"].device if problems else "cuda")
+    for s in streams:
+        if s != cur:
+            s.wait_stream(cur)
     rc = lib().bakron_solve_batch(arr, len(descs), _ptr(ws), ws.numel(), sarr, len(streams))
+    for s in streams:
+        if s != cur:
+            cur.wait_stream(s)
     if rc != BAKRON_SUCCESS:
         raise BakronError(rc, "bakron_solve_batch")
     return outs

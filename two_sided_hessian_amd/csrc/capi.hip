@@ -6,7 +6,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
-#include <tuple>
+#include <utility>
 #include <vector>
 
 #include "../../include/bakron.h"
@@ -153,7 +153,7 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
     // leading blocks becomes final; the solve's first work (copies, block
     // lists) starts at once, and each later kernel of it waits for the
     // smallest leading blocks that hold its tiles.
-    hipStream_t sa = bk::side_stream(stream, 0), sb = bk::side_stream(stream, 1);
+    hipStream_t sa = bk::side_stream(0), sb = bk::side_stream(1);
     bk::SolveWait wait;
     wait.lead[0].count = bk::factor_leads(n, wait.lead[0].size);
     wait.lead[1].count = bk::factor_leads(m, wait.lead[1].size);
@@ -357,14 +357,17 @@ const char* kernel_name(int kind)
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 
-hipStream_t side_stream(hipStream_t caller, int slot)
+hipStream_t side_stream(int slot)
 {
+    // kSideSlots streams per device, created on first use: the pool does not
+    // grow with the number of caller streams.
     static std::mutex mu;
-    static std::map<std::tuple<int, hipStream_t, int>, hipStream_t> table;
+    static std::map<std::pair<int, int>, hipStream_t> table;
+    if (slot < 0 || slot >= kSideSlots) return nullptr;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return nullptr;
     std::lock_guard<std::mutex> lock(mu);
-    hipStream_t& st = table[std::make_tuple(dev, caller, slot)];
+    hipStream_t& st = table[std::make_pair(dev, slot)];
     if (!st && hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess) st = nullptr;
     return st;
 }

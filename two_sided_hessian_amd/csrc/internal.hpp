@@ -82,11 +82,16 @@ inline void launch_shm(Prof* p, int kind, double flops, double bytes, void (*ker
 }
 
 // A library-owned stream (default priority, non-blocking) for work that a
-// call forks off the caller's stream `caller` and joins back with events.
-// One per (device, caller stream, slot), created on first use and kept for
-// the life of the process, so that calls on different caller streams never
-// queue behind each other.  nullptr when it cannot be created.
-hipStream_t side_stream(hipStream_t caller, int slot);
+// call forks off the caller's stream and joins back with events.  A fixed
+// pool of kSideSlots streams per device, created on first use and kept for
+// the life of the process (so the number of streams never grows with the
+// caller's streams).  Calls from different caller streams share the pool:
+// their side work is then served in the order it was enqueued, and since
+// every wait is on an event recorded before it, no call can wait on another
+// call's later work.  nullptr when the stream cannot be created or slot is
+// out of range.
+constexpr int kSideSlots = 4;
+hipStream_t side_stream(int slot);
 
 // Drain the stream, sum the per-launch event times per kernel kind into
 // stats (at most max_stats entries, in KernelKind order), release events.

@@ -442,6 +442,7 @@ constexpr int kMaxKTiles = kMaxDim / kTile;   // K extent of a block, in tiles
 #define BAKRON_SPLIT_DEPTH 4
 #endif
 constexpr int kSplitDepth = BAKRON_SPLIT_DEPTH;   // nodes above this depth may be split
+static_assert(kSplitDepth <= kSideSlots, "one library stream per split depth");
 #ifndef BAKRON_SPLIT3_DEPTH
 #define BAKRON_SPLIT3_DEPTH 3
 #endif
@@ -1314,7 +1315,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     }
     for (int d = 0; d < kSplitDepth; ++d) {
         R.Ysplit[d] = d < p.sg.split_depth ? reinterpret_cast<float*>(w + p.off_ysplit[d]) : nullptr;
-        R.far[d] = d < p.sg.split_depth ? side_stream(s, d) : nullptr;
+        R.far[d] = d < p.sg.split_depth ? side_stream(d) : nullptr;
         if (d < p.sg.split_depth && !R.far[d]) p.sg.split_depth = p.sg.split3_depth = 0;   // no stream: nothing is split
     }
     LeafArgs& g = R.leaf;
