@@ -16,8 +16,8 @@ Prints ONE JSON line.  `value` is seconds per step (time-like: lower is
 better).  `roofline` describes the kernel with the largest share of the
 step, timed with HIP events around each of its launches (the *_profiled
 entry points, on the stream the kernels run on) in a separate pass over the
-same inputs.  `cpu_baseline` is the float64 oracle (C, OpenMP) on a bounded
-leading block of the same workload, scaled by the cubic work ratio.
+same inputs.  `cpu_baseline` is the float64 oracle (numpy factorisations,
+C / OpenMP recursive solve) on the whole layer, timed on the host cores.
 
 Only --gpus 1 is supported: the solve of one matrix runs on one GPU.
 """
@@ -48,8 +48,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="sq8192_mixed")
-    ap.add_argument("--cpu-sample", type=int, default=4608,
-                    help="edge of the leading block the oracle baseline solves (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=-1,
+                    help="edge of the leading block the oracle baseline solves (-1 = the whole layer, 0 = skip)")
     ap.add_argument("--no-profile", action="store_true", help="skip the per-kernel roofline pass")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the secondary paths (the one-sided case B = I) measured beside the step")
@@ -80,6 +80,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T = {k: torch.from_numpy(np.ascontiguousarray(d[k])).to(dev) for k in ("W", "A", "B", "scale", "zero", "maxq")}
+    # the grid contract is checked once here; the calls below reuse the same
+    # grid and skip the check (it reads the grid back to the host)
+    B.check_grid(T["scale"], T["zero"], T["maxq"])
     fa = (torch.empty((n, n), device=dev), torch.empty((n, n), device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
     fb = (torch.empty((m, m), device=dev), torch.empty((m, m), device=dev), torch.zeros(1, dtype=torch.int32, device=dev))
     ws_fa = B._binding.workspace(B.factor_workspace_bytes(n), dev)
@@ -99,7 +102,7 @@ def main():
 
     def fused():
         B.quantize(T["W"], T["A"], T["B"], T["scale"], T["zero"], T["maxq"], 0.01, out=qout, ws=ws_q,
-                   stream=stream)
+                   stream=stream, check=False)
 
     sA = sB = None
     fork, joinA, joinB = (torch.cuda.Event() for _ in range(3))
@@ -132,7 +135,7 @@ def main():
         if ev is not None:
             ev.record(stream)
         B.solve(T["W"], fa[0], fa[1], fb[0], fb[1], T["scale"], T["zero"], T["maxq"], out=out, ws=ws_s,
-                stream=stream, profile=profile)
+                stream=stream, profile=profile, check=False)
 
     for _ in range(args.warmup):
         fused()
@@ -184,7 +187,7 @@ def main():
     solve_s = float(np.median(solve_ms)) / 1e3
 
     roofline = roofline_mfma = None
-    kernels = None
+    kernels = stages = None
     if not args.no_profile:
         prof = []
         separate(profile=prof)
@@ -209,9 +212,14 @@ def main():
         roofline = roofline_entry(*dom, traffic)
         mf = [kv for kv in main if kernel_bound(kv[0]) == "mfma"]
         if mf:
-            # the MFMA kernel that carries the most algorithmic work
+            # the MFMA kernel with the most block products; its flops are the
+            # executed block products (recomputation of the divide and
+            # conquer included), so its fraction is an executed-work one
             roofline_mfma = roofline_entry(*max(mf, key=lambda kv: kv[1]["alg_flops"]), traffic)
+            roofline_mfma["work"] = "executed block products"
+        stages = stage_fractions(agg, m, n)
         log(f"[bench] kernels: {json.dumps(kernels)}")
+        log(f"[bench] propagation stages: {json.dumps(stages)}")
 
     nxt = None
     if not args.no_next:
@@ -221,8 +229,8 @@ def main():
         nxt["batch"] = bench_batch(B, WL, dev, args)
 
     cpu = None
-    if args.cpu_sample > 0:
-        cpu = cpu_baseline(d, args.cpu_sample, m, n)
+    if args.cpu_sample != 0:
+        cpu = cpu_baseline(d, max(m, n) if args.cpu_sample < 0 else args.cpu_sample, m, n)
 
     res = {
         "metric": "seconds per m×n BaKron solve (8192×8192 fp32) + achieved fp32 MFMA TFLOP/s",
@@ -250,6 +258,7 @@ def main():
         "objective": obj,
         "roofline": roofline,
         "roofline_mfma": roofline_mfma,
+        "stages": stages,
         "kernels": kernels,
         "next": nxt,
         "cpu_baseline": cpu,
@@ -271,7 +280,7 @@ def bench_gptq(B, T, fa, m, n, args, traffic):
 
     def call(profile=None):
         B.gptq(T["W"], fa[0], fa[1], T["scale"], T["zero"], T["maxq"], out=out, ws=ws, stream=stream,
-               profile=profile)
+               profile=profile, check=False)
 
     for _ in range(args.warmup):
         call()
@@ -372,6 +381,7 @@ def bench_batch(B, WL, dev, args, layers=16, name="sq1024"):
         T = {key: torch.from_numpy(np.ascontiguousarray(d[key])).to(dev) for key in ("W", "A", "B", "scale", "zero", "maxq")}
         LA, PA, _ = B.factor(T["A"], 0.01)
         LB, PB, _ = B.factor(T["B"], 0.01)
+        B.check_grid(T["scale"], T["zero"], T["maxq"])
         probs.append({"W": T["W"], "LA": LA, "PA": PA, "LB": LB, "PB": PB, "scale": T["scale"],
                       "zero": T["zero"], "maxq": T["maxq"]})
     torch.cuda.synchronize()
@@ -385,7 +395,7 @@ def bench_batch(B, WL, dev, args, layers=16, name="sq1024"):
             for s in streams:
                 if s is not main:
                     s.wait_stream(main)
-            B.solve_batch(probs, streams)
+            B.solve_batch(probs, streams, check=False)
             for s in streams:
                 if s is not main:
                     main.wait_stream(s)
@@ -418,7 +428,18 @@ MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", 
                 "k_gptq_update_t", "k_moment<false>", "k_moment<true>"}
 HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info", "k_gptq_load",
                "k_row_sqnorms"}
-PEAK_FP32_VECTOR_TFLOPS = 157.3   # MI355X fp32 vector
+# fp32 vector peak of the instructions this build issues: 256 CUs x 4 SIMDs
+# x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s.  MI355X's published
+# 157.3 TFLOP/s fp32 vector figure counts packed fp32 (two FMAs per lane per
+# instruction), which the library is compiled without.
+PEAK_FP32_VECTOR_TFLOPS = 78.6
+PEAK_FP32_VECTOR_PACKED_TFLOPS = 157.3
+
+# Kernels of the two propagation stages of the solve (k_prop_pair runs both
+# stages of a two-leaf node; its time is split between them in proportion to
+# their block products, equal by construction).
+STAGE1_KERNELS = ("k_prop_rows", "k_prop_rows_t", "k_prop_rows_far", "k_prop_rows_t_far")
+STAGE2_KERNELS = ("k_prop_cols", "k_prop_cols_t", "k_prop_cols_far", "k_prop_cols_t_far")
 
 
 def kernel_bound(name):
@@ -472,11 +493,39 @@ def roofline_entry(name, v, traffic):
     tr = None
     if traffic and name in traffic.get("kernels", {}):
         tr = traffic["kernels"][name]["hbm_bytes_per_launch"]
-    return {"kernel": name, "bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
-            "frac": round(ach / peak, 4), "traffic": tr, "launches": v["launches"],
-            "avg_launch_us": round(1e6 * secs / v["launches"], 3),
-            "alg_flops_per_launch": v["alg_flops"] / v["launches"],
-            "alg_bytes_per_launch": v["alg_bytes"] / v["launches"]}
+    r = {"kernel": name, "bound": bound, "achieved": round(ach, 3), "peak": peak, "unit": unit,
+         "frac": round(ach / peak, 4), "traffic": tr, "launches": v["launches"],
+         "avg_launch_us": round(1e6 * secs / v["launches"], 3),
+         "alg_flops_per_launch": v["alg_flops"] / v["launches"],
+         "alg_bytes_per_launch": v["alg_bytes"] / v["launches"]}
+    if bound == "alu":
+        r["peak_note"] = ("non-packed fp32 FMA (the build disables packed fp32); against the packed "
+                          f"{PEAK_FP32_VECTOR_PACKED_TFLOPS} TFLOP/s the fraction is "
+                          f"{round(ach / PEAK_FP32_VECTOR_PACKED_TFLOPS, 4)}")
+    return r
+
+
+def stage_fractions(agg, m, n):
+    """Algorithmic rate of each propagation stage: its share of the solve's
+    algorithmic work (stage 1 the triangular product E P_A^T, m n (n + 1)
+    flops; stage 2 P_B Y, m (m + 1) n flops; the leaf's in-tile parts of both
+    included, since the total is the whole product) over the summed duration
+    of the stage's kernels, and the executed block products of those kernels
+    for comparison (the divide and conquer recomputes partial products)."""
+    out = {}
+    pair = agg.get("k_prop_pair", {"total_ms": 0.0, "alg_flops": 0.0, "launches": 0})
+    for stage, names, alg in (("stage1", STAGE1_KERNELS, float(m) * n * (n + 1)),
+                              ("stage2", STAGE2_KERNELS, float(m) * (m + 1) * n)):
+        ms = sum(agg[k]["total_ms"] for k in names if k in agg) + 0.5 * pair["total_ms"]
+        ex = sum(agg[k]["alg_flops"] for k in names if k in agg) + 0.5 * pair["alg_flops"]
+        if ms <= 0:
+            continue
+        out[stage] = {"kernels_ms": round(ms, 4), "alg_flops": alg,
+                      "alg_tflops": round(alg / (ms * 1e-3) / 1e12, 3),
+                      "alg_frac": round(alg / (ms * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                      "executed_flops": ex,
+                      "executed_tflops": round(ex / (ms * 1e-3) / 1e12, 3)}
+    return out
 
 
 def copy_calibration(nbytes):
@@ -492,11 +541,24 @@ def copy_calibration(nbytes):
     print(json.dumps({"copy_bytes": 4 * n, "copies": 5}), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(d, sample, m, n):
-    """The float64 oracle, timed on the host cores, on the leading
-    sample x sample block of the same layer (same grid rows, the leading
-    blocks of A and B), scaled to the full layer by the work ratio
-    mn(m+n) / (ms ns (ms+ns))."""
+    """The float64 oracle, timed on the host cores: both factorisations
+    (damping, reverse Cholesky, normalised inverse; numpy / LAPACK) and the
+    recursive solve (C, OpenMP) of the leading sample x sample block of the
+    same layer (same grid rows, the leading blocks of A and B) -- by default
+    the whole layer, so nothing is extrapolated.  A smaller block is scaled
+    to the full layer by the work ratio mn(m+n) / (ms ns (ms+ns))."""
     from oracle import recursive as O2
     from oracle import reference as R
     ms, ns = min(m, sample), min(n, sample)
@@ -504,15 +566,24 @@ def cpu_baseline(d, sample, m, n):
     os.environ.setdefault("OMP_NUM_THREADS", str(cores))
     threads = int(os.environ["OMP_NUM_THREADS"])
     W = d["W"][:ms, :ns]
+    log(f"[bench] cpu oracle on {ms}x{ns} with {threads} threads ...")
     t0 = time.perf_counter()
     fa, fb = R.factor(d["A"][:ns, :ns]), R.factor(d["B"][:ms, :ms])
+    tf = time.perf_counter() - t0
+    log(f"[bench] cpu oracle factors: {tf:.2f}s")
     O2.bakron_recursive(W, fa["P"], fb["P"], d["scale"][:ms], d["zero"][:ms], d["maxq"][:ms])
     t = time.perf_counter() - t0
     scale = (float(m) * n * (m + n)) / (float(ms) * ns * (ms + ns))
-    log(f"[bench] cpu oracle on {ms}x{ns}: {t:.2f}s with {threads} threads (x{scale:.1f} to full size)")
+    model = cpu_model()
+    log(f"[bench] cpu oracle on {ms}x{ns}: {t:.2f}s ({tf:.2f}s factors) with {threads} threads on {model}")
+    if (ms, ns) == (m, n):
+        sample_txt = (f"the whole {m}x{n} layer: both float64 factorisations ({tf:.2f}s) and the recursive "
+                      f"float64 solve, measured, on {model}")
+    else:
+        sample_txt = (f"leading {ms}x{ns} block of the same layer (factors + recursive solve, float64), "
+                      f"{t:.2f}s measured on {model}, scaled by the cubic work ratio {scale:.2f}")
     return {"value": round(t * scale, 3), "unit": "s", "cores": threads, "kind": "oracle",
-            "sample": f"leading {ms}x{ns} block of the same layer (factor + recursive solve, float64), "
-                      f"{t:.2f}s measured, scaled by the cubic work ratio {scale:.2f}"}
+            "cpu_model": model, "measured_s": round(t, 3), "sample": sample_txt}
 
 
 if __name__ == "__main__":

@@ -51,6 +51,8 @@ extern "C" {
 #define BAKRON_ERR_BAD_ARG (-4)      /* damp_frac out of range, or a matrix pointer that
                                         must be 16-byte aligned is not */
 #define BAKRON_ERR_HIP (-5)          /* a HIP launch call failed */
+#define BAKRON_ERR_TOO_LARGE (-6)    /* the problem needs more scratch than the fixed
+                                        maximum of bakron_solve_noalloc */
 
 /* Largest supported m or n. */
 #define BAKRON_MAX_DIM 65536
@@ -161,6 +163,63 @@ int bakron_solve(const float* W, int64_t m, int64_t n,
                  const float* scale, const float* zero, const int32_t* maxq,
                  float* V, uint8_t* codes, float* err, double* objective,
                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * bakron_solve_grouped -- bakron_solve with one grid per (output row, group of
+ * group_size input columns) instead of one per row ([A] abstract: the base
+ * quantizer is modular).  Entry (i, j) is rounded on grid entry
+ * i * G + j / group_size of the arrays below, G = ceil(n / group_size)
+ * (static groups: every grid is a fixed input, as the per-row grid is, so
+ * the rounding rule of an entry does not depend on the order entries are
+ * visited in and [S] Theorem 3.2 still holds; a caller typically computes
+ * the grids from the original W's group slices).
+ *
+ * group_size [in] a positive multiple of 64 (BAKRON_ERR_BAD_ARG otherwise);
+ *                 group_size >= n gives G = 1, the per-row case.
+ * scale, zero, maxq [in] m x G row-major arrays, with the contract of
+ *                 bakron_solve's per-row grid on every entry.
+ * Everything else (arguments, workspace: bakron_solve_workspace_bytes,
+ * streams, errors) is bakron_solve's.
+ */
+int bakron_solve_grouped(const float* W, int64_t m, int64_t n,
+                         const float* L_A, const float* P_A,
+                         const float* L_B, const float* P_B,
+                         const float* scale, const float* zero, const int32_t* maxq,
+                         int64_t group_size,
+                         float* V, uint8_t* codes, float* err, double* objective,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes that bakron_solve_antidiagonal needs for an m x n weight
+ * (0 when m == 0 or n == 0): two Mp x Np float buffers, an Np x Np one, a
+ * padded Mp x Mp one when m is not a multiple of 64 and Mp doubles
+ * (Mp, Np: m, n rounded up to 64).  Host only.
+ */
+size_t bakron_solve_antidiagonal_workspace_bytes(int64_t m, int64_t n);
+
+/*
+ * bakron_solve_antidiagonal -- BaKron-antidiagonal ([S] derivation, second
+ * variant; Theorem 3.2; timed against BaKron in [S] Table 3): the same
+ * rounding as bakron_solve, computed one entry anti-diagonal i + j = k at a
+ * time.  The entries of D_k do not update one another, so they are rounded
+ * together, and their raw errors E_k reach every later entry through one
+ * rank-|D_k| product W~ -= P_B E_k P_A^T: m + n - 1 dependent steps but
+ * about m^2 n^2 / 2 multiply-adds (bakron_solve's divide and conquer needs
+ * mn(m + n) / 2).  The rounding rule and arithmetic of every entry are
+ * bakron_solve's (float32, the decision float32(w~ / scale) + zero); the
+ * products sum in another order, so codes may part from bakron_solve's only
+ * where a decision lies within float32 rounding of a boundary.
+ *
+ * Arguments, grid contract and errors are those of bakron_solve; workspace:
+ * bakron_solve_antidiagonal_workspace_bytes.  All work runs on `stream`
+ * (two kernel launches per anti-diagonal).
+ */
+int bakron_solve_antidiagonal(const float* W, int64_t m, int64_t n,
+                              const float* L_A, const float* P_A,
+                              const float* L_B, const float* P_B,
+                              const float* scale, const float* zero, const int32_t* maxq,
+                              float* V, uint8_t* codes, float* err, double* objective,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Workspace bytes that bakron_quantize needs for an m x n weight (0 when
@@ -288,6 +347,17 @@ int bakron_gptq(const float* W, int64_t m, int64_t n, const float* L_A, const fl
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * bakron_gptq_grouped -- bakron_gptq with per-group grids, read as in
+ * bakron_solve_grouped (group_size a positive multiple of 64; scale, zero and
+ * maxq m x ceil(n / group_size) row-major).  Workspace:
+ * bakron_gptq_workspace_bytes.
+ */
+int bakron_gptq_grouped(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                        const float* scale, const float* zero, const int32_t* maxq, int64_t group_size,
+                        float* V, uint8_t* codes, float* err, double* objective,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Kronecker factors from per-sample inputs ([S], Hessian choices): with
  * input activations a_t (n) and output gradients b_t (m) of N samples,
  *   K-FAC-style independence:          A = E[a a^T],        B = E[b b^T];
@@ -325,6 +395,41 @@ int bakron_row_sqnorms(const float* X, int64_t N, int64_t n, float* out, hipStre
  */
 int bakron_moment(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M,
                   hipStream_t stream);
+
+/*
+ * bakron_solve_noalloc -- bakron_solve with no workspace argument, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  It calls no hipMalloc,
+ * hipFree or other allocating routine, creates no stream or event, and
+ * enqueues only kernel launches on `stream`.
+ *
+ * Scratch: a file-scope device array of BAKRON_NOALLOC_SCRATCH_BYTES (256 MiB)
+ * inside the library; each GPU the library runs on holds its own copy until
+ * the process ends.  The problem fits when its unsplit solve workspace,
+ * bakron_solve_batch_workspace_bytes of the one layer on one stream, is at
+ * most that size (for m and n multiples of 64: 12 m n bytes plus a little,
+ * e.g. up to 4096 x 4096); larger problems return BAKRON_ERR_TOO_LARGE and
+ * enqueue nothing.  The scratch is looked up on the first call on each
+ * device (with that device current).
+ *
+ * Every call on one GPU uses that GPU's one scratch array: calls that overlap
+ * on one GPU (different streams not ordered against each other, or
+ * different host threads) race and their results are undefined.  Calls
+ * ordered on one stream are safe; nothing in the scratch must start at zero,
+ * so a call does not depend on what the previous one left there.
+ *
+ * Arguments, results and errors are those of bakron_solve (the results are
+ * bakron_solve's bit for bit), without workspace and workspace_bytes; all
+ * work runs on `stream` itself (no library-owned streams).
+ */
+#define BAKRON_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+int bakron_solve_noalloc(const float* W, int64_t m, int64_t n,
+                         const float* L_A, const float* P_A,
+                         const float* L_B, const float* P_B,
+                         const float* scale, const float* zero, const int32_t* maxq,
+                         float* V, uint8_t* codes, float* err, double* objective,
+                         hipStream_t stream);
 
 /*
  * Profiling.  The *_profiled calls enqueue exactly the work of the plain
@@ -369,6 +474,14 @@ int bakron_gptq_profiled(const float* W, int64_t m, int64_t n, const float* L_A,
                          float* V, uint8_t* codes, float* err, double* objective,
                          void* workspace, size_t workspace_bytes, hipStream_t stream,
                          bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
+
+int bakron_solve_antidiagonal_profiled(const float* W, int64_t m, int64_t n,
+                                       const float* L_A, const float* P_A,
+                                       const float* L_B, const float* P_B,
+                                       const float* scale, const float* zero, const int32_t* maxq,
+                                       float* V, uint8_t* codes, float* err, double* objective,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                       bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats);
 
 int bakron_moment_profiled(const float* X, int64_t N, int64_t n, const float* w, float scale, float* M,
                            hipStream_t stream, bakron_kernel_stat* stats, int32_t max_stats,

@@ -20,7 +20,9 @@
  * `leaf` x `leaf` entries run the naive rule: quantize one entry, then
  * W~[i', j'] -= e * PB[i', i] * PA[j', j] over the leaf's bottom-right part.
  *
- * Base quantizer (per output row, uniform grid): the decision
+ * Base quantizer (uniform grid per output row, or per (row, group of `group`
+ * input columns): entry (i, j) uses grid entry i * gld + j / group, so a
+ * per-row grid is group >= n, gld = 1; the grids are fixed inputs): the decision
  * x = float32(float32(w) / s) + z is taken in float32 arithmetic, the code is
  * clamp(rint(x), 0, maxq) (round half to even), the value is s (c - z) in
  * float64, and the raw error is e = w~ - value.
@@ -53,6 +55,7 @@ typedef struct {
     const float* s;
     const float* z;
     const int32_t* maxq;
+    int64_t group, gld;  /* grid of entry (i, j): index i * gld + j / group */
     double* Wt;         /* m x n working weights */
     double* E;          /* m x n raw errors */
     int32_t* codes;     /* m x n */
@@ -102,12 +105,13 @@ static void leaf_solve(ctx_t* X, int64_t r0, int64_t r1, int64_t c0, int64_t c1)
             int32_t c;
             double v;
             double w = X->Wt[i * n + j];
-            const float x = quant(w, X->s[i], X->z[i], X->maxq[i], &c, &v);
+            const int64_t gi = i * X->gld + j / X->group;
+            const float x = quant(w, X->s[gi], X->z[gi], X->maxq[gi], &c, &v);
             if (X->follow) {
                 const int32_t g = X->follow[i * n + j];
-                if ((g == c + 1 || g == c - 1) && margin_of(x, X->maxq[i]) < X->tau) {
+                if ((g == c + 1 || g == c - 1) && margin_of(x, X->maxq[gi]) < X->tau) {
                     c = g;
-                    v = (double)X->s[i] * ((double)c - (double)X->z[i]);
+                    v = (double)X->s[gi] * ((double)c - (double)X->z[gi]);
                     X->adoptions += 1;
                 }
             }
@@ -198,24 +202,28 @@ static void solve_block(ctx_t* X, int64_t r0, int64_t r1, int64_t c0, int64_t c1
 
 /*
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
- * W, PA, PB: float64 row-major; s, z: float32 grid; maxq: int32.
+ * W, PA, PB: float64 row-major; s, z: float32 grid; maxq: int32; entry
+ * (i, j) uses grid entry i * gld + j / group (per row: group >= n, gld = 1;
+ * per group of g columns: group = g, gld = ceil(n / g)).
  * Outputs codes (int32), V and E (float64), all m x n row-major.
  * follow (nullable, m x n int32) and tau select the tie-following mode;
  * *adoptions (nullable) receives the number of codes taken over.
  */
-int oracle_bakron_recursive_follow(int64_t m, int64_t n, const double* W, const double* PA,
-                                   const double* PB, const float* s, const float* z,
-                                   const int32_t* maxq, int64_t leaf, int32_t* codes,
-                                   double* V, double* E, const int32_t* follow, double tau,
-                                   int64_t* adoptions)
+int oracle_bakron_recursive_grouped(int64_t m, int64_t n, const double* W, const double* PA,
+                                    const double* PB, const float* s, const float* z,
+                                    const int32_t* maxq, int64_t group, int64_t gld, int64_t leaf,
+                                    int32_t* codes, double* V, double* E, const int32_t* follow,
+                                    double tau, int64_t* adoptions)
 {
     if (adoptions) *adoptions = 0;
-    if (m < 0 || n < 0 || leaf < 1) return -1;
+    if (m < 0 || n < 0 || leaf < 1 || group < 1 || gld < 1) return -1;
     if (m == 0 || n == 0) return 0;
     if (!W || !PA || !PB || !s || !z || !maxq || !codes || !V || !E) return -1;
+    if ((n - 1) / group >= gld) return -1;   /* the last column's group must exist */
     ctx_t X;
     X.m = m; X.n = n; X.leaf = leaf;
     X.PA = PA; X.PB = PB; X.s = s; X.z = z; X.maxq = maxq;
+    X.group = group; X.gld = gld;
     X.codes = codes; X.V = V; X.E = E;
     X.follow = follow; X.tau = tau; X.adoptions = 0;
     X.Wt = (double*)malloc(sizeof(double) * (size_t)(m * n));
@@ -229,6 +237,17 @@ int oracle_bakron_recursive_follow(int64_t m, int64_t n, const double* W, const 
     free(X.T);
     if (adoptions) *adoptions = X.adoptions;
     return 0;
+}
+
+/* Per-row grids (s, z, maxq of length m). */
+int oracle_bakron_recursive_follow(int64_t m, int64_t n, const double* W, const double* PA,
+                                   const double* PB, const float* s, const float* z,
+                                   const int32_t* maxq, int64_t leaf, int32_t* codes,
+                                   double* V, double* E, const int32_t* follow, double tau,
+                                   int64_t* adoptions)
+{
+    return oracle_bakron_recursive_grouped(m, n, W, PA, PB, s, z, maxq, n > 0 ? n : 1, 1, leaf, codes, V, E,
+                                           follow, tau, adoptions);
 }
 
 int oracle_bakron_recursive(int64_t m, int64_t n, const double* W, const double* PA,

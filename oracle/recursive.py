@@ -42,16 +42,22 @@ def _load():
         g.restype = ctypes.c_int
         g.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 6 + \
                      [ctypes.c_int64] + [ctypes.c_void_p] * 4 + [ctypes.c_double, ctypes.c_void_p]
+        h = lib.oracle_bakron_recursive_grouped
+        h.restype = ctypes.c_int
+        h.argtypes = [ctypes.c_int64, ctypes.c_int64] + [ctypes.c_void_p] * 6 + \
+                     [ctypes.c_int64] * 3 + [ctypes.c_void_p] * 4 + [ctypes.c_double, ctypes.c_void_p]
         _lib = lib
     return _lib
 
 
 def bakron_recursive(W, PA, PB, s, z, maxq, leaf: int = 32, threads: int | None = None, follow=None,
-                     tau: float = 1e-4):
+                     tau: float = 1e-4, group_size: int | None = None):
     """Returns (codes int32, V float64, E float64), all m x n.
 
     With ``follow`` (m x n codes of another implementation) the oracle runs in
-    tie-following mode (see recursive.c) and returns (codes, V, E, adoptions)."""
+    tie-following mode (see recursive.c) and returns (codes, V, E, adoptions).
+    Grids are per row (length m), or with ``group_size`` g per (row, group of
+    g columns), m x ceil(n / g)."""
     lib = _load()
     W = np.ascontiguousarray(W, dtype=np.float64)
     PA = np.ascontiguousarray(PA, dtype=np.float64)
@@ -60,28 +66,32 @@ def bakron_recursive(W, PA, PB, s, z, maxq, leaf: int = 32, threads: int | None 
     z = np.ascontiguousarray(z, dtype=np.float32)
     maxq = np.ascontiguousarray(maxq, dtype=np.int32)
     m, n = W.shape
-    if PA.shape != (n, n) or PB.shape != (m, m) or s.shape != (m,) or z.shape != (m,) or maxq.shape != (m,):
+    if group_size is None:
+        gshape, group, gld = (m,), max(n, 1), 1
+    else:
+        group = int(group_size)
+        gld = -(-n // group)
+        gshape = (m, gld)
+    if PA.shape != (n, n) or PB.shape != (m, m) or s.shape != gshape or z.shape != gshape or maxq.shape != gshape:
         raise ValueError("shape mismatch")
     codes = np.zeros((m, n), dtype=np.int32)
     V = np.zeros((m, n))
     E = np.zeros((m, n))
     if threads is not None:
         os.environ["OMP_NUM_THREADS"] = str(int(threads))
-    if follow is None:
-        rc = lib.oracle_bakron_recursive(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
-                                         s.ctypes.data, z.ctypes.data, maxq.ctypes.data, int(leaf),
-                                         codes.ctypes.data, V.ctypes.data, E.ctypes.data)
-        if rc != 0:
-            raise RuntimeError("oracle_bakron_recursive failed with %d" % rc)
-        return codes, V, E
-    fol = np.ascontiguousarray(follow, dtype=np.int32)
-    if fol.shape != (m, n):
-        raise ValueError("follow must be m x n")
+    fol = None
+    if follow is not None:
+        fol = np.ascontiguousarray(follow, dtype=np.int32)
+        if fol.shape != (m, n):
+            raise ValueError("follow must be m x n")
     adopt = ctypes.c_int64(0)
-    rc = lib.oracle_bakron_recursive_follow(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
-                                            s.ctypes.data, z.ctypes.data, maxq.ctypes.data, int(leaf),
-                                            codes.ctypes.data, V.ctypes.data, E.ctypes.data, fol.ctypes.data,
-                                            float(tau), ctypes.byref(adopt))
+    rc = lib.oracle_bakron_recursive_grouped(m, n, W.ctypes.data, PA.ctypes.data, PB.ctypes.data,
+                                             s.ctypes.data, z.ctypes.data, maxq.ctypes.data, group, gld, int(leaf),
+                                             codes.ctypes.data, V.ctypes.data, E.ctypes.data,
+                                             None if fol is None else fol.ctypes.data, float(tau),
+                                             ctypes.byref(adopt))
     if rc != 0:
-        raise RuntimeError("oracle_bakron_recursive_follow failed with %d" % rc)
+        raise RuntimeError("oracle_bakron_recursive_grouped failed with %d" % rc)
+    if follow is None:
+        return codes, V, E
     return codes, V, E, int(adopt.value)

@@ -27,6 +27,14 @@ Readings taken where the pages are silent (each is listed in the design doc):
   precision of the kernels, so that both sides decide in the same
   precision.  Everything else here is float64.
 * A clipped entry keeps its full error (GPTQ convention).
+* Per-group grids (the base quantizer is modular, [A]): with a group size g,
+  entry (i, j) is rounded on the grid (s, z, maxq)[i, j // g] -- static
+  groups along the input dimension, each grid a fixed input (computed by the
+  caller from the original W).  A grid that depended on the working weights
+  at the group's first column would depend on the order the entries are
+  visited in, and the forms below (Theorem 3.2) would no longer agree.
+  Every form takes the grid either per output row (1-D arrays, group_size
+  None) or per (row, group) (m x G arrays, G = ceil(n / group_size)).
 """
 from __future__ import annotations
 
@@ -36,7 +44,7 @@ __all__ = [
     "damp", "rev_cholesky", "normalized_inverse", "factor", "quantize",
     "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform", "gptq_columns",
     "kron_moment", "row_sqnorms", "kfac_factors", "shampoo_factors",
-    "objective", "objective_from_errors", "implied_errors", "implied_errors_p", "validate",
+    "objective", "objective_from_errors", "implied_errors", "implied_errors_p", "validate", "entry_grid",
     "order_colmajor", "order_rowmajor", "order_antidiagonal",
 ]
 
@@ -138,13 +146,35 @@ def quantize(w, s, z, maxq):
     return c, v
 
 
-def _values(codes, s, z):
-    return np.asarray(s, np.float64)[:, None] * (np.asarray(codes, np.float64) - np.asarray(z, np.float64)[:, None])
+def entry_grid(s, z, maxq, m, n, group_size=None):
+    """The grid of every entry as three m x n arrays: (s, z, maxq)[i] for a
+    per-row grid (1-D inputs, group_size None), (s, z, maxq)[i, j // g] for
+    per-group grids (m x G inputs, group_size g)."""
+    s, z, maxq = np.asarray(s), np.asarray(z), np.asarray(maxq)
+    if group_size is None:
+        if s.ndim != 1:
+            raise ValueError("per-row grids are 1-D; pass group_size with m x G grids")
+        cols = np.zeros(n, dtype=np.int64)
+        s, z, maxq = s[:, None], z[:, None], maxq[:, None]
+    else:
+        g = int(group_size)
+        G = -(-n // g) if n else 0
+        if s.shape != (m, G) or z.shape != (m, G) or maxq.shape != (m, G):
+            raise ValueError(f"per-group grids must be {m} x {G}")
+        cols = np.arange(n) // g
+    return (np.ascontiguousarray(s[:, cols]), np.ascontiguousarray(z[:, cols]),
+            np.ascontiguousarray(maxq[:, cols]))
+
+
+def _values(codes, s, z, group_size=None):
+    codes = np.asarray(codes, np.float64)
+    S, Z, _ = entry_grid(s, z, np.zeros(np.shape(s), np.int32), *codes.shape, group_size)
+    return S.astype(np.float64) * (codes - Z.astype(np.float64))
 
 
 # --------------------------------------------------- O1a: brute force on vec(W)
 
-def gptq_vectorized(W, Ad, Bd, s, z, maxq):
+def gptq_vectorized(W, Ad, Bd, s, z, maxq, group_size=None):
     """GPTQ run directly on vec(W) with the explicit Hessian H = Ad (x) Bd.
 
     This is the definition BaKron-naive starts from ([S], derivation: GPTQ in
@@ -158,6 +188,7 @@ def gptq_vectorized(W, Ad, Bd, s, z, maxq):
     m, n = W.shape
     if m * n > 4096:
         raise ValueError("brute force is limited to m*n <= 4096")
+    S, Z, Q = entry_grid(s, z, maxq, m, n, group_size)
     H = np.kron(np.asarray(Ad, np.float64), np.asarray(Bd, np.float64))
     Hinv = np.linalg.inv(H)
     Hinv = 0.5 * (Hinv + Hinv.T)
@@ -166,8 +197,8 @@ def gptq_vectorized(W, Ad, Bd, s, z, maxq):
     codes = np.zeros(m * n)
     vals = np.zeros(m * n)
     for p in range(m * n):
-        i = p % m
-        c, v = quantize(w[p], s[i], z[i], maxq[i])
+        i, j = p % m, p // m
+        c, v = quantize(w[p], S[i, j], Z[i, j], Q[i, j])
         codes[p], vals[p] = c, v
         err = (w[p] - v) / U[p, p]
         w[p:] -= err * U[p, p:]
@@ -188,7 +219,7 @@ def order_antidiagonal(m, n):
     return [(i, k - i) for k in range(m + n - 1) for i in range(max(0, k - n + 1), min(m - 1, k) + 1)]
 
 
-def bakron_naive(W, PA, PB, s, z, maxq, order=None):
+def bakron_naive(W, PA, PB, s, z, maxq, order=None, group_size=None):
     """BaKron-naive in the matrix domain ([S], derivation, first variant).
 
     One entry at a time; after quantizing (i, j) with raw error e, every entry
@@ -202,12 +233,13 @@ def bakron_naive(W, PA, PB, s, z, maxq, order=None):
     m, n = W.shape
     PA = np.asarray(PA, np.float64)
     PB = np.asarray(PB, np.float64)
+    S, Z, Q = entry_grid(s, z, maxq, m, n, group_size)
     Wt = W.copy()
     C = np.zeros((m, n))
     V = np.zeros((m, n))
     E = np.zeros((m, n))
     for (i, j) in (order if order is not None else order_colmajor(m, n)):
-        c, v = quantize(Wt[i, j], s[i], z[i], maxq[i])
+        c, v = quantize(Wt[i, j], S[i, j], Z[i, j], Q[i, j])
         e = Wt[i, j] - v
         C[i, j], V[i, j], E[i, j] = c, v, e
         Wt[i:, j:] -= e * np.outer(PB[i:, i], PA[j:, j])
@@ -216,7 +248,7 @@ def bakron_naive(W, PA, PB, s, z, maxq, order=None):
 
 # ------------------------------------- one-sided case B = I (GPTQ), by column
 
-def gptq_columns(W, PA, s, z, maxq, rows=None, follow=None, tau=1e-4):
+def gptq_columns(W, PA, s, z, maxq, rows=None, follow=None, tau=1e-4, group_size=None):
     """The one-sided case B = I of the rounding ([S] setup: GPTQ's Hessian is
     A (x) I; [N5]).  With P_B = I the update of BaKron-naive,
     W~[i', j'] -= e P_B[i', i] P_A[j', j], only reaches later columns of the
@@ -233,10 +265,10 @@ def gptq_columns(W, PA, s, z, maxq, rows=None, follow=None, tau=1e-4):
     """
     W = np.asarray(W, dtype=np.float64)
     PA = np.asarray(PA, np.float64)
-    s, z, maxq = np.asarray(s), np.asarray(z), np.asarray(maxq)
+    S, Z, Q = entry_grid(s, z, maxq, W.shape[0], W.shape[1], group_size)
     if rows is not None:
         rows = np.asarray(rows)
-        W, s, z, maxq = W[rows], s[rows], z[rows], maxq[rows]
+        W, S, Z, Q = W[rows], S[rows], Z[rows], Q[rows]
     m, n = W.shape
     Wt = W.copy()
     C = np.zeros((m, n))
@@ -244,6 +276,7 @@ def gptq_columns(W, PA, s, z, maxq, rows=None, follow=None, tau=1e-4):
     E = np.zeros((m, n))
     adopted = 0
     for j in range(n):
+        s, z, maxq = S[:, j], Z[:, j], Q[:, j]
         c, v = quantize(Wt[:, j], s, z, maxq)
         if follow is not None:
             x = (Wt[:, j].astype(_f32) / s.astype(_f32)).astype(_f32) + z.astype(_f32)
@@ -265,7 +298,7 @@ def gptq_columns(W, PA, s, z, maxq, rows=None, follow=None, tau=1e-4):
 
 # ------------------------------------------------ O1c: BaKron-antidiagonal
 
-def bakron_antidiagonal(W, PA, PB, s, z, maxq):
+def bakron_antidiagonal(W, PA, PB, s, z, maxq, group_size=None):
     """BaKron-antidiagonal ([S], derivation, second variant).
 
     All entries with i + j = k are quantized together (they do not update one
@@ -278,6 +311,7 @@ def bakron_antidiagonal(W, PA, PB, s, z, maxq):
     m, n = W.shape
     PA = np.asarray(PA, np.float64)
     PB = np.asarray(PB, np.float64)
+    S, Z, Q = entry_grid(s, z, maxq, m, n, group_size)
     Wt = W.copy()
     C = np.zeros((m, n))
     V = np.zeros((m, n))
@@ -285,7 +319,7 @@ def bakron_antidiagonal(W, PA, PB, s, z, maxq):
     for k in range(m + n - 1):
         ii = np.arange(max(0, k - n + 1), min(m - 1, k) + 1)
         jj = k - ii
-        c, v = quantize(Wt[ii, jj], np.asarray(s)[ii], np.asarray(z)[ii], np.asarray(maxq)[ii])
+        c, v = quantize(Wt[ii, jj], S[ii, jj], Z[ii, jj], Q[ii, jj])
         e = Wt[ii, jj] - v
         C[ii, jj], V[ii, jj], E[ii, jj] = c, v, e
         Ek = np.zeros((m, n))
@@ -296,7 +330,7 @@ def bakron_antidiagonal(W, PA, PB, s, z, maxq):
 
 # ------------------------------------------------ O1d: inverse-free L-form
 
-def bakron_lform(W, LA, LB, s, z, maxq, order=None):
+def bakron_lform(W, LA, LB, s, z, maxq, order=None, group_size=None):
     """The same rounding written with L(A), L(B) only (no inverse).
 
     From W - V = PB E PA^T and PB^-1 = diag(LB)^-1 LB (likewise for A), the
@@ -310,6 +344,7 @@ def bakron_lform(W, LA, LB, s, z, maxq, order=None):
     m, n = W.shape
     LA = np.asarray(LA, np.float64)
     LB = np.asarray(LB, np.float64)
+    S, Z, Q = entry_grid(s, z, maxq, m, n, group_size)
     D = np.zeros((m, n))          # (W - V) on processed entries, 0 elsewhere
     C = np.zeros((m, n))
     V = np.zeros((m, n))
@@ -317,7 +352,7 @@ def bakron_lform(W, LA, LB, s, z, maxq, order=None):
     for (i, j) in (order if order is not None else order_colmajor(m, n)):
         acc = LB[i, : i + 1] @ D[: i + 1, : j + 1] @ LA[j, : j + 1]
         wt = W[i, j] + acc / (LB[i, i] * LA[j, j])
-        c, v = quantize(wt, s[i], z[i], maxq[i])
+        c, v = quantize(wt, S[i, j], Z[i, j], Q[i, j])
         C[i, j], V[i, j], E[i, j] = c, v, wt - v
         D[i, j] = W[i, j] - v
     return C, V, E
@@ -367,7 +402,7 @@ def implied_errors_p(W, V, PA, PB) -> np.ndarray:
 # ----------------------------------------------------------------- validator
 
 def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None,
-             return_errors=False) -> dict:
+             return_errors=False, group_size=None) -> dict:
     """Check that ``codes`` is a BaKron output for (W, A (x) B, grid), any size.
 
     For a sequence of rounding decisions, the value entry (i, j) is rounded
@@ -388,15 +423,13 @@ def validate(W, codes, s, z, maxq, LA=None, LB=None, tau=1e-4, PA=None, PB=None,
     W = np.asarray(W, np.float64)
     m, n = W.shape
     codes = np.asarray(codes, np.float64)
-    V = _values(codes, s, z)
+    ss, zz, mq = entry_grid(s, z, maxq, m, n, group_size)
+    V = ss.astype(np.float64) * (codes - zz.astype(np.float64))
     if PA is not None:
         E = implied_errors_p(W, V, PA, PB)
     else:
         E = implied_errors(W, V, LA, LB)
     Wt = V + E
-    ss = np.broadcast_to(np.asarray(s)[:, None], (m, n))
-    zz = np.broadcast_to(np.asarray(z)[:, None], (m, n))
-    mq = np.broadcast_to(np.asarray(maxq)[:, None], (m, n))
     cexp, _ = quantize(Wt, ss, zz, mq)
     x = (Wt.astype(_f32) / ss.astype(_f32)).astype(_f32) + zz.astype(_f32)
     x = x.astype(np.float64)

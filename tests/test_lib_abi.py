@@ -34,7 +34,10 @@ def test_header_declares_the_api():
                             "bakron_gptq_workspace_bytes", "bakron_gptq", "bakron_gptq_profiled",
                             "bakron_row_sqnorms", "bakron_moment", "bakron_moment_profiled",
                             "bakron_solve_batch_workspace_bytes", "bakron_solve_batch",
-                            "bakron_quantize_workspace_bytes", "bakron_quantize"])
+                            "bakron_quantize_workspace_bytes", "bakron_quantize", "bakron_solve_noalloc",
+                            "bakron_solve_grouped", "bakron_gptq_grouped",
+                            "bakron_solve_antidiagonal_workspace_bytes", "bakron_solve_antidiagonal",
+                            "bakron_solve_antidiagonal_profiled"])
 
 
 def test_library_exports_every_declared_symbol(B):
@@ -49,7 +52,8 @@ def test_header_constants_match_binding(B):
     src = open(HEADER).read()
     from two_sided_hessian_amd import _binding as bb
     for k in ("BAKRON_SUCCESS", "BAKRON_ERR_NULL_POINTER", "BAKRON_ERR_BAD_SIZE", "BAKRON_ERR_WORKSPACE",
-              "BAKRON_ERR_BAD_ARG", "BAKRON_ERR_HIP", "BAKRON_MAX_DIM", "BAKRON_MAX_KERNEL_KINDS"):
+              "BAKRON_ERR_BAD_ARG", "BAKRON_ERR_HIP", "BAKRON_ERR_TOO_LARGE", "BAKRON_MAX_DIM",
+              "BAKRON_MAX_KERNEL_KINDS"):
         v = re.search(r"#define\s+%s\s+\(?(-?\d+)\)?" % k, src).group(1)
         assert int(v) == getattr(bb, k), k
 
@@ -166,6 +170,46 @@ def test_host_side_argument_errors(B):
     assert L.bakron_solve_batch(arr, 2, fake, 100, st, 2) == -3
     assert L.bakron_solve_batch(arr, 2, fake, 1 << 40, st, 0) == -4
     assert L.bakron_solve_batch(arr, 0, None, 0, None, 0) == 0
+    # bakron_solve_noalloc(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective, stream):
+    # the argument checks of bakron_solve, then the size check against its
+    # fixed scratch, all before any device call
+    na = [fake, 64, 64, fake, fake, fake, fake, fake, fake, fake, fake, fake, None, None, None]
+    a = list(na); a[4] = None
+    assert L.bakron_solve_noalloc(*a) == -1
+    a = list(na); a[2] = -5
+    assert L.bakron_solve_noalloc(*a) == -2
+    a = list(na); a[1] = 0
+    assert L.bakron_solve_noalloc(*a) == 0
+    a = list(na); a[13] = fake; a[5] = None         # objective requested without L_B
+    assert L.bakron_solve_noalloc(*a) == -1
+    a = list(na); a[6] = ctypes.c_void_p(4104)      # misaligned P_B
+    assert L.bakron_solve_noalloc(*a) == -4
+    a = list(na); a[1], a[2] = 8192, 8192           # 12 m n bytes, far beyond 256 MiB
+    assert L.bakron_solve_noalloc(*a) == -6
+    a = list(na); a[1], a[2] = 4096, 8192           # 384 MiB
+    assert L.bakron_solve_noalloc(*a) == -6
+    assert "noalloc" in B.strerror(-6)
+    # the unsplit workspace of a 4096 x 4096 layer fits the scratch
+    lay = Layer(f, 4096, 4096, f, f, f, f, f, f, f, f, f, None, None)
+    assert L.bakron_solve_batch_workspace_bytes((Layer * 1)(lay), 1, 1) <= B._binding.BAKRON_NOALLOC_SCRATCH_BYTES
+    # grouped grids: the group size must be a positive multiple of 64
+    sg = [fake, 64, 200, fake, fake, fake, fake, fake, fake, fake, 128, fake, fake, None, None, fake, 1 << 30, None]
+    for bad in (0, -64, 96, 1):
+        a = list(sg); a[10] = bad
+        assert L.bakron_solve_grouped(*a) == -4, bad
+    a = list(sg); a[0] = None
+    assert L.bakron_solve_grouped(*a) == -1
+    a = list(sg); a[16] = 100
+    assert L.bakron_solve_grouped(*a) == -3
+    a = list(sg); a[1] = 0
+    assert L.bakron_solve_grouped(*a) == 0
+    gg = [fake, 64, 200, fake, fake, fake, fake, fake, 64, fake, fake, None, None, fake, 1 << 30, None]
+    a = list(gg); a[8] = 32
+    assert L.bakron_gptq_grouped(*a) == -4
+    a = list(gg); a[4] = None
+    assert L.bakron_gptq_grouped(*a) == -1
+    a = list(gg); a[14] = 64
+    assert L.bakron_gptq_grouped(*a) == -3
     # one slice per stream, each sized for its largest layer
     one = L.bakron_solve_batch_workspace_bytes(arr, 2, 1)
     two = L.bakron_solve_batch_workspace_bytes(arr, 2, 2)

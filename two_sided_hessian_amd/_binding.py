@@ -22,7 +22,9 @@ BAKRON_ERR_BAD_SIZE = -2
 BAKRON_ERR_WORKSPACE = -3
 BAKRON_ERR_BAD_ARG = -4
 BAKRON_ERR_HIP = -5
+BAKRON_ERR_TOO_LARGE = -6
 BAKRON_MAX_DIM = 65536
+BAKRON_NOALLOC_SCRATCH_BYTES = 256 << 20
 
 # name -> (restype, argtypes); mirrors include/bakron.h
 _VP, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -34,10 +36,19 @@ SIGNATURES = {
     "bakron_solve_workspace_bytes": (_SZ, [_I64, _I64]),
     "bakron_solve": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
                                     _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "bakron_solve_grouped": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64,
+                                            _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
+    "bakron_gptq_grouped": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _I64, _VP, _VP, _VP, _VP,
+                                           _VP, _SZ, _VP]),
+    "bakron_solve_antidiagonal_workspace_bytes": (_SZ, [_I64, _I64]),
+    "bakron_solve_antidiagonal": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                                 _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "bakron_gptq_workspace_bytes": (_SZ, [_I64, _I64]),
     "bakron_gptq": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
     "bakron_row_sqnorms": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP]),
     "bakron_moment": (ctypes.c_int, [_VP, _I64, _I64, _VP, ctypes.c_float, _VP, _VP]),
+    "bakron_solve_noalloc": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, _VP, _VP, _VP, _VP, _VP,
+                                            _VP, _VP, _VP, _VP, _VP]),
     "bakron_quantize_workspace_bytes": (_SZ, [_I64, _I64]),
     "bakron_quantize": (ctypes.c_int, [_VP, _I64, _I64, _VP, _VP, ctypes.c_float, _VP, _VP, _VP,
                                        _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP]),
@@ -68,6 +79,8 @@ _PSTAT = ctypes.POINTER(KernelStat)
 SIGNATURES["bakron_factor_profiled"] = (ctypes.c_int, SIGNATURES["bakron_factor"][1] + [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_solve_profiled"] = (ctypes.c_int, SIGNATURES["bakron_solve"][1] + [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_gptq_profiled"] = (ctypes.c_int, SIGNATURES["bakron_gptq"][1] + [_PSTAT, ctypes.c_int32, _VP])
+SIGNATURES["bakron_solve_antidiagonal_profiled"] = (ctypes.c_int, SIGNATURES["bakron_solve_antidiagonal"][1] +
+                                                   [_PSTAT, ctypes.c_int32, _VP])
 SIGNATURES["bakron_moment_profiled"] = (ctypes.c_int, SIGNATURES["bakron_moment"][1] + [_PSTAT, ctypes.c_int32, _VP])
 
 _lib = None
@@ -209,19 +222,32 @@ def factor(A: torch.Tensor, damp_frac: float = 0.01, *, out=None, ws=None, strea
     return L, P, info
 
 
+def _grid_shape(m, n, group_size):
+    if group_size is None:
+        return (m,)
+    if group_size <= 0 or group_size % 64:
+        raise ValueError("group_size must be a positive multiple of 64")
+    return (m, -(-n // group_size))
+
+
 def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objective=True,
-          out=None, ws=None, stream=None, profile=None, check=True):
+          out=None, ws=None, stream=None, profile=None, check=True, group_size=None):
     """bakron_solve: returns dict(V, codes, err?, objective?) of device tensors.
     ``profile``: as in factor().  ``check``: check the grid contract first
     (check_grid; it reads the grid back to the host, so a caller that runs
-    the same grid many times may check it once and pass check=False)."""
+    the same grid many times may check it once and pass check=False).
+    ``group_size``: per-group grids (bakron_solve_grouped; scale, zero, maxq
+    m x ceil(n / group_size))."""
     m, n = W.shape
+    gshape = _grid_shape(m, n, group_size)
     _check_dev("W", W, torch.float32, (m, n))
     _check_dev("P_A", PA, torch.float32, (n, n))
     _check_dev("P_B", PB, torch.float32, (m, m))
-    _check_dev("scale", scale, torch.float32, (m,))
-    _check_dev("zero", zero, torch.float32, (m,))
-    _check_dev("maxq", maxq, torch.int32, (m,))
+    _check_dev("scale", scale, torch.float32, gshape)
+    _check_dev("zero", zero, torch.float32, gshape)
+    _check_dev("maxq", maxq, torch.int32, gshape)
+    if group_size is not None and profile is not None:
+        raise ValueError("the profiled solve takes per-row grids only")
     if want_objective:
         _check_dev("L_A", LA, torch.float32, (n, n))
         _check_dev("L_B", LB, torch.float32, (m, m))
@@ -244,6 +270,11 @@ def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objectiv
             _ptr(LB) if want_objective else None, _ptr(PB), _ptr(scale), _ptr(zero),
             _ptr(maxq), _ptr(out["V"]), _ptr(out["codes"]), _ptr(out.get("err")),
             _ptr(out.get("objective")), _ptr(ws), ws.numel(), _stream(stream)]
+    if group_size is not None:
+        rc = lib().bakron_solve_grouped(*(args[:10] + [int(group_size)] + args[10:]))
+        if rc != BAKRON_SUCCESS:
+            raise BakronError(rc, "bakron_solve_grouped")
+        return out
     if profile is None:
         rc = lib().bakron_solve(*args)
     else:
@@ -252,6 +283,82 @@ def solve(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objectiv
         profile.extend(_stats_list(arr, cnt))
     if rc != BAKRON_SUCCESS:
         raise BakronError(rc, "bakron_solve")
+    return out
+
+
+def solve_noalloc(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objective=True, out=None,
+                  stream=None, check=True):
+    """bakron_solve_noalloc (no workspace: the library's fixed device scratch;
+    the results are bakron_solve's).  Returns dict(V, codes, err?,
+    objective?); with ``out`` given, allocates nothing.  ``check``: as in
+    solve()."""
+    m, n = W.shape
+    _check_dev("W", W, torch.float32, (m, n))
+    _check_dev("P_A", PA, torch.float32, (n, n))
+    _check_dev("P_B", PB, torch.float32, (m, m))
+    _check_dev("scale", scale, torch.float32, (m,))
+    _check_dev("zero", zero, torch.float32, (m,))
+    _check_dev("maxq", maxq, torch.int32, (m,))
+    if want_objective:
+        _check_dev("L_A", LA, torch.float32, (n, n))
+        _check_dev("L_B", LB, torch.float32, (m, m))
+    if check:
+        check_grid(scale, zero, maxq)
+    dev = W.device
+    if out is None:
+        out = {"V": torch.empty((m, n), dtype=torch.float32, device=dev),
+               "codes": torch.empty((m, n), dtype=torch.uint8, device=dev)}
+        if want_err:
+            out["err"] = torch.empty((m, n), dtype=torch.float32, device=dev)
+        if want_objective:
+            out["objective"] = torch.empty((1,), dtype=torch.float64, device=dev)
+    rc = lib().bakron_solve_noalloc(_ptr(W), m, n, _ptr(LA) if want_objective else None, _ptr(PA),
+                                    _ptr(LB) if want_objective else None, _ptr(PB), _ptr(scale), _ptr(zero),
+                                    _ptr(maxq), _ptr(out["V"]), _ptr(out["codes"]), _ptr(out.get("err")),
+                                    _ptr(out.get("objective")), _stream(stream))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_solve_noalloc")
+    return out
+
+
+def solve_antidiagonal(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_objective=True, out=None,
+                       ws=None, stream=None, profile=None, check=True):
+    """bakron_solve_antidiagonal (one entry anti-diagonal per step): returns
+    dict(V, codes, err?, objective?) of device tensors.  ``profile``: as in
+    factor(); ``check``: as in solve()."""
+    m, n = W.shape
+    _check_dev("W", W, torch.float32, (m, n))
+    _check_dev("P_A", PA, torch.float32, (n, n))
+    _check_dev("P_B", PB, torch.float32, (m, m))
+    _check_dev("scale", scale, torch.float32, (m,))
+    _check_dev("zero", zero, torch.float32, (m,))
+    _check_dev("maxq", maxq, torch.int32, (m,))
+    if want_objective:
+        _check_dev("L_A", LA, torch.float32, (n, n))
+        _check_dev("L_B", LB, torch.float32, (m, m))
+    if check:
+        check_grid(scale, zero, maxq)
+    dev = W.device
+    if out is None:
+        out = {"V": torch.empty((m, n), dtype=torch.float32, device=dev),
+               "codes": torch.empty((m, n), dtype=torch.uint8, device=dev)}
+        if want_err:
+            out["err"] = torch.empty((m, n), dtype=torch.float32, device=dev)
+        if want_objective:
+            out["objective"] = torch.empty((1,), dtype=torch.float64, device=dev)
+    if ws is None:
+        ws = workspace(lib().bakron_solve_antidiagonal_workspace_bytes(m, n), dev)
+    args = [_ptr(W), m, n, _ptr(LA) if want_objective else None, _ptr(PA), _ptr(LB) if want_objective else None,
+            _ptr(PB), _ptr(scale), _ptr(zero), _ptr(maxq), _ptr(out["V"]), _ptr(out["codes"]), _ptr(out.get("err")),
+            _ptr(out.get("objective")), _ptr(ws), ws.numel(), _stream(stream)]
+    if profile is None:
+        rc = lib().bakron_solve_antidiagonal(*args)
+    else:
+        arr, cnt = _stats_out()
+        rc = lib().bakron_solve_antidiagonal_profiled(*args, arr, BAKRON_MAX_KERNEL_KINDS, ctypes.byref(cnt))
+        profile.extend(_stats_list(arr, cnt))
+    if rc != BAKRON_SUCCESS:
+        raise BakronError(rc, "bakron_solve_antidiagonal")
     return out
 
 
@@ -303,16 +410,19 @@ def quantize(W, A, B, scale, zero, maxq, damp_frac: float = 0.01, *, want_err=Fa
 
 
 def gptq(W, LA, PA, scale, zero, maxq, *, want_err=False, want_objective=True, out=None, ws=None, stream=None,
-         profile=None, check=True):
+         profile=None, check=True, group_size=None):
     """bakron_gptq (the one-sided case B = I): returns dict(V, codes, err?,
-    objective?) of device tensors.  ``profile``: as in factor(); ``check``:
-    as in solve()."""
+    objective?) of device tensors.  ``profile``: as in factor(); ``check``
+    and ``group_size`` (bakron_gptq_grouped): as in solve()."""
     m, n = W.shape
+    gshape = _grid_shape(m, n, group_size)
     _check_dev("W", W, torch.float32, (m, n))
     _check_dev("P_A", PA, torch.float32, (n, n))
-    _check_dev("scale", scale, torch.float32, (m,))
-    _check_dev("zero", zero, torch.float32, (m,))
-    _check_dev("maxq", maxq, torch.int32, (m,))
+    _check_dev("scale", scale, torch.float32, gshape)
+    _check_dev("zero", zero, torch.float32, gshape)
+    _check_dev("maxq", maxq, torch.int32, gshape)
+    if group_size is not None and profile is not None:
+        raise ValueError("the profiled one-sided call takes per-row grids only")
     if want_objective:
         _check_dev("L_A", LA, torch.float32, (n, n))
     if check:
@@ -333,6 +443,11 @@ def gptq(W, LA, PA, scale, zero, maxq, *, want_err=False, want_objective=True, o
     args = [_ptr(W), m, n, _ptr(LA) if want_objective else None, _ptr(PA), _ptr(scale), _ptr(zero), _ptr(maxq),
             _ptr(out["V"]), _ptr(out["codes"]), _ptr(out.get("err")), _ptr(out.get("objective")), _ptr(ws),
             ws.numel(), _stream(stream)]
+    if group_size is not None:
+        rc = lib().bakron_gptq_grouped(*(args[:8] + [int(group_size)] + args[8:]))
+        if rc != BAKRON_SUCCESS:
+            raise BakronError(rc, "bakron_gptq_grouped")
+        return out
     if profile is None:
         rc = lib().bakron_gptq(*args)
     else:

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libbakron.so")
-SOURCES = ["factor.hip", "solve.hip", "gptq.hip", "kfac.hip", "capi.hip"]
+SOURCES = ["factor.hip", "solve.hip", "gptq.hip", "kfac.hip", "antidiag.hip", "capi.hip", "noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -25,6 +25,7 @@ const char* bakron_strerror(int code)
     case BAKRON_ERR_WORKSPACE: return "workspace NULL, too small or not 256-byte aligned";
     case BAKRON_ERR_BAD_ARG: return "scalar argument out of range";
     case BAKRON_ERR_HIP: return "HIP kernel launch failed";
+    case BAKRON_ERR_TOO_LARGE: return "problem needs more scratch than bakron_solve_noalloc's fixed maximum";
     default: return "unknown bakron error code";
     }
 }
@@ -117,6 +118,69 @@ int bakron_solve_profiled(const float* W, int64_t m, int64_t n, const float* L_A
     bk::Prof prof;
     const int rc = bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective,
                                      workspace, stream, &prof);
+    const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
+    return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
+}
+
+int bakron_solve_grouped(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                         const float* L_B, const float* P_B, const float* scale, const float* zero,
+                         const int32_t* maxq, int64_t group_size, float* V, uint8_t* codes, float* err,
+                         double* objective, void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (group_size <= 0 || group_size % bk::kTile != 0) return BAKRON_ERR_BAD_ARG;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !P_A || !P_B || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && (!L_A || !L_B)) return BAKRON_ERR_NULL_POINTER;
+    if (!bk::aligned16(P_A) || !bk::aligned16(P_B)) return BAKRON_ERR_BAD_ARG;
+    const int w = check_ws(workspace, workspace_bytes, bk::solve_workspace_bytes(m, n));
+    if (w) return w;
+    return bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective,
+                             workspace, stream, nullptr, true, nullptr, group_size)
+               ? BAKRON_ERR_HIP
+               : BAKRON_SUCCESS;
+}
+
+size_t bakron_solve_antidiagonal_workspace_bytes(int64_t m, int64_t n)
+{
+    if (m <= 0 || n <= 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return 0;
+    return bk::antidiag_workspace_bytes(m, n);
+}
+
+int bakron_solve_antidiagonal(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                              const float* L_B, const float* P_B, const float* scale, const float* zero,
+                              const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !P_A || !P_B || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && (!L_A || !L_B)) return BAKRON_ERR_NULL_POINTER;
+    const int w = check_ws(workspace, workspace_bytes, bk::antidiag_workspace_bytes(m, n));
+    if (w) return w;
+    return bk::antidiag_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective, workspace,
+                                stream, nullptr)
+               ? BAKRON_ERR_HIP
+               : BAKRON_SUCCESS;
+}
+
+int bakron_solve_antidiagonal_profiled(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                                       const float* L_B, const float* P_B, const float* scale, const float* zero,
+                                       const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
+                                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                       bakron_kernel_stat* stats, int32_t max_stats, int32_t* n_stats)
+{
+    if (!n_stats || (max_stats > 0 && !stats)) return BAKRON_ERR_NULL_POINTER;
+    *n_stats = 0;
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    if (!W || !P_A || !P_B || !scale || !zero || !maxq || !V || !codes) return BAKRON_ERR_NULL_POINTER;
+    if (objective && (!L_A || !L_B)) return BAKRON_ERR_NULL_POINTER;
+    const int w = check_ws(workspace, workspace_bytes, bk::antidiag_workspace_bytes(m, n));
+    if (w) return w;
+    bk::Prof prof;
+    const int rc = bk::antidiag_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective,
+                                        workspace, stream, &prof);
     const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
     return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
 }
@@ -282,6 +346,22 @@ int bakron_gptq(const float* W, int64_t m, int64_t n, const float* L_A, const fl
                : BAKRON_SUCCESS;
 }
 
+int bakron_gptq_grouped(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
+                        const float* scale, const float* zero, const int32_t* maxq, int64_t group_size, float* V,
+                        uint8_t* codes, float* err, double* objective, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream)
+{
+    if (m < 0 || n < 0 || m > BAKRON_MAX_DIM || n > BAKRON_MAX_DIM) return BAKRON_ERR_BAD_SIZE;
+    if (group_size <= 0 || group_size % bk::kTile != 0) return BAKRON_ERR_BAD_ARG;
+    if (m == 0 || n == 0) return BAKRON_SUCCESS;
+    const int c = check_gptq(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, objective, workspace, workspace_bytes);
+    if (c) return c;
+    return bk::gptq_enqueue(W, m, n, L_A, P_A, scale, zero, maxq, V, codes, err, objective, workspace, stream,
+                            nullptr, group_size)
+               ? BAKRON_ERR_HIP
+               : BAKRON_SUCCESS;
+}
+
 int bakron_gptq_profiled(const float* W, int64_t m, int64_t n, const float* L_A, const float* P_A,
                          const float* scale, const float* zero, const int32_t* maxq, float* V, uint8_t* codes,
                          float* err, double* objective, void* workspace, size_t workspace_bytes, hipStream_t stream,
@@ -353,7 +433,7 @@ const char* kernel_name(int kind)
         "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish", "k_gptq_load",
         "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj", "k_row_sqnorms", "k_moment<false>",
         "k_moment<true>", "k_prop_rows_far", "k_prop_rows_t_far", "k_prop_cols_far", "k_prop_cols_t_far",
-        "k_prop_pair"};
+        "k_prop_pair", "k_ad_prep", "k_ad_quant", "k_ad_update"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 

@@ -31,6 +31,8 @@
 //   PAp Np x Np  padded copy of P_A, only when n is not a multiple of 64
 #include <algorithm>
 
+#include <limits.h>
+
 #include "gemm.hpp"
 #include "internal.hpp"
 
@@ -69,9 +71,11 @@ struct SweepArgs {
     int64_t ldw;
     const float* PA;      // P_A (pitch lda)
     int64_t lda;
-    const float* scale;
+    const float* scale;   // grid of row i in this column block: index i * gld + gcol
     const float* zero;
     const int32_t* maxq;
+    int64_t gld;          // grid pitch: 1 (per row) or the number of column groups
+    int gtiles;           // 64-column blocks per column group (huge for per-row grids)
     int m, n;
     uint8_t* codes;       // m x n outputs (pitch n)
     float* V;
@@ -188,9 +192,10 @@ __global__ __launch_bounds__(256) void k_gptq_sweep(SweepArgs g)
     const f32x4 wb = *reinterpret_cast<const f32x4*>(wp + 4);
     float w[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
     const bool row_ok = grow < g.m;
-    const float sc = row_ok ? g.scale[grow] : 1.f;
-    const float zc = row_ok ? g.zero[grow] : 0.f;
-    const float mq = row_ok ? (float)g.maxq[grow] : 0.f;
+    const int64_t gi = grow * g.gld + g.J / g.gtiles;   // the block lies in one column group
+    const float sc = row_ok ? g.scale[gi] : 1.f;
+    const float zc = row_ok ? g.zero[gi] : 0.f;
+    const float mq = row_ok ? (float)g.maxq[gi] : 0.f;
     const float sinv = 1.f / sc;   // correctly rounded
     // columns of this block that exist (all 64 unless n is ragged); a
     // padding row keeps zero errors through col_ok = false
@@ -447,7 +452,7 @@ size_t gptq_workspace_bytes(int64_t m, int64_t n)
 
 int gptq_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA, const float* scale,
                  const float* zero, const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                 void* ws, hipStream_t s, Prof* prof)
+                 void* ws, hipStream_t s, Prof* prof, int64_t group_size)
 {
     // Rows are padded to a multiple of 64 so that the 64 x 64 update tiles
     // stay inside the workspace; sweeps cover the same padded rows.
@@ -477,6 +482,8 @@ int gptq_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const fl
     g.scale = scale;
     g.zero = zero;
     g.maxq = maxq;
+    g.gld = group_size > 0 ? ceil_div(n, group_size) : 1;
+    g.gtiles = group_size > 0 ? (int)(group_size / kTile) : INT_MAX;
     g.m = (int)m;
     g.n = (int)n;
     g.codes = codes;

@@ -27,7 +27,7 @@ enum KernelKind {
     KK_F_CLEAR, KK_F_MEAN, KK_F_LOAD, KK_F_DIAG, KK_F_PANEL, KK_F_PANEL_T, KK_F_SYRK_T, KK_F_RIGHT, KK_F_RIGHT_T,
     KK_F_LEFT, KK_F_LEFT_T, KK_F_FINISH, KK_G_LOAD, KK_G_SWEEP, KK_G_UPDATE, KK_G_UPDATE_T, KK_G_OBJ,
     KK_K_SQNORM, KK_K_MOMENT, KK_K_MOMENT_W, KK_PROP_ROWS_FAR, KK_PROP_ROWS_T_FAR, KK_PROP_COLS_FAR,
-    KK_PROP_COLS_T_FAR, KK_PROP_PAIR, KK_COUNT
+    KK_PROP_COLS_T_FAR, KK_PROP_PAIR, KK_AD_PREP, KK_AD_QUANT, KK_AD_UPDATE, KK_COUNT
 };
 static_assert(KK_COUNT <= BAKRON_MAX_KERNEL_KINDS, "kernel kinds exceed the ABI's statistics capacity");
 
@@ -135,16 +135,26 @@ struct SolveWait {
     FactorLeads lead[2];
     hipEvent_t full[2];
 };
+// group_size 0: one grid per row (scale, zero, maxq of length m); otherwise
+// a multiple of 64: one grid per (row, group of group_size columns), m x
+// ceil(n / group_size) row-major.
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,
                   const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                  void* ws, hipStream_t stream, Prof* prof, bool split = true, const SolveWait* wait = nullptr);
+                  void* ws, hipStream_t stream, Prof* prof, bool split = true, const SolveWait* wait = nullptr,
+                  int64_t group_size = 0);
+
+// BaKron-antidiagonal: one entry anti-diagonal per step (antidiag.hip)
+size_t antidiag_workspace_bytes(int64_t m, int64_t n);
+int antidiag_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA, const float* LB,
+                     const float* PB, const float* scale, const float* zero, const int32_t* maxq, float* V,
+                     uint8_t* codes, float* err, double* objective, void* ws, hipStream_t stream, Prof* prof);
 
 // One-sided case B = I (gptq.hip)
 size_t gptq_workspace_bytes(int64_t m, int64_t n);
 int gptq_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA, const float* scale,
                  const float* zero, const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                 void* ws, hipStream_t stream, Prof* prof);
+                 void* ws, hipStream_t stream, Prof* prof, int64_t group_size = 0);
 
 // Kronecker factors from per-sample inputs (kfac.hip)
 int sqnorms_enqueue(const float* X, int64_t N, int64_t n, float* out, hipStream_t s, Prof* prof);

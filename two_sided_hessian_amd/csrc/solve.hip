@@ -83,9 +83,11 @@ struct LeafArgs {
     int64_t lda;
     const float* PB;      // P_B (pitch ldb)
     int64_t ldb;
-    const float* scale;
+    const float* scale;   // grid of row i, tile column J: index i * gld + J / gtiles
     const float* zero;
     const int32_t* maxq;
+    int64_t gld;          // grid pitch: 1 (per row) or the number of column groups
+    int gtiles;           // tiles per column group (group size / 64; huge for per-row grids)
     int m, n;
     uint8_t* codes;       // m x n outputs (pitch n)
     float* V;
@@ -301,9 +303,11 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
     L.am1 = a > 0 ? a - 1 : 0;
     L.pbm1 = a > 0 ? g.PB[(r0 + a) * g.ldb + r0 + a - 1] : 0.f;   // P_B[a][a-1]
     L.row_ok = grow < g.m;
-    L.sc = L.row_ok ? g.scale[grow] : 1.f;
-    L.zc = L.row_ok ? g.zero[grow] : 0.f;
-    L.mq = L.row_ok ? (float)g.maxq[grow] : 0.f;
+    const int gcol = J / g.gtiles;   // this tile's column group (every column of a tile is in one group)
+    const int64_t gi = grow * g.gld + gcol;
+    L.sc = L.row_ok ? g.scale[gi] : 1.f;
+    L.zc = L.row_ok ? g.zero[gi] : 0.f;
+    L.mq = L.row_ok ? (float)g.maxq[gi] : 0.f;
     L.sinv = 1.f / L.sc;   // correctly rounded
     L.c0 = c0;
     L.n = g.n;
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
         *reinterpret_cast<f32x4*>(g.E + orow * g.ldw + c0 + cs + 4 * q) =
             *reinterpret_cast<const f32x4*>(sF + row * kLP + cs + 4 * q);
     if (orow < g.m) {
-        const float so = g.scale[orow], zo = g.zero[orow];
+        const float so = g.scale[orow * g.gld + gcol], zo = g.zero[orow * g.gld + gcol];
         if (g.vec_out) {
             *reinterpret_cast<uint2*>(g.codes + orow * g.n + c0 + cs) =
                 *reinterpret_cast<const uint2*>(sC + row * 64 + cs);
@@ -1290,7 +1294,7 @@ size_t solve_workspace_bytes(int64_t m, int64_t n, bool split)
 int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const float* PA,
                   const float* LB, const float* PB, const float* scale, const float* zero,
                   const int32_t* maxq, float* V, uint8_t* codes, float* err, double* objective,
-                  void* ws, hipStream_t s, Prof* prof, bool split, const SolveWait* wait)
+                  void* ws, hipStream_t s, Prof* prof, bool split, const SolveWait* wait, int64_t group_size)
 {
     SolvePlan p = plan_solve(m, n, split);
     char* w = static_cast<char*>(ws);
@@ -1350,6 +1354,8 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     g.scale = scale;
     g.zero = zero;
     g.maxq = maxq;
+    g.gld = group_size > 0 ? ceil_div(n, group_size) : 1;
+    g.gtiles = group_size > 0 ? (int)(group_size / kTile) : INT_MAX;
     g.m = (int)m;
     g.n = (int)n;
     g.codes = codes;

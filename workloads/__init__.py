@@ -23,6 +23,10 @@ scales and G; then, for mixed precision, the row permutation):
 * Grid of row i: s_i = (max_j W_ij - min_j W_ij) / maxq_i and
   z_i = -min_j W_ij / s_i (fractional zero point), computed in float64 and
   then rounded to float32; both sides use those float32 values.
+* Per-group grids (``group_size`` g): the same min-max rule on each row's
+  slice of g columns of the original W (static groups; the last group may
+  be shorter), giving m x ceil(n / g) arrays; every group of a row keeps
+  the row's maxq.
 * W, A, B are rounded to float32 at the end.
 
 The named configurations stand in for the transformer layers that the pages
@@ -36,7 +40,8 @@ import hashlib
 
 import numpy as np
 
-__all__ = ["Spec", "CONFIGS", "by_name", "generate", "samples", "make_problem", "grid_minmax", "digest"]
+__all__ = ["Spec", "CONFIGS", "by_name", "generate", "samples", "make_problem", "grid_minmax", "grid_groups",
+           "digest"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -90,6 +95,22 @@ def grid_minmax(W: np.ndarray, maxq: np.ndarray):
     return s.astype(np.float32), z.astype(np.float32)
 
 
+def grid_groups(W: np.ndarray, maxq: np.ndarray, group_size: int):
+    """Asymmetric min-max grids per (row, group of group_size columns) of the
+    original W: scale, zero (float32) and maxq (int32), each m x G."""
+    W = np.asarray(W, dtype=np.float64)
+    m, n = W.shape
+    g = int(group_size)
+    if g < 1:
+        raise ValueError("group_size must be positive")
+    G = -(-n // g)
+    s = np.empty((m, G), np.float32)
+    z = np.empty((m, G), np.float32)
+    for k in range(G):
+        s[:, k], z[:, k] = grid_minmax(W[:, k * g:(k + 1) * g], maxq)
+    return s, z, np.repeat(np.asarray(maxq, np.int32)[:, None], G, axis=1)
+
+
 def _draw_samples(rng, dim, samples, lognormal):
     """dim x samples draws (feature-major), with log-normal channel scales."""
     if lognormal:
@@ -109,11 +130,12 @@ def _draw_w(rng, spec):
     raise ValueError(spec.w_dist)
 
 
-def generate(spec: Spec, seed: int | None = None, global_grid: bool = False) -> dict:
+def generate(spec: Spec, seed: int | None = None, global_grid: bool = False, group_size: int | None = None) -> dict:
     """Draw one workload; returns float32 W, A, B, scale, zero and int32 maxq.
 
     ``global_grid`` replaces the per-row grid by one grid for the whole
-    matrix (same step and zero point on every row; needed when n == 1)."""
+    matrix (same step and zero point on every row; needed when n == 1).
+    ``group_size`` gives per-group grids (scale, zero, maxq m x G) instead."""
     rng = np.random.default_rng(spec.seed if seed is None else seed)
     m, n = spec.m, spec.n
     W = _draw_w(rng, spec)
@@ -128,7 +150,9 @@ def generate(spec: Spec, seed: int | None = None, global_grid: bool = False) -> 
         rows = rng.permutation(m)[: spec.mixed_low_rows]
         maxq[rows] = 2 ** (spec.bits - 1) - 1
     W32 = W.astype(np.float32)
-    if global_grid:
+    if group_size is not None:
+        s, z, maxq = grid_groups(W32, maxq, group_size)
+    elif global_grid:
         s, z = grid_minmax(W32.reshape(1, -1), maxq[:1])
         s = np.full(m, s[0], dtype=np.float32)
         z = np.full(m, z[0], dtype=np.float32)
@@ -161,11 +185,12 @@ def samples(spec: Spec, seed: int | None = None) -> dict:
 
 
 def make_problem(m: int, n: int, seed: int, bits: int = 3, samples: int | None = None,
-                 lognormal: bool = True, w_scale: float = 0.02, global_grid: bool = False) -> dict:
+                 lognormal: bool = True, w_scale: float = 0.02, global_grid: bool = False,
+                 group_size: int | None = None) -> dict:
     """A small workload with the same recipe at an arbitrary shape (tests)."""
     spec = Spec(f"p{m}x{n}s{seed}", m, n, "normal", w_scale,
                 samples if samples is not None else 2 * max(m, n), lognormal, bits, seed=seed)
-    return generate(spec, global_grid=global_grid)
+    return generate(spec, global_grid=global_grid, group_size=group_size)
 
 
 def digest(d: dict) -> str:
