@@ -55,9 +55,29 @@ def main():
                     help="skip the secondary paths (the one-sided case B = I) measured beside the step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration) and exit")
+    ap.add_argument("--pmc-digest", nargs="+", metavar="DIR",
+                    help="only summarise rocprofv3 --pmc output directories (per kernel, per dispatch) and exit")
+    ap.add_argument("--traffic-digest", nargs=4, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE"),
+                    help="only turn FETCH_SIZE / WRITE_SIZE runs and their copy calibrations into "
+                         "profiles/traffic_<config>.{json,md} and exit")
+    ap.add_argument("--stats-digest", metavar="DIR",
+                    help="only summarise a rocprofv3 --kernel-trace --stats output directory and exit "
+                         "(with --bench-log, the per-kernel times of that bench run's profiled pass beside it)")
+    ap.add_argument("--bench-log", default="", help="stderr of the bench run that --stats-digest profiled")
+    ap.add_argument("--digest-title", default="", help="title line of the --pmc-digest summary")
+    ap.add_argument("--digest-command", default="", help="command line recorded in a digest")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+    if args.pmc_digest:
+        print(pmc_digest(args.pmc_digest, args.digest_title, args.digest_command))
+        return
+    if args.traffic_digest:
+        traffic_digest(args.traffic_digest, args.config, args.digest_command)
+        return
+    if args.stats_digest:
+        print(stats_digest(args.stats_digest, args.bench_log, args.digest_title, args.digest_command))
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -227,6 +247,8 @@ def main():
         nxt = {"gptq": bench_gptq(B, T, fa, m, n, args, traffic)}
         nxt.update(bench_factors(B, WL, spec, dev, args, traffic))
         nxt["batch"] = bench_batch(B, WL, dev, args)
+        nxt["grouped"] = bench_grouped(B, WL, spec, T, fa, fb, dev, args)
+        nxt["antidiagonal"] = bench_antidiagonal(B, WL, T, fa, fb, m, n, dev, args)
 
     cpu = None
     if args.cpu_sample != 0:
@@ -416,6 +438,100 @@ def bench_batch(B, WL, dev, args, layers=16, name="sq1024"):
     return res
 
 
+def bench_grouped(B, WL, spec, T, fa, fb, dev, args, group=128):
+    """Per-group grids (groups of `group` input columns, grids from the
+    original W's group slices) on the same layer and the step's factors: the
+    two-sided solve (bakron_solve_grouped) and the one-sided call
+    (bakron_gptq_grouped), mean time over args.steps calls after args.warmup."""
+    import torch
+    m, n = spec.m, spec.n
+    d = WL.generate(spec, group_size=group)
+    g = [torch.from_numpy(np.ascontiguousarray(d[k])).to(dev) for k in ("scale", "zero", "maxq")]
+    B.check_grid(*g)
+    ws = B._binding.workspace(B.solve_workspace_bytes(m, n), dev)
+    out = {"V": torch.empty((m, n), device=dev), "codes": torch.empty((m, n), dtype=torch.uint8, device=dev),
+           "objective": torch.empty(1, dtype=torch.float64, device=dev)}
+    stream = torch.cuda.current_stream()
+    res = {"group_size": group, "grid": f"{m}x{g[0].shape[1]}"}
+    for name, fn in (("solve_grouped", lambda: B.solve(T["W"], fa[0], fa[1], fb[0], fb[1], *g, out=out, ws=ws,
+                                                       stream=stream, check=False, group_size=group)),
+                     ("gptq_grouped", lambda: B.gptq(T["W"], fa[0], fa[1], *g, out=out, ws=ws, stream=stream,
+                                                     check=False, group_size=group))):
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        res[name] = {"ms": round(ms, 4), "objective": float(out["objective"].item())}
+        log(f"[bench] {name} (groups of {group}): {ms:.3f} ms")
+    return res
+
+
+def bench_antidiagonal(B, WL, T, fa, fb, m, n, dev, args, limit_s=60.0):
+    """BaKron-antidiagonal (bakron_solve_antidiagonal: m + n - 1 dependent
+    steps, each a rank-|D| update of the bottom-right remainder) against the
+    solve: one call on the 4096 x 4096 Student-t layer (its own GPU factors)
+    and one on this layer (the step's factors) when the 4096^2 time predicts
+    it within `limit_s` (the work grows as m^2 n^2).  Algorithmic work
+    m (m + 1) n (n + 1) / 2 flops: every entry pushes its error into its
+    whole bottom-right block."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def one(W, LA, PA, LB, PB, s, z, q, mm, nn):
+        ws = B._binding.workspace(B.lib().bakron_solve_antidiagonal_workspace_bytes(mm, nn), dev)
+        out = {"V": torch.empty((mm, nn), device=dev), "codes": torch.empty((mm, nn), dtype=torch.uint8, device=dev),
+               "objective": torch.empty(1, dtype=torch.float64, device=dev)}
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        B.solve_antidiagonal(W, LA, PA, LB, PB, s, z, q, out=out, ws=ws, stream=stream, check=False)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        sec = ev[0].elapsed_time(ev[1]) / 1e3
+        alg = float(mm) * (mm + 1) * nn * (nn + 1) / 2.0
+        return {"s": round(sec, 4), "alg_tflops": round(alg / sec / 1e12, 3),
+                "alg_frac": round(alg / sec / 1e12 / PEAK_FP32_MFMA_TFLOPS, 4),
+                "objective": float(out["objective"].item())}
+
+    res = {"entry": "bakron_solve_antidiagonal"}
+    spec = WL.by_name("sq4096_t5")
+    d = WL.generate(spec)
+    t = {k: torch.from_numpy(np.ascontiguousarray(d[k])).to(dev) for k in ("W", "A", "B", "scale", "zero", "maxq")}
+    LA, PA, _ = B.factor(t["A"], 0.01)
+    LB, PB, _ = B.factor(t["B"], 0.01)
+    ws_s = B._binding.workspace(B.solve_workspace_bytes(spec.m, spec.n), dev)
+    B.solve(t["W"], LA, PA, LB, PB, t["scale"], t["zero"], t["maxq"], ws=ws_s, check=False)   # warm
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(args.steps):
+        B.solve(t["W"], LA, PA, LB, PB, t["scale"], t["zero"], t["maxq"], ws=ws_s, check=False)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    solve_s = ev[0].elapsed_time(ev[1]) / args.steps / 1e3
+    r = one(t["W"], LA, PA, LB, PB, t["scale"], t["zero"], t["maxq"], spec.m, spec.n)
+    r["solve_s"] = round(solve_s, 6)
+    r["vs_solve"] = round(r["s"] / solve_s, 1)
+    res[spec.name] = r
+    log(f"[bench] antidiagonal {spec.name}: {r['s']:.3f} s ({r['alg_tflops']} TFLOP/s algorithmic), "
+        f"solve {solve_s * 1e3:.3f} ms, ratio {r['vs_solve']}")
+    del t, LA, PA, LB, PB, ws_s
+    predicted = r["s"] * (float(m) * m * n * n) / (float(spec.m) ** 2 * spec.n ** 2)
+    if predicted <= limit_s:
+        r = one(T["W"], fa[0], fa[1], fb[0], fb[1], T["scale"], T["zero"], T["maxq"], m, n)
+        res[f"{m}x{n}"] = r
+        log(f"[bench] antidiagonal {m}x{n}: {r['s']:.3f} s ({r['alg_tflops']} TFLOP/s algorithmic)")
+    else:
+        res[f"{m}x{n}"] = {"skipped": f"predicted {predicted:.0f} s > {limit_s:.0f} s"}
+    return res
+
+
 # Which roofline bounds each kernel: the dense contractions run on the fp32
 # MFMA units; the copy, damping and finishing passes stream HBM; the rest
 # (the leaf sweep, the diagonal-block factor, the schedule and the objective
@@ -539,6 +655,195 @@ def copy_calibration(nbytes):
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": 4 * n, "copies": 5}), flush=True)
+
+
+def _kernel_key(name):
+    """Short kernel name from a profiler's demangled one: the function name
+    with its template arguments, without return type, namespaces or
+    parameters (e.g. 'k_f_tile<1>')."""
+    n = name.strip().replace("(anonymous namespace)::", "")
+    if n.startswith("void "):
+        n = n[5:]
+    depth, cut = 0, len(n)
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    n = n[:cut]
+    depth, start = 0, 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == ":" and depth == 0 and i + 1 < len(n) and n[i + 1] == ":":
+            start = i + 2
+    return n[start:].replace(" ", "")
+
+
+def _read_counters(directory):
+    """{kernel: {counter: [value per dispatch]}} from the counter-collection
+    CSV files rocprofv3 wrote under `directory`."""
+    import csv
+    import glob
+    out = {}
+    files = glob.glob(os.path.join(directory, "**", "*counter_collection*.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection csv under {directory}")
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                k = _kernel_key(row["Kernel_Name"])
+                c = row["Counter_Name"]
+                out.setdefault(k, {}).setdefault(c, []).append(float(row["Counter_Value"]))
+    return out
+
+
+PMC_DERIVED = (
+    # name, formula over per-dispatch means, meaning
+    ("valu/wave", lambda c: c["SQ_INSTS_VALU"] / c["SQ_WAVES"], "VALU instructions issued per wave"),
+    ("lds/wave", lambda c: c["SQ_INSTS_LDS"] / c["SQ_WAVES"], "LDS instructions issued per wave"),
+    ("conflict/lds", lambda c: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"],
+     "LDS bank-conflict cycles per LDS instruction"),
+    ("ldswait/wavecyc", lambda c: c["SQ_WAIT_INST_LDS"] / c["SQ_WAVE_CYCLES"],
+     "share of wave cycles spent waiting to issue an LDS instruction"),
+    ("valuactive/wavecyc", lambda c: c["SQ_ACTIVE_INST_VALU"] / c["SQ_WAVE_CYCLES"],
+     "share of wave cycles issuing VALU instructions"),
+    ("mfma_gflop", lambda c: 512.0 * c["SQ_INSTS_VALU_MFMA_MOPS_F32"] / 1e9,
+     "fp32 MFMA work executed (MOPS x 512 flops), GFLOP per dispatch"),
+    ("mfma_busy", lambda c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8.0 * 1024.0),
+     "MFMA busy share of a SIMD: busy cycles (summed over the 1024 SIMDs) over the dispatch's GPU-active "
+     "cycles (GRBM_GUI_ACTIVE, summed over the 8 XCDs)"),
+    ("l2_hit", lambda c: c["TCC_HIT_sum"] / (c["TCC_HIT_sum"] + c["TCC_MISS_sum"]), "L2 hit rate"),
+)
+
+
+def pmc_digest(dirs, title, command):
+    """Markdown summary of rocprofv3 --pmc runs: per kernel, the number of
+    dispatches and the mean of each counter per dispatch, then the derived
+    ratios whose counters were collected."""
+    per = {}
+    for d in dirs:
+        for k, cs in _read_counters(d).items():
+            dst = per.setdefault(k, {})
+            for c, vals in cs.items():
+                dst.setdefault(c, []).extend(vals)
+    counters = sorted({c for cs in per.values() for c in cs})
+    lines = [f"# {title}" if title else "# rocprofv3 counters", ""]
+    if command:
+        lines += ["Commands (from the repository root on the GPU box):", "", "```", command, "```", ""]
+    lines += ["Mean per dispatch of each counter (a counter is summed over the whole GPU for a dispatch).", ""]
+    lines.append("| kernel | dispatches | " + " | ".join(counters) + " |")
+    lines.append("|---|---|" + "---|" * len(counters))
+    order = sorted(per.items(), key=lambda kv: -max(len(v) for v in kv[1].values()))
+    for k, cs in order:
+        nd = max(len(v) for v in cs.values())
+        lines.append(f"| {k} | {nd} | " + " | ".join(
+            (f"{np.mean(cs[c]):.4g}" if c in cs else "") for c in counters) + " |")
+    lines += ["", "Derived (only where the counters were collected):", ""]
+    lines.append("| kernel | " + " | ".join(d[0] for d in PMC_DERIVED) + " |")
+    lines.append("|---|" + "---|" * len(PMC_DERIVED))
+    for k, cs in order:
+        means = {c: float(np.mean(v)) for c, v in cs.items()}
+        vals = []
+        for _, f, _ in PMC_DERIVED:
+            try:
+                vals.append(f"{f(means):.4g}")
+            except (KeyError, ZeroDivisionError):
+                vals.append("")
+        if any(vals):
+            lines.append(f"| {k} | " + " | ".join(vals) + " |")
+    lines += [""] + [f"- {n}: {m}" for n, _, m in PMC_DERIVED]
+    return "\n".join(lines)
+
+
+def stats_digest(directory, bench_log, title, command):
+    """Markdown summary of a rocprofv3 --kernel-trace --stats run: calls,
+    total and mean duration per kernel (short names), next to the mean
+    launch time the bench's own profiled pass measured with HIP events (from
+    its stderr), and the bench's step line."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats csv under {directory}")
+    rows = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                k = _kernel_key(r["Name"])
+                a = rows.setdefault(k, [0, 0.0])
+                a[0] += int(r["Calls"])
+                a[1] += float(r["TotalDurationNs"])
+    bench_us, step = {}, ""
+    if bench_log:
+        with open(bench_log) as fh:
+            for line in fh:
+                if line.startswith("[bench] kernels: "):
+                    for k, v in json.loads(line[len("[bench] kernels: "):]).items():
+                        bench_us[k] = v["avg_us"]
+                elif "ms/step" in line:
+                    step = line.strip()
+    lines = [f"# {title}" if title else "# Kernel time", ""]
+    if command:
+        lines += ["Command (from the repository root on the GPU box):", "", "```", command, "```", ""]
+    if step:
+        lines += ["Bench line of the same run: `" + step + "`", ""]
+    lines += ["| kernel | calls | total ms | avg us (rocprof) | avg us (bench, HIP events) |", "|---|---|---|---|---|"]
+    for k, (calls, ns) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
+        b = bench_us.get(k, "")
+        lines.append(f"| {k} | {calls} | {ns / 1e6:.3f} | {ns / 1e3 / calls:.2f} | {b} |")
+    return "\n".join(lines)
+
+
+def traffic_digest(dirs, workload, command):
+    """HBM bytes per dispatch from FETCH_SIZE and WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the counter reads for a plain 1 GiB device
+    copy (bench.py --copy-calibration); written with the kernel sources'
+    digest to profiles/traffic_<workload>.json and .md."""
+    fetch, write, cal_f, cal_w = (_read_counters(d) for d in dirs)
+
+    def copy_kib(cal, counter):
+        vals = [v for k, cs in cal.items() for c, vs in cs.items() if c == counter for v in vs]
+        return float(np.median(vals))
+
+    copy_kib_total = 1 << 20   # the calibration copies 1 GiB
+    fac_f = copy_kib_total / copy_kib(cal_f, "FETCH_SIZE")
+    fac_w = copy_kib_total / copy_kib(cal_w, "WRITE_SIZE")
+    kernels = {}
+    for k in sorted(set(fetch) | set(write)):
+        fv = fetch.get(k, {}).get("FETCH_SIZE", [])
+        wv = write.get(k, {}).get("WRITE_SIZE", [])
+        f = float(np.mean(fv)) if fv else 0.0
+        w = float(np.mean(wv)) if wv else 0.0
+        kernels[k] = {"dispatches": max(len(fv), len(wv)), "fetch_kib_per_dispatch": round(f, 1),
+                      "write_kib_per_dispatch": round(w, 1),
+                      "hbm_bytes_per_launch": int(round(1024.0 * (f * fac_f + w * fac_w)))}
+    out = {"workload": workload, "sources_sha256": sources_digest(), "commands": command,
+           "calibration": {"copy_bytes": 1 << 30, "FETCH_SIZE": {"factor": fac_f}, "WRITE_SIZE": {"factor": fac_w}},
+           "kernels": kernels}
+    base = os.path.join(ROOT, "profiles", f"traffic_{workload}")
+    with open(base + ".json", "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    lines = [f"# HBM traffic per dispatch, {workload}", "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch, mean over the dispatches of the run), each in a run of "
+             "its own, scaled by what the same counter reads for a plain 1 GiB device copy.", "",
+             "```", command, "```", "",
+             f"Copy calibration factors: FETCH_SIZE {fac_f:.4f}, WRITE_SIZE {fac_w:.4f}.", "",
+             f"Kernel sources sha256 (bench.py uses these numbers only while it matches): `{out['sources_sha256']}`",
+             "", "| kernel | dispatches | FETCH KiB | WRITE KiB | HBM bytes per launch (calibrated) |",
+             "|---|---|---|---|---|"]
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["hbm_bytes_per_launch"] * kv[1]["dispatches"]):
+        lines.append(f"| {k} | {v['dispatches']} | {v['fetch_kib_per_dispatch']} | {v['write_kib_per_dispatch']} | "
+                     f"{v['hbm_bytes_per_launch']:,} |")
+    with open(base + ".md", "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(base + ".json")
 
 
 def cpu_model():

@@ -41,7 +41,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "damp", "rev_cholesky", "normalized_inverse", "factor", "quantize",
+    "damp", "rev_cholesky", "normalized_inverse", "factor", "factor_float32", "quantize",
     "gptq_vectorized", "bakron_naive", "bakron_antidiagonal", "bakron_lform", "gptq_columns",
     "kron_moment", "row_sqnorms", "kfac_factors", "shampoo_factors",
     "objective", "objective_from_errors", "implied_errors", "implied_errors_p", "validate", "entry_grid",
@@ -127,6 +127,26 @@ def factor(A: np.ndarray, frac: float = 0.01) -> dict:
     Ad = damp(A, frac)
     L = rev_cholesky(Ad)
     return {"Ad": Ad, "L": L, "P": normalized_inverse(L)}
+
+
+def factor_float32(A: np.ndarray, frac: float = 0.01) -> dict:
+    """The same factor step carried out in float32 arithmetic by the
+    library routines (LAPACK's single-precision Cholesky and triangular
+    solve): a float32 factorisation independent of the HIP path, whose
+    rounding errors (about n u cond(A_d)) are of the kind a float32 solver's
+    factors carry.  Used only to measure how far two valid float32 runs can
+    land from the float64 one (tests/golden/trajectory_spread.py)."""
+    from scipy.linalg import solve_triangular
+    A = np.asarray(A, dtype=np.float32)
+    n = A.shape[0]
+    A = ((A + A.T) * np.float32(0.5)).astype(np.float32)
+    add = np.float32(frac) * np.float32(np.mean(np.diag(A).astype(np.float64)))
+    Ad = A + add * np.eye(n, dtype=np.float32)
+    C = np.linalg.cholesky(Ad[::-1, ::-1])              # float32 in, float32 factor
+    L = np.ascontiguousarray(C.T[::-1, ::-1])
+    Li = solve_triangular(L, np.eye(n, dtype=np.float32), lower=True)
+    P = (np.tril(Li) * np.diag(L)[None, :]).astype(np.float32)
+    return {"Ad": Ad, "L": L, "P": P}
 
 
 # ------------------------------------------------------------ base quantizer

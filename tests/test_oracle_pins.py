@@ -199,6 +199,23 @@ def test_rev_cholesky_definition(n, seed):
     np.testing.assert_allclose(L @ (P / np.diag(L)[None, :]), np.eye(n), atol=1e-9)
 
 
+@pytest.mark.parametrize("n,seed", [(5, 1), (64, 2), (130, 3)])
+def test_factor_float32_is_a_float32_factorisation(n, seed):
+    # float32 arrays out, A_d = L^T L within float32 backward error, the
+    # float64 factor within float32 forward error, unit diagonal of P
+    d = make_problem(4, n, seed, global_grid=True)
+    f32, f64 = R.factor_float32(d["A"]), R.factor(d["A"])
+    assert f32["L"].dtype == np.float32 and f32["P"].dtype == np.float32
+    L = f32["L"].astype(np.float64)
+    assert np.array_equal(L, np.tril(L)) and np.all(np.diag(L) > 0)
+    u = 2.0 ** -24
+    Ad = f64["Ad"]
+    assert np.linalg.norm(L.T @ L - Ad) <= 10 * n * u * np.linalg.norm(Ad)
+    np.testing.assert_allclose(np.diag(f32["P"]), 1.0, atol=4 * u)
+    kappa = np.linalg.cond(Ad)
+    assert np.linalg.norm(f32["P"] - f64["P"]) <= 10 * n * u * kappa * np.linalg.norm(f64["P"])
+
+
 def test_rev_cholesky_rejects_indefinite():
     A = np.array([[1.0, 2.0], [2.0, 1.0]])
     with pytest.raises(np.linalg.LinAlgError):

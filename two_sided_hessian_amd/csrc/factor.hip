@@ -569,6 +569,16 @@ __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, flo
 #define BAKRON_LEAD_GRID 96
 #endif
 constexpr unsigned kLeadGrid = BAKRON_LEAD_GRID;
+// ... and only while the top node's products are small enough to finish
+// beside the solve's first subtree on that grid: at 8192 (1024 blocks) they
+// take about 3.5 ms there against about 3.9 ms of solve; at 14336 (3136
+// blocks) they would take about five times longer than the subtree, and the
+// full grid is faster (measured: fused 62.0 ms against 56.1 ms as three calls
+// at 4096 x 14336 with the cap).
+#ifndef BAKRON_LEAD_MAX_BLOCKS
+#define BAKRON_LEAD_MAX_BLOCKS 1024
+#endif
+constexpr unsigned kLeadMaxBlocks = BAKRON_LEAD_MAX_BLOCKS;
 constexpr size_t kLeadPad = 160 * 1024 - kLeafLdsBytes - sizeof(float) * Gemm<2, 2, RowK, KRow>::LDS_FLOATS + 1024;
 
 __global__ __launch_bounds__(256) void k_f_right_lead(const float* __restrict__ Lbuf, const float* __restrict__ Pbuf,
@@ -866,7 +876,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
             // Li21 = U Li11 (on the spine U P11 = P21, P11 being finished)
             launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf, R.Pbuf, T,
                    R.ld, o1, o2, n1, n2);
-        } else if (R.leads && o == 0 && nsz == R.ld) {
+        } else if (R.leads && o == 0 && nsz == R.ld && g.x * g.y <= kLeadMaxBlocks) {
             static std::once_flag attrs;
             std::call_once(attrs, [] {
                 (void)hipFuncSetAttribute((const void*)k_f_right_lead, hipFuncAttributeMaxDynamicSharedMemorySize,

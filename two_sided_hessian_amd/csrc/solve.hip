@@ -396,7 +396,18 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
 // groups of kXcdGroup consecutive entries are sent to one XCD: within each
 // run of 8 * kXcdGroup workgroups, p -> entry (p % 8) * kXcdGroup + p / 8.
 // The longest-first order survives at the granularity of a run.
-constexpr int kXcdGroup = 4;
+#ifndef BAKRON_XCD_GROUP
+#define BAKRON_XCD_GROUP 4
+#endif
+constexpr int kXcdGroup = BAKRON_XCD_GROUP;
+
+// The 64 x 64 tile kernels of the small nodes can map their work items the
+// same way (consecutive items share an operand strip: the error strip of a
+// tile row in stage 1, the Y strip of a tile column in stage 2).
+#ifndef BAKRON_T_XCD
+#define BAKRON_T_XCD 0
+#endif
+constexpr bool kTileXcd = BAKRON_T_XCD != 0;
 
 __device__ __forceinline__ unsigned xcd_entry(unsigned p, unsigned n)
 {
@@ -756,7 +767,8 @@ __device__ __forceinline__ void prop_rows_t_body(const float* __restrict__ E, co
 {
     __shared__ __align__(16) float lds[kLds64];
     const int wave = threadIdx.x >> 6;
-    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+    for (unsigned qq = blockIdx.x; qq < count; qq += gridDim.x) {
+        const unsigned q = kTileXcd ? xcd_entry(qq, count) : qq;
         const int I = rows_lo(K0, Nt) + (int)(q / span);
         const RowSpan s(I, K0, mid, y0, y1, Nt);
         const int Jp = s.th - (int)(q % span);
@@ -795,7 +807,8 @@ __device__ __forceinline__ void prop_cols_t_body(const float* __restrict__ Y, co
 {
     __shared__ __align__(16) float lds[kLds64];
     const int wave = threadIdx.x >> 6;
-    for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
+    for (unsigned qq = blockIdx.x; qq < count; qq += gridDim.x) {
+        const unsigned q = kTileXcd ? xcd_entry(qq, count) : qq;
         const int J = cols_lo(t0, Mt) + (int)(q / span);
         const ColSpan s(J, K0, mid, t0, t1, Mt);
         const int Ip = s.th - (int)(q % span);
