@@ -25,15 +25,19 @@ streams, then the solve.  The checks:
     rounding boundary (both roundings are valid there, and the trajectories
     would part), gives the same code at every entry, with at most 1e-4 of the
     entries followed;
-  - end to end: against the oracle's solve with its float64 factors, the
-    objective within max(1e-3, 5 x the spread recorded in
-    tests/golden/trajectory_spread.json), the relative objective gap between
-    float64 oracle runs on the float64 factors and on float32 ones (the
+  - end to end, against the oracle's solve with its float64 factors.  Where
+    the spread recorded in tests/golden/trajectory_spread.json (float64
+    oracle runs on the float64 factors against runs on float32 ones: the
     float64 factors rounded to float32, and factors computed in float32 by
-    LAPACK, whose errors are of the kind the GPU's float32 factors carry);
-    the codes within 1e-4 of the entries where neither shows a differing
-    code (elsewhere the count is printed: a trajectory that parts at one
-    entry legitimately differs at many).
+    LAPACK) shows no differing code, the trajectories do not part: the
+    objective within 1e-3 and the codes within 1e-4 of the entries.  Where it
+    does, a near-tie decision taken the other way cascades, and the
+    objective of a valid run moves at the 1e-3 level (at 4096 x 14336 the
+    oracle's own free-running run on the GPU's factors differs from the run
+    that follows the GPU at 106 near-ties by 2.8e-3): there the check is a
+    sanity bound, the objective within max(1e-2, 5 x the recorded objective
+    spread), and the signed gap and the differing codes are printed; the
+    judged comparison is the same-factor one above.
 The checks of one configuration are separate tests sharing one GPU run
 (a module fixture, one configuration held at a time), so that none of them
 runs for long without reporting.
@@ -180,10 +184,10 @@ def test_config_oracle_end_to_end(run):
     sp = SPREAD[name]
     spread_obj = max(sp["objective_rel"], sp["lapack32_objective_rel"])
     spread_codes = max(sp["differ_frac"], sp["lapack32_differ_frac"])
-    bar = max(1e-3, 5 * spread_obj)
+    bar = 1e-3 if spread_codes == 0.0 else max(1e-2, 5 * spread_obj)
     print(f"{name}: end to end, {diff} codes of {m * n} differ from the float64 oracle (recorded spread "
-          f"{spread_codes:.4f}), objective gpu {o_gpu:.8e} oracle {o_or:.8e} rel {abs(o_gpu - o_or) / o_or:.3e} "
-          f"(bar {bar:.3e})", flush=True)
+          f"{spread_codes:.4f} of the codes, {spread_obj:.2e} of the objective), objective gpu {o_gpu:.8e} "
+          f"oracle {o_or:.8e}, gpu - oracle {(o_gpu - o_or) / o_or:+.3e} (bar {bar:.1e})", flush=True)
     assert o_gpu == pytest.approx(o_or, rel=bar)
     if spread_codes == 0.0:
         assert diff <= max(1, 1e-4 * m * n)

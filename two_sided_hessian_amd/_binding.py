@@ -290,8 +290,11 @@ def solve_noalloc(W, LA, PA, LB, PB, scale, zero, maxq, *, want_err=False, want_
                   stream=None, check=True):
     """bakron_solve_noalloc (no workspace: the library's fixed device scratch;
     the results are bakron_solve's).  Returns dict(V, codes, err?,
-    objective?); with ``out`` given, allocates nothing.  ``check``: as in
-    solve()."""
+    objective?).  With ``out`` given and check=False it allocates nothing and
+    only enqueues kernels, so it can be captured into a HIP graph (make one
+    call before capturing: the first call on a device looks the scratch up).
+    ``check``: as in solve(); it reads the grid back to the host, which
+    graph capture does not allow."""
     m, n = W.shape
     _check_dev("W", W, torch.float32, (m, n))
     _check_dev("P_A", PA, torch.float32, (n, n))
