@@ -537,7 +537,7 @@ def bench_antidiagonal(B, WL, T, fa, fb, m, n, dev, args, limit_s=60.0):
 # (the leaf sweep, the diagonal-block factor, the schedule and the objective
 # reduction) are chains of dependent vector arithmetic and LDS traffic,
 # priced against the fp32 vector peak.
-MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_prop_pair", "k_prop_rows_far",
+MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_prop_rows_far",
                 "k_prop_rows_t_far",
                 "k_prop_cols_far", "k_prop_cols_t_far", "k_f_panel", "k_f_right",
                 "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_gptq_update",
@@ -551,9 +551,9 @@ HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_cl
 PEAK_FP32_VECTOR_TFLOPS = 78.6
 PEAK_FP32_VECTOR_PACKED_TFLOPS = 157.3
 
-# Kernels of the two propagation stages of the solve (k_prop_pair runs both
-# stages of a two-leaf node; its time is split between them in proportion to
-# their block products, equal by construction).
+# Kernels of the two propagation stages of the solve.  (The propagation of a
+# node of two leaves runs inside the second leaf, k_leaf: its few microseconds
+# of block products are counted neither here nor in a stage's time.)
 STAGE1_KERNELS = ("k_prop_rows", "k_prop_rows_t", "k_prop_rows_far", "k_prop_rows_t_far")
 STAGE2_KERNELS = ("k_prop_cols", "k_prop_cols_t", "k_prop_cols_far", "k_prop_cols_t_far")
 
@@ -629,11 +629,10 @@ def stage_fractions(agg, m, n):
     of the stage's kernels, and the executed block products of those kernels
     for comparison (the divide and conquer recomputes partial products)."""
     out = {}
-    pair = agg.get("k_prop_pair", {"total_ms": 0.0, "alg_flops": 0.0, "launches": 0})
     for stage, names, alg in (("stage1", STAGE1_KERNELS, float(m) * n * (n + 1)),
                               ("stage2", STAGE2_KERNELS, float(m) * (m + 1) * n)):
-        ms = sum(agg[k]["total_ms"] for k in names if k in agg) + 0.5 * pair["total_ms"]
-        ex = sum(agg[k]["alg_flops"] for k in names if k in agg) + 0.5 * pair["alg_flops"]
+        ms = sum(agg[k]["total_ms"] for k in names if k in agg)
+        ex = sum(agg[k]["alg_flops"] for k in names if k in agg)
         if ms <= 0:
             continue
         out[stage] = {"kernels_ms": round(ms, 4), "alg_flops": alg,

@@ -98,6 +98,7 @@ struct LeafArgs {
     int Nt;
     int K;                // tile anti-diagonal
     int I_lo;             // first tile row on it
+    int pair;             // 1: K - 1 and K form a node of two leaves, whose propagation the leaf applies first
     int vec_out;          // outputs may use 16-byte stores
 };
 
@@ -242,9 +243,88 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[8
     __syncthreads();
 }
 
+// The propagation of a node of two leaves (K0, K0 + 1, K0 + 2) into its
+// target tile (Ip, Jp) on anti-diagonal K0 + 1, at the start of that tile's
+// leaf.  The sources are the rows I in [max(0, Ip - 1), min(K0, Ip)], each
+// with the one source tile (I, K0 - I):
+//   Y_I = E[I, K0 - I] P_A[Jp, K0 - I]^T            (stage 1, K = 64)
+//   W~[Ip, Jp] -= sum_I P_B[Ip, I] Y_I              (stage 2, I ascending)
+// The Y tiles stay in LDS (sY0, sY1: 64 x kLP each); fragments come straight
+// from global memory into registers, with the MFMAs of the tile kernels in
+// their order and Y rounded as those kernels store it, so the updated tile is
+// theirs bit for bit.  It lands in sW, the leaf's copy of the tile.  Stage 1
+// runs on eight waves (wave w: source w / 4, quadrant w % 4), stage 2 on
+// the first four.
+__device__ __forceinline__ void leaf_pair_update(const LeafArgs& g, int Ip, int Jp, float* __restrict__ sY0,
+                                                 float* __restrict__ sY1, float* __restrict__ sW)
+{
+    const int K0 = g.K - 1;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, quad = wave & 3;
+    const int ml = lane & 31, kl = 4 * (lane >> 5);
+    const int ra = 32 * (quad >> 1) + ml, rb = 32 * (quad & 1) + ml;
+    const int Ilo = max(0, Ip - 1), Ihi = min(K0, Ip);
+    const int I = Ilo + (wave >> 2);
+    if (I <= Ihi) {
+        const int J = K0 - I;
+        const float* a0 = g.E + (int64_t)I * 64 * g.ldw + (int64_t)J * 64;
+        const float* b0 = g.PA + (int64_t)Jp * 64 * g.lda + (int64_t)J * 64;
+        f32x4 a[8], b[8];
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * g.ldw + 8 * st + kl);
+            b[st] = *reinterpret_cast<const f32x4*>(b0 + (int64_t)rb * g.lda + 8 * st + kl);
+        }
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int st = 0; st < 8; ++st)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], b[st][q], acc, 0, 0, 0);
+        float* y = (I == Ilo ? sY0 : sY1) + 32 * (quad >> 1) * kLP + 32 * (quad & 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float one = 1.f, none = 0.f;   // as stage 1 stores Y: 1 acc + 0 0
+            y[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kLP + ml] = one * acc[r] + none * none;
+        }
+    }
+    __syncthreads();
+    if (wave < 4) {
+        f32x16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int Is = Ilo; Is <= Ihi; ++Is) {
+            const float* a0 = g.PB + (int64_t)Ip * 64 * g.ldb + (int64_t)Is * 64;
+            const float* y = (Is == Ilo ? sY0 : sY1) + rb;
+            f32x4 a[8];
+#pragma unroll
+            for (int st = 0; st < 8; ++st)
+                a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * g.ldb + 8 * st + kl);
+#pragma unroll
+            for (int st = 0; st < 8; ++st) {
+                const float* c = y + (8 * st + kl) * kLP;
+                const f32x4 bv = {c[0], c[kLP], c[2 * kLP], c[3 * kLP]};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], bv[q], acc, 0, 0, 0);
+            }
+        }
+        // W~ - acc, as the tile kernels' epilogue forms it (alpha acc + beta old)
+        const float* wq = g.Wt + ((int64_t)Ip * 64 + 32 * (quad >> 1)) * g.ldw + (int64_t)Jp * 64 + 32 * (quad & 1);
+        float* sq = sW + 32 * (quad >> 1) * 64 + 32 * (quad & 1);
+        const float alpha = -1.f, beta = 1.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            sq[row * 64 + ml] = alpha * acc[r] + beta * wq[(int64_t)row * g.ldw + ml];
+        }
+    }
+    __syncthreads();   // the Y tiles read before the leaf clears their arrays
+}
+
 __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
 {
     __shared__ float sW[64 * 64];
+    // sS and sUT hold the two Y tiles of a two-leaf node's propagation first
     __shared__ __align__(16) float sS[64 * kLP];    // sS[b][j] = P_A[b + j][b], zero past the tile
     __shared__ __align__(16) float sUT[64 * kLP];   // sUT[b][a] = U[a][b]
     __shared__ __align__(16) float sF[64 * kLP];    // raw errors e[a][b]
@@ -258,6 +338,7 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
     const int a = t >> 3, sg = t & 7;
     if (t < 8) sZ[t] = 0.f;
     const int64_t r0 = (int64_t)I * 64, c0 = (int64_t)J * 64;
+    if (g.pair) leaf_pair_update(g, I, J, sS, sUT, sW);
 
     for (int idx = t; idx < 64 * kLP; idx += 512) {
         sS[idx] = 0.f;
@@ -269,8 +350,10 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
     for (int u = 0; u < 2; ++u) {
         const int f = t + 512 * u;
         const int row = f >> 4, cq = 4 * (f & 15);
-        const f32x4 w = *reinterpret_cast<const f32x4*>(g.Wt + (r0 + row) * g.ldw + c0 + cq);
-        *reinterpret_cast<f32x4*>(sW + row * 64 + cq) = w;
+        if (!g.pair) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(g.Wt + (r0 + row) * g.ldw + c0 + cq);
+            *reinterpret_cast<f32x4*>(sW + row * 64 + cq) = w;
+        }
         pa[u] = *reinterpret_cast<const f32x4*>(g.PA + (c0 + row) * g.lda + c0 + cq);
     }
     __syncthreads();   // zeroing done before the skewed scatter
@@ -838,73 +921,6 @@ __global__ __launch_bounds__(256) void k_prop_cols_t_far(const float* __restrict
     prop_cols_t_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, span, count);
 }
 
-// Nodes of two leaves, (K0, K0 + 1, K0 + 2): both stages in one launch, one
-// workgroup per target tile (I', J') on anti-diagonal K0 + 1.  Its sources
-// are the rows I in [max(0, I' - 1), min(K0, I')], each with the one source
-// tile (I, K0 - I), and every Y tile it needs is needed by no other target:
-//   Y_I = E[I, K0 - I] P_A[J', K0 - I]^T            (stage 1, K = 64)
-//   W~[I', J'] -= sum_I P_B[I', I] Y_I              (stage 2, I ascending)
-// The Y tiles stay in LDS.  Fragments come straight from global memory into
-// registers (the K extents are 64 and 128), with the MFMAs of the tile
-// kernels in their order, and Y rounded as those kernels store it, so the
-// results are theirs bit for bit.
-constexpr int kYP = 68;   // LDS pitch of a Y tile
-__global__ __launch_bounds__(256) void k_prop_pair(const float* __restrict__ E, const float* __restrict__ PA,
-                                                   const float* __restrict__ PB, float* __restrict__ Wt,
-                                                   int64_t ldw, int64_t lda, int64_t ldb, int K0, int I_lo)
-{
-    __shared__ __align__(16) float sY[2 * 64 * kYP];
-    const int Ip = I_lo + (int)blockIdx.x, Jp = K0 + 1 - Ip;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int ml = lane & 31, kl = 4 * (lane >> 5);
-    const int ra = 32 * (wave >> 1) + ml, rb = 32 * (wave & 1) + ml;
-    const int Ilo = max(0, Ip - 1), Ihi = min(K0, Ip);
-    for (int I = Ilo; I <= Ihi; ++I) {
-        const int J = K0 - I;
-        const float* a0 = E + (int64_t)I * 64 * ldw + (int64_t)J * 64;
-        const float* b0 = PA + (int64_t)Jp * 64 * lda + (int64_t)J * 64;
-        f32x4 a[8], b[8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * ldw + 8 * st + kl);
-            b[st] = *reinterpret_cast<const f32x4*>(b0 + (int64_t)rb * lda + 8 * st + kl);
-        }
-        f32x16 acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], b[st][q], acc, 0, 0, 0);
-        float* y = sY + (I - Ilo) * 64 * kYP + 32 * (wave >> 1) * kYP + 32 * (wave & 1);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float one = 1.f, none = 0.f;   // as stage 1 stores Y: 1 acc + 0 0
-            y[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kYP + ml] = one * acc[r] + none * none;
-        }
-    }
-    __syncthreads();
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    for (int I = Ilo; I <= Ihi; ++I) {
-        const float* a0 = PB + (int64_t)Ip * 64 * ldb + (int64_t)I * 64;
-        const float* y = sY + (I - Ilo) * 64 * kYP + rb;
-        f32x4 a[8];
-#pragma unroll
-        for (int st = 0; st < 8; ++st) a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * ldb + 8 * st + kl);
-#pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            const float* c = y + (8 * st + kl) * kYP;
-            const f32x4 bv = {c[0], c[kYP], c[2 * kYP], c[3 * kYP]};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], bv[q], acc, 0, 0, 0);
-        }
-    }
-    const int64_t r = (int64_t)Ip * 64 + 32 * (wave >> 1), c = (int64_t)Jp * 64 + 32 * (wave & 1);
-    wave_store32(Wt + r * ldw + c, ldw, -1.f, 1.f, acc);
-}
-
 __global__ __launch_bounds__(256) void k_obj_reduce(const double* __restrict__ part, int64_t count,
                                                     double* __restrict__ out)
 {
@@ -1064,17 +1080,29 @@ constexpr double kTileB = 4.0 * 64 * 64;                 // bytes of one fp32 ti
 constexpr double kFull = 64.0 * 64.0 * 64.0;             // multiply-adds of a full block product
 constexpr double kTriB = 64.0 * 64.0 * 65.0 / 2.0;       // ... with a triangular diagonal block
 
-void enqueue_leaf(SolveRun& R, int K)
+// pair: K - 1 and K are the two leaves of one node, and the leaf applies
+// that node's propagation first.
+void enqueue_leaf(SolveRun& R, int K, bool pair = false)
 {
     const int I_lo = std::max(0, K - (R.Nt - 1));
     const int I_hi = std::min(R.Mt - 1, K);
     const int count = I_hi - I_lo + 1;
     R.leaf.K = K;
     R.leaf.I_lo = I_lo;
+    R.leaf.pair = pair ? 1 : 0;
     // per tile: the two in-tile triangular products (U = E P_A^T, P_B U);
     // bytes: W~, P_A and P_B diagonal blocks in; E and V out (+ err), codes
-    const double flops = count * 2.0 * 2.0 * kTriB;
-    const double bytes = count * (5.0 * kTileB + (R.leaf.err ? kTileB : 0.0) + 64.0 * 64.0);
+    double flops = count * 2.0 * 2.0 * kTriB;
+    double bytes = count * (5.0 * kTileB + (R.leaf.err ? kTileB : 0.0) + 64.0 * 64.0);
+    if (pair) {
+        // per source tile, over both stages: one diagonal (triangular) and
+        // one full block product; E, P_A and P_B tiles in
+        for (int Ip = I_lo; Ip <= I_hi; ++Ip) {
+            const int srcs = std::min(K - 1, Ip) - std::max(0, Ip - 1) + 1;
+            flops += srcs * 2.0 * (kTriB + kFull);
+            bytes += srcs * 3.0 * kTileB;
+        }
+    }
     launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(512), R.s, R.leaf);
 }
 
@@ -1252,27 +1280,11 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits
 }
 
 // `waits`: far parts of ancestors due before the propagation of this node
-// and of the nodes down its left spine.
+// and of the nodes down its left spine.  A node of two leaves runs its
+// propagation inside the second leaf (BAKRON_PAIR_FUSE).
 #ifndef BAKRON_PAIR_FUSE
 #define BAKRON_PAIR_FUSE 1
 #endif
-// The propagation of a node of two leaves (K0, K0 + 1, K0 + 2) (k_prop_pair).
-void enqueue_pair(SolveRun& R, int K0)
-{
-    const int I_lo = std::max(0, K0 + 1 - (R.Nt - 1)), I_hi = std::min(R.Mt - 1, K0 + 1);
-    if (I_hi < I_lo) return;
-    double fl = 0.0, by = 0.0;
-    for (int Ip = I_lo; Ip <= I_hi; ++Ip) {
-        const int srcs = std::min(K0, Ip) - std::max(0, Ip - 1) + 1;
-        // per source: a diagonal and a full block product in each stage;
-        // E, P_A and P_B tiles in, W~ read and written
-        fl += srcs * 2.0 * 2.0 * (kTriB + kFull) / 2.0;
-        by += srcs * 3.0 * kTileB + 2.0 * kTileB;
-    }
-    launch(R.prof, KK_PROP_PAIR, fl, by, k_prop_pair, dim3((unsigned)(I_hi - I_lo + 1)), dim3(256), R.s,
-           (const float*)R.leaf.E, R.leaf.PA, R.leaf.PB, R.leaf.Wt, R.leaf.ldw, R.leaf.lda, R.leaf.ldb, K0, I_lo);
-}
-
 void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits)
 {
     if (K1 - K0 == 1) {   // (the nodes that carry waits are never leaves)
@@ -1285,14 +1297,13 @@ void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& wait
     for (int j = 0; j < kMaxParts; ++j) down.e[j] = j + 1 < kMaxParts ? waits.e[j + 1] : nullptr;
     solve_rec(R, K0, mid, d + 1, 2 * p, down);
     if (waits.e[0] && hipStreamWaitEvent(R.s, waits.e[0], 0) != hipSuccess) R.failed = true;
-    SpineWaits done;
     ensure_full(R, K1 - 1);
-    if (BAKRON_PAIR_FUSE && K1 - K0 == 2) {   // (never cut in parts)
-        for (hipEvent_t& e : done.e) e = nullptr;
-        enqueue_pair(R, K0);
-    } else {
-        enqueue_prop(R, K0, mid, K1, d, p, done);
+    if (BAKRON_PAIR_FUSE && K1 - K0 == 2) {   // (never cut in parts) the second leaf propagates first
+        enqueue_leaf(R, K0 + 1, true);
+        return;
     }
+    SpineWaits done;
+    enqueue_prop(R, K0, mid, K1, d, p, done);
     solve_rec(R, mid, K1, d + 1, 2 * p + 1, done);
 }
 
