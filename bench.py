@@ -253,6 +253,7 @@ def main():
     cpu = None
     if args.cpu_sample != 0:
         cpu = cpu_baseline(d, max(m, n) if args.cpu_sample < 0 else args.cpu_sample, m, n)
+        cpu["small_forms"] = cpu_small_forms(WL)
 
     res = {
         "metric": "seconds per m×n BaKron solve (8192×8192 fp32) + achieved fp32 MFMA TFLOP/s",
@@ -888,6 +889,47 @@ def cpu_baseline(d, sample, m, n):
                       f"{t:.2f}s measured on {model}, scaled by the cubic work ratio {scale:.2f}")
     return {"value": round(t * scale, 3), "unit": "s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "measured_s": round(t, 3), "sample": sample_txt}
+
+
+def cpu_small_forms(WL):
+    """Every oracle form timed once on the 64 x 64 workload (seconds, float64,
+    host cores): brute-force GPTQ on vec(W) with the explicit Kronecker
+    Hessian, BaKron-naive (column-major order), BaKron-antidiagonal and the
+    recursive C solve, each including its own factorisation."""
+    from oracle import recursive as O2
+    from oracle import reference as R
+    d = WL.generate(WL.by_name("tiny64"))
+    out = {"workload": "tiny64 (64x64)"}
+
+    def timed(name, fn):
+        t0 = time.perf_counter()
+        fn()
+        out[name] = round(time.perf_counter() - t0, 4)
+
+    def factors():
+        return R.factor(d["A"]), R.factor(d["B"])
+
+    def brute():
+        R.gptq_vectorized(d["W"], R.damp(d["A"]), R.damp(d["B"]), d["scale"], d["zero"], d["maxq"])
+
+    def naive():
+        fa, fb = factors()
+        R.bakron_naive(d["W"], fa["P"], fb["P"], d["scale"], d["zero"], d["maxq"])
+
+    def antidiag():
+        fa, fb = factors()
+        R.bakron_antidiagonal(d["W"], fa["P"], fb["P"], d["scale"], d["zero"], d["maxq"])
+
+    def recursive():
+        fa, fb = factors()
+        O2.bakron_recursive(d["W"], fa["P"], fb["P"], d["scale"], d["zero"], d["maxq"])
+
+    timed("brute_force_vec_gptq_s", brute)
+    timed("naive_s", naive)
+    timed("antidiagonal_s", antidiag)
+    timed("recursive_s", recursive)
+    log(f"[bench] cpu oracle forms on 64x64: {out}")
+    return out
 
 
 if __name__ == "__main__":
