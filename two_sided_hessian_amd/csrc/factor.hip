@@ -569,16 +569,23 @@ __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, flo
 #define BAKRON_LEAD_GRID 96
 #endif
 constexpr unsigned kLeadGrid = BAKRON_LEAD_GRID;
-// ... and only while the top node's products are small enough to finish
-// beside the solve's first subtree on that grid: at 8192 (1024 blocks) they
-// take about 3.5 ms there against about 3.9 ms of solve; at 14336 (3136
-// blocks) they would take about five times longer than the subtree, and the
-// full grid is faster (measured: fused 62.0 ms against 56.1 ms as three calls
-// at 4096 x 14336 with the cap).
+// That grid suits top nodes whose products finish beside the solve's first
+// subtree on it: at 8192 (1024 blocks) they take about 3.5 ms there against
+// about 3.9 ms of solve.  A larger top node (14336: 3136 blocks) would take
+// about five times longer than the subtree on 96 workgroups, so its products
+// get kLeadGridBig workgroups instead, one per CU on most of the GPU, and
+// leave the rest of the CUs to the solve's first leaves (at 4096 x 14336 the
+// fused call then takes 52.7-53.1 ms, against 54.5 ms with the products on
+// the full grid and 62 ms on 96 workgroups; 208-224 workgroups were best,
+// 160 or 240 and more no better than the full grid).
 #ifndef BAKRON_LEAD_MAX_BLOCKS
 #define BAKRON_LEAD_MAX_BLOCKS 1024
 #endif
 constexpr unsigned kLeadMaxBlocks = BAKRON_LEAD_MAX_BLOCKS;
+#ifndef BAKRON_LEAD_GRID_BIG
+#define BAKRON_LEAD_GRID_BIG 224
+#endif
+constexpr unsigned kLeadGridBig = BAKRON_LEAD_GRID_BIG;   // 0: the full grid for larger top nodes
 constexpr size_t kLeadPad = 160 * 1024 - kLeafLdsBytes - sizeof(float) * Gemm<2, 2, RowK, KRow>::LDS_FLOATS + 1024;
 
 __global__ __launch_bounds__(256) void k_f_right_lead(const float* __restrict__ Lbuf, const float* __restrict__ Pbuf,
@@ -876,7 +883,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
             // Li21 = U Li11 (on the spine U P11 = P21, P11 being finished)
             launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf, R.Pbuf, T,
                    R.ld, o1, o2, n1, n2);
-        } else if (R.leads && o == 0 && nsz == R.ld && g.x * g.y <= kLeadMaxBlocks) {
+        } else if (R.leads && o == 0 && nsz == R.ld && (g.x * g.y <= kLeadMaxBlocks || kLeadGridBig > 0)) {
             static std::once_flag attrs;
             std::call_once(attrs, [] {
                 (void)hipFuncSetAttribute((const void*)k_f_right_lead, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -884,7 +891,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
                 (void)hipFuncSetAttribute((const void*)k_f_left_lead, hipFuncAttributeMaxDynamicSharedMemorySize,
                                           (int)kLeadPad);
             });
-            const unsigned cnt = g.x * g.y, grid = std::min(cnt, kLeadGrid);
+            const unsigned cnt = g.x * g.y, grid = std::min(cnt, cnt <= kLeadMaxBlocks ? kLeadGrid : kLeadGridBig);
             launch_shm(R.prof, KK_F_RIGHT, fr, br, k_f_right_lead, dim3(grid), dim3(256), kLeadPad, R.s,
                        (const float*)R.Lbuf, (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2, g.y, cnt);
             launch_shm(R.prof, KK_F_LEFT, fl, bl, k_f_left_lead, dim3(grid), dim3(256), kLeadPad, R.s,

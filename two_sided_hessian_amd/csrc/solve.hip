@@ -1091,18 +1091,12 @@ void enqueue_leaf(SolveRun& R, int K, bool pair = false)
     R.leaf.I_lo = I_lo;
     R.leaf.pair = pair ? 1 : 0;
     // per tile: the two in-tile triangular products (U = E P_A^T, P_B U);
-    // bytes: W~, P_A and P_B diagonal blocks in; E and V out (+ err), codes
-    double flops = count * 2.0 * 2.0 * kTriB;
-    double bytes = count * (5.0 * kTileB + (R.leaf.err ? kTileB : 0.0) + 64.0 * 64.0);
-    if (pair) {
-        // per source tile, over both stages: one diagonal (triangular) and
-        // one full block product; E, P_A and P_B tiles in
-        for (int Ip = I_lo; Ip <= I_hi; ++Ip) {
-            const int srcs = std::min(K - 1, Ip) - std::max(0, Ip - 1) + 1;
-            flops += srcs * 2.0 * (kTriB + kFull);
-            bytes += srcs * 3.0 * kTileB;
-        }
-    }
+    // bytes: W~, P_A and P_B diagonal blocks in; E and V out (+ err), codes.
+    // (A leaf that first applies its two-leaf node's propagation does that
+    // node's block products too, on the MFMA units; they are not counted
+    // here, so the leaf's rate is that of its sweep.)
+    const double flops = count * 2.0 * 2.0 * kTriB;
+    const double bytes = count * (5.0 * kTileB + (R.leaf.err ? kTileB : 0.0) + 64.0 * 64.0);
     launch(R.prof, KK_LEAF, flops, bytes, k_leaf, dim3(count), dim3(512), R.s, R.leaf);
 }
 
