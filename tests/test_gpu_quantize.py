@@ -7,7 +7,9 @@ pins that overlap (and the point where the solve waits for the whole factors)
 to the plain order.  Shapes cover dimensions with and without the early
 leading block (multiples of 64 above 128, and ragged or small ones), m != n,
 degenerate single-row and two-column layers, two calls in a row on one
-workspace, and the full 8192^2 workload.
+workspace, factors whose top node runs its last products on the larger
+capped grid (a side of 8320: 33 x 33 blocks of 128), and the full 8192^2
+workload.
 
 Pages: [S] paper summary "FastKron: Efficient Quantization with
 Kronecker-Factored Hessians" (derivation, Theorem 3.2, Corollary 3.4).
@@ -94,3 +96,21 @@ def test_quantize_equals_separate_calls_at_full_size():
     torch.cuda.synchronize()
     for key in KEYS:
         assert torch.equal(out[key], ref[key]), key
+
+
+@pytest.mark.parametrize("shape", [(256, 8320), (8320, 256)], ids=["256x8320", "8320x256"])
+def test_quantize_equals_separate_calls_large_top_node(shape):
+    # a factor of 8320 has 33 x 33 blocks of 128 at its top node, more than
+    # the 1024 the small capped grid takes: its last two products run on the
+    # larger capped grid beside the solve
+    m, n = shape
+    d = make_problem(m, n, 91)
+    print(f"quantize vs separate: {m}x{n}", flush=True)
+    T = {k: to_dev(d[k]) for k in ("W", "A", "B", "scale", "zero", "maxq")}
+    ref = separate(T)
+    torch.cuda.synchronize()
+    out = B.quantize(T["W"], T["A"], T["B"], T["scale"], T["zero"], T["maxq"], 0.01, want_err=True)
+    torch.cuda.synchronize()
+    for key in KEYS:
+        assert torch.equal(out[key], ref[key]), (shape, key)
+    assert int(out["info_A"].item()) == 0 and int(out["info_B"].item()) == 0
