@@ -24,7 +24,8 @@
 //    (K0 <= I + J < mid, J <= J'); stage 2 subtracts
 //    sum_I P_B[I', I] Y[I, J'] from every target tile (mid <= I' + J' < K1).
 //    Both are fp32 MFMA GEMMs whose K range follows the staircase of the
-//    tile band.
+//    tile band.  A node of two leaves (K0, K0 + 1, K0 + 2) has no launch of
+//    its own: the leaf of K0 + 1 applies both stages to its tile first.
 //  * On the upper levels a node's propagation is cut by target
 //    anti-diagonal into parts with different due times; only the first is
 //    on the caller's stream, the others run on library-owned streams beside
