@@ -522,7 +522,8 @@ typedef Gemm<4, 1, RowK, KRow> ColBlk;   // stage 2: 256 rows x 64 cols (one til
 // most w_d = ceil(Kt / 2^d) anti-diagonals wide, so a stage has at most
 // max(Mt, Nt) * ceil(w_d / 4) blocks: that is the list capacity cap[d], and
 // the list of (d, p, stage, part) starts at
-// base[d] + (4p + 2 stage + part) * cap[d].
+// base[d] + (kNodeLists p + kMaxParts stage + part) * cap[d], the early
+// pass's (below) at base[d] + (kNodeLists p + 2 kMaxParts) * cap[d].
 // An entry packs (tile row or column) << 16 | block index.
 //
 // Parts.  The right child [mid, K1) of a node first solves [mid, m2),
@@ -534,6 +535,20 @@ typedef Gemm<4, 1, RowK, KRow> ColBlk;   // stage 2: 256 rows x 64 cols (one til
 // the near part forms Y[I, J'] for J' < m2 - I (what near targets read),
 // the far part the remaining columns J' < K1 - I; far targets read both.
 // An unsplit node is one part: targets [mid, K1), Y columns J' < K1 - I.
+//
+// Early sources.  Stage 1 of an upper node sums over the source tiles of
+// [K0, mid), but those of [K0, q), q = (K0 + mid) / 2 (the left child's
+// split point), are final once [K0, q) is solved, long before mid.  So on
+// the upper levels (depth < early_depth, left child at least kEarlyMin
+// wide, right child at least kSplitMin wide: the split nodes) stage 1 runs
+// in two source passes: the early pass forms Y[I, J'] over the sources
+// [K0, q) for every Y column of the node (J' < K1 - I), on the depth's own
+// stream as soon as [K0, q) is solved; the node's parts then add the
+// sources [q, mid) to it (Y = late + early on rows I < q, which hold early
+// sources).  The near part on the caller's stream is left with the late
+// sources only.  Where a node is not split (bakron_solve_batch, the
+// allocation-free entry point, no library stream) the same two passes run
+// in place on the caller's stream, so every schedule rounds alike.
 
 constexpr int kMaxDepth = 12;                 // Kt <= 2047 needs 11 levels of internal nodes
 constexpr int kMaxKTiles = kMaxDim / kTile;   // K extent of a block, in tiles
@@ -554,14 +569,37 @@ constexpr int kMaxParts = BAKRON_MAX_PARTS;
 #define BAKRON_SPLIT_MIN 8
 #endif
 constexpr int kSplitMin = BAKRON_SPLIT_MIN;       // ... when the right child is at least this wide
+#ifndef BAKRON_EARLY_DEPTH
+#define BAKRON_EARLY_DEPTH 1
+#endif
+constexpr int kEarlyDepth = BAKRON_EARLY_DEPTH;   // nodes above this depth may take an early source pass
+#ifndef BAKRON_EARLY_MIN
+#define BAKRON_EARLY_MIN 8
+#endif
+constexpr int kEarlyMin = BAKRON_EARLY_MIN;       // ... when the left child is at least this wide
+static_assert(kEarlyMin >= 4, "the left child of an early node has a left child of its own");
+#ifndef BAKRON_EARLY_GRID
+#define BAKRON_EARLY_GRID 192
+#endif
+constexpr unsigned kEarlyGrid = BAKRON_EARLY_GRID;   // workgroups of an early pass on a library stream
+// block lists per node: (stage, part) at kMaxParts stage + part, then the early pass
+constexpr int kNodeLists = 2 * kMaxParts + 1;
 
 struct SchedGeom {
     int Mt, Nt, Kt, levels;
     int split_depth;    // nodes above this depth may be cut in parts (0: none)
     int split3_depth;   // ... and in up to kMaxParts parts above this one
+    int early_depth;    // nodes above this depth may take an early source pass (not changed by unsplit runs)
     int64_t base[kMaxDepth];
     int64_t cap[kMaxDepth];
 };
+
+// Whether node (d, [K0, K1)) forms stage 1 in an early and a late source
+// pass (split at (K0 + mid) / 2).
+__host__ __device__ inline bool node_early(const SchedGeom& g, int d, int K0, int mid, int K1)
+{
+    return d < g.early_depth && mid - K0 >= kEarlyMin && K1 - mid >= kSplitMin;
+}
 
 // Parts of node (d, [K0, K1)): 1 (unsplit), 2 (targets [mid, m2) and
 // [m2, K1)) or 3 (the first of those cut again at m3 = (mid + m2) / 2, the
@@ -626,7 +664,9 @@ __host__ __device__ inline int cols_lo(int t0, int Mt) { return max(0, t0 - (Mt 
 __host__ __device__ inline int cols_hi(int t1, int Nt) { return min(Nt - 1, t1 - 1); }
 
 // One workgroup per (heap slot, stage, part): counting sort of the part's
-// blocks by K extent, descending.
+// blocks by K extent, descending.  Stage 2 is the early source pass (part 0
+// only): stage 1 over the sources [K0, q) and every Y column of the node;
+// stage 1 of an early node's parts then takes the sources [q, mid).
 __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict__ out)
 {
     __shared__ int cnt[kMaxKTiles + 1];
@@ -646,19 +686,25 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     const int mid = (K0 + K1) / 2;
     const int parts = node_parts(g, d, mid, K1);
     if (part >= parts) return;
+    const bool early = node_early(g, d, K0, mid, K1);
+    if (stage == 2 && (!early || part > 0)) return;
     const PartRange pr(parts, part, K0, mid, K1);
-    const int y0 = pr.y0;
-    uint32_t* list = out + g.base[d] + (int64_t)(2 * kMaxParts * p + kMaxParts * stage + part) * g.cap[d];
-    const int lo = stage == 0 ? rows_lo(K0, g.Nt) : cols_lo(pr.t0, g.Mt);
-    const int hi = stage == 0 ? rows_hi(mid, g.Mt) : cols_hi(pr.t1, g.Nt);
+    // the stage-1 pass this list is for: sources [sk0, smid), Y columns [y0, y1)
+    const int q = (K0 + mid) / 2;
+    const int sk0 = stage == 2 ? K0 : (early ? q : K0), smid = stage == 2 ? q : mid;
+    const int y0 = stage == 2 ? K0 : pr.y0, y1 = stage == 2 ? K1 : pr.y1;
+    uint32_t* list = out + g.base[d] + (int64_t)(kNodeLists * p + kMaxParts * stage + part) * g.cap[d];
+    const bool rows = stage != 1;
+    const int lo = rows ? rows_lo(sk0, g.Nt) : cols_lo(pr.t0, g.Mt);
+    const int hi = rows ? rows_hi(smid, g.Mt) : cols_hi(pr.t1, g.Nt);
 
     for (int k = t; k <= kMaxKTiles; k += 256) cnt[k] = 0;
     if (t == 0) kmax = 0;
     __syncthreads();
     int km = 0;
     for (int u = lo + t; u <= hi; u += 256) {
-        if (stage == 0) {
-            const RowSpan s(u, K0, mid, y0, pr.y1, g.Nt);
+        if (rows) {
+            const RowSpan s(u, sk0, smid, y0, y1, g.Nt);
             for (int b = 0; b < s.blocks(); ++b) {
                 const int k = s.ktiles(b);
                 atomicAdd(&cnt[k], 1);
@@ -685,8 +731,8 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
     }
     __syncthreads();
     for (int u = lo + t; u <= hi; u += 256) {
-        if (stage == 0) {
-            const RowSpan s(u, K0, mid, y0, pr.y1, g.Nt);
+        if (rows) {
+            const RowSpan s(u, sk0, smid, y0, y1, g.Nt);
             for (int b = 0; b < s.blocks(); ++b) list[atomicAdd(&cnt[s.ktiles(b)], 1)] = ((uint32_t)u << 16) | (uint32_t)b;
         } else {
             const ColSpan s(u, K0, mid, pr.t0, pr.t1, g.Mt);
@@ -702,6 +748,8 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
 // of its part,
 //   Y[I, J'] = sum_{J = sl .. min(sh, J')} E[I, J] P_A[J', J]^T.
 // P_A[J', J] is zero for J > J', so the block uses K = sl .. min(sh, jh).
+// A late source pass is launched with K0 = q; on its rows I < acc_rows
+// (= q) it adds the early pass's Y instead of storing over it.
 //
 // A launch covers `count` list entries with gridDim.x <= count workgroups,
 // each taking entries blockIdx.x, blockIdx.x + gridDim.x, ... (a far part
@@ -713,7 +761,7 @@ __global__ __launch_bounds__(256) void k_sched(SchedGeom g, uint32_t* __restrict
 __device__ __forceinline__ void prop_rows_body(const float* __restrict__ E, const float* __restrict__ PA,
                                                float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                int K0, int mid, int y0, int y1, int Mt, int Nt,
-                                               const uint32_t* __restrict__ list, unsigned count)
+                                               const uint32_t* __restrict__ list, unsigned count, int acc_rows)
 {
     __shared__ __align__(16) float lds[RowBlk::LDS_FLOATS];
     for (unsigned q = blockIdx.x; q < count; q += gridDim.x) {
@@ -730,7 +778,8 @@ __device__ __forceinline__ void prop_rows_body(const float* __restrict__ E, cons
         acc_zero(acc);
         block_gemm<1, 4, RowK, RowK>(E + r0 * ldw, ldw, 64, PA + (int64_t)j0 * 64 * lda, lda,
                                      64 * (jh - j0 + 1), kb, ke, lds, acc);
-        block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, 0.f, acc);
+        block_store<1, 4>(Y + r0 * ldw + (int64_t)j0 * 64, ldw, 64, 64 * (jh - j0 + 1), 1.f, I < acc_rows ? 1.f : 0.f,
+                          acc);
     }
 }
 // One stage-1 list entry's geometry: tile row I, target columns j0 .. jh,
@@ -764,7 +813,8 @@ struct RowEntry {
 __global__ __launch_bounds__(512) void k_prop_rows_far(const float* __restrict__ E, const float* __restrict__ PA,
                                                         float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                         int K0, int mid, int y0, int y1, int Mt, int Nt,
-                                                        const uint32_t* __restrict__ list, unsigned count)
+                                                        const uint32_t* __restrict__ list, unsigned count,
+                                                        int acc_rows)
 {
     __shared__ __align__(16) float lds[2 * RowBlk::LDS_FLOATS];
     const int h = threadIdx.x >> 8;
@@ -783,16 +833,16 @@ __global__ __launch_bounds__(512) void k_prop_rows_far(const float* __restrict__
         acc_zero(acc);
         dual_block_gemm<1, 4, RowK, RowK>(E + r0 * ldw, ldw, 64, PA + cc * lda, lda, cols, ok ? c.kb : 0,
                                           ok ? c.ke : 0, nmax, lds + h * RowBlk::LDS_FLOATS, acc);
-        if (ok) block_store<1, 4>(Y + r0 * ldw + cc, ldw, 64, cols, 1.f, 0.f, acc);
+        if (ok) block_store<1, 4>(Y + r0 * ldw + cc, ldw, 64, cols, 1.f, c.I < acc_rows ? 1.f : 0.f, acc);
     }
 }
 
 __global__ __launch_bounds__(256, 2) void k_prop_rows(const float* __restrict__ E, const float* __restrict__ PA,
                                                    float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                    int K0, int mid, int y0, int y1, int Mt, int Nt,
-                                                   const uint32_t* __restrict__ list, unsigned count)
+                                                   const uint32_t* __restrict__ list, unsigned count, int acc_rows)
 {
-    prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count);
+    prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count, acc_rows);
 }
 
 // Stage 2 of node (K0, mid, K1), one part: block (column J, b) from the
@@ -847,7 +897,7 @@ __global__ __launch_bounds__(256, 2) void k_prop_cols_far(const float* __restric
 __device__ __forceinline__ void prop_rows_t_body(const float* __restrict__ E, const float* __restrict__ PA,
                                                  float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                  int K0, int mid, int y0, int y1, int Nt, unsigned span,
-                                                 unsigned count)
+                                                 unsigned count, int acc_rows)
 {
     __shared__ __align__(16) float lds[kLds64];
     const int wave = threadIdx.x >> 6;
@@ -864,22 +914,22 @@ __device__ __forceinline__ void prop_rows_t_body(const float* __restrict__ E, co
                                  64 * (min(s.sh, Jp) + 1), lds, acc);
         const int64_t r = (int64_t)I * 64 + 32 * (wave >> 1);
         const int64_t c = (int64_t)Jp * 64 + 32 * (wave & 1);
-        wave_store32(Y + r * ldw + c, ldw, 1.f, 0.f, acc);
+        wave_store32(Y + r * ldw + c, ldw, 1.f, I < acc_rows ? 1.f : 0.f, acc);
     }
 }
 __global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E, const float* __restrict__ PA,
                                                      float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                      int K0, int mid, int y0, int y1, int Nt, unsigned span,
-                                                     unsigned count)
+                                                     unsigned count, int acc_rows)
 {
-    prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count);
+    prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count, acc_rows);
 }
 __global__ __launch_bounds__(256) void k_prop_rows_t_far(const float* __restrict__ E, const float* __restrict__ PA,
                                                          float* __restrict__ Y, int64_t ldw, int64_t lda,
                                                          int K0, int mid, int y0, int y1, int Nt, unsigned span,
-                                                         unsigned count)
+                                                         unsigned count, int acc_rows)
 {
-    prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count);
+    prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count, acc_rows);
 }
 
 // Stage 2: item (x, y) updates Wt[I', J] for column J = cols_lo + y and
@@ -966,13 +1016,14 @@ void plan_sched(SchedGeom& g, int64_t& entries, int Mt, int Nt)
            ceil_div(ceil_div(g.Kt, (int64_t)1 << g.split_depth), 2) >= kSplitMin)
         ++g.split_depth;
     g.split3_depth = std::min(kSplit3Depth, g.split_depth);
+    g.early_depth = std::min(kEarlyDepth, g.split_depth);
     const int64_t R = std::max(Mt, Nt);
     int64_t off = 0;
     for (int d = 0; d < kMaxDepth; ++d) {
         const int64_t w = ceil_div(g.Kt, (int64_t)1 << d);
         g.base[d] = off;
         g.cap[d] = R * ceil_div(w, 4);
-        if (d < g.levels) off += ((int64_t)1 << d) * 2 * kMaxParts * g.cap[d];   // 2 stages x kMaxParts parts per node
+        if (d < g.levels) off += ((int64_t)1 << d) * kNodeLists * g.cap[d];   // 2 stages x kMaxParts parts + the early pass
     }
     entries = off;
 }
@@ -1064,6 +1115,17 @@ void ensure_full(SolveRun& R, int khi)
     }
 }
 
+// The same for work on another stream (an early source pass): that stream
+// waits; the caller's stream is not affected.
+void ensure_full_on(SolveRun& R, hipStream_t st, int khi)
+{
+    for (int f = 0; f < 2; ++f) {
+        int k = 0;
+        while (k < R.nwait[f] && R.Kq[f][k] <= khi) ++k;
+        if (k < R.nwait[f] && hipStreamWaitEvent(st, R.ev[f][k], 0) != hipSuccess) R.failed = true;
+    }
+}
+
 hipEvent_t new_event(SolveRun& R)
 {
     hipEvent_t e = nullptr;
@@ -1141,9 +1203,10 @@ constexpr size_t kFarPadBlock = pad_to_exclude(sizeof(float) * RowBlk::LDS_FLOAT
 constexpr size_t kFarPadTile = BAKRON_FAR_PAD_TILE ? pad_to_exclude(sizeof(float) * kLds64) : 0;
 static_assert(sizeof(float) * RowBlk::LDS_FLOATS == sizeof(float) * ColBlk::LDS_FLOATS, "one pad for both stages");
 
-// Stage 1 of one part of node (K0, mid, K1) on stream st into Y.
+// Stage 1 of one part of node (K0, mid, K1) on stream st into Y (sources
+// [K0, mid); rows I < acc_rows add to Y).
 void enqueue_stage1(SolveRun& R, int K0, int mid, int y0, int y1, const uint32_t* list, float* Y, hipStream_t st,
-                    bool far)
+                    bool far, int acc_rows, unsigned grid_cap = kFarGrid)
 {
     const int Mt = R.Mt, Nt = R.Nt;
     const int I_lo = rows_lo(K0, Nt), I_hi = rows_hi(mid, Mt);
@@ -1172,17 +1235,18 @@ void enqueue_stage1(SolveRun& R, int K0, int mid, int y0, int y1, const uint32_t
         for (uint8_t u : pa_used) by += u ? kTileB : 0.0;
     if (far && blocks >= kFarBlockMin) {
         const unsigned n = (unsigned)blocks;
-        launch(R.prof, KK_PROP_ROWS_FAR, fl, by, k_prop_rows_far, dim3(std::min((n + 1) / 2, kFarGrid)), dim3(512),
-               st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid, y0, y1, Mt, Nt, list, n);
+        launch(R.prof, KK_PROP_ROWS_FAR, fl, by, k_prop_rows_far, dim3(std::min((n + 1) / 2, grid_cap)), dim3(512),
+               st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid, y0, y1, Mt, Nt, list, n,
+               acc_rows);
     } else if (blocks >= kBlockLaunchMin) {
         const unsigned n = (unsigned)blocks;
         launch(R.prof, KK_PROP_ROWS, fl, by, k_prop_rows, dim3(n), dim3(256), st, (const float*)R.leaf.E, R.leaf.PA,
-               Y, R.leaf.ldw, R.leaf.lda, K0, mid, y0, y1, Mt, Nt, list, n);
+               Y, R.leaf.ldw, R.leaf.lda, K0, mid, y0, y1, Mt, Nt, list, n, acc_rows);
     } else if (blocks > 0) {
         const unsigned n = (unsigned)span * (unsigned)(I_hi - I_lo + 1);
-        launch_shm(R.prof, far ? KK_PROP_ROWS_T_FAR : KK_PROP_ROWS_T, fl, by, far ? k_prop_rows_t_far : k_prop_rows_t, dim3(far ? std::min(n, kFarGrid) : n), dim3(256),
+        launch_shm(R.prof, far ? KK_PROP_ROWS_T_FAR : KK_PROP_ROWS_T, fl, by, far ? k_prop_rows_t_far : k_prop_rows_t, dim3(far ? std::min(n, grid_cap) : n), dim3(256),
                    far ? kFarPadTile : 0, st, (const float*)R.leaf.E, R.leaf.PA, Y, R.leaf.ldw, R.leaf.lda, K0, mid,
-                   y0, y1, Nt, (unsigned)span, n);
+                   y0, y1, Nt, (unsigned)span, n, acc_rows);
     }
 }
 
@@ -1234,6 +1298,29 @@ struct SpineWaits {
     hipEvent_t e[kMaxParts];
 };
 
+// An early source pass (the node's stage 1 over the sources [K0, q), every
+// Y column) on stream fs, once the caller's stream has solved [K0, q) and
+// enqueued the left child's propagation; `done` is recorded after it.
+struct EarlyPass {
+    int K0, mid, K1, d, p;
+    hipEvent_t done;
+};
+
+void enqueue_early(SolveRun& R, EarlyPass& e, hipStream_t fs)
+{
+    const SchedGeom& g = *R.sg;
+    hipEvent_t ready = new_event(R);   // the errors of [K0, q) are final
+    if (!ready || hipEventRecord(ready, R.s) != hipSuccess || hipStreamWaitEvent(fs, ready, 0) != hipSuccess) {
+        R.failed = true;
+        return;
+    }
+    ensure_full_on(R, fs, e.K1 - 1);   // P_A rows up to K1 - 1
+    const uint32_t* list = R.sched + g.base[e.d] + (int64_t)(kNodeLists * e.p + 2 * kMaxParts) * g.cap[e.d];
+    enqueue_stage1(R, e.K0, (e.K0 + e.mid) / 2, e.K0, e.K1, list, R.Ysplit[e.d], fs, true, 0, kEarlyGrid);
+    e.done = new_event(R);
+    if (!e.done || hipEventRecord(e.done, fs) != hipSuccess) R.failed = true;
+}
+
 // Node (K0, mid, K1) at heap position (d, p).  Unsplit: both stages on the
 // caller's stream.  Cut in parts: the first part on the caller's stream,
 // the others in order on the depth's own stream once the first part's
@@ -1241,15 +1328,28 @@ struct SpineWaits {
 // with an event, due before the propagation of the node parts - 1 - k
 // levels down the left spine of the right child (the first work on the
 // caller's stream that touches the part's targets): returned in `done`.
-void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits& done)
+// An early node's stage 1 takes the late sources [q, mid) on top of its
+// early pass: that pass ran on the depth's stream (early_done, waited for
+// here) or, when the node is not split, runs here first.
+void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits& done, hipEvent_t early_done)
 {
     for (hipEvent_t& e : done.e) e = nullptr;
     const SchedGeom& g = *R.sg;
-    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(2 * kMaxParts * p) * g.cap[d];   // (stage, part) at (kMaxParts stage + part) cap
+    const uint32_t* lists = R.sched + g.base[d] + (int64_t)(kNodeLists * p) * g.cap[d];   // (stage, part) at (kMaxParts stage + part) cap
     const int parts = node_parts(g, d, mid, K1);
     float* Y = parts > 1 ? R.Ysplit[d] : R.Y;
+    const bool early = node_early(g, d, K0, mid, K1);
+    const int q = (K0 + mid) / 2;
+    const int sk0 = early ? q : K0, acc_rows = early ? q : 0;   // the stage-1 sources of the parts: [sk0, mid)
+    if (early) {
+        if (early_done) {
+            if (hipStreamWaitEvent(R.s, early_done, 0) != hipSuccess) R.failed = true;
+        } else {
+            enqueue_stage1(R, K0, q, K0, K1, lists + 2 * kMaxParts * g.cap[d], Y, R.s, false, 0);
+        }
+    }
     const PartRange p0(parts, 0, K0, mid, K1);
-    enqueue_stage1(R, K0, mid, p0.y0, p0.y1, lists, Y, R.s, false);
+    enqueue_stage1(R, sk0, mid, p0.y0, p0.y1, lists, Y, R.s, false, acc_rows);
     if (parts == 1) {
         enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + kMaxParts * g.cap[d], Y, R.s, false);
         return;
@@ -1263,7 +1363,7 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits
     enqueue_stage2(R, K0, mid, p0.t0, p0.t1, lists + kMaxParts * g.cap[d], Y, R.s, false);
     for (int part = 1; part < parts; ++part) {
         const PartRange pr(parts, part, K0, mid, K1);
-        enqueue_stage1(R, K0, mid, pr.y0, pr.y1, lists + part * g.cap[d], Y, R.far[d], true);
+        enqueue_stage1(R, sk0, mid, pr.y0, pr.y1, lists + part * g.cap[d], Y, R.far[d], true, acc_rows);
         enqueue_stage2(R, K0, mid, pr.t0, pr.t1, lists + (kMaxParts + part) * g.cap[d], Y, R.far[d], true);
         hipEvent_t ev = new_event(R);
         if (!ev || hipEventRecord(ev, R.far[d]) != hipSuccess) {
@@ -1275,14 +1375,20 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits
 }
 
 // `waits`: far parts of ancestors due before the propagation of this node
-// and of the nodes down its left spine.  A node of two leaves runs its
-// propagation inside the second leaf (BAKRON_PAIR_FUSE).
+// and of the nodes down its left spine.  `parent`: the early pass of the
+// parent node when this is its left child.  It is enqueued after this
+// node's propagation, behind this node's far parts on their stream (or on
+// the parent's stream when this node is not split): the caller's stream
+// then runs the leaves of this node's right child, and the early pass takes
+// CUs beside them rather than beside this node's near part or its far
+// parts.  A node of two leaves runs its propagation inside the second leaf
+// (BAKRON_PAIR_FUSE).
 #ifndef BAKRON_PAIR_FUSE
 #define BAKRON_PAIR_FUSE 1
 #endif
-void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits)
+void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits, EarlyPass* parent)
 {
-    if (K1 - K0 == 1) {   // (the nodes that carry waits are never leaves)
+    if (K1 - K0 == 1) {   // (the nodes that carry waits or an early pass are never leaves)
         ensure_full(R, K0);
         enqueue_leaf(R, K0);
         return;
@@ -1290,7 +1396,10 @@ void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& wait
     const int mid = (K0 + K1) / 2;
     SpineWaits down;
     for (int j = 0; j < kMaxParts; ++j) down.e[j] = j + 1 < kMaxParts ? waits.e[j + 1] : nullptr;
-    solve_rec(R, K0, mid, d + 1, 2 * p, down);
+    // a split early node runs its early pass on its depth's stream
+    EarlyPass mine{K0, mid, K1, d, p, nullptr};
+    const bool early_far = node_early(*R.sg, d, K0, mid, K1) && node_parts(*R.sg, d, mid, K1) > 1;
+    solve_rec(R, K0, mid, d + 1, 2 * p, down, early_far ? &mine : nullptr);
     if (waits.e[0] && hipStreamWaitEvent(R.s, waits.e[0], 0) != hipSuccess) R.failed = true;
     ensure_full(R, K1 - 1);
     if (BAKRON_PAIR_FUSE && K1 - K0 == 2) {   // (never cut in parts) the second leaf propagates first
@@ -1298,8 +1407,9 @@ void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& wait
         return;
     }
     SpineWaits done;
-    enqueue_prop(R, K0, mid, K1, d, p, done);
-    solve_rec(R, mid, K1, d + 1, 2 * p + 1, done);
+    enqueue_prop(R, K0, mid, K1, d, p, done, mine.done);
+    if (parent) enqueue_early(R, *parent, node_parts(*R.sg, d, mid, K1) > 1 ? R.far[d] : R.far[parent->d]);
+    solve_rec(R, mid, K1, d + 1, 2 * p + 1, done, nullptr);
 }
 
 }  // namespace
@@ -1395,7 +1505,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     R.sched = sched;
     if (p.sg.levels > 0)
         launch(prof, KK_SCHED, 0.0, 4.0 * (double)p.sched_entries, k_sched,
-               dim3((unsigned)((1u << p.sg.levels) - 1u), 2u, (unsigned)kMaxParts), dim3(256), s, p.sg, sched);
+               dim3((unsigned)((1u << p.sg.levels) - 1u), 3u, (unsigned)kMaxParts), dim3(256), s, p.sg, sched);
     if (p.sg.split_depth > 0) {
         static std::once_flag attrs;
         std::call_once(attrs, [] {
@@ -1411,7 +1521,7 @@ int solve_enqueue(const float* W, int64_t m, int64_t n, const float* LA, const f
     }
     SpineWaits none;
     for (hipEvent_t& e : none.e) e = nullptr;
-    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, none);
+    solve_rec(R, 0, R.Mt + R.Nt - 1, 0, 0, none, nullptr);
     ensure_full(R, INT_MAX - 1);   // s is ordered after the factors in any case
     // every far part is waited for by the right child of its node, so all
     // of them are ordered before the rest of the work on s
