@@ -91,7 +91,12 @@ size_t bakron_factor_workspace_bytes(int64_t n);
  *              LAPACK.  Written on the device; read it after synchronising.
  *              L and P are undefined when info != 0.
  * workspace, workspace_bytes [in] scratch, >= bakron_factor_workspace_bytes(n).
- * stream [in]  HIP stream (0 = legacy default stream).
+ * stream [in]  HIP stream (0 = legacy default stream).  Factors of 8192 and
+ *              more (whose top level runs on 128 x 128 blocks) also run part
+ *              of the top level's products on one of the library-owned
+ *              streams of bakron_solve, forked from and joined back into
+ *              `stream` within the call: the result is ordered on `stream`
+ *              like the rest.
  */
 int bakron_factor(const float* A, int64_t n, float damp_frac, float* L, float* P,
                   int32_t* info, void* workspace, size_t workspace_bytes,

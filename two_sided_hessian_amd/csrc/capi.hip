@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <utility>
@@ -49,6 +50,15 @@ static int check_ws(const void* ws, size_t have, size_t need)
     return BAKRON_SUCCESS;
 }
 
+// The library stream for a standalone factorisation's side work (library
+// slots 2 and 3 in turn, so that two factorisations issued one after the
+// other, e.g. of A and B, do not queue behind each other's side work).
+static hipStream_t factor_side_stream()
+{
+    static std::atomic<unsigned> next{0};
+    return bk::side_stream(2 + (int)(next.fetch_add(1u, std::memory_order_relaxed) & 1u));
+}
+
 int bakron_factor(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
                   void* workspace, size_t workspace_bytes, hipStream_t stream)
 {
@@ -59,8 +69,10 @@ int bakron_factor(const float* A, int64_t n, float damp_frac, float* L, float* P
     if (!bk::aligned16(L) || !bk::aligned16(P)) return BAKRON_ERR_BAD_ARG;
     const int w = check_ws(workspace, workspace_bytes, bk::factor_workspace_bytes(n));
     if (w) return w;
-    return bk::factor_enqueue(A, n, damp_frac, L, P, info, workspace, stream, nullptr) ? BAKRON_ERR_HIP
-                                                                                        : BAKRON_SUCCESS;
+    return bk::factor_enqueue(A, n, damp_frac, L, P, info, workspace, stream, nullptr, nullptr, nullptr,
+                              factor_side_stream())
+               ? BAKRON_ERR_HIP
+               : BAKRON_SUCCESS;
 }
 
 int bakron_factor_profiled(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
@@ -77,7 +89,8 @@ int bakron_factor_profiled(const float* A, int64_t n, float damp_frac, float* L,
     const int w = check_ws(workspace, workspace_bytes, bk::factor_workspace_bytes(n));
     if (w) return w;
     bk::Prof prof;
-    const int rc = bk::factor_enqueue(A, n, damp_frac, L, P, info, workspace, stream, &prof);
+    const int rc = bk::factor_enqueue(A, n, damp_frac, L, P, info, workspace, stream, &prof, nullptr, nullptr,
+                                      factor_side_stream());
     const int rp = bk::prof_collect(prof, stream, stats, max_stats, n_stats);
     return (rc || rp) ? BAKRON_ERR_HIP : BAKRON_SUCCESS;
 }
@@ -235,11 +248,17 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
         int next = 3;
         for (int f = 0; f < 2; ++f)
             for (int k = 0; k < wait.lead[f].count; ++k) wait.lead[f].ev[k] = ev[next++];
+        // The two factors' launches are issued interleaved (each is a chain of
+        // latency-bound launches; issued one factor after the other, the
+        // second chain would start only after the host had issued the first).
+        bk::FactorCalls qa, qb;
         if (hipEventRecord(ev[0], stream) != hipSuccess || hipStreamWaitEvent(sa, ev[0], 0) != hipSuccess ||
             hipStreamWaitEvent(sb, ev[0], 0) != hipSuccess ||
-            bk::factor_enqueue(A, n, damp_frac, L_A, P_A, info_A, ws_a, sa, nullptr, &wait.lead[0]) ||
-            hipEventRecord(ev[1], sa) != hipSuccess ||
-            bk::factor_enqueue(B, m, damp_frac, L_B, P_B, info_B, ws_b, sb, nullptr, &wait.lead[1]) ||
+            bk::factor_enqueue(A, n, damp_frac, L_A, P_A, info_A, ws_a, sa, nullptr, &wait.lead[0], &qa,
+                               bk::side_stream(2)) ||
+            bk::factor_enqueue(B, m, damp_frac, L_B, P_B, info_B, ws_b, sb, nullptr, &wait.lead[1], &qb,
+                               bk::side_stream(3)) ||
+            bk::run_interleaved(qa, qb) || hipEventRecord(ev[1], sa) != hipSuccess ||
             hipEventRecord(ev[2], sb) != hipSuccess ||
             bk::solve_enqueue(W, m, n, L_A, P_A, L_B, P_B, scale, zero, maxq, V, codes, err, objective, ws_s,
                               stream, nullptr, true, &wait))
@@ -433,7 +452,7 @@ const char* kernel_name(int kind)
         "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish", "k_gptq_load",
         "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj", "k_row_sqnorms", "k_moment<false>",
         "k_moment<true>", "k_prop_rows_far", "k_prop_rows_t_far", "k_prop_cols_far", "k_prop_cols_t_far",
-        "k_ad_prep", "k_ad_quant", "k_ad_update"};
+        "k_ad_prep", "k_ad_quant", "k_ad_update", "k_f_update"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 

@@ -29,6 +29,7 @@
 // the finished P11 directly (see factor_rec), so a solve can start on the
 // leading blocks while the rest of the factorisation runs.
 #include <algorithm>
+#include <memory>
 #include <mutex>
 
 #include "gemm.hpp"
@@ -559,6 +560,22 @@ __global__ __launch_bounds__(256) void k_f_left(const float* __restrict__ T, flo
     block_store<2, 2>(Pbuf + (o2 + r0) * ld + o1 + c0, ld, n2 - r0, n1 - c0, -1.f, 0.f, acc);
 }
 
+// A[ro + r][co + c] -= sum_{k < nk} L[ko + k][ro + r] L[ko + k][co + c] over
+// the nr x nc rectangle (the update of pending columns co .. co + nc - 1 by
+// the finished rows ko .. ko + nk - 1; see factor_rec).
+__global__ __launch_bounds__(256) void k_f_update(const float* __restrict__ Lbuf, float* __restrict__ Pbuf,
+                                                  int64_t ld, int64_t ro, int64_t co, int64_t ko, int nr, int nc,
+                                                  int nk)
+{
+    __shared__ __align__(16) float lds[Gemm<2, 2, KRow, KRow>::LDS_FLOATS];
+    const int r0 = blockIdx.y * FBM, c0 = blockIdx.x * FBN;
+    Acc acc;
+    acc_zero(acc);
+    block_gemm<2, 2, KRow, KRow>(Lbuf + ko * ld + ro + r0, ld, nr - r0, Lbuf + ko * ld + co + c0, ld, nc - c0, 0, nk,
+                                 lds, acc);
+    block_store<2, 2>(Pbuf + (ro + r0) * ld + co + c0, ld, nr - r0, nc - c0, -1.f, 1.f, acc);
+}
+
 // The top level's T and Li21 products while a solve runs beside them on the
 // factor's leading block (factor_enqueue with `lead`): at most kLeadGrid
 // workgroups, each looping over blocks q = blockIdx.x, + gridDim.x, ... in
@@ -790,32 +807,108 @@ struct FactorRun {
     bool early;                // the leading spine finishes its blocks early (see factor_rec)
     const FactorLeads* leads;  // nullable: events of the leading blocks, recorded as they become final
     int64_t n;
+    FactorCalls* defer;        // nullable: stream operations are appended here instead of issued
+    hipStream_t side;          // nullable: a library stream for the right-looking pieces (factor_rec)
+    std::shared_ptr<std::vector<hipEvent_t>> events;   // destroyed with the last operation that holds them
 };
+
+int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
+
+hipEvent_t new_event(const FactorRun& R)
+{
+    hipEvent_t e = nullptr;
+    if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return nullptr;
+    R.events->push_back(e);
+    return e;
+}
+
+// One stream operation of the factorisation (f returns 0 or -1): issued at
+// once, or appended to R.defer.
+template <class F>
+int emit(const FactorRun& R, F f)
+{
+    if (R.defer) {
+        R.defer->emplace_back(std::move(f));
+        return 0;
+    }
+    return f();
+}
 
 // Records the event of the leading block [0, size)^2 (size below n).
 int record_lead(const FactorRun& R, int64_t size)
 {
     if (!R.leads) return 0;
     for (int k = 0; k < R.leads->count; ++k)
-        if (R.leads->size[k] == size) return hipEventRecord(R.leads->ev[k], R.s) == hipSuccess ? 0 : -1;
+        if (R.leads->size[k] == size) {
+            const hipEvent_t e = R.leads->ev[k];
+            const hipStream_t s = R.s;
+            return emit(R, [e, s] { return hipEventRecord(e, s) == hipSuccess ? 0 : -1; });
+        }
     return 0;
 }
 
 // The finish pass over rows [i0, i1) and columns [j0, j1) (multiples of 4):
 // P = Li diag(L) below the diagonal, zeros above both diagonals.
-void enqueue_finish(const FactorRun& R, int64_t i0, int64_t i1, int64_t j0, int64_t j1)
+int enqueue_finish(const FactorRun& R, int64_t i0, int64_t i1, int64_t j0, int64_t j1)
 {
     const double rows = (double)(i1 - i0), cols = (double)(j1 - j0);
     dim3 g((unsigned)ceil_div(j1 - j0, 1024), (unsigned)std::min<int64_t>(i1 - i0, 256));
-    launch(R.prof, KK_F_FINISH, rows * cols / 2.0, 4.0 * 4.0 * rows * cols, k_f_finish, g, dim3(256), R.s,
-           R.Lbuf, R.Pbuf, R.ld, i0, i1, j0, j1, R.n, (float*)nullptr, (float*)nullptr);
+    return emit(R, [=] {
+        launch(R.prof, KK_F_FINISH, rows * cols / 2.0, 4.0 * 4.0 * rows * cols, k_f_finish, g, dim3(256), R.s,
+               R.Lbuf, R.Pbuf, R.ld, i0, i1, j0, j1, R.n, (float*)nullptr, (float*)nullptr);
+        return launch_ok();
+    });
 }
 
 // Algorithmic work (fp32 flops = 2 x multiply-adds on the nonzero triangle /
 // block support) and bytes (each operand read once, each output written once).
 inline double tri(double k) { return k * (k + 1.0) / 2.0; }
 
-int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
+// The panel L21 = Li22^T A21 (L21: rows o2 .. o2 + n2 - 1, columns o1 ..
+// o1 + n1 - 1) on stream st: 128 x 128 blocks while they fill the GPU, else
+// 64 x 64 tiles.
+int emit_panel(const FactorRun& R, hipStream_t st, int64_t o1, int64_t o2, int n1, int n2)
+{
+    const bool tiles = ceil_div(n1, FBN) * ceil_div(n2, FBM) < kFactorBlockMin;
+    const dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
+    const dim3 gt((unsigned)(n1 / kTile), (unsigned)(n2 / kTile));
+    const double d1 = n1, d2 = n2;
+    const double fl = 2.0 * d1 * tri(d2), by = 4.0 * (tri(d2) + 2.0 * d2 * d1);
+    return emit(R, [=] {
+        if (tiles)
+            launch(R.prof, KK_F_PANEL_T, fl, by, k_f_tile<0>, gt, dim3(256), st, R.Lbuf, R.Pbuf, (float*)nullptr,
+                   R.ld, o1, o2, n1, n2);
+        else
+            launch(R.prof, KK_F_PANEL, fl, by, k_f_panel, g, dim3(256), st, R.Pbuf, R.Lbuf, R.ld, o1, o2, n1, n2);
+        return launch_ok();
+    });
+}
+
+// The SYRK A11 -= L21^T L21 on the lower tiles of A11 (o1 .. o1 + n1 - 1),
+// L21 rows o2 .. o2 + n2 - 1, on stream st.
+int emit_syrk(const FactorRun& R, hipStream_t st, int64_t o1, int64_t o2, int n1, int n2)
+{
+    const double d1 = n1, d2 = n2;
+    const double fl = 2.0 * d2 * tri(d1), by = 4.0 * (d2 * d1 + 2.0 * tri(d1));
+    const int64_t tb = n1 / kTile, nsyrk = tb * (tb + 1) / 2;
+    return emit(R, [=] {
+        launch(R.prof, KK_F_SYRK_T, fl, by, k_f_tile<1>, dim3((unsigned)nsyrk), dim3(256), st, R.Lbuf, R.Pbuf,
+               (float*)nullptr, R.ld, o1, o2, n1, n2);
+        return launch_ok();
+    });
+}
+
+// A node whose panel and SYRK are split right-looking (see factor_rec)
+// passes its leading range to its trailing child, which fills in `done`.
+struct Pending {
+    int64_t o;          // the node's leading half: columns o .. o + n - 1
+    int n;
+    hipEvent_t done;    // recorded on the side stream after the child's share
+};
+
+#ifndef BAKRON_RIGHT_LOOKING
+#define BAKRON_RIGHT_LOOKING 1
+#endif
 
 // On the leading spine (o == 0, with `early`) every node ends with its
 // whole block [0, nsz)^2 finished (P = Li diag(L), zeros above both
@@ -825,19 +918,34 @@ int launch_ok() { return hipGetLastError() == hipSuccess ? 0 : -1; }
 // P21 = Li21 diag(L11) = -Li22 L21 Li11 diag(L11) = -Li22 T', and it then
 // finishes its trailing block.  Off the spine the blocks stay unscaled (the
 // products of the levels above read Li).
-int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
+//
+// Right-looking split (block levels, with a side stream).  The node's panel
+// L21 = Li22^T A21 and SYRK A11 -= L21^T L21 wait for the whole trailing
+// half C = [C1 | C2].  But the rows of C2 are final once C2 and C's own panel
+// L[C2, C1] are: then, on the side stream, L[C2, A] = Li_C2^T A[C2, A], the
+// update A[C1, A] -= L[C2, C1]^T L[C2, A] of the rows still pending, and
+// the SYRK share A11 -= L[C2, A]^T L[C2, A] run beside C1's factorisation
+// (a chain of small launches).  C1 does the same with its own halves, and
+// so on down C's leading spine, so after C only the rows of C's leading-most
+// base block are left on the chain: their rows of L21 and their SYRK share.
+// The same products in a different grouping (block Gaussian elimination of
+// Li_C^T A21 by the blocks of C's leading spine), so the factor's rounding
+// changes but not its accuracy.  `up`: the parent's pending columns when
+// this node is C or a node of C's leading spine.
+int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* up)
 {
     const bool spine = R.early && o == 0;
     if (nsz <= 2 * kTile) {
         // factor (b^3 / 3 multiply-adds) and inverse (b^3 / 6) of the block
         const double b = (double)nsz;
-        launch(R.prof, KK_F_DIAG, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
-               R.Lbuf, R.Pbuf, R.ld, o, (int)nsz, R.info);
-        if (spine) {
-            enqueue_finish(R, 0, nsz, 0, nsz);
-            if (launch_ok() || record_lead(R, nsz)) return -1;
-        }
-        return launch_ok();
+        if (emit(R, [=] {
+                launch(R.prof, KK_F_DIAG, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
+                       R.Lbuf, R.Pbuf, R.ld, o, (int)nsz, R.info);
+                return launch_ok();
+            }))
+            return -1;
+        if (spine && (enqueue_finish(R, 0, nsz, 0, nsz) || record_lead(R, nsz))) return -1;
+        return 0;
     }
     const int64_t nt = nsz / kTile;
     const int n1 = (int)(kTile * (nt / 2));
@@ -846,43 +954,87 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
     const double d1 = n1, d2 = n2;
     if (depth >= kFactorDepths) return -1;
     float* const T = R.T + R.tbase[depth];
-    if (factor_rec(R, o2, n2, depth + 1)) return -1;
     // 128 x 128 blocks while they fill the GPU, else 64 x 64 tiles
     const bool tiles = ceil_div(n1, FBN) * ceil_div(n2, FBM) < kFactorBlockMin;
     const dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
     const dim3 gt((unsigned)(n1 / kTile), (unsigned)(n2 / kTile));
-    const double fl_panel = 2.0 * d1 * tri(d2), by_panel = 4.0 * (tri(d2) + 2.0 * d2 * d1);
-    if (tiles)
-        launch(R.prof, KK_F_PANEL_T, fl_panel, by_panel, k_f_tile<0>, gt, dim3(256), R.s, R.Lbuf, R.Pbuf,
-               T, R.ld, o1, o2, n1, n2);
-    else
-        launch(R.prof, KK_F_PANEL, fl_panel, by_panel, k_f_panel, g, dim3(256), R.s, R.Pbuf, R.Lbuf, R.ld, o1, o2,
-               n1, n2);
-    {
-        // SYRK on 64 x 64 tiles at every level: its K extent is uniform, so
-        // the finer grid only helps (a triangle of 128-blocks quantizes badly
-        // over the CUs, e.g. 528 blocks at n1 = 4096).  On the tile levels
-        // the same launch forms U = -Li22 L21.
-        const double fl = 2.0 * d2 * tri(d1), by = 4.0 * (d2 * d1 + 2.0 * tri(d1));
-        const int64_t tb = n1 / kTile, nsyrk = tb * (tb + 1) / 2;
+    const bool rl = BAKRON_RIGHT_LOOKING && !tiles && R.side && n2 > 2 * kTile;
+    // This node as the trailing half of a right-looking parent (`up`): once
+    // its own panel is formed, its rows o2 .. o2 + n2 - 1 are final for the
+    // parent's columns too.  On the side stream: those rows of the parent's
+    // panel, the update of this node's rows o1 .. o2 - 1 for the parent's
+    // columns, and the parent's SYRK share of the final rows.
+    auto parent_share = [&]() -> int {
+        if (!up) return 0;
+        const hipEvent_t ready = new_event(R), done = new_event(R);
+        if (!ready || !done) return -1;
+        const hipStream_t s = R.s, side = R.side;
+        const int64_t po = up->o;
+        const int pn = up->n;
+        const double fu = 2.0 * d1 * pn * d2, bu = 4.0 * (2.0 * d1 * pn + d2 * (d1 + pn));
+        const dim3 gu((unsigned)ceil_div(pn, FBN), (unsigned)ceil_div(n1, FBM));
+        if (emit(R, [=] {
+                return (hipEventRecord(ready, s) == hipSuccess && hipStreamWaitEvent(side, ready, 0) == hipSuccess)
+                           ? 0
+                           : -1;
+            }) ||
+            emit_panel(R, side, po, o2, pn, n2) ||
+            emit(R, [=] {
+                launch(R.prof, KK_F_UPDATE, fu, bu, k_f_update, gu, dim3(256), side, (const float*)R.Lbuf, R.Pbuf,
+                       R.ld, o1, po, o2, n1, pn, n2);
+                return launch_ok();
+            }) ||
+            emit_syrk(R, side, po, o2, pn, n2) ||
+            emit(R, [=] { return hipEventRecord(done, side) == hipSuccess ? 0 : -1; }))
+            return -1;
+        up->done = done;
+        return 0;
+    };
+    Pending mine{o1, n1, nullptr};
+    if (factor_rec(R, o2, n2, depth + 1, rl ? &mine : nullptr)) return -1;
+    if (rl) {
+        // the side stream's share (rows of C2) is done; the rows of C1 here
+        const hipEvent_t e = mine.done;
+        const hipStream_t s = R.s;
+        if (!e || emit(R, [=] { return hipStreamWaitEvent(s, e, 0) == hipSuccess ? 0 : -1; })) return -1;
+        int c1 = n2;   // the rows left: C's leading-most base block
+        while (c1 > 2 * kTile) c1 = (int)(kTile * ((c1 / kTile) / 2));
+        if (emit_panel(R, R.s, o1, o2, n1, c1) || parent_share() || emit_syrk(R, R.s, o1, o2, n1, c1)) return -1;
+    } else {
+        if (emit_panel(R, R.s, o1, o2, n1, n2) || parent_share()) return -1;
         if (tiles) {
+            // SYRK on 64 x 64 tiles at every level: its K extent is uniform, so
+            // the finer grid only helps (a triangle of 128-blocks quantizes badly
+            // over the CUs, e.g. 528 blocks at n1 = 4096).  On the tile levels
+            // the same launch forms U = -Li22 L21.
+            const double fl = 2.0 * d2 * tri(d1), by = 4.0 * (d2 * d1 + 2.0 * tri(d1));
             const double fu = 2.0 * d1 * tri(d2), bu = 4.0 * (2.0 * d2 * d1 + tri(d2));
-            launch(R.prof, KK_F_LEFT_T, fl + fu, by + bu, k_f_tile<3>, dim3((unsigned)(nsyrk + gt.x * gt.y)),
-                   dim3(256), R.s, R.Lbuf, R.Pbuf, T, R.ld, o1, o2, n1, n2);
-        } else {
-            launch(R.prof, KK_F_SYRK_T, fl, by, k_f_tile<1>, dim3((unsigned)nsyrk), dim3(256), R.s, R.Lbuf, R.Pbuf,
-                   T, R.ld, o1, o2, n1, n2);
+            const int64_t tb = n1 / kTile, nsyrk = tb * (tb + 1) / 2;
+            if (emit(R, [=] {
+                    launch(R.prof, KK_F_LEFT_T, fl + fu, by + bu, k_f_tile<3>, dim3((unsigned)(nsyrk + gt.x * gt.y)),
+                           dim3(256), R.s, R.Lbuf, R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                    return launch_ok();
+                }))
+                return -1;
+        } else if (emit_syrk(R, R.s, o1, o2, n1, n2)) {
+            return -1;
         }
     }
-    if (launch_ok()) return -1;
-    if (factor_rec(R, o1, n1, depth + 1)) return -1;
+    // the parent's pending rows continue down the leading half (its trailing
+    // rows go to the side stream there too), so that only this node's
+    // leading-most base block is left for the parent's chain
+    if (factor_rec(R, o1, n1, depth + 1, n1 > 2 * kTile ? up : nullptr)) return -1;
     {
         const double fr = 2.0 * d2 * tri(d1), br = 4.0 * (2.0 * d2 * d1 + tri(d1));
         const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
         if (tiles) {
             // Li21 = U Li11 (on the spine U P11 = P21, P11 being finished)
-            launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf, R.Pbuf, T,
-                   R.ld, o1, o2, n1, n2);
+            if (emit(R, [=] {
+                    launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf,
+                           R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                    return launch_ok();
+                }))
+                return -1;
         } else if (R.leads && o == 0 && nsz == R.ld && (g.x * g.y <= kLeadMaxBlocks || kLeadGridBig > 0)) {
             static std::once_flag attrs;
             std::call_once(attrs, [] {
@@ -892,23 +1044,31 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth)
                                           (int)kLeadPad);
             });
             const unsigned cnt = g.x * g.y, grid = std::min(cnt, cnt <= kLeadMaxBlocks ? kLeadGrid : kLeadGridBig);
-            launch_shm(R.prof, KK_F_RIGHT, fr, br, k_f_right_lead, dim3(grid), dim3(256), kLeadPad, R.s,
-                       (const float*)R.Lbuf, (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2, g.y, cnt);
-            launch_shm(R.prof, KK_F_LEFT, fl, bl, k_f_left_lead, dim3(grid), dim3(256), kLeadPad, R.s,
-                       (const float*)T, R.Pbuf, R.ld, o1, o2, n1, n2, g.x, g.y, cnt);
+            if (emit(R, [=] {
+                    launch_shm(R.prof, KK_F_RIGHT, fr, br, k_f_right_lead, dim3(grid), dim3(256), kLeadPad, R.s,
+                               (const float*)R.Lbuf, (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2, g.y, cnt);
+                    launch_shm(R.prof, KK_F_LEFT, fl, bl, k_f_left_lead, dim3(grid), dim3(256), kLeadPad, R.s,
+                               (const float*)T, R.Pbuf, R.ld, o1, o2, n1, n2, g.x, g.y, cnt);
+                    return launch_ok();
+                }))
+                return -1;
         } else {
-            launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, dim3(g.y, g.x), dim3(256), R.s, (const float*)R.Lbuf,
-                   (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2);
-            launch(R.prof, KK_F_LEFT, fl, bl, k_f_left, g, dim3(256), R.s, (const float*)T, R.Pbuf, R.ld, o1, o2,
-                   n1, n2);
+            if (emit(R, [=] {
+                    launch(R.prof, KK_F_RIGHT, fr, br, k_f_right, dim3(g.y, g.x), dim3(256), R.s,
+                           (const float*)R.Lbuf, (const float*)R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                    launch(R.prof, KK_F_LEFT, fl, bl, k_f_left, g, dim3(256), R.s, (const float*)T, R.Pbuf, R.ld, o1,
+                           o2, n1, n2);
+                    return launch_ok();
+                }))
+                return -1;
         }
     }
     if (spine) {   // the trailing block, and the zeros right of the leading block (P21 is done)
-        enqueue_finish(R, n1, nsz, n1, nsz);
-        enqueue_finish(R, 0, n1, n1, nsz);
-        if (launch_ok() || (nsz < R.ld && record_lead(R, nsz))) return -1;
+        if (enqueue_finish(R, n1, nsz, n1, nsz) || enqueue_finish(R, 0, n1, n1, nsz) ||
+            (nsz < R.ld && record_lead(R, nsz)))
+            return -1;
     }
-    return launch_ok();
+    return 0;
 }
 
 }  // namespace
@@ -933,7 +1093,8 @@ int factor_leads(int64_t n, int64_t* sizes)
 }
 
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
-                   void* ws, hipStream_t s, Prof* prof, const FactorLeads* leads)
+                   void* ws, hipStream_t s, Prof* prof, const FactorLeads* leads, FactorCalls* defer,
+                   hipStream_t side)
 {
     const FactorPlan p = plan_factor(n);
     char* w = static_cast<char*>(ws);
@@ -951,25 +1112,55 @@ int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* 
     R.n = n;
     R.Lbuf = p.padded ? reinterpret_cast<float*>(w + p.off_L) : L;
     R.Pbuf = p.padded ? reinterpret_cast<float*>(w + p.off_P) : P;
+    R.defer = defer;
+    R.side = side;
+    R.events = std::shared_ptr<std::vector<hipEvent_t>>(new std::vector<hipEvent_t>(), [](std::vector<hipEvent_t>* v) {
+        for (hipEvent_t e : *v) (void)hipEventDestroy(e);
+        delete v;
+    });
     const double dn = (double)n, dN = (double)p.Np;
+    const int64_t Np = p.Np;
+    float* const Lb = R.Lbuf;
+    float* const Pb = R.Pbuf;
 
-    launch(prof, KK_F_CLEAR, 0.0, 4.0, k_clear_info, dim3(1), dim3(64), s, info);
-    launch(prof, KK_F_MEAN, 0.0, 4.0 * dn, k_diag_mean, dim3(1), dim3(256), s, A, n, mean);
     {
-        dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 32768));
+        dim3 g((unsigned)ceil_div(Np, 1024), (unsigned)std::min<int64_t>(Np, 32768));
         const int vec = (n % 4 == 0 && aligned16(A)) ? 1 : 0;
-        launch(prof, KK_F_LOAD, dn, 4.0 * (tri(dn) + dN * dN), k_load_damped, g, dim3(256), s, A, n, R.Pbuf,
-               p.Np, p.Np, (const float*)mean, damp_frac, vec);
+        if (emit(R, [=] {
+                launch(prof, KK_F_CLEAR, 0.0, 4.0, k_clear_info, dim3(1), dim3(64), s, info);
+                launch(prof, KK_F_MEAN, 0.0, 4.0 * dn, k_diag_mean, dim3(1), dim3(256), s, A, n, mean);
+                launch(prof, KK_F_LOAD, dn, 4.0 * (tri(dn) + dN * dN), k_load_damped, g, dim3(256), s, A, n, Pb, Np,
+                       Np, (const float*)mean, damp_frac, vec);
+                return launch_ok();
+            }))
+            return -1;
     }
-    if (launch_ok()) return -1;
-    if (factor_rec(R, 0, p.Np, 0)) return -1;
+    if (factor_rec(R, 0, Np, 0, nullptr)) return -1;
+    if (defer) {   // the events live until the deferred list is destroyed
+        auto keep = R.events;
+        defer->emplace_back([keep] { return 0; });
+    }
     if (!R.early) {   // (on the early path every block of the spine has been finished)
-        dim3 g((unsigned)ceil_div(p.Np, 1024), (unsigned)std::min<int64_t>(p.Np, 256));
-        launch(prof, KK_F_FINISH, dn * dn / 2.0, 4.0 * (2.0 * tri(dN) + 2.0 * dn * dn), k_f_finish, g, dim3(256),
-               s, R.Lbuf, R.Pbuf, p.Np, (int64_t)0, p.Np, (int64_t)0, p.Np, n, p.padded ? L : (float*)nullptr,
-               p.padded ? P : (float*)nullptr);
+        dim3 g((unsigned)ceil_div(Np, 1024), (unsigned)std::min<int64_t>(Np, 256));
+        float* const Lo = p.padded ? L : nullptr;
+        float* const Po = p.padded ? P : nullptr;
+        return emit(R, [=] {
+            launch(prof, KK_F_FINISH, dn * dn / 2.0, 4.0 * (2.0 * tri(dN) + 2.0 * dn * dn), k_f_finish, g,
+                   dim3(256), s, Lb, Pb, Np, (int64_t)0, Np, (int64_t)0, Np, n, Lo, Po);
+            return launch_ok();
+        });
     }
-    return launch_ok();
+    return 0;
+}
+
+int run_interleaved(FactorCalls& a, FactorCalls& b)
+{
+    const size_t n = std::max(a.size(), b.size());
+    for (size_t i = 0; i < n; ++i) {
+        if (i < a.size() && a[i]()) return -1;
+        if (i < b.size() && b[i]()) return -1;
+    }
+    return 0;
 }
 
 }  // namespace bk

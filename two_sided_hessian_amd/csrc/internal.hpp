@@ -6,6 +6,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <functional>
 #include <vector>
 
 #include "../../include/bakron.h"
@@ -27,7 +28,7 @@ enum KernelKind {
     KK_F_CLEAR, KK_F_MEAN, KK_F_LOAD, KK_F_DIAG, KK_F_PANEL, KK_F_PANEL_T, KK_F_SYRK_T, KK_F_RIGHT, KK_F_RIGHT_T,
     KK_F_LEFT, KK_F_LEFT_T, KK_F_FINISH, KK_G_LOAD, KK_G_SWEEP, KK_G_UPDATE, KK_G_UPDATE_T, KK_G_OBJ,
     KK_K_SQNORM, KK_K_MOMENT, KK_K_MOMENT_W, KK_PROP_ROWS_FAR, KK_PROP_ROWS_T_FAR, KK_PROP_COLS_FAR,
-    KK_PROP_COLS_T_FAR, KK_AD_PREP, KK_AD_QUANT, KK_AD_UPDATE, KK_COUNT
+    KK_PROP_COLS_T_FAR, KK_AD_PREP, KK_AD_QUANT, KK_AD_UPDATE, KK_F_UPDATE, KK_COUNT
 };
 static_assert(KK_COUNT <= BAKRON_MAX_KERNEL_KINDS, "kernel kinds exceed the ABI's statistics capacity");
 
@@ -120,8 +121,18 @@ struct FactorLeads {
     hipEvent_t ev[kMaxLeads];
 };
 int factor_leads(int64_t n, int64_t* sizes);
+// With `defer`, factor_enqueue appends its stream operations (launches and
+// event records, in stream order) to the list instead of issuing them: the
+// fused call issues two factors' lists interleaved, so that both chains of
+// latency-bound launches start at once.  Each call returns 0 or -1.
+using FactorCalls = std::vector<std::function<int()>>;
+// `side` (nullable): a library stream for work of the upper levels that
+// can run beside the factor's chain of small launches (see factor_rec).
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
-                   void* ws, hipStream_t stream, Prof* prof, const FactorLeads* leads = nullptr);
+                   void* ws, hipStream_t stream, Prof* prof, const FactorLeads* leads = nullptr,
+                   FactorCalls* defer = nullptr, hipStream_t side = nullptr);
+// Issues two lists one call of each at a time; -1 on the first failure.
+int run_interleaved(FactorCalls& a, FactorCalls& b);
 
 // Solve (solve.hip).  With `split`, the far parts of the upper nodes run on
 // library-owned streams, ordered against `stream` by events.
