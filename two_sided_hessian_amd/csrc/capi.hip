@@ -50,9 +50,9 @@ static int check_ws(const void* ws, size_t have, size_t need)
     return BAKRON_SUCCESS;
 }
 
-// The library stream for a standalone factorisation's side work (library
-// slots 2 and 3 in turn, so that two factorisations issued one after the
-// other, e.g. of A and B, do not queue behind each other's side work).
+// The library stream for a standalone factorisation's right-looking side
+// work: slots 2 and 3 in turn, so that two factorisations issued one after
+// the other (A and B) use two streams.
 static hipStream_t factor_side_stream()
 {
     static std::atomic<unsigned> next{0};
@@ -251,6 +251,7 @@ int bakron_quantize(const float* W, int64_t m, int64_t n, const float* A, const 
         // The two factors' launches are issued interleaved (each is a chain of
         // latency-bound launches; issued one factor after the other, the
         // second chain would start only after the host had issued the first).
+        // Their right-looking side work runs on library slots 2 and 3.
         bk::FactorCalls qa, qb;
         if (hipEventRecord(ev[0], stream) != hipSuccess || hipStreamWaitEvent(sa, ev[0], 0) != hipSuccess ||
             hipStreamWaitEvent(sb, ev[0], 0) != hipSuccess ||

@@ -646,8 +646,9 @@ __global__ __launch_bounds__(256) void k_f_left_lead(const float* __restrict__ T
 // Li21 = (-Li22 L21) Li11: U = -Li22 L21 needs only the panel, so it shares
 // one launch with the SYRK, and one product U Li11 is left for after the
 // leading block's factorisation.  MODE: 0 panel; 1 syrk; 2 Li21 = U Li11;
-// 3 syrk (first tb (tb + 1) / 2 workgroups) and U = -Li22 L21.  T is U
-// (n2 x n1, leading dimension n1).
+// 3 syrk (first tb (tb + 1) / 2 workgroups) and U = -Li22 L21; 4 U alone
+// (a right-looking node, whose SYRK ran in pieces).  T is U (n2 x n1,
+// leading dimension n1).
 template <int MODE>
 __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
                                                 float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
@@ -656,9 +657,9 @@ __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float*
     __shared__ __align__(16) float lds[kLds64];
     int r0, c0;
     bool syrk = (MODE == 1);
-    if (MODE == 3) {
+    if (MODE == 3 || MODE == 4) {
         const int tb = n1 / 64;
-        const int q = (int)blockIdx.x - tb * (tb + 1) / 2;
+        const int q = (int)blockIdx.x - (MODE == 3 ? tb * (tb + 1) / 2 : 0);
         syrk = q < 0;
         if (!syrk) {   // U tiles, heaviest (largest K, last row tiles) first
             r0 = 64 * (n2 / 64 - 1 - q / tb);
@@ -808,7 +809,7 @@ struct FactorRun {
     const FactorLeads* leads;  // nullable: events of the leading blocks, recorded as they become final
     int64_t n;
     FactorCalls* defer;        // nullable: stream operations are appended here instead of issued
-    hipStream_t side;          // nullable: a library stream for the right-looking pieces (factor_rec)
+    hipStream_t side;          // the stream of the right-looking pieces (factor_rec); null: s itself
     std::shared_ptr<std::vector<hipEvent_t>> events;   // destroyed with the last operation that holds them
 };
 
@@ -909,6 +910,16 @@ struct Pending {
 #ifndef BAKRON_RIGHT_LOOKING
 #define BAKRON_RIGHT_LOOKING 1
 #endif
+// Tile-level nodes of at least this size (and every block level) are split
+// right-looking; such a node forms U = -Li22 L21 on the side stream too.
+// (The 7168 halves of a 14336 factor: 0.7-0.9 ms off the fused call at
+// 4096 x 14336 and its transpose.  From 4096 down, the two factors of
+// separate calls, issued one after the other, queue their side work behind
+// each other's on the hardware queue that library slots 2 and 3 share.)
+#ifndef BAKRON_RL_MIN
+#define BAKRON_RL_MIN 7168
+#endif
+constexpr int64_t kRLMin = BAKRON_RL_MIN;
 
 // On the leading spine (o == 0, with `early`) every node ends with its
 // whole block [0, nsz)^2 finished (P = Li diag(L), zeros above both
@@ -958,7 +969,8 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
     const bool tiles = ceil_div(n1, FBN) * ceil_div(n2, FBM) < kFactorBlockMin;
     const dim3 g((unsigned)ceil_div(n1, FBN), (unsigned)ceil_div(n2, FBM));
     const dim3 gt((unsigned)(n1 / kTile), (unsigned)(n2 / kTile));
-    const bool rl = BAKRON_RIGHT_LOOKING && !tiles && R.side && n2 > 2 * kTile;
+    const bool rl = BAKRON_RIGHT_LOOKING && (!tiles || nsz >= kRLMin) && n2 > 2 * kTile;
+    hipEvent_t u_done = nullptr;   // a right-looking tile-level node forms U on the side stream
     // This node as the trailing half of a right-looking parent (`up`): once
     // its own panel is formed, its rows o2 .. o2 + n2 - 1 are final for the
     // parent's columns too.  On the side stream: those rows of the parent's
@@ -968,7 +980,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
         if (!up) return 0;
         const hipEvent_t ready = new_event(R), done = new_event(R);
         if (!ready || !done) return -1;
-        const hipStream_t s = R.s, side = R.side;
+        const hipStream_t s = R.s, side = R.side ? R.side : R.s;
         const int64_t po = up->o;
         const int pn = up->n;
         const double fu = 2.0 * d1 * pn * d2, bu = 4.0 * (2.0 * d1 * pn + d2 * (d1 + pn));
@@ -999,7 +1011,30 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
         if (!e || emit(R, [=] { return hipStreamWaitEvent(s, e, 0) == hipSuccess ? 0 : -1; })) return -1;
         int c1 = n2;   // the rows left: C's leading-most base block
         while (c1 > 2 * kTile) c1 = (int)(kTile * ((c1 / kTile) / 2));
-        if (emit_panel(R, R.s, o1, o2, n1, c1) || parent_share() || emit_syrk(R, R.s, o1, o2, n1, c1)) return -1;
+        if (emit_panel(R, R.s, o1, o2, n1, c1) || parent_share()) return -1;
+        if (tiles) {
+            // U = -Li22 L21 (L21 is complete now) on the side stream, beside
+            // the leading half's factorisation; Li21 = U Li11 waits for it
+            const hipEvent_t ready = new_event(R);
+            u_done = new_event(R);
+            if (!ready || !u_done) return -1;
+            const hipStream_t side = R.side ? R.side : R.s;
+            const double fu = 2.0 * d1 * tri(d2), bu = 4.0 * (2.0 * d2 * d1 + tri(d2));
+            const hipEvent_t ud = u_done;
+            if (emit(R, [=] {
+                    return (hipEventRecord(ready, s) == hipSuccess && hipStreamWaitEvent(side, ready, 0) == hipSuccess)
+                               ? 0
+                               : -1;
+                }) ||
+                emit(R, [=] {
+                    launch(R.prof, KK_F_LEFT_T, fu, bu, k_f_tile<4>, dim3(gt.x * gt.y), dim3(256), side, R.Lbuf,
+                           R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                    return launch_ok();
+                }) ||
+                emit(R, [=] { return hipEventRecord(ud, side) == hipSuccess ? 0 : -1; }))
+                return -1;
+        }
+        if (emit_syrk(R, R.s, o1, o2, n1, c1)) return -1;
     } else {
         if (emit_panel(R, R.s, o1, o2, n1, n2) || parent_share()) return -1;
         if (tiles) {
@@ -1029,6 +1064,11 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
         const double fl = 2.0 * d1 * tri(d2), bl = 4.0 * (2.0 * d2 * d1 + tri(d2));
         if (tiles) {
             // Li21 = U Li11 (on the spine U P11 = P21, P11 being finished)
+            if (u_done) {
+                const hipEvent_t e = u_done;
+                const hipStream_t s = R.s;
+                if (emit(R, [=] { return hipStreamWaitEvent(s, e, 0) == hipSuccess ? 0 : -1; })) return -1;
+            }
             if (emit(R, [=] {
                     launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf,
                            R.Pbuf, T, R.ld, o1, o2, n1, n2);

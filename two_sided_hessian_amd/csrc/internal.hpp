@@ -126,8 +126,9 @@ int factor_leads(int64_t n, int64_t* sizes);
 // fused call issues two factors' lists interleaved, so that both chains of
 // latency-bound launches start at once.  Each call returns 0 or -1.
 using FactorCalls = std::vector<std::function<int()>>;
-// `side` (nullable): a library stream for work of the upper levels that
-// can run beside the factor's chain of small launches (see factor_rec).
+// `side`: a stream for work of the upper levels that can run beside the
+// factor's chain of small launches (see factor_rec); null runs that work in
+// order on `stream`, with the same arithmetic.
 int factor_enqueue(const float* A, int64_t n, float damp_frac, float* L, float* P, int32_t* info,
                    void* ws, hipStream_t stream, Prof* prof, const FactorLeads* leads = nullptr,
                    FactorCalls* defer = nullptr, hipStream_t side = nullptr);
