@@ -25,7 +25,8 @@
 //    sum_I P_B[I', I] Y[I, J'] from every target tile (mid <= I' + J' < K1).
 //    Both are fp32 MFMA GEMMs whose K range follows the staircase of the
 //    tile band.  A node of two leaves (K0, K0 + 1, K0 + 2) has no launch of
-//    its own: the leaf of K0 + 1 applies both stages to its tile first.
+//    its own: the leaf of K0 + 1 applies both stages to its tile first
+//    (leaf_prologue, which also serves wider nodes when kFold allows).
 //  * On the upper levels a node's propagation is cut by target
 //    anti-diagonal into parts with different due times; only the first is
 //    on the caller's stream, the others run on library-owned streams beside
@@ -99,7 +100,7 @@ struct LeafArgs {
     int Nt;
     int K;                // tile anti-diagonal
     int I_lo;             // first tile row on it
-    int pair;             // 1: K - 1 and K form a node of two leaves, whose propagation the leaf applies first
+    int nsrc;             // > 0: the leaf first applies the errors of anti-diagonals K - nsrc .. K - 1 (a narrow node's)
     int vec_out;          // outputs may use 16-byte stores
 };
 
@@ -244,88 +245,99 @@ __device__ __forceinline__ void leaf_step(const LeafRow& L, int d0, float (&R)[8
     __syncthreads();
 }
 
-// The propagation of a node of two leaves (K0, K0 + 1, K0 + 2) into its
-// target tile (Ip, Jp) on anti-diagonal K0 + 1, at the start of that tile's
-// leaf.  The sources are the rows I in [max(0, Ip - 1), min(K0, Ip)], each
-// with the one source tile (I, K0 - I):
-//   Y_I = E[I, K0 - I] P_A[Jp, K0 - I]^T            (stage 1, K = 64)
-//   W~[Ip, Jp] -= sum_I P_B[Ip, I] Y_I              (stage 2, I ascending)
-// The Y tiles stay in LDS (sY0, sY1: 64 x kLP each); fragments come straight
-// from global memory into registers, with the MFMAs of the tile kernels in
-// their order and Y rounded as those kernels store it, so the updated tile is
-// theirs bit for bit.  It lands in sW, the leaf's copy of the tile.  Stage 1
-// runs on eight waves (wave w: source w / 4, quadrant w % 4), stage 2 on
-// the first four.
-__device__ __forceinline__ void leaf_pair_update(const LeafArgs& g, int Ip, int Jp, float* __restrict__ sY0,
-                                                 float* __restrict__ sY1, float* __restrict__ sW)
+// A narrow node's propagation, applied by its leaves.  A node of at most
+// kFold anti-diagonals [K0, K1) has no propagation launches: the leaf of
+// anti-diagonal K in it first applies, to each of its tiles (It, Jt), the
+// errors of the node's earlier anti-diagonals [K0, K) = [K - nsrc, K):
+//   Y_I = sum_J E[I, J] P_A[Jt, J]^T        (stage 1; J <= Jt, I + J in [K - nsrc, K))
+//   W~[It, Jt] -= sum_I P_B[It, I] Y_I       (stage 2, I = It - nsrc .. It ascending)
+// Errors of anti-diagonals before K0 reached W~ through the propagation of
+// the nodes above.  Rows are taken two at a time: stage 1 of a row on four
+// waves (one 32 x 32 quadrant each; the row's source tiles accumulated in
+// ascending order), its Y tile in LDS (sY0, sY1: 64 x kLP each), then stage
+// 2 of both rows on the first four waves, accumulating in registers.
+// Fragments come straight from global memory; Y is rounded as the tile
+// kernels store it (with one source tile per row, nsrc = 1, the result is
+// theirs bit for bit).  The updated tile lands in sW, the leaf's copy.
+__device__ __forceinline__ void leaf_prologue(const LeafArgs& g, int It, int Jt, float* __restrict__ sY0,
+                                              float* __restrict__ sY1, float* __restrict__ sW)
 {
-    const int K0 = g.K - 1;
+    const int K = g.K, ns = g.nsrc;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, quad = wave & 3;
     const int ml = lane & 31, kl = 4 * (lane >> 5);
     const int ra = 32 * (quad >> 1) + ml, rb = 32 * (quad & 1) + ml;
-    const int Ilo = max(0, Ip - 1), Ihi = min(K0, Ip);
-    const int I = Ilo + (wave >> 2);
-    if (I <= Ihi) {
-        const int J = K0 - I;
-        const float* a0 = g.E + (int64_t)I * 64 * g.ldw + (int64_t)J * 64;
-        const float* b0 = g.PA + (int64_t)Jp * 64 * g.lda + (int64_t)J * 64;
-        f32x4 a[8], b[8];
+    const int Ilo = max(0, It - ns), Ihi = min(It, K - 1);   // rows with a source tile J <= Jt
+    f32x16 acc2;
 #pragma unroll
-        for (int st = 0; st < 8; ++st) {
-            a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * g.ldw + 8 * st + kl);
-            b[st] = *reinterpret_cast<const f32x4*>(b0 + (int64_t)rb * g.lda + 8 * st + kl);
-        }
-        f32x16 acc;
+    for (int r = 0; r < 16; ++r) acc2[r] = 0.f;
+    for (int I0 = Ilo; I0 <= Ihi; I0 += 2) {
+        const int I = I0 + (wave >> 2);
+        if (I <= Ihi) {
+            const int jlo = max(0, K - ns - I), jhi = min(K - 1 - I, Jt);
+            f32x16 acc;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+            for (int J = jlo; J <= jhi; ++J) {
+                const float* a0 = g.E + (int64_t)I * 64 * g.ldw + (int64_t)J * 64;
+                const float* b0 = g.PA + (int64_t)Jt * 64 * g.lda + (int64_t)J * 64;
+                f32x4 a[8], b[8];
 #pragma unroll
-        for (int st = 0; st < 8; ++st)
+                for (int st = 0; st < 8; ++st) {
+                    a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * g.ldw + 8 * st + kl);
+                    b[st] = *reinterpret_cast<const f32x4*>(b0 + (int64_t)rb * g.lda + 8 * st + kl);
+                }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], b[st][q], acc, 0, 0, 0);
-        float* y = (I == Ilo ? sY0 : sY1) + 32 * (quad >> 1) * kLP + 32 * (quad & 1);
+                for (int st = 0; st < 8; ++st)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float one = 1.f, none = 0.f;   // as stage 1 stores Y: 1 acc + 0 0
-            y[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kLP + ml] = one * acc[r] + none * none;
-        }
-    }
-    __syncthreads();
-    if (wave < 4) {
-        f32x16 acc;
+                    for (int q = 0; q < 4; ++q)
+                        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], b[st][q], acc, 0, 0, 0);
+            }
+            float* y = (I == I0 ? sY0 : sY1) + 32 * (quad >> 1) * kLP + 32 * (quad & 1);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-        for (int Is = Ilo; Is <= Ihi; ++Is) {
-            const float* a0 = g.PB + (int64_t)Ip * 64 * g.ldb + (int64_t)Is * 64;
-            const float* y = (Is == Ilo ? sY0 : sY1) + rb;
-            f32x4 a[8];
-#pragma unroll
-            for (int st = 0; st < 8; ++st)
-                a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * g.ldb + 8 * st + kl);
-#pragma unroll
-            for (int st = 0; st < 8; ++st) {
-                const float* c = y + (8 * st + kl) * kLP;
-                const f32x4 bv = {c[0], c[kLP], c[2 * kLP], c[3 * kLP]};
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], bv[q], acc, 0, 0, 0);
+            for (int r = 0; r < 16; ++r) {
+                const float one = 1.f, none = 0.f;   // as stage 1 stores Y: 1 acc + 0 0
+                y[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kLP + ml] = one * acc[r] + none * none;
             }
         }
+        __syncthreads();
+        if (wave < 4) {
+            for (int Is = I0; Is <= min(I0 + 1, Ihi); ++Is) {
+                const float* a0 = g.PB + (int64_t)It * 64 * g.ldb + (int64_t)Is * 64;
+                const float* y = (Is == I0 ? sY0 : sY1) + rb;
+                f32x4 a[8];
+#pragma unroll
+                for (int st = 0; st < 8; ++st)
+                    a[st] = *reinterpret_cast<const f32x4*>(a0 + (int64_t)ra * g.ldb + 8 * st + kl);
+#pragma unroll
+                for (int st = 0; st < 8; ++st) {
+                    const float* c = y + (8 * st + kl) * kLP;
+                    const f32x4 bv = {c[0], c[kLP], c[2 * kLP], c[3 * kLP]};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        acc2 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[st][q], bv[q], acc2, 0, 0, 0);
+                }
+            }
+        }
+        __syncthreads();   // the Y tiles are read before the next rows (or the leaf) overwrite them
+    }
+    if (wave < 4) {
         // W~ - acc, as the tile kernels' epilogue forms it (alpha acc + beta old)
-        const float* wq = g.Wt + ((int64_t)Ip * 64 + 32 * (quad >> 1)) * g.ldw + (int64_t)Jp * 64 + 32 * (quad & 1);
+        const float* wq = g.Wt + ((int64_t)It * 64 + 32 * (quad >> 1)) * g.ldw + (int64_t)Jt * 64 + 32 * (quad & 1);
         float* sq = sW + 32 * (quad >> 1) * 64 + 32 * (quad & 1);
         const float alpha = -1.f, beta = 1.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            sq[row * 64 + ml] = alpha * acc[r] + beta * wq[(int64_t)row * g.ldw + ml];
+            sq[row * 64 + ml] = alpha * acc2[r] + beta * wq[(int64_t)row * g.ldw + ml];
         }
     }
-    __syncthreads();   // the Y tiles read before the leaf clears their arrays
+    __syncthreads();
 }
 
 __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
 {
     __shared__ float sW[64 * 64];
-    // sS and sUT hold the two Y tiles of a two-leaf node's propagation first
+    // sS and sUT hold the Y tiles of a narrow node's propagation first
     __shared__ __align__(16) float sS[64 * kLP];    // sS[b][j] = P_A[b + j][b], zero past the tile
     __shared__ __align__(16) float sUT[64 * kLP];   // sUT[b][a] = U[a][b]
     __shared__ __align__(16) float sF[64 * kLP];    // raw errors e[a][b]
@@ -339,7 +351,7 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
     const int a = t >> 3, sg = t & 7;
     if (t < 8) sZ[t] = 0.f;
     const int64_t r0 = (int64_t)I * 64, c0 = (int64_t)J * 64;
-    if (g.pair) leaf_pair_update(g, I, J, sS, sUT, sW);
+    if (g.nsrc) leaf_prologue(g, I, J, sS, sUT, sW);
 
     for (int idx = t; idx < 64 * kLP; idx += 512) {
         sS[idx] = 0.f;
@@ -351,7 +363,7 @@ __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
     for (int u = 0; u < 2; ++u) {
         const int f = t + 512 * u;
         const int row = f >> 4, cq = 4 * (f & 15);
-        if (!g.pair) {
+        if (!g.nsrc) {
             const f32x4 w = *reinterpret_cast<const f32x4*>(g.Wt + (r0 + row) * g.ldw + c0 + cq);
             *reinterpret_cast<f32x4*>(sW + row * 64 + cq) = w;
         }
@@ -1143,19 +1155,19 @@ constexpr double kTileB = 4.0 * 64 * 64;                 // bytes of one fp32 ti
 constexpr double kFull = 64.0 * 64.0 * 64.0;             // multiply-adds of a full block product
 constexpr double kTriB = 64.0 * 64.0 * 65.0 / 2.0;       // ... with a triangular diagonal block
 
-// pair: K - 1 and K are the two leaves of one node, and the leaf applies
-// that node's propagation first.
-void enqueue_leaf(SolveRun& R, int K, bool pair = false)
+// nsrc > 0: K is the (nsrc + 1)-th leaf of a narrow node, and the leaf
+// applies the errors of the node's earlier leaves first.
+void enqueue_leaf(SolveRun& R, int K, int nsrc = 0)
 {
     const int I_lo = std::max(0, K - (R.Nt - 1));
     const int I_hi = std::min(R.Mt - 1, K);
     const int count = I_hi - I_lo + 1;
     R.leaf.K = K;
     R.leaf.I_lo = I_lo;
-    R.leaf.pair = pair ? 1 : 0;
+    R.leaf.nsrc = nsrc;
     // per tile: the two in-tile triangular products (U = E P_A^T, P_B U);
     // bytes: W~, P_A and P_B diagonal blocks in; E and V out (+ err), codes.
-    // (A leaf that first applies its two-leaf node's propagation does that
+    // (A leaf that first applies its narrow node's propagation does that
     // node's block products too, on the MFMA units; they are not counted
     // here, so the leaf's rate is that of its sweep.)
     const double flops = count * 2.0 * 2.0 * kTriB;
@@ -1381,16 +1393,36 @@ void enqueue_prop(SolveRun& R, int K0, int mid, int K1, int d, int p, SpineWaits
 // the parent's stream when this node is not split): the caller's stream
 // then runs the leaves of this node's right child, and the early pass takes
 // CUs beside them rather than beside this node's near part or its far
-// parts.  A node of two leaves runs its propagation inside the second leaf
-// (BAKRON_PAIR_FUSE).
-#ifndef BAKRON_PAIR_FUSE
-#define BAKRON_PAIR_FUSE 1
+// parts.  A node of at most kFold anti-diagonals has no propagation
+// launches: each of its leaves applies the errors of the node's earlier
+// leaves first (leaf_prologue), and the waits come before the leaves at the
+// recursion's propagation points.
+// (Three or four anti-diagonals: each leaf's prologue then does up to 13
+// block products on its one CU, which costs more than the two tile
+// launches it saves.)
+#ifndef BAKRON_FOLD
+#define BAKRON_FOLD 2
 #endif
+constexpr int kFold = BAKRON_FOLD;
 void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& waits, EarlyPass* parent)
 {
     if (K1 - K0 == 1) {   // (the nodes that carry waits or an early pass are never leaves)
         ensure_full(R, K0);
         enqueue_leaf(R, K0);
+        return;
+    }
+    if (K1 - K0 <= kFold) {   // (never split, never an early node)
+        int mids[kMaxParts];   // propagation point of the node j levels down the left spine
+        for (int j = 0, hi = K1; j < kMaxParts; ++j) {
+            mids[j] = hi - K0 >= 2 ? (K0 + hi) / 2 : -1;
+            hi = mids[j] < 0 ? hi : mids[j];
+        }
+        for (int K = K0; K < K1; ++K) {
+            for (int j = kMaxParts - 1; j >= 0; --j)
+                if (waits.e[j] && K == mids[j] && hipStreamWaitEvent(R.s, waits.e[j], 0) != hipSuccess) R.failed = true;
+            ensure_full(R, K);
+            enqueue_leaf(R, K, K - K0);
+        }
         return;
     }
     const int mid = (K0 + K1) / 2;
@@ -1402,10 +1434,6 @@ void solve_rec(SolveRun& R, int K0, int K1, int d, int p, const SpineWaits& wait
     solve_rec(R, K0, mid, d + 1, 2 * p, down, early_far ? &mine : nullptr);
     if (waits.e[0] && hipStreamWaitEvent(R.s, waits.e[0], 0) != hipSuccess) R.failed = true;
     ensure_full(R, K1 - 1);
-    if (BAKRON_PAIR_FUSE && K1 - K0 == 2) {   // (never cut in parts) the second leaf propagates first
-        enqueue_leaf(R, K0 + 1, true);
-        return;
-    }
     SpineWaits done;
     enqueue_prop(R, K0, mid, K1, d, p, done, mine.done);
     if (parent) enqueue_early(R, *parent, node_parts(*R.sg, d, mid, K1) > 1 ? R.far[d] : R.far[parent->d]);
