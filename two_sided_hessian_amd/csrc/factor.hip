@@ -110,6 +110,12 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
 
 constexpr int kDP = 132;   // LDS pitch (floats) of the block and its inverse
 
+// Issue priority of k_f_diag's waves over those of the products (the side
+// stream's and the other factor's) where they share a CU.
+#ifndef BAKRON_DIAG_PRIO
+#define BAKRON_DIAG_PRIO 3
+#endif
+
 // Value of v in lane `src` (any lane of the wave).
 __device__ __forceinline__ float lane_get(float v, int src)
 {
@@ -383,6 +389,7 @@ __device__ __forceinline__ void syrk_tile4(float* __restrict__ sA, const float* 
 __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
                                                 int64_t o, int nb, int32_t* __restrict__ info)
 {
+    if (BAKRON_DIAG_PRIO > 0) __builtin_amdgcn_s_setprio(BAKRON_DIAG_PRIO);   // the chain's latency-bound step
     __shared__ __align__(16) float sA[128 * kDP];   // the block, then L
     __shared__ __align__(16) float sX[128 * kDP];   // L^-1
     __shared__ int sfail;

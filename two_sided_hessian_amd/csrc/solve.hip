@@ -53,6 +53,17 @@
 
 namespace bk {
 
+// Waves of the caller's stream's kernels (the leaves and the near parts of
+// the propagation, the solve's critical path) take issue priority over the
+// far parts' waves where the two share a CU.
+#ifndef BAKRON_NEAR_PRIO
+#define BAKRON_NEAR_PRIO 2
+#endif
+__device__ __forceinline__ void near_priority()
+{
+    if (BAKRON_NEAR_PRIO > 0) __builtin_amdgcn_s_setprio(BAKRON_NEAR_PRIO);
+}
+
 // dst (R x C, pitch ldd) = src (rows x cols, pitch lds) with zeros outside.
 // C and ldd are multiples of 4: each thread writes four adjacent columns
 // with one 16-byte store, reading them with one 16-byte load where they lie
@@ -336,6 +347,7 @@ __device__ __forceinline__ void leaf_prologue(const LeafArgs& g, int It, int Jt,
 
 __global__ __launch_bounds__(512) void k_leaf(LeafArgs g)
 {
+    near_priority();
     __shared__ float sW[64 * 64];
     // sS and sUT hold the Y tiles of a narrow node's propagation first
     __shared__ __align__(16) float sS[64 * kLP];    // sS[b][j] = P_A[b + j][b], zero past the tile
@@ -854,6 +866,7 @@ __global__ __launch_bounds__(256, 2) void k_prop_rows(const float* __restrict__ 
                                                    int K0, int mid, int y0, int y1, int Mt, int Nt,
                                                    const uint32_t* __restrict__ list, unsigned count, int acc_rows)
 {
+    near_priority();
     prop_rows_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Mt, Nt, list, count, acc_rows);
 }
 
@@ -889,6 +902,7 @@ __global__ __launch_bounds__(256, 2) void k_prop_cols(const float* __restrict__ 
                                                       int K0, int mid, int t0, int t1, int Mt, int Nt,
                                                       const uint32_t* __restrict__ list, unsigned count)
 {
+    near_priority();
     prop_cols_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, Nt, list, count);
 }
 __global__ __launch_bounds__(256, 2) void k_prop_cols_far(const float* __restrict__ Y, const float* __restrict__ PB,
@@ -934,6 +948,7 @@ __global__ __launch_bounds__(256) void k_prop_rows_t(const float* __restrict__ E
                                                      int K0, int mid, int y0, int y1, int Nt, unsigned span,
                                                      unsigned count, int acc_rows)
 {
+    near_priority();
     prop_rows_t_body(E, PA, Y, ldw, lda, K0, mid, y0, y1, Nt, span, count, acc_rows);
 }
 __global__ __launch_bounds__(256) void k_prop_rows_t_far(const float* __restrict__ E, const float* __restrict__ PA,
@@ -974,6 +989,7 @@ __global__ __launch_bounds__(256) void k_prop_cols_t(const float* __restrict__ Y
                                                      int K0, int mid, int t0, int t1, int Mt, unsigned span,
                                                      unsigned count)
 {
+    near_priority();
     prop_cols_t_body(Y, PB, Wt, ldw, ldb, K0, mid, t0, t1, Mt, span, count);
 }
 __global__ __launch_bounds__(256) void k_prop_cols_t_far(const float* __restrict__ Y, const float* __restrict__ PB,
