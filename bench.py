@@ -541,7 +541,7 @@ def bench_antidiagonal(B, WL, T, fa, fb, m, n, dev, args, limit_s=60.0):
 MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", "k_prop_rows_far",
                 "k_prop_rows_t_far",
                 "k_prop_cols_far", "k_prop_cols_t_far", "k_f_panel", "k_f_right",
-                "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_f_update",
+                "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_f_tile<4>", "k_f_update",
                 "k_gptq_update",
                 "k_gptq_update_t", "k_moment<false>", "k_moment<true>"}
 HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info", "k_gptq_load",

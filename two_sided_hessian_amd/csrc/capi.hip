@@ -453,7 +453,7 @@ const char* kernel_name(int kind)
         "k_f_tile<1>", "k_f_right", "k_f_tile<2>", "k_f_left", "k_f_tile<3>", "k_f_finish", "k_gptq_load",
         "k_gptq_sweep", "k_gptq_update", "k_gptq_update_t", "k_gptq_obj", "k_row_sqnorms", "k_moment<false>",
         "k_moment<true>", "k_prop_rows_far", "k_prop_rows_t_far", "k_prop_cols_far", "k_prop_cols_t_far",
-        "k_ad_prep", "k_ad_quant", "k_ad_update", "k_f_update"};
+        "k_ad_prep", "k_ad_quant", "k_ad_update", "k_f_update", "k_f_tile<4>"};
     return (kind >= 0 && kind < KK_COUNT) ? names[kind] : "?";
 }
 

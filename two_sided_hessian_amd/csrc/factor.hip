@@ -115,6 +115,10 @@ constexpr int kDP = 132;   // LDS pitch (floats) of the block and its inverse
 #ifndef BAKRON_DIAG_PRIO
 #define BAKRON_DIAG_PRIO 3
 #endif
+// ... and of the tile products launched on the chain (not the side stream's)
+#ifndef BAKRON_CHAIN_PRIO
+#define BAKRON_CHAIN_PRIO 2
+#endif
 
 // Value of v in lane `src` (any lane of the wave).
 __device__ __forceinline__ float lane_get(float v, int src)
@@ -659,8 +663,9 @@ __global__ __launch_bounds__(256) void k_f_left_lead(const float* __restrict__ T
 template <int MODE>
 __global__ __launch_bounds__(256) void k_f_tile(float* __restrict__ Lbuf, float* __restrict__ Pbuf,
                                                 float* __restrict__ T, int64_t ld, int64_t o1, int64_t o2,
-                                                int n1, int n2)
+                                                int n1, int n2, int chain)
 {
+    if (BAKRON_CHAIN_PRIO > 0 && chain) __builtin_amdgcn_s_setprio(BAKRON_CHAIN_PRIO);   // on the factor's chain
     __shared__ __align__(16) float lds[kLds64];
     int r0, c0;
     bool syrk = (MODE == 1);
@@ -885,7 +890,7 @@ int emit_panel(const FactorRun& R, hipStream_t st, int64_t o1, int64_t o2, int n
     return emit(R, [=] {
         if (tiles)
             launch(R.prof, KK_F_PANEL_T, fl, by, k_f_tile<0>, gt, dim3(256), st, R.Lbuf, R.Pbuf, (float*)nullptr,
-                   R.ld, o1, o2, n1, n2);
+                   R.ld, o1, o2, n1, n2, st == R.s ? 1 : 0);
         else
             launch(R.prof, KK_F_PANEL, fl, by, k_f_panel, g, dim3(256), st, R.Pbuf, R.Lbuf, R.ld, o1, o2, n1, n2);
         return launch_ok();
@@ -901,7 +906,7 @@ int emit_syrk(const FactorRun& R, hipStream_t st, int64_t o1, int64_t o2, int n1
     const int64_t tb = n1 / kTile, nsyrk = tb * (tb + 1) / 2;
     return emit(R, [=] {
         launch(R.prof, KK_F_SYRK_T, fl, by, k_f_tile<1>, dim3((unsigned)nsyrk), dim3(256), st, R.Lbuf, R.Pbuf,
-               (float*)nullptr, R.ld, o1, o2, n1, n2);
+               (float*)nullptr, R.ld, o1, o2, n1, n2, st == R.s ? 1 : 0);
         return launch_ok();
     });
 }
@@ -1034,8 +1039,8 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
                                : -1;
                 }) ||
                 emit(R, [=] {
-                    launch(R.prof, KK_F_LEFT_T, fu, bu, k_f_tile<4>, dim3(gt.x * gt.y), dim3(256), side, R.Lbuf,
-                           R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                    launch(R.prof, KK_F_U_T, fu, bu, k_f_tile<4>, dim3(gt.x * gt.y), dim3(256), side, R.Lbuf,
+                           R.Pbuf, T, R.ld, o1, o2, n1, n2, side == R.s ? 1 : 0);
                     return launch_ok();
                 }) ||
                 emit(R, [=] { return hipEventRecord(ud, side) == hipSuccess ? 0 : -1; }))
@@ -1054,7 +1059,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
             const int64_t tb = n1 / kTile, nsyrk = tb * (tb + 1) / 2;
             if (emit(R, [=] {
                     launch(R.prof, KK_F_LEFT_T, fl + fu, by + bu, k_f_tile<3>, dim3((unsigned)(nsyrk + gt.x * gt.y)),
-                           dim3(256), R.s, R.Lbuf, R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                           dim3(256), R.s, R.Lbuf, R.Pbuf, T, R.ld, o1, o2, n1, n2, 1);
                     return launch_ok();
                 }))
                 return -1;
@@ -1078,7 +1083,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
             }
             if (emit(R, [=] {
                     launch(R.prof, KK_F_RIGHT_T, fr, br, k_f_tile<2>, dim3(gt.y, gt.x), dim3(256), R.s, R.Lbuf,
-                           R.Pbuf, T, R.ld, o1, o2, n1, n2);
+                           R.Pbuf, T, R.ld, o1, o2, n1, n2, 1);
                     return launch_ok();
                 }))
                 return -1;

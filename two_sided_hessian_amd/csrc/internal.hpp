@@ -28,7 +28,7 @@ enum KernelKind {
     KK_F_CLEAR, KK_F_MEAN, KK_F_LOAD, KK_F_DIAG, KK_F_PANEL, KK_F_PANEL_T, KK_F_SYRK_T, KK_F_RIGHT, KK_F_RIGHT_T,
     KK_F_LEFT, KK_F_LEFT_T, KK_F_FINISH, KK_G_LOAD, KK_G_SWEEP, KK_G_UPDATE, KK_G_UPDATE_T, KK_G_OBJ,
     KK_K_SQNORM, KK_K_MOMENT, KK_K_MOMENT_W, KK_PROP_ROWS_FAR, KK_PROP_ROWS_T_FAR, KK_PROP_COLS_FAR,
-    KK_PROP_COLS_T_FAR, KK_AD_PREP, KK_AD_QUANT, KK_AD_UPDATE, KK_F_UPDATE, KK_COUNT
+    KK_PROP_COLS_T_FAR, KK_AD_PREP, KK_AD_QUANT, KK_AD_UPDATE, KK_F_UPDATE, KK_F_U_T, KK_COUNT
 };
 static_assert(KK_COUNT <= BAKRON_MAX_KERNEL_KINDS, "kernel kinds exceed the ABI's statistics capacity");
 
