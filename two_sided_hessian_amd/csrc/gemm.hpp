@@ -173,6 +173,16 @@ struct Direct {
 
 // Direct loads count against vmcnt until their data is in LDS.
 __device__ __forceinline__ void wait_direct_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same, leaving one 64-row chunk of both operands in flight: each wave
+// issues Direct<64, *>::PER_WAVE = 2 loads per operand and chunk, and loads
+// complete in order.
+#ifndef BAKRON_TILE_PREFETCH2
+#define BAKRON_TILE_PREFETCH2 1
+#endif
+__device__ __forceinline__ void wait_direct_loads_but_one_chunk64()
+{
+    asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+}
 
 template <int WM, int WN, int ALAY, int BLAY>
 struct Gemm {
@@ -407,14 +417,29 @@ __device__ __forceinline__ void block_gemm64(const float* __restrict__ A, int64_
         typedef Direct<64, ALAY> OA;
         typedef Direct<64, BLAY> OB;
         constexpr int BUF = OA::FLOATS + OB::FLOATS;
+        static_assert(OA::PER_WAVE + OB::PER_WAVE == 4, "vmcnt(4) leaves one chunk of both operands in flight");
         const int nchunk = (k1 - k0) / kBK;
         if (nchunk <= 0) return;
+        // the first two chunks are issued together (both buffers are free), so
+        // a launch with one tile per CU waits for one load latency, not two
         OA::issue(A, lda, 64, k0, lds);
         OB::issue(B, ldb, 64, k0, lds + OA::FLOATS);
+        if (BAKRON_TILE_PREFETCH2 && nchunk > 1) {
+            OA::issue(A, lda, 64, k0 + kBK, lds + BUF);
+            OB::issue(B, ldb, 64, k0 + kBK, lds + BUF + OA::FLOATS);
+        }
         for (int c = 0; c < nchunk; ++c) {
-            wait_direct_loads();
-            __syncthreads();
-            if (c + 1 < nchunk) {
+            if (BAKRON_TILE_PREFETCH2 && c == 0 && nchunk > 1) {
+                // chunk 1 may still be in flight; no LDS access precedes this
+                // one in the call, so a bare barrier (no fence, which would
+                // wait for every load) is enough to publish chunk 0
+                wait_direct_loads_but_one_chunk64();
+                __builtin_amdgcn_s_barrier();
+            } else {
+                wait_direct_loads();
+                __syncthreads();
+            }
+            if (c + 1 < nchunk && !(BAKRON_TILE_PREFETCH2 && c == 0)) {
                 float* nb = lds + ((c + 1) & 1) * BUF;
                 OA::issue(A, lda, 64, k0 + (c + 1) * kBK, nb);
                 OB::issue(B, ldb, 64, k0 + (c + 1) * kBK, nb + OA::FLOATS);
