@@ -110,6 +110,15 @@ __global__ __launch_bounds__(256) void k_load_damped(const float* __restrict__ A
 
 constexpr int kDP = 132;   // LDS pitch (floats) of the block and its inverse
 
+// Threads of k_f_diag: wave 0 runs the pivot chain (chol16), the others the
+// update of the upper-left part beside it and, after the factorisation, the
+// 16 x 16 inverses (one round on eight waves, two on four).
+#ifndef BAKRON_DIAG_THREADS
+#define BAKRON_DIAG_THREADS 512
+#endif
+constexpr int kDiagThreads = BAKRON_DIAG_THREADS;
+static_assert(kDiagThreads == 256 || kDiagThreads == 512, "four or eight waves");
+
 // Issue priority of k_f_diag's waves over those of the products (the side
 // stream's and the other factor's) where they share a CU.
 #ifndef BAKRON_DIAG_PRIO
@@ -390,7 +399,7 @@ __device__ __forceinline__ void syrk_tile4(float* __restrict__ sA, const float* 
     }
 }
 
-__global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
+__global__ __launch_bounds__(kDiagThreads) void k_f_diag(float* __restrict__ Lbuf, float* __restrict__ Pbuf, int64_t ld,
                                                 int64_t o, int nb, int32_t* __restrict__ info)
 {
     if (BAKRON_DIAG_PRIO > 0) __builtin_amdgcn_s_setprio(BAKRON_DIAG_PRIO);   // the chain's latency-bound step
@@ -400,15 +409,16 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
     const int t = threadIdx.x, wave = t >> 6;
     const int nf4 = nb / 4;
     {   // all global loads in flight before the LDS stores
-        f32x4 v[16];
+        constexpr int NU = 128 * 128 / 4 / kDiagThreads;
+        f32x4 v[NU];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int f = t + 256 * u;
+        for (int u = 0; u < NU; ++u) {
+            const int f = t + kDiagThreads * u;
             if (f < nb * nf4) v[u] = *reinterpret_cast<const f32x4*>(Pbuf + (o + f / nf4) * ld + o + 4 * (f % nf4));
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int f = t + 256 * u;
+        for (int u = 0; u < NU; ++u) {
+            const int f = t + kDiagThreads * u;
             if (f < nb * nf4) *reinterpret_cast<f32x4*>(sA + (f / nf4) * kDP + 4 * (f % nf4)) = v[u];
         }
     }
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
             const int f = chol16(sA + 16 * (b - 1) * (kDP + 1), Pr + W - 16);
             if (t == 0 && f >= 0 && sfail < 0) sfail = 16 * (b - 1) + f;
         } else {
-            for (int idx = t - 64; idx < ntile; idx += 192) {
+            for (int idx = t - 64; idx < ntile; idx += kDiagThreads - 64) {
                 int br = (int)((sqrtf(8.f * idx + 1.f) - 1.f) * 0.5f);
                 while ((br + 1) * (br + 2) / 2 <= idx) ++br;
                 while (br * (br + 1) / 2 > idx) --br;
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
     // inverse: the 16-blocks (inv16, one wave each), then merged pairs of
     // 2 x 16 blocks (one wave each), 2 x 32 (MFMA, one wave each), 2 x 64
     // (MFMA, four waves); T goes to the upper block of each pair
-    for (int k = wave; k < nb / 16; k += 4) inv16(sA + 16 * k * (kDP + 1), sX + 16 * k * (kDP + 1));
+    for (int k = wave; k < nb / 16; k += kDiagThreads / 64) inv16(sA + 16 * k * (kDP + 1), sX + 16 * k * (kDP + 1));
     __syncthreads();
     if (wave < nb / 32) inv_merge16(sA, sX, 32 * wave);
     __syncthreads();
@@ -493,16 +503,20 @@ __global__ __launch_bounds__(256) void k_f_diag(float* __restrict__ Lbuf, float*
         lds_put32(sX + d * kDP + d + 32, z, 1.f);   // clear T: X's upper part must be zero for the next level
     }
     __syncthreads();
-    if (nb == 128) {
-        const f32x16 acc = lds_mm64<RowK, KRow>(sA + 64 * kDP, sX);                  // T = L21 X11
-        lds_put64(sX + 64, acc, 1.f);
+    if (nb == 128) {   // on the first four waves
+        if (wave < 4) {
+            const f32x16 acc = lds_mm64<RowK, KRow>(sA + 64 * kDP, sX);                  // T = L21 X11
+            lds_put64(sX + 64, acc, 1.f);
+        }
         __syncthreads();
-        const f32x16 acc2 = lds_mm64<RowK, KRow>(sX + 64 * (kDP + 1), sX + 64);       // X21 = -X22 T
-        lds_put64(sX + 64 * kDP, acc2, -1.f);
+        if (wave < 4) {
+            const f32x16 acc2 = lds_mm64<RowK, KRow>(sX + 64 * (kDP + 1), sX + 64);       // X21 = -X22 T
+            lds_put64(sX + 64 * kDP, acc2, -1.f);
+        }
         __syncthreads();
     }
 
-    for (int f = t; f < nb * nf4; f += 256) {
+    for (int f = t; f < nb * nf4; f += kDiagThreads) {
         const int r = f / nf4, c = 4 * (f % nf4);
         f32x4 l = *reinterpret_cast<const f32x4*>(sA + r * kDP + c);
         f32x4 x = *reinterpret_cast<const f32x4*>(sX + r * kDP + c);
@@ -962,7 +976,7 @@ int factor_rec(const FactorRun& R, int64_t o, int64_t nsz, int depth, Pending* u
         // factor (b^3 / 3 multiply-adds) and inverse (b^3 / 6) of the block
         const double b = (double)nsz;
         if (emit(R, [=] {
-                launch(R.prof, KK_F_DIAG, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(256), R.s,
+                launch(R.prof, KK_F_DIAG, b * b * b, 4.0 * (tri(b) + 2.0 * b * b), k_f_diag, dim3(1), dim3(kDiagThreads), R.s,
                        R.Lbuf, R.Pbuf, R.ld, o, (int)nsz, R.info);
                 return launch_ok();
             }))
