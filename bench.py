@@ -798,7 +798,63 @@ def stats_digest(directory, bench_log, title, command):
     for k, (calls, ns) in sorted(rows.items(), key=lambda kv: -kv[1][1]):
         b = bench_us.get(k, "")
         lines.append(f"| {k} | {calls} | {ns / 1e6:.3f} | {ns / 1e3 / calls:.2f} | {b} |")
+    lines += leaf_width_table(directory)
     return "\n".join(lines)
+
+
+def leaf_width_table(directory):
+    """Leaf launches of a kernel trace grouped by their workgroups (tiles on
+    the anti-diagonal): a leaf's in-tile sweep is the same at every width, so
+    a difference between the groups is what the rest of the GPU does to it.
+    Each group is split by whether, at the launch's midpoint, the workgroups
+    of the other running kernels (at most 256 counted per kernel) plus the
+    leaf's own exceed the 256 CUs, i.e. whether some of its tiles had to
+    share a CU."""
+    import bisect
+    import csv
+    import glob
+    files = glob.glob(os.path.join(directory, "**", "*kernel_trace.csv"), recursive=True)
+    leaves, edges = [], []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                wg = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+                t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+                if _kernel_key(r["Kernel_Name"]) == "k_leaf":
+                    leaves.append((t0, t1, wg))
+                else:
+                    edges += [(t0, min(wg, 256)), (t1, -min(wg, 256))]
+    if not leaves:
+        return []
+    edges.sort()
+    times = [t for t, _ in edges]
+    running, acc = [], 0
+    for _, d in edges:
+        acc += d
+        running.append(acc)
+    groups = {}
+    for t0, t1, wg in leaves:
+        i = bisect.bisect_right(times, (t0 + t1) // 2) - 1
+        others = running[i] if i >= 0 else 0
+        hi = 1 << max(0, (wg - 1).bit_length())   # groups (hi/2, hi]
+        g = groups.setdefault(hi, [0, 0, 0, 0])
+        k = 2 if others + wg > 256 else 0
+        g[k] += 1
+        g[k + 1] += t1 - t0
+    out = ["", "`k_leaf` launches by tiles per launch (from the kernel trace), and split by whether the other "
+           "kernels' workgroups running at the launch's midpoint left a CU for each of its tiles:", "",
+           "| tiles | calls | avg us | calls with a CU per tile | avg us | calls short of CUs | avg us |",
+           "|---|---|---|---|---|---|---|"]
+
+    def avg(ns, c):
+        return f"{ns / 1e3 / c:.2f}" if c else ""
+
+    for hi in sorted(groups):
+        c0, n0, c1, n1 = groups[hi]
+        lo = hi // 2 + 1
+        label = f"{hi}" if lo >= hi else f"{lo}-{hi}"
+        out.append(f"| {label} | {c0 + c1} | {avg(n0 + n1, c0 + c1)} | {c0} | {avg(n0, c0)} | {c1} | {avg(n1, c1)} |")
+    return out
 
 
 def traffic_digest(dirs, workload, command):
