@@ -444,14 +444,22 @@ __global__ __launch_bounds__(kDiagThreads) void k_f_diag(float* __restrict__ Lbu
             float p[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) p[r] = Pr[r * kDP + t];
+            // L_bb's lower triangle (the same for every lane) and the
+            // reciprocals of its diagonal, all read before the substitution,
+            // whose dependent chain is then one multiply and one fma a row
+            f32x4 lr[16][4];
+            float rd[16];
+#pragma unroll
+            for (int tt = 15; tt >= 0; --tt)
+#pragma unroll
+                for (int v = 0; v <= tt / 4; ++v) lr[tt][v] = *reinterpret_cast<const f32x4*>(Lbb + tt * kDP + 4 * v);
+#pragma unroll
+            for (int tt = 15; tt >= 0; --tt) rd[tt] = __builtin_amdgcn_rcpf(lr[tt][tt / 4][tt % 4]);
 #pragma unroll
             for (int tt = 15; tt >= 0; --tt) {
-                f32x4 lr[4];   // row tt of L_bb, the same for every lane
+                p[tt] *= rd[tt];
 #pragma unroll
-                for (int v = 0; v <= tt / 4; ++v) lr[v] = *reinterpret_cast<const f32x4*>(Lbb + tt * kDP + 4 * v);
-                p[tt] *= __builtin_amdgcn_rcpf(lr[tt / 4][tt % 4]);
-#pragma unroll
-                for (int r = 0; r < tt; ++r) p[r] = fmaf(-lr[r / 4][r % 4], p[tt], p[r]);
+                for (int r = 0; r < tt; ++r) p[r] = fmaf(-lr[tt][r / 4][r % 4], p[tt], p[r]);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) Pr[r * kDP + t] = p[r];
