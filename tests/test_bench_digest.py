@@ -1,7 +1,9 @@
 """Host logic of bench.py's profiler digests, on the CPU: the short kernel
 names, the kernel-trace summary and its leaf table (launches grouped by
-width and split by whether the other kernels left a CU per tile), checked on
-small synthetic files in rocprofv3's CSV layout with hand-worked answers."""
+width and split by whether the other kernels left a CU per tile), the HBM
+traffic scaled by the copy calibration (and the bench's use of it only for
+matching kernel sources), and the derived counter ratios; checked on small
+synthetic files in rocprofv3's CSV layout with hand-worked answers."""
 import csv
 import json
 
@@ -101,3 +103,54 @@ def test_stats_digest_sums_and_orders_kernels(tmp_path):
     assert [r[0] for r in t] == ["k_leaf", "k_prop_cols_t"]     # by total time
     assert t[0] == ["k_leaf", "4", "0.160", "40.00", "39.5"]
     assert t[1] == ["k_prop_cols_t", "10", "0.050", "5.00", ""]
+
+
+COUNTER_HEADER = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+
+
+def _counters(path, rows):
+    path.mkdir()
+    _write_csv(path / "run_counter_collection.csv", COUNTER_HEADER,
+               [[str(i), k, c, str(v)] for i, (k, c, v) in enumerate(rows)])
+
+
+def test_traffic_digest_scales_by_the_copy_calibration(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "sources_digest", lambda: "sha-A")
+    (tmp_path / "profiles").mkdir()
+    copy = "void at::native::copy_kernel(int)"
+    # a 1 GiB copy that FETCH_SIZE reports as 512 MiB (factor 2) and WRITE_SIZE as 1 GiB (factor 1)
+    _counters(tmp_path / "cf", [(copy, "FETCH_SIZE", 524288.0)])
+    _counters(tmp_path / "cw", [(copy, "WRITE_SIZE", 1048576.0)])
+    _counters(tmp_path / "f", [(LEAF, "FETCH_SIZE", 3000.0), (LEAF, "FETCH_SIZE", 3400.0)])
+    _counters(tmp_path / "w", [(LEAF, "WRITE_SIZE", 2300.0)])
+    bench.traffic_digest([str(tmp_path / d) for d in ("f", "w", "cf", "cw")], "tiny", "cmd")
+    t = json.loads((tmp_path / "profiles" / "traffic_tiny.json").read_text())
+    assert t["sources_sha256"] == "sha-A"
+    assert t["calibration"]["FETCH_SIZE"]["factor"] == 2.0 and t["calibration"]["WRITE_SIZE"]["factor"] == 1.0
+    leaf = t["kernels"]["k_leaf"]
+    assert leaf["dispatches"] == 2
+    assert leaf["hbm_bytes_per_launch"] == 1024 * (3200 * 2 + 2300)   # KiB means, scaled, in bytes
+    # the bench uses the numbers only while the kernel sources are the ones they were taken on
+    assert bench.load_traffic("tiny")["kernels"]["k_leaf"]["hbm_bytes_per_launch"] == 8908800
+    monkeypatch.setattr(bench, "sources_digest", lambda: "sha-B")
+    assert bench.load_traffic("tiny") is None
+    assert bench.load_traffic("absent") is None
+
+
+def test_pmc_digest_derived_ratios(tmp_path):
+    k = "void bk::k_prop_rows(float const*)"
+    _counters(tmp_path / "a", [(k, "SQ_INSTS_VALU", 100.0), (k, "SQ_INSTS_VALU", 300.0),
+                               (k, "SQ_WAVES", 4.0), (k, "SQ_WAVES", 4.0)])
+    _counters(tmp_path / "b", [(k, "SQ_VALU_MFMA_BUSY_CYCLES", 512000.0), (k, "GRBM_GUI_ACTIVE", 8000.0),
+                               (k, "TCC_HIT_sum", 30.0), (k, "TCC_MISS_sum", 10.0)])
+    lines = bench.pmc_digest([str(tmp_path / "a"), str(tmp_path / "b")], "T", "").split("\n")
+    mean = _table(lines, "kernel")[0]
+    assert mean[:2] == ["k_prop_rows", "2"]
+    derived = _table(lines[lines.index("Derived (only where the counters were collected):"):], "kernel")[0]
+    names = [d[0] for d in bench.PMC_DERIVED]
+    got = dict(zip(names, derived[1:]))
+    assert got["valu/wave"] == "50"            # mean 200 VALU over mean 4 waves
+    assert got["mfma_busy"] == "0.5"           # 512,000 busy cycles over 1,000 active cycles x 1024 SIMDs
+    assert got["l2_hit"] == "0.75"
+    assert got["lds/wave"] == ""               # counters not collected
