@@ -543,9 +543,9 @@ MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", 
                 "k_prop_cols_far", "k_prop_cols_t_far", "k_f_panel", "k_f_right",
                 "k_f_left", "k_f_tile<0>", "k_f_tile<1>", "k_f_tile<2>", "k_f_tile<3>", "k_f_tile<4>", "k_f_update",
                 "k_gptq_update",
-                "k_gptq_update_t", "k_moment<false>", "k_moment<true>"}
+                "k_gptq_update_t", "k_moment<false>", "k_moment<true>", "k_ad_update"}
 HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info", "k_gptq_load",
-               "k_row_sqnorms"}
+               "k_row_sqnorms", "k_ad_prep", "k_ad_quant"}
 # fp32 vector peak of the instructions this build issues: 256 CUs x 4 SIMDs
 # x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s.  MI355X's published
 # 157.3 TFLOP/s fp32 vector figure counts packed fp32 (two FMAs per lane per

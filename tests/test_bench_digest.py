@@ -154,3 +154,44 @@ def test_pmc_digest_derived_ratios(tmp_path):
     assert got["mfma_busy"] == "0.5"           # 512,000 busy cycles over 1,000 active cycles x 1024 SIMDs
     assert got["l2_hit"] == "0.75"
     assert got["lds/wave"] == ""               # counters not collected
+
+
+def test_roofline_entry_by_bound():
+    traffic = {"kernels": {"k_prop_rows": {"hbm_bytes_per_launch": 123}}}
+    # MFMA: 2e11 flops in 2 ms = 100 TFLOP/s against the fp32 matrix peak
+    r = bench.roofline_entry("k_prop_rows", {"launches": 4, "total_ms": 2.0, "alg_flops": 2e11, "alg_bytes": 1e9},
+                             traffic)
+    assert (r["bound"], r["unit"], r["peak"]) == ("mfma", "TFLOP/s", bench.PEAK_FP32_MFMA_TFLOPS)
+    assert r["achieved"] == 100.0 and r["frac"] == round(100.0 / 157.3, 4)
+    assert r["avg_launch_us"] == 500.0 and r["traffic"] == 123
+    assert r["alg_flops_per_launch"] == 5e10
+    # the leaf: fp32 vector peak of the non-packed instructions, with the packed figure in a note
+    r = bench.roofline_entry("k_leaf", {"launches": 2, "total_ms": 1.0, "alg_flops": 7.86e10, "alg_bytes": 0.0}, None)
+    assert (r["bound"], r["peak"], r["traffic"]) == ("alu", 78.6, None)
+    assert r["achieved"] == 78.6 and r["frac"] == 1.0 and "157.3" in r["peak_note"]
+    # HBM: bytes over time in GB/s against 8 TB/s
+    r = bench.roofline_entry("k_copy_pad", {"launches": 1, "total_ms": 1.0, "alg_flops": 0.0, "alg_bytes": 4e9}, None)
+    assert (r["bound"], r["unit"], r["achieved"], r["frac"]) == ("hbm", "GB/s", 4000.0, 0.5)
+
+
+def test_kernel_bounds_cover_the_library_kernels():
+    # every MFMA kernel of the recursion and propagation is priced against the matrix peak
+    for k in ("k_prop_rows", "k_prop_cols_t_far", "k_f_tile<4>", "k_f_update", "k_ad_update", "k_moment<true>"):
+        assert bench.kernel_bound(k) == "mfma", k
+    for k in ("k_load_damped", "k_f_finish", "k_ad_quant"):
+        assert bench.kernel_bound(k) == "hbm", k
+    for k in ("k_leaf", "k_f_diag", "k_gptq_sweep"):
+        assert bench.kernel_bound(k) == "alu", k
+
+
+def test_stage_fractions():
+    m, n = 64, 128
+    agg = {"k_prop_rows": {"total_ms": 1.0, "alg_flops": 3e9}, "k_prop_rows_far": {"total_ms": 1.0, "alg_flops": 1e9},
+           "k_prop_cols_t": {"total_ms": 0.5, "alg_flops": 1e9}, "k_leaf": {"total_ms": 9.0, "alg_flops": 1e9}}
+    st = bench.stage_fractions(agg, m, n)
+    s1, s2 = st["stage1"], st["stage2"]
+    assert s1["kernels_ms"] == 2.0 and s1["alg_flops"] == m * n * (n + 1)   # E P_A^T, triangular
+    assert s1["alg_tflops"] == round(m * n * (n + 1) / 2e-3 / 1e12, 3)
+    assert s1["executed_tflops"] == 2.0                                     # 4e9 flops in 2 ms
+    assert s2["kernels_ms"] == 0.5 and s2["alg_flops"] == m * (m + 1) * n   # P_B Y
+    assert bench.stage_fractions({"k_leaf": {"total_ms": 1.0, "alg_flops": 1.0}}, m, n) == {}
