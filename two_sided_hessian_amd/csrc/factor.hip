@@ -210,8 +210,8 @@ __device__ __forceinline__ int chol16(float* __restrict__ S, const float* __rest
             s[u] = fmaf(-m2, r1p, fmaf(-m1, rk[u], s[u]));
         }
     };
-#pragma unroll 1
-    for (int g = 3; g >= 0; --g) {
+#pragma unroll
+    for (int g = 3; g >= 0; --g) {   // unrolled: lane indices and exchange addresses are constants
         chol2(4 * g + 3, 3, 2);
         chol2(4 * g + 1, 1, 0);
     }
@@ -260,7 +260,7 @@ __device__ __forceinline__ void inv16(const float* __restrict__ S, float* __rest
             r[u] = fmaf(-c2, r1p, fmaf(-c1, rk[u], r[u]));
         }
     };
-#pragma unroll 1
+#pragma unroll
     for (int g = 0; g < 4; ++g) {
         inv2(4 * g, 0, 1);
         inv2(4 * g + 2, 2, 3);
