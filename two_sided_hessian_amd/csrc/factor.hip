@@ -428,7 +428,7 @@ __global__ __launch_bounds__(kDiagThreads) void k_f_diag(float* __restrict__ Lbu
     // factor, 16 rows at a time from the bottom, with a one-block lookahead:
     // once the panel of block b is formed, wave 0 factors diagonal block
     // b - 1 (chol16, which applies that block's share of the update itself)
-    // while waves 1 - 3 apply the rest of block b's update to the remaining
+    // while waves 1 - 7 apply the rest of block b's update to the remaining
     // upper-left part.
     if (wave == 0) {
         const int b = nb / 16 - 1;
