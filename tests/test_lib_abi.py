@@ -84,6 +84,21 @@ def test_host_only_calls(B):
     assert B.gptq_workspace_bytes(100, 70) >= 2 * 128 * 128 * 4 + 128 * 128 * 4
 
 
+def test_workspace_sizes_at_the_largest_dimension(B):
+    # BAKRON_MAX_DIM = 65536: the sizes are computed in 64-bit (a 65536^2 float32 matrix alone is 16 GiB),
+    # grow with the problem and cover their lower bounds; one more row or column is refused (0)
+    M = 65536
+    f32 = 4 * M * M
+    assert B.solve_workspace_bytes(M, M) >= 3 * f32
+    assert B.solve_workspace_bytes(M, M) > B.solve_workspace_bytes(M - 64, M - 64) > 0
+    assert B.factor_workspace_bytes(M) >= 4 * sum((M // 2 >> d) ** 2 for d in range(9))
+    assert B.factor_workspace_bytes(M) > B.factor_workspace_bytes(M - 64) > 0
+    assert B.quantize_workspace_bytes(M, M) >= (2 * B.factor_workspace_bytes(M) + B.solve_workspace_bytes(M, M))
+    assert B.gptq_workspace_bytes(M, M) >= 2 * f32
+    assert B.solve_workspace_bytes(M + 1, 64) == 0 and B.factor_workspace_bytes(M + 1) == 0
+    assert B.gptq_workspace_bytes(64, M + 1) == 0 and B.quantize_workspace_bytes(M + 1, 64) == 0
+
+
 def test_host_side_argument_errors(B):
     L = B.lib()
     fake = ctypes.c_void_p(4096)       # never dereferenced: every call below fails its host checks
