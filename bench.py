@@ -546,7 +546,7 @@ MFMA_KERNELS = {"k_prop_rows", "k_prop_rows_t", "k_prop_cols", "k_prop_cols_t", 
                 "k_gptq_update_t", "k_moment<false>", "k_moment<true>", "k_ad_update"}
 HBM_KERNELS = {"k_copy_pad", "k_load_damped", "k_f_finish", "k_diag_mean", "k_clear_info", "k_gptq_load",
                "k_row_sqnorms", "k_ad_prep", "k_ad_quant"}
-# fp32 vector peak of the instructions this build issues: 256 CUs x 4 SIMDs
+# fp32 vector peak of the instructions the library's kernels issue: 256 CUs x 4 SIMDs
 # x 16 lanes x 2 flops (FMA) x 2.4 GHz = 78.6 TFLOP/s.  MI355X's published
 # 157.3 TFLOP/s fp32 vector figure counts packed fp32 (two FMAs per lane per
 # instruction), which the library is compiled without.
@@ -736,7 +736,7 @@ def pmc_digest(dirs, title, command):
     counters = sorted({c for cs in per.values() for c in cs})
     lines = [f"# {title}" if title else "# rocprofv3 counters", ""]
     if command:
-        lines += ["Commands (from the repository root on the GPU box):", "", "```", command, "```", ""]
+        lines += ["Commands (from the repository root, on a machine with the GPU):", "", "```", command, "```", ""]
     lines += ["Mean per dispatch of each counter (a counter is summed over the whole GPU for a dispatch).", ""]
     lines.append("| kernel | dispatches | " + " | ".join(counters) + " |")
     lines.append("|---|---|" + "---|" * len(counters))
@@ -791,7 +791,7 @@ def stats_digest(directory, bench_log, title, command):
                     step = line.strip()
     lines = [f"# {title}" if title else "# Kernel time", ""]
     if command:
-        lines += ["Command (from the repository root on the GPU box):", "", "```", command, "```", ""]
+        lines += ["Command (from the repository root, on a machine with the GPU):", "", "```", command, "```", ""]
     if step:
         lines += ["Bench line of the same run: `" + step + "`", ""]
     lines += ["| kernel | calls | total ms | avg us (rocprof) | avg us (bench, HIP events) |", "|---|---|---|---|---|"]

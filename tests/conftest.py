@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run on a GPU machine only; elsewhere they are skipped, not failed.
+    # GPU tests run only where a GPU is visible; elsewhere they are skipped, not failed.
     try:
         import torch
         have_gpu = torch.cuda.is_available()
